@@ -1,0 +1,88 @@
+/*
+ * oracle.h -- plain f64 CPU oracle for the group-quantised expert FFN and the
+ * bf16 dense matvec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library exists to check the GPU library
+ * against.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline load it; the product path never does.  It shares no source with the
+ * GPU library: it has its own unpacker, its own dequantiser and its own loops.
+ *
+ * Everything is computed from the definitions, slowly and in f64:
+ *   - each weight is dequantised explicitly, w = (code - Z) / Z * s
+ *     (Metal Compute Kernels, S-MoE docs, section "Fused FFN Kernels -- One
+ *     Simdgroup Per Output Row": affine codes with Z = 7.5 at 4 bits and 1.5
+ *     at 2 bits, one scale per column group);
+ *   - each row dot product runs over the columns in ascending order with one
+ *     f64 accumulator;
+ *   - SiLU(t) = t / (1 + exp(-t)).
+ *
+ * Packed format (the pages leave the bit order open; this is the reading
+ * adopted everywhere in this repository): a row of `cols` codes occupies
+ * cols*bits/8 bytes; at 4 bits byte k holds code 2k in its low nibble and code
+ * 2k+1 in its high nibble; at 2 bits byte k holds codes 4k..4k+3 starting at
+ * the least significant bit pair.  Scales are f32, row-major [rows][cols/group],
+ * scale g covering columns g*group .. g*group+group-1 of its row.
+ *
+ * Return value of every int function: 0 on success, -1 on an argument the
+ * definitions do not cover (bits not 2 or 4, a group that does not divide the
+ * row, a non-positive size, a NULL pointer).
+ */
+#ifndef SMOE_ORACLE_H
+#define SMOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    const uint8_t *codes;   /* [rows][cols*bits/8] */
+    const float *scales;    /* [rows][cols/group]  */
+} oracle_qmat;
+
+typedef struct {
+    oracle_qmat gate;       /* [d_ff][d_model] */
+    oracle_qmat up;         /* [d_ff][d_model] */
+    oracle_qmat down;       /* [d_model][d_ff] */
+} oracle_expert;
+
+/* Number of OpenMP threads the oracle's row loops use (1 without OpenMP). */
+int oracle_threads(void);
+
+/* One code per output byte: out[r*cols + j] = code of row r, column j. */
+int oracle_unpack(const uint8_t *codes, int bits, long rows, long cols, uint8_t *out);
+
+/* Explicit dequantisation: w[r*cols + j] = (code - Z) / Z * scale[r][j/group]. */
+int oracle_dequant(const uint8_t *codes, const float *scales, int bits, int group,
+                   long rows, long cols, double *w);
+
+/* y[r] = sum_j w(r, j) * x[j], j ascending, f64 accumulator. */
+int oracle_qmatvec(const uint8_t *codes, const float *scales, int bits, int group,
+                   long rows, long cols, const double *x, double *y);
+
+double oracle_silu(double t);
+
+/* hidden[i] = SiLU(g_i) * u_i with g = G x, u = U x (one expert). */
+int oracle_gate_up(const oracle_qmat *gate, const oracle_qmat *up, int bits, int group,
+                   long d_ff, long d_model, const float *x, double *hidden);
+
+/* out[j] = (D hidden)[j] (one expert). */
+int oracle_down(const oracle_qmat *down, int bits, int group, long d_model, long d_ff,
+                const double *hidden, double *out);
+
+/* Token t, for t in [0, T):
+ *   out[t][:] = sum_e route_w[t][e] * down_e( SiLU(gate_e x[t]) * (up_e x[t]) ),
+ * experts in ascending order; route_w == NULL means every weight is 1. */
+int oracle_expert_ffn(const oracle_expert *experts, int n_experts, const float *route_w,
+                      int bits, int group, long d_model, long d_ff, long T,
+                      const float *x, double *out);
+
+/* y[r] = sum_j bf16_to_f32(W[r][j]) * x[j], j ascending, f64 accumulator.
+ * W holds raw bf16 bit patterns. */
+int oracle_matvec_bf16(const uint16_t *W, long rows, long cols, const float *x, double *y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

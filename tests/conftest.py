@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; parity against the oracle")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    """The f64 CPU oracle, compiled from source if no build is present."""
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    oracle.lib()
+    return oracle

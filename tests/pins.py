@@ -1,0 +1,311 @@
+"""Pins for the f64 oracle that do not depend on the oracle itself.
+
+Each check compares what a given build of ``oracle.c`` returns with something
+fixed outside it: hand-worked closed forms (``golden/``), exact rational
+arithmetic through the page's per-group affine identity, an independent
+bit-level unpacker, IEEE bf16 bit patterns, and mathematical identities of
+SiLU.  The checks take a ``ctypes.CDLL`` so that the same pins can be run on
+deliberately broken copies of the oracle (see ``test_oracle_mutants.py``).
+
+Sources: Metal Compute Kernels (S-MoE docs), sections "Fused FFN Kernels --
+One Simdgroup Per Output Row" (affine codes, Z, group scales, SiLU(gate)*up,
+down projection), "Layout assumptions the kernels rely on" (group and chunk
+contract) and "Coalesced Dense Matvec -- the Same Contract for bf16".
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+vp, cl, ci = ctypes.c_void_p, ctypes.c_long, ctypes.c_int
+
+
+def bind(L):
+    L.oracle_unpack.argtypes = [vp, ci, cl, cl, vp]
+    L.oracle_qmatvec.argtypes = [vp, vp, ci, ci, cl, cl, vp, vp]
+    L.oracle_silu.argtypes = [ctypes.c_double]
+    L.oracle_silu.restype = ctypes.c_double
+    L.oracle_gate_up.argtypes = [vp, vp, ci, ci, cl, cl, vp, vp]
+    L.oracle_down.argtypes = [vp, ci, ci, cl, cl, vp, vp]
+    L.oracle_expert_ffn.argtypes = [vp, ci, vp, ci, ci, cl, cl, cl, vp, vp]
+    L.oracle_matvec_bf16.argtypes = [vp, cl, cl, vp, vp]
+    return L
+
+
+def _p(a):
+    return a.ctypes.data_as(vp)
+
+
+class _QMat(ctypes.Structure):
+    _fields_ = [("codes", vp), ("scales", vp)]
+
+
+class _Expert(ctypes.Structure):
+    _fields_ = [("gate", _QMat), ("up", _QMat), ("down", _QMat)]
+
+
+def qmatvec(L, codes, scales, bits, group, x):
+    rows = codes.shape[0]
+    cols = codes.shape[1] * 8 // bits
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    x = np.ascontiguousarray(x, np.float64)
+    y = np.empty(rows, np.float64)
+    rc = L.oracle_qmatvec(_p(codes), _p(scales), bits, group, rows, cols, _p(x), _p(y))
+    assert rc == 0
+    return y
+
+
+def unpack(L, codes, bits):
+    rows = codes.shape[0]
+    cols = codes.shape[1] * 8 // bits
+    codes = np.ascontiguousarray(codes, np.uint8)
+    out = np.empty((rows, cols), np.uint8)
+    assert L.oracle_unpack(_p(codes), bits, rows, cols, _p(out)) == 0
+    return out
+
+
+def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Independent packer for test inputs: lay each code's bits out LSB first
+    and let numpy pack the bit stream little-endian within each byte."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, cols = codes.shape
+    bitplanes = ((codes[..., None] >> np.arange(bits, dtype=np.uint8)) & 1).astype(np.uint8)
+    return np.packbits(bitplanes.reshape(rows, cols * bits), axis=1, bitorder="little")
+
+
+def unpack_bits(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Independent unpacker: explode bytes to bits (LSB first), regroup."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    stream = np.unpackbits(packed, axis=1, bitorder="little").reshape(rows, -1, bits)
+    weights = (1 << np.arange(bits)).astype(np.uint8)
+    return (stream * weights).sum(axis=2).astype(np.uint8)
+
+
+def affine_exact(codes: np.ndarray, scales, bits: int, group: int, x) -> list:
+    """Row dot products in exact rationals through the page's per-group
+    identity: sum_j w_j x_j = sum_g s_g * ((sum_{j in g} code_j x_j) / Z - sum_{j in g} x_j)."""
+    Z = Fraction(15, 2) if bits == 4 else Fraction(3, 2)
+    xs = [Fraction(float(v)) for v in x]
+    out = []
+    for r in range(codes.shape[0]):
+        total = Fraction(0)
+        for g in range(codes.shape[1] // group):
+            cols = range(g * group, (g + 1) * group)
+            cx = sum(int(codes[r, j]) * xs[j] for j in cols)
+            sx = sum(xs[j] for j in cols)
+            total += Fraction(float(scales[r][g])) * (cx / Z - sx)
+        out.append(total)
+    return out
+
+
+def load_worked_examples():
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+def load_bf16_patterns():
+    with open(os.path.join(GOLDEN, "bf16_patterns.json")) as f:
+        return json.load(f)["patterns"]
+
+
+# --------------------------------------------------------------------------
+# Core pins, each returning a list of failure strings (empty = pass).
+# --------------------------------------------------------------------------
+
+def pin_worked_examples(L):
+    fails = []
+    for ex in load_worked_examples():
+        bits = ex["bits"]
+        packed = np.array([list(bytes.fromhex(h)) for h in ex["packed_hex"]], np.uint8)
+        codes = np.array(ex["codes"], np.uint8)
+        if not np.array_equal(unpack(L, packed, bits), codes):
+            fails.append(f"{ex['name']}: unpacked codes differ from the hand-packed bytes")
+        y = qmatvec(L, packed, np.array(ex["scales"], np.float32), bits, ex["group"],
+                    np.array(ex["x"], np.float64))
+        for r, e in enumerate(ex["expected"]):
+            want = float(Fraction(e))
+            if abs(y[r] - want) > 8 * np.finfo(np.float64).eps * max(1.0, abs(want)):
+                fails.append(f"{ex['name']} row {r}: {y[r]!r} != {e}")
+    return fails
+
+
+def pin_unpack_exhaustive(L):
+    """Every code value at every in-byte position, against the bit-level unpacker."""
+    fails = []
+    for bits in (4, 2):
+        per = 8 // bits
+        allbytes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+        got = unpack(L, allbytes, bits)
+        want = unpack_bits(allbytes, bits)
+        if not np.array_equal(got, want):
+            fails.append(f"Q{bits}: unpack disagrees with bit-level unpack")
+        # each code value alone at each position, others zero
+        for pos in range(per):
+            for v in range(1 << bits):
+                codes = np.zeros((1, 2 * per), np.uint8)
+                codes[0, per + pos] = v
+                if not np.array_equal(unpack(L, pack_bits(codes, bits), bits), codes):
+                    fails.append(f"Q{bits}: value {v} at position {pos} not recovered")
+    return fails
+
+
+def pin_affine_identity(L, seed=7):
+    """Random tiny matrices with dyadic scales and dyadic x: the oracle's f64
+    explicit-dequant sum must equal the exact rational affine-epilogue value
+    to within the f64 rounding of its own sum."""
+    rng = np.random.default_rng(seed)
+    fails = []
+    for bits, rows, cols, group in ((4, 3, 128, 64), (4, 4, 256, 64), (2, 3, 128, 64),
+                                    (2, 2, 256, 128), (4, 2, 96, 32)):
+        codes = rng.integers(0, 1 << bits, size=(rows, cols), dtype=np.uint8)
+        scales = (rng.integers(1, 64, size=(rows, cols // group)) / 1024.0).astype(np.float32)
+        x = rng.integers(-512, 512, size=cols) / 128.0
+        y = qmatvec(L, pack_bits(codes, bits), scales, bits, group, x)
+        exact = affine_exact(codes, scales, bits, group, x)
+        Z = 7.5 if bits == 4 else 1.5
+        for r in range(rows):
+            mag = sum(abs((int(c) - Z) / Z * float(scales[r][j // group]) * x[j])
+                      for j, c in enumerate(codes[r]))
+            bound = 4 * cols * np.finfo(np.float64).eps * max(mag, 1e-300)
+            if abs(y[r] - float(exact[r])) > bound:
+                fails.append(f"Q{bits} {rows}x{cols} g{group} row {r}: "
+                             f"{y[r]!r} vs exact {float(exact[r])!r}")
+    return fails
+
+
+def pin_silu(L):
+    """SiLU(t) = t * sigmoid(t): SiLU(ln 3) = (3/4) ln 3 and SiLU(-ln 3) = -(1/4) ln 3
+    because sigmoid(ln 3) = 3/4; SiLU(0) = 0; SiLU(t) - SiLU(-t) = t; SiLU(t) -> t for
+    large t and -> 0 for very negative t."""
+    fails = []
+    s = L.oracle_silu
+    ln3 = math.log(3.0)
+    checks = [(s(ln3), 0.75 * ln3), (s(-ln3), -0.25 * ln3), (s(0.0), 0.0),
+              (s(40.0), 40.0), (s(-800.0), 0.0)]
+    for got, want in checks:
+        if abs(got - want) > 4e-16 * max(1.0, abs(want)):
+            fails.append(f"silu: {got!r} != {want!r}")
+    for t in (0.1, 0.5, 1.0, 2.5, 7.0):
+        if abs((s(t) - s(-t)) - t) > 4e-16 * max(1.0, t):
+            fails.append(f"silu({t}) - silu(-{t}) != {t}")
+    return fails
+
+
+def pin_bf16(L):
+    """IEEE bf16 patterns widen exactly; small-integer rows sum exactly."""
+    fails = []
+    pats = load_bf16_patterns()
+    W = np.array([[int(p["bits"], 16)] for p in pats], np.uint16)
+    x = np.ones(1, np.float32)
+    y = np.empty(len(pats), np.float64)
+    assert L.oracle_matvec_bf16(_p(W), len(pats), 1, _p(x), _p(y)) == 0
+    for p, v in zip(pats, y):
+        if v != float(p["value"]):
+            fails.append(f"bf16 {p['bits']}: {v!r} != {p['value']}")
+    # integers -8..8 are exact in bf16 (bits = f32 bits >> 16); with integer x the
+    # dot product is an exact integer
+    rng = np.random.default_rng(3)
+    ints = rng.integers(-8, 9, size=(5, 64)).astype(np.float32)
+    Wi = (ints.view(np.uint32) >> 16).astype(np.uint16)
+    xi = rng.integers(-100, 101, size=64).astype(np.float32)
+    yi = np.empty(5, np.float64)
+    assert L.oracle_matvec_bf16(_p(Wi), 5, 64, _p(xi), _p(yi)) == 0
+    want = ints.astype(np.int64) @ xi.astype(np.int64)
+    if not np.array_equal(yi, want.astype(np.float64)):
+        fails.append("bf16 integer matvec not exact")
+    return fails
+
+
+def make_expert(rng, d_model, d_ff, bits, group):
+    def m(rows, cols):
+        codes = rng.integers(0, 1 << bits, size=(rows, cols), dtype=np.uint8)
+        scales = rng.uniform(0.01, 0.05, size=(rows, cols // group)).astype(np.float32)
+        return pack_bits(codes, bits), scales
+    return dict(gate=m(d_ff, d_model), up=m(d_ff, d_model), down=m(d_model, d_ff))
+
+
+def expert_struct(experts):
+    arr = (_Expert * len(experts))()
+    for k, e in enumerate(experts):
+        arr[k] = _Expert(*[_QMat(_p(e[n][0]), _p(e[n][1])) for n in ("gate", "up", "down")])
+    return arr
+
+
+def ffn(L, experts, bits, group, d_model, d_ff, X, R=None):
+    X = np.ascontiguousarray(X, np.float32).reshape(-1, d_model)
+    T = X.shape[0]
+    out = np.empty((T, d_model), np.float64)
+    pr = None
+    if R is not None:
+        R = np.ascontiguousarray(R, np.float32).reshape(T, len(experts))
+        pr = _p(R)
+    arr = expert_struct(experts)
+    assert L.oracle_expert_ffn(arr, len(experts), pr, bits, group, d_model, d_ff, T,
+                               _p(X), _p(out)) == 0
+    return out
+
+
+def numpy_ffn_one(e, bits, group, x):
+    """Independent route: bit-level unpack, vectorised dequant, BLAS products."""
+    Z = 7.5 if bits == 4 else 1.5
+
+    def W(name):
+        packed, scales = e[name]
+        c = unpack_bits(packed, bits).astype(np.float64)
+        s = np.repeat(scales.astype(np.float64), group, axis=1)
+        return (c - Z) / Z * s
+    x = np.asarray(x, np.float64)
+    g, u = W("gate") @ x, W("up") @ x
+    h = g / (1.0 + np.exp(-g)) * u
+    return W("down") @ h
+
+
+def pin_ffn_composition(L, seed=11):
+    """Multi-expert, multi-token FFN against the BLAS route, the router-weighted
+    combine, and the one-hot / zero-scale special cases."""
+    fails = []
+    rng = np.random.default_rng(seed)
+    for bits in (4, 2):
+        d_model, d_ff, group = 128, 192, 64
+        exps = [make_expert(rng, d_model, d_ff, bits, group) for _ in range(3)]
+        X = rng.standard_normal((2, d_model)).astype(np.float32)
+        R = rng.uniform(0.1, 1.0, size=(2, 3)).astype(np.float32)
+        out = ffn(L, exps, bits, group, d_model, d_ff, X, R)
+        for t in range(2):
+            want = sum(float(R[t, k]) * numpy_ffn_one(exps[k], bits, group, X[t]) for k in range(3))
+            err = np.max(np.abs(out[t] - want)) / max(1.0, np.max(np.abs(want)))
+            if err > 1e-12:
+                fails.append(f"Q{bits} token {t}: FFN vs BLAS route rel err {err:.3g}")
+        onehot = np.zeros((2, 3), np.float32)
+        onehot[:, 0] = 1.0
+        sel = ffn(L, exps, bits, group, d_model, d_ff, X, onehot)
+        solo = ffn(L, exps[:1], bits, group, d_model, d_ff, X, None)
+        if not np.array_equal(sel, solo):
+            fails.append(f"Q{bits}: one-hot router does not select expert 0")
+        # zero up-projection scales: hidden = SiLU(g) * 0 = 0, so the output is 0
+        z = dict(exps[0])
+        z["up"] = (exps[0]["up"][0], np.zeros_like(exps[0]["up"][1]))
+        zero = ffn(L, [z], bits, group, d_model, d_ff, X, None)
+        if np.any(zero != 0.0):
+            fails.append(f"Q{bits}: zero up scales do not give a zero output")
+    return fails
+
+
+CORE_PINS = [pin_worked_examples, pin_unpack_exhaustive, pin_affine_identity, pin_silu,
+             pin_bf16, pin_ffn_composition]
+
+
+def run_core_pins(L):
+    fails = []
+    for pin in CORE_PINS:
+        fails += [f"{pin.__name__}: {m}" for m in pin(L)]
+    return fails

@@ -1,0 +1,41 @@
+"""Mutation evidence: copies of the oracle with one planted mistake each must
+fail at least one pin.  Mistakes are planted in a copy of oracle.c, compiled
+with gcc into a temporary library; nothing touches a GPU."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import pins
+
+ORACLE_C = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "oracle", "oracle.c")
+
+MUTANTS = {
+    "nibble_order": ("(row[j / 2] >> (4 * (j % 2)))", "(row[j / 2] >> (4 * (1 - j % 2)))"),
+    "pair_order": ("(row[j / 4] >> (2 * (j % 4)))", "(row[j / 4] >> (2 * (3 - j % 4)))"),
+    "zero_point": ("return bits == 4 ? 7.5 : 1.5;", "return bits == 4 ? 8.0 : 2.0;"),
+    "weight_sign": ("((double)code_at(row, bits, j) - Z) / Z * s",
+                    "(Z - (double)code_at(row, bits, j)) / Z * s"),
+    "scale_index": ("j / group]", "(j / 64) % (cols / group)]"),
+    "row_stride": ("codes + r * (cols * bits / 8)", "codes + r * (cols / 2)"),
+    "silu_sign": ("t / (1.0 + exp(-t))", "t / (1.0 + exp(t))"),
+    "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "combine_overwrite": ("o[j] += r * y[j]", "o[j] = r * y[j]"),
+    "hidden_product": ("hidden[i] = oracle_silu(g[i]) * u[i]", "hidden[i] = oracle_silu(u[i]) * g[i]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(ORACLE_C).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    (tmp_path / "oracle.h").write_text(open(ORACLE_C.replace(".c", ".h")).read())
+    (tmp_path / "oracle.c").write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-o", str(so),
+                    str(tmp_path / "oracle.c"), "-lm"], check=True)
+    L = pins.bind(ctypes.CDLL(str(so)))
+    assert pins.run_core_pins(L), f"mutant {name} passed every pin"

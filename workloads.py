@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs shared by the oracle, the tests and the benchmark.
+
+This module draws random numbers and shapes them into the arrays the
+expert-FFN and bf16-matvec workloads take.  It holds none of the method's
+arithmetic: no unpacking of codes, no dequantisation, no dot products and no
+activation.  Packed code bytes are drawn directly as independent uniform
+bytes: a uniform byte is, bit for bit, two independent uniform 4-bit codes or
+four independent uniform 2-bit codes, so no packing step is needed here and
+neither side of the comparison has to trust the other's bit order.
+
+Every array comes from its own PCG64 stream keyed by ``SeedSequence([seed,
+*tags])``.  Only the raw 64-bit words of that bit generator are used
+(``random_raw``), and uniform and normal variates are derived from them here
+by a fixed recipe, so the bytes do not depend on numpy's ``Generator``
+sampling methods:
+
+* uniform on [lo, hi): ``lo + (hi - lo) * (u >> 11) * 2**-53`` in f64, then f32;
+* standard normal: Box-Muller on two such uniforms in f64, then f32;
+* bf16 weights: f32 normal times sigma, rounded to bf16 by round-to-nearest-even
+  on the f32 bit pattern.
+
+Workload shapes follow the Metal Compute Kernels page of the S-MoE docs
+(d_model 4096 staged input, 1536-row gate_up grids, the bf16 projection table
+and the LM head), with f32 scales per 64-column group.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Stream tags.  Each (seed, tags) pair names one independent stream.
+_MAT = {"gate": 0, "up": 1, "down": 2}
+_KIND_CODES, _KIND_SCALES = 0, 1
+_TAG_X, _TAG_ROUTER, _TAG_XBATCH, _TAG_BF16_W, _TAG_BF16_X = 100, 101, 102, 200, 201
+
+_CHUNK = 1 << 22  # variates generated per block, to bound temporary memory
+
+
+def _stream(seed: int, tags) -> np.random.PCG64:
+    return np.random.PCG64(np.random.SeedSequence([int(seed)] + [int(t) for t in tags]))
+
+
+def random_bytes(seed: int, tags, nbytes: int) -> np.ndarray:
+    """``nbytes`` independent uniform bytes (uint8)."""
+    n64 = (nbytes + 7) // 8
+    raw = _stream(seed, tags).random_raw(n64).astype("<u8", copy=False)
+    return raw.view(np.uint8)[:nbytes].copy()
+
+
+def _unit_uniform(bg: np.random.PCG64, n: int) -> np.ndarray:
+    """n doubles in [0, 1) with 53 random bits each."""
+    return (bg.random_raw(n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def uniform_f32(seed: int, tags, n: int, lo: float, hi: float) -> np.ndarray:
+    bg = _stream(seed, tags)
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        out[s:s + m] = (lo + (hi - lo) * _unit_uniform(bg, m)).astype(np.float32)
+    return out
+
+
+def normal_f32(seed: int, tags, n: int, sigma: float = 1.0) -> np.ndarray:
+    """n standard-normal variates times ``sigma`` (Box-Muller in f64), as f32."""
+    bg = _stream(seed, tags)
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        half = (m + 1) // 2
+        u1 = 1.0 - _unit_uniform(bg, half)          # (0, 1]: log is finite
+        u2 = _unit_uniform(bg, half)
+        r = np.sqrt(-2.0 * np.log(u1))
+        z = np.empty(2 * half, dtype=np.float64)
+        z[0::2] = r * np.cos(2.0 * np.pi * u2)
+        z[1::2] = r * np.sin(2.0 * np.pi * u2)
+        out[s:s + m] = (z[:m] * sigma).astype(np.float32)
+    return out
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round f32 values to bf16 (round to nearest, ties to even); uint16 bits.
+
+    Inputs here are finite, so no NaN handling is needed.
+    """
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_normal(seed: int, tags, rows: int, cols: int, sigma: float) -> np.ndarray:
+    """bf16 bits [rows, cols] of N(0, sigma^2), generated in row blocks."""
+    out = np.empty((rows, cols), dtype=np.uint16)
+    block = max(1, _CHUNK // cols)
+    for b, r0 in enumerate(range(0, rows, block)):
+        r1 = min(rows, r0 + block)
+        vals = normal_f32(seed, tuple(tags) + (b,), (r1 - r0) * cols, sigma)
+        out[r0:r1] = f32_to_bf16_bits(vals).reshape(r1 - r0, cols)
+    return out
+
+
+def softmax_f32(logits: np.ndarray) -> np.ndarray:
+    """Router weights: softmax over the last axis in f64, returned as f32."""
+    l64 = logits.astype(np.float64)
+    e = np.exp(l64 - l64.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Quantised expert weights
+# ----------------------------------------------------------------------------
+
+@dataclass
+class QMat:
+    """One packed matrix: ``codes`` uint8 [rows, cols*bits/8], ``scales`` f32 [rows, cols/group]."""
+    codes: np.ndarray
+    scales: np.ndarray
+
+
+@dataclass
+class Expert:
+    gate: QMat   # [d_ff, d_model]
+    up: QMat     # [d_ff, d_model]
+    down: QMat   # [d_model, d_ff]
+
+
+@dataclass
+class ExpertGroup:
+    bits: int
+    group: int
+    d_model: int
+    d_ff: int
+    experts: list = field(default_factory=list)
+
+    def byte_count(self) -> int:
+        return sum(m.codes.nbytes + m.scales.nbytes
+                   for e in self.experts for m in (e.gate, e.up, e.down))
+
+
+def qmat(seed: int, expert: int, name: str, rows: int, cols: int, bits: int, group: int,
+         scale_lo: float = 0.01, scale_hi: float = 0.05) -> QMat:
+    if (cols * bits) % 8 or cols % group:
+        raise ValueError("cols must fill whole bytes and whole groups")
+    m = _MAT[name]
+    codes = random_bytes(seed, (expert, m, _KIND_CODES), rows * cols * bits // 8)
+    scales = uniform_f32(seed, (expert, m, _KIND_SCALES), rows * (cols // group), scale_lo, scale_hi)
+    return QMat(codes.reshape(rows, cols * bits // 8), scales.reshape(rows, cols // group))
+
+
+def expert_group(seed: int, n_experts: int, d_model: int, d_ff: int, bits: int,
+                 group: int = 64) -> ExpertGroup:
+    g = ExpertGroup(bits=bits, group=group, d_model=d_model, d_ff=d_ff)
+    for e in range(n_experts):
+        g.experts.append(Expert(
+            gate=qmat(seed, e, "gate", d_ff, d_model, bits, group),
+            up=qmat(seed, e, "up", d_ff, d_model, bits, group),
+            down=qmat(seed, e, "down", d_model, d_ff, bits, group)))
+    return g
+
+
+def activation(seed: int, d_model: int) -> np.ndarray:
+    return normal_f32(seed, (_TAG_X,), d_model)
+
+
+def activation_batch(seed: int, T: int, d_model: int) -> np.ndarray:
+    return normal_f32(seed, (_TAG_XBATCH,), T * d_model).reshape(T, d_model)
+
+
+def router_weights(seed: int, n_experts: int, T: int = 1) -> np.ndarray:
+    """f32 [T, n_experts]: softmax of N(0,1) f32 logits per token."""
+    return softmax_f32(normal_f32(seed, (_TAG_ROUTER,), T * n_experts).reshape(T, n_experts))
+
+
+# ----------------------------------------------------------------------------
+# Named workloads
+# ----------------------------------------------------------------------------
+
+TINY = dict(name="q4_tiny_1expert_256x512", seed=0, n_experts=1, d_model=256, d_ff=512, bits=4)
+Q4_GROUP8 = dict(name="q4_8expert_4096x1536", seed=1, n_experts=8, d_model=4096, d_ff=1536, bits=4)
+Q2_GROUP8 = dict(name="q2_8expert_4096x1536", seed=2, n_experts=8, d_model=4096, d_ff=1536, bits=2)
+BF16_SHAPES = [  # (rows, cols, role, seed)
+    (8192, 4096, "q_proj", 30),
+    (4096, 8192, "o_proj", 31),
+    (512, 4096, "kv_proj", 32),
+    (151936, 4096, "lm_head", 33),
+]
+BATCH_TOKENS = {16: 40, 64: 41, 256: 42}   # T -> seed of X; weights are Q4_GROUP8's
+
+
+def make_group(spec: dict) -> ExpertGroup:
+    return expert_group(spec["seed"], spec["n_experts"], spec["d_model"], spec["d_ff"], spec["bits"])
+
+
+def make_decode_inputs(spec: dict):
+    """(ExpertGroup, x f32 [d_model], router f32 [n_experts]) for a decode group."""
+    g = make_group(spec)
+    x = activation(spec["seed"], spec["d_model"])
+    r = router_weights(spec["seed"], spec["n_experts"])[0]
+    return g, x, r
+
+
+def make_bf16(rows: int, cols: int, seed: int, sigma: float = 0.02):
+    """(W bf16 bits uint16 [rows, cols], x f32 [cols])."""
+    W = bf16_normal(seed, (_TAG_BF16_W,), rows, cols, sigma)
+    x = normal_f32(seed, (_TAG_BF16_X,), cols)
+    return W, x
+
+
+def make_batch_inputs(T: int, seed: int | None = None, d_model: int = 4096):
+    """(X f32 [T, d_model], router f32 [T, 8]) for the token-batch workload."""
+    seed = BATCH_TOKENS[T] if seed is None else seed
+    return activation_batch(seed, T, d_model), router_weights(seed, 8, T)
