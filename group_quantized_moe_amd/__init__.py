@@ -1,0 +1,181 @@
+"""Python binding of libsmoe.so (group-quantised routed-expert FFN decode path
+and bf16 matvec on MI355X).
+
+Argument marshalling only: every function takes torch tensors that live on the
+GPU, checks dtype / device / contiguity, reads sizes off the tensor shapes, and
+passes raw device pointers plus the current HIP stream to the C function of
+the same name (declared in include/smoe.h).  No step of the computation runs
+here.  If the library is missing the first call raises; nothing falls back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmoe.so")
+
+SMOE_OK = 0
+SMOE_MAX_EXPERTS = 16
+
+EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
+           "matvec_bf16_workspace", "matvec_bf16", "smoe_status_str")
+
+
+class SmoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {smoe_status_str(status)} (status {status})")
+
+
+class QMat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class Expert(ctypes.Structure):
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libsmoe.so is not built ({LIB_PATH}); run "
+                               "`python -m group_quantized_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.smoe_gate_up.argtypes = [vp, vp, i, i, i, i, vp, vp, vp]
+        L.smoe_down.argtypes = [vp, i, i, i, i, vp, vp, vp]
+        L.smoe_expert_ffn_workspace.argtypes = [i, i, i, i]
+        L.smoe_expert_ffn_workspace.restype = sz
+        L.smoe_expert_ffn.argtypes = [vp, i, vp, i, i, i, i, i, vp, vp, vp, sz, vp]
+        L.matvec_bf16_workspace.argtypes = [i, i]
+        L.matvec_bf16_workspace.restype = sz
+        L.matvec_bf16.argtypes = [vp, i, i, vp, vp, vp, sz, vp]
+        L.smoe_status_str.argtypes = [i]
+        L.smoe_status_str.restype = ctypes.c_char_p
+        for name in ("smoe_gate_up", "smoe_down", "smoe_expert_ffn", "matvec_bf16"):
+            getattr(L, name).restype = i
+        _lib = L
+    return _lib
+
+
+def smoe_status_str(status: int) -> str:
+    return lib().smoe_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SMOE_OK:
+        raise SmoeError(fn, status)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _qmat(codes, scales, name):
+    import torch
+    return QMat(_dev(codes, torch.uint8, name + ".codes"), _dev(scales, torch.float32, name + ".scales"))
+
+
+def _dims(codes, bits):
+    """(rows, cols) of a packed matrix [rows, cols*bits/8]."""
+    return codes.shape[0], codes.shape[1] * 8 // bits
+
+
+def smoe_gate_up(gate_codes, gate_scales, up_codes, up_scales, bits, group, x, hidden, stream=None):
+    """hidden[d_ff] = SiLU(G x) * (U x); G, U packed [d_ff, d_model*bits/8]."""
+    import torch
+    d_ff, d_model = _dims(gate_codes, bits)
+    G, U = _qmat(gate_codes, gate_scales, "gate"), _qmat(up_codes, up_scales, "up")
+    _check("smoe_gate_up", lib().smoe_gate_up(
+        ctypes.byref(G), ctypes.byref(U), bits, group, d_ff, d_model,
+        _dev(x, torch.float32, "x"), _dev(hidden, torch.float32, "hidden"), _stream(stream)))
+
+
+def smoe_down(down_codes, down_scales, bits, group, hidden, out, stream=None):
+    """out[d_model] = D hidden; D packed [d_model, d_ff*bits/8]."""
+    import torch
+    d_model, d_ff = _dims(down_codes, bits)
+    D = _qmat(down_codes, down_scales, "down")
+    _check("smoe_down", lib().smoe_down(
+        ctypes.byref(D), bits, group, d_model, d_ff, _dev(hidden, torch.float32, "hidden"),
+        _dev(out, torch.float32, "out"), _stream(stream)))
+
+
+def smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T=1) -> int:
+    return int(lib().smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T))
+
+
+def _expert_array(experts):
+    """experts: sequence of objects with .gate/.up/.down, each with .codes/.scales
+    (torch GPU tensors), or 6-tuples (gc, gs, uc, us, dc, ds)."""
+    arr = (Expert * len(experts))()
+    for k, e in enumerate(experts):
+        if isinstance(e, (tuple, list)):
+            gc, gs, uc, us, dc, ds = e
+        else:
+            gc, gs, uc, us, dc, ds = (e.gate.codes, e.gate.scales, e.up.codes, e.up.scales,
+                                      e.down.codes, e.down.scales)
+        arr[k] = Expert(_qmat(gc, gs, f"experts[{k}].gate"), _qmat(uc, us, f"experts[{k}].up"),
+                        _qmat(dc, ds, f"experts[{k}].down"))
+    return arr
+
+
+def _first_gate_codes(experts):
+    e = experts[0]
+    return e[0] if isinstance(e, (tuple, list)) else e.gate.codes
+
+
+def smoe_expert_ffn(experts, bits, group, x, out, route_w=None, workspace=None, stream=None):
+    """out[T, d_model] = sum_e route_w[t, e] * FFN_e(x[t]).
+
+    x, out: f32 [T, d_model] (or [d_model] for one token); route_w: f32 [T, n] or None;
+    workspace: uint8 GPU tensor of at least smoe_expert_ffn_workspace(...) bytes."""
+    import torch
+    d_ff, d_model = _dims(_first_gate_codes(experts), bits)
+    T = x.numel() // d_model
+    arr = _expert_array(experts)
+    pr = None if route_w is None else _dev(route_w, torch.float32, "route_w")
+    if workspace is None:
+        raise ValueError("smoe_expert_ffn needs a caller-owned workspace tensor")
+    pw = _dev(workspace, torch.uint8, "workspace")
+    _check("smoe_expert_ffn", lib().smoe_expert_ffn(
+        arr, len(experts), pr, bits, group, d_model, d_ff, T, _dev(x, torch.float32, "x"),
+        _dev(out, torch.float32, "out"), pw, workspace.numel(), _stream(stream)))
+
+
+def matvec_bf16_workspace(rows, cols) -> int:
+    return int(lib().matvec_bf16_workspace(rows, cols))
+
+
+def matvec_bf16(W, x, y, workspace=None, stream=None):
+    """y[rows] = W x with W bf16 [rows, cols] (torch.bfloat16 or raw int16 bits)."""
+    import torch
+    if W.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError("W must be torch.bfloat16 (or int16 bit patterns)")
+    rows, cols = W.shape
+    _dev(W, W.dtype, "W")
+    pw, nw = (None, 0) if workspace is None else (_dev(workspace, torch.uint8, "workspace"),
+                                                    workspace.numel())
+    _check("matvec_bf16", lib().matvec_bf16(
+        W.data_ptr(), rows, cols, _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"),
+        pw, nw, _stream(stream)))

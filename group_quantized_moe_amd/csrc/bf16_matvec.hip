@@ -1,0 +1,152 @@
+// Dense bf16 matvec y = W x on gfx950 (Metal Compute Kernels, S-MoE docs,
+// "Coalesced Dense Matvec -- the Same Contract for bf16": 16-byte chunks of
+// eight bf16 values, widened to f32 by shifting each half of a dword into the
+// upper 16 bits, which is exact; f32 input; f32 output).
+//
+// Same mapping as the quantised kernels: nw waves split a row's chunks into
+// contiguous slices, LPR lanes share a row inside a wave, every lane keeps its
+// x slice in registers and streams ITER row steps of 16-byte loads issued up
+// front; DPP reduction inside the wave, LDS across waves.
+#include "launch.h"
+
+namespace smoe {
+namespace {
+
+// Element 2m of a row sits in the low half of dword m, element 2m+1 in the high half.
+__device__ __forceinline__ float bf16_chunk_dot(const uint4 q, const float *xv, float acc0)
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float a0 = acc0, a1 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        a0 = fmaf(__uint_as_float(w[m] << 16), xv[2 * m], a0);
+        a1 = fmaf(__uint_as_float(w[m] & 0xFFFF0000u), xv[2 * m + 1], a1);
+    }
+    return a0 + a1;
+}
+
+template <int LPR, int NCH, int ITER>
+__global__ __launch_bounds__(512) void k_matvec_bf16(const Bf16Args a)
+{
+    constexpr int RS = 64 / LPR;
+    constexpr int RB = RS * ITER;
+    extern __shared__ float red[];  // [nw][RB]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int lr = lane % LPR, slot = lane / LPR;
+    const int cpr = a.cols / 8;
+    const int sl = (cpr + nw - 1) / nw;
+    const int row0 = blockIdx.x * RB;
+    const uint8_t *W = reinterpret_cast<const uint8_t *>(a.W);
+    const size_t row_bytes = (size_t)a.cols * 2;
+
+    int c[NCH];
+    bool valid[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int cs = lr + LPR * k;
+        c[k] = wave * sl + cs;
+        valid[k] = cs < sl && c[k] < cpr;
+    }
+
+    uint4 q[ITER][NCH];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int r = row0 + slot + RS * it;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            q[it][k] = (valid[k] && r < a.rows) ? load16(W + (size_t)r * row_bytes + (size_t)c[k] * 16)
+                                                : make_uint4(0, 0, 0, 0);
+    }
+
+    float xv[NCH][8];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        if (valid[k]) {
+            const float4 *src = reinterpret_cast<const float4 *>(a.x + (size_t)c[k] * 8);
+            const float4 u = src[0], v = src[1];
+            xv[k][0] = u.x; xv[k][1] = u.y; xv[k][2] = u.z; xv[k][3] = u.w;
+            xv[k][4] = v.x; xv[k][5] = v.y; xv[k][6] = v.z; xv[k][7] = v.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xv[k][j] = 0.0f;
+        }
+    }
+
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) acc = bf16_chunk_dot(q[it][k], xv[k], acc);
+        acc = lane_group_sum<LPR>(acc);
+        if (lr == 0) red[wave * RB + slot + RS * it] = acc;
+    }
+    __syncthreads();
+    for (int t = tid; t < RB; t += blockDim.x) {
+        const int r = row0 + t;
+        if (r < a.rows) {
+            float y = 0.0f;
+            for (int w = 0; w < nw; ++w) y += red[w * RB + t];
+            a.y[r] = y;
+        }
+    }
+}
+
+template <int LPR, int NCH, int ITER>
+hipError_t run_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream_t st)
+{
+    constexpr int RB = (64 / LPR) * ITER;
+    const dim3 grid((a.rows + RB - 1) / RB), block(64 * cfg.nw);
+    hipLaunchKernelGGL((k_matvec_bf16<LPR, NCH, ITER>), grid, block, sizeof(float) * RB * cfg.nw, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define SMOE_BMAP_ITERS(F, L, N) F(L, N, 1) F(L, N, 2) F(L, N, 4) F(L, N, 8)
+#define SMOE_BMAP_NCHS(F, L) SMOE_BMAP_ITERS(F, L, 1) SMOE_BMAP_ITERS(F, L, 2) SMOE_BMAP_ITERS(F, L, 4) SMOE_BMAP_ITERS(F, L, 8)
+#define SMOE_BMAP_ALL(F) SMOE_BMAP_NCHS(F, 4) SMOE_BMAP_NCHS(F, 16) SMOE_BMAP_NCHS(F, 64)
+
+bool choose_bf16map(int chunks, int rows, MapConfig *cfg)
+{
+    // 16 lanes per row when the slice allows it (short DPP reduction, four rows
+    // per wave step), otherwise 4, or 64 for the widest rows; blocks of up to
+    // 8 waves, as many as keep every lane busy.
+    static const int kNw[] = {8, 4, 6, 2, 1};
+    double best = 1e30;
+    MapConfig pick{0, 0, 0, 0};
+    for (int lpr : {16, 4, 64})
+        for (int nch : {1, 2, 4, 8})
+            for (int nw : kNw) {
+                const int sl = (chunks + nw - 1) / nw;
+                if (sl > lpr * nch) continue;
+                const double waste = 1.0 - (double)chunks / (nw * lpr * nch);
+                const double pen = 10.0 * waste + (lpr == 16 ? 0.0 : 0.5) + 0.05 * nch + (nw == 8 ? 0.0 : 0.3);
+                if (pen < best) {
+                    best = pen;
+                    pick = MapConfig{nw, lpr, nch, 1};
+                }
+            }
+    if (!pick.nw) return false;
+    const int rs = 64 / pick.lpr;
+    for (int iter : {8, 4, 2, 1}) {
+        const long blocks = (rows + rs * iter - 1) / (rs * iter);
+        if (iter == 1 || blocks * pick.nw >= 4096) {
+            pick.iter = iter;
+            break;
+        }
+    }
+    *cfg = pick;
+    return true;
+}
+
+hipError_t launch_matvec_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream_t st)
+{
+#define SMOE_RUN(L, N, I) \
+    if (cfg.lpr == L && cfg.nch == N && cfg.iter == I) return run_bf16<L, N, I>(cfg, a, st);
+    SMOE_BMAP_ALL(SMOE_RUN)
+#undef SMOE_RUN
+    return hipErrorInvalidConfiguration;
+}
+
+}  // namespace smoe

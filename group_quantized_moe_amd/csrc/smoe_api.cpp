@@ -1,0 +1,304 @@
+// C ABI of libsmoe.so: host-side argument checks, lane-mapping choice and
+// kernel launches.  Every check runs before any HIP call, so an out-of-contract
+// argument returns an error with nothing enqueued (and needs no GPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/smoe.h"
+#include "launch.h"
+
+using smoe::MapConfig;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device properties, queried once per device ("device limits are queried,
+// never guessed").
+struct DeviceInfo {
+    bool ok;
+    int cus;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+int check_device(DeviceInfo *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMOE_ERR_DEVICE;
+    std::call_once(g_dev_once[dev], [dev] {
+        hipDeviceProp_t p;
+        DeviceInfo d{false, 0};
+        if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
+            d.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+            d.cus = p.multiProcessorCount;
+        }
+        g_dev[dev] = d;
+    });
+    if (!g_dev[dev].ok) return SMOE_ERR_DEVICE;
+    if (out) *out = g_dev[dev];
+    return SMOE_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || !na || !nb) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int check_format(int bits, int group)
+{
+    if (bits != 4 && bits != 2) return SMOE_ERR_BITS;
+    const int unit = 128 / bits;  // codes in a 16-byte chunk
+    if (group <= 0 || group % unit) return SMOE_ERR_GROUP;
+    return SMOE_OK;
+}
+
+// rows x cols quantised matrix: sizes, group divisibility, pointers, alignment.
+int check_qmat(const smoe_qmat *m, int bits, int group, long rows, long cols)
+{
+    if (!m || !m->codes || !m->scales) return SMOE_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || cols % (128 / bits) || cols > SMOE_MAX_QCOLS) return SMOE_ERR_SHAPE;
+    if (cols % group) return SMOE_ERR_GROUP;
+    if (!aligned(m->codes, 16) || !aligned(m->scales, 4)) return SMOE_ERR_ALIGN;
+    return SMOE_OK;
+}
+
+size_t qmat_code_bytes(int bits, long rows, long cols) { return (size_t)rows * cols * bits / 8; }
+size_t qmat_scale_bytes(int group, long rows, long cols) { return (size_t)rows * (cols / group) * 4; }
+
+// out overlaps either array of a quantised matrix.
+bool overlaps_qmat(const void *out, size_t nout, const smoe_qmat *m, int bits, int group, long rows,
+                   long cols)
+{
+    return overlap(out, nout, m->codes, qmat_code_bytes(bits, rows, cols)) ||
+           overlap(out, nout, m->scales, qmat_scale_bytes(group, rows, cols));
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SMOE_OK : SMOE_ERR_LAUNCH; }
+
+// Workspace layout of the decode path (T == 1):
+//   hidden   f32 [n_experts][d_ff]
+//   partial  f32 [n_experts][d_model]
+//   counters i32 [d_model]    (one per row tile of the down pass; d_model bounds it)
+struct DecodeWorkspace {
+    size_t hidden, partial, counters, total;
+};
+
+DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
+{
+    DecodeWorkspace w;
+    w.hidden = 0;
+    w.partial = w.hidden + align256((size_t)n_experts * d_ff * 4);
+    w.counters = w.partial + align256((size_t)n_experts * d_model * 4);
+    w.total = w.counters + align256((size_t)d_model * 4);
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *smoe_status_str(int status)
+{
+    switch (status) {
+    case SMOE_OK: return "ok";
+    case SMOE_ERR_NULL: return "a required pointer is NULL";
+    case SMOE_ERR_BITS: return "bits must be 2 or 4";
+    case SMOE_ERR_GROUP: return "group must be a multiple of 32 (4-bit) or 64 (2-bit) and divide cols";
+    case SMOE_ERR_SHAPE: return "a size is out of range or not a multiple of the 16-byte chunk width";
+    case SMOE_ERR_ALIGN: return "codes/W must be 16-byte aligned and f32 arrays 4-byte aligned";
+    case SMOE_ERR_WORKSPACE: return "workspace missing or smaller than the *_workspace() size";
+    case SMOE_ERR_ALIAS: return "an output overlaps an input or the workspace";
+    case SMOE_ERR_DEVICE: return "current device is not gfx950 (MI355X) or could not be queried";
+    case SMOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+    }
+}
+
+int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group, int d_ff,
+                 int d_model, const float *x, float *hidden, void *stream)
+{
+    int rc = check_format(bits, group);
+    if (rc) return rc;
+    if (!x || !hidden) return SMOE_ERR_NULL;
+    if ((rc = check_qmat(gate, bits, group, d_ff, d_model))) return rc;
+    if ((rc = check_qmat(up, bits, group, d_ff, d_model))) return rc;
+    if (!aligned(x, 16) || !aligned(hidden, 4)) return SMOE_ERR_ALIGN;
+    const size_t nh = (size_t)d_ff * 4;
+    if (overlap(hidden, nh, x, (size_t)d_model * 4) ||
+        overlaps_qmat(hidden, nh, gate, bits, group, d_ff, d_model) ||
+        overlaps_qmat(hidden, nh, up, bits, group, d_ff, d_model))
+        return SMOE_ERR_ALIAS;
+    MapConfig cfg;
+    if (!smoe::choose_qmap(bits, d_model * bits / 128, d_ff, 1, &cfg)) return SMOE_ERR_SHAPE;
+    if ((rc = check_device(nullptr))) return rc;
+
+    smoe::GateUpArgs a{};
+    a.gate[0] = {gate->codes, gate->scales};
+    a.up[0] = {up->codes, up->scales};
+    a.x = x;
+    a.hidden = hidden;
+    a.counters = nullptr;
+    a.n_counters = 0;
+    a.d_model = d_model;
+    a.d_ff = d_ff;
+    a.group = group;
+    a.blocks_per_expert = (d_ff + cfg.rows_per_block() - 1) / cfg.rows_per_block();
+    return launch_status(smoe::launch_gate_up(bits, cfg, a, 1, (hipStream_t)stream));
+}
+
+int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff, const float *hidden,
+              float *out, void *stream)
+{
+    int rc = check_format(bits, group);
+    if (rc) return rc;
+    if (!hidden || !out) return SMOE_ERR_NULL;
+    if ((rc = check_qmat(down, bits, group, d_model, d_ff))) return rc;
+    if (!aligned(hidden, 16) || !aligned(out, 4)) return SMOE_ERR_ALIGN;
+    const size_t no = (size_t)d_model * 4;
+    if (overlap(out, no, hidden, (size_t)d_ff * 4) ||
+        overlaps_qmat(out, no, down, bits, group, d_model, d_ff))
+        return SMOE_ERR_ALIAS;
+    MapConfig cfg;
+    if (!smoe::choose_qmap(bits, d_ff * bits / 128, d_model, 1, &cfg)) return SMOE_ERR_SHAPE;
+    if ((rc = check_device(nullptr))) return rc;
+
+    smoe::DownArgs a{};
+    a.down[0] = {down->codes, down->scales};
+    a.hidden = hidden;
+    a.route_w = nullptr;
+    a.out = out;
+    a.partial = nullptr;
+    a.counters = nullptr;
+    a.d_model = d_model;
+    a.d_ff = d_ff;
+    a.group = group;
+    a.n_experts = 1;
+    a.row_blocks = (d_model + cfg.rows_per_block() - 1) / cfg.rows_per_block();
+    return launch_status(smoe::launch_down(bits, cfg, a, (hipStream_t)stream));
+}
+
+size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
+{
+    if (n_experts <= 0 || d_model <= 0 || d_ff <= 0 || T <= 0) return 0;
+    if (T == 1) return decode_workspace(n_experts, d_model, d_ff).total;
+    return 0;  // token batch: not available in this build
+}
+
+int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int bits,
+                    int group, int d_model, int d_ff, int T, const float *x, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    int rc = check_format(bits, group);
+    if (rc) return rc;
+    if (!experts || !x || !out) return SMOE_ERR_NULL;
+    if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS || T < 1) return SMOE_ERR_SHAPE;
+    for (int e = 0; e < n_experts; ++e) {
+        if ((rc = check_qmat(&experts[e].gate, bits, group, d_ff, d_model))) return rc;
+        if ((rc = check_qmat(&experts[e].up, bits, group, d_ff, d_model))) return rc;
+        if ((rc = check_qmat(&experts[e].down, bits, group, d_model, d_ff))) return rc;
+    }
+    if (!aligned(x, 16) || !aligned(out, 4) || (route_w && !aligned(route_w, 4)))
+        return SMOE_ERR_ALIGN;
+    if (T != 1) return SMOE_ERR_SHAPE;  // token batch: not available in this build
+
+    const size_t need = smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T);
+    if (!workspace || workspace_bytes < need) return SMOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SMOE_ERR_ALIGN;
+    const size_t no = (size_t)T * d_model * 4;
+    if (overlap(out, no, x, (size_t)T * d_model * 4) || overlap(out, no, workspace, need) ||
+        overlap(out, no, route_w, route_w ? (size_t)T * n_experts * 4 : 0) ||
+        overlap(workspace, need, x, (size_t)T * d_model * 4) ||
+        overlap(workspace, need, route_w, route_w ? (size_t)T * n_experts * 4 : 0))
+        return SMOE_ERR_ALIAS;
+    for (int e = 0; e < n_experts; ++e) {
+        const smoe_expert &ex = experts[e];
+        if (overlaps_qmat(out, no, &ex.gate, bits, group, d_ff, d_model) ||
+            overlaps_qmat(out, no, &ex.up, bits, group, d_ff, d_model) ||
+            overlaps_qmat(out, no, &ex.down, bits, group, d_model, d_ff) ||
+            overlaps_qmat(workspace, need, &ex.gate, bits, group, d_ff, d_model) ||
+            overlaps_qmat(workspace, need, &ex.up, bits, group, d_ff, d_model) ||
+            overlaps_qmat(workspace, need, &ex.down, bits, group, d_model, d_ff))
+            return SMOE_ERR_ALIAS;
+    }
+    MapConfig gu, dn;
+    if (!smoe::choose_qmap(bits, d_model * bits / 128, d_ff, n_experts, &gu)) return SMOE_ERR_SHAPE;
+    if (!smoe::choose_qmap(bits, d_ff * bits / 128, d_model, n_experts, &dn)) return SMOE_ERR_SHAPE;
+    if ((rc = check_device(nullptr))) return rc;
+
+    const DecodeWorkspace w = decode_workspace(n_experts, d_model, d_ff);
+    char *ws = static_cast<char *>(workspace);
+    float *hidden = reinterpret_cast<float *>(ws + w.hidden);
+    float *partial = reinterpret_cast<float *>(ws + w.partial);
+    int *counters = reinterpret_cast<int *>(ws + w.counters);
+    const int row_blocks = (d_model + dn.rows_per_block() - 1) / dn.rows_per_block();
+    hipStream_t st = (hipStream_t)stream;
+
+    smoe::GateUpArgs g{};
+    smoe::DownArgs d{};
+    for (int e = 0; e < n_experts; ++e) {
+        g.gate[e] = {experts[e].gate.codes, experts[e].gate.scales};
+        g.up[e] = {experts[e].up.codes, experts[e].up.scales};
+        d.down[e] = {experts[e].down.codes, experts[e].down.scales};
+    }
+    g.x = x;
+    g.hidden = hidden;
+    g.counters = n_experts > 1 ? counters : nullptr;
+    g.n_counters = n_experts > 1 ? row_blocks : 0;
+    g.d_model = d_model;
+    g.d_ff = d_ff;
+    g.group = group;
+    g.blocks_per_expert = (d_ff + gu.rows_per_block() - 1) / gu.rows_per_block();
+    if ((rc = launch_status(smoe::launch_gate_up(bits, gu, g, n_experts, st)))) return rc;
+
+    d.hidden = hidden;
+    d.route_w = route_w;
+    d.out = out;
+    d.partial = partial;
+    d.counters = counters;
+    d.d_model = d_model;
+    d.d_ff = d_ff;
+    d.group = group;
+    d.n_experts = n_experts;
+    d.row_blocks = row_blocks;
+    return launch_status(smoe::launch_down(bits, dn, d, st));
+}
+
+size_t matvec_bf16_workspace(int rows, int cols)
+{
+    (void)rows;
+    (void)cols;
+    return 0;
+}
+
+int matvec_bf16(const uint16_t *W, int rows, int cols, const float *x, float *y, void *workspace,
+                size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!W || !x || !y) return SMOE_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || cols % 8 || cols > SMOE_MAX_BF16_COLS) return SMOE_ERR_SHAPE;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return SMOE_ERR_ALIGN;
+    const size_t ny = (size_t)rows * 4;
+    if (overlap(y, ny, W, (size_t)rows * cols * 2) || overlap(y, ny, x, (size_t)cols * 4))
+        return SMOE_ERR_ALIAS;
+    MapConfig cfg;
+    if (!smoe::choose_bf16map(cols / 8, rows, &cfg)) return SMOE_ERR_SHAPE;
+    int rc = check_device(nullptr);
+    if (rc) return rc;
+    smoe::Bf16Args a{W, x, y, rows, cols};
+    return launch_status(smoe::launch_matvec_bf16(cfg, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

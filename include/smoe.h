@@ -1,0 +1,146 @@
+/*
+ * smoe.h -- C ABI of libsmoe.so: the group-quantised routed-expert FFN decode
+ * path and its bf16 dense-matvec twin on one AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the Metal Compute Kernels page of the S-MoE docs:
+ *
+ *  - smoe_gate_up   hidden = SiLU(G x) * (U x), gate and up reading one shared
+ *                   input vector ("Fused FFN Kernels -- One Simdgroup Per
+ *                   Output Row").
+ *  - smoe_down      out = D hidden (same section).
+ *  - smoe_expert_ffn  the two passes for a group of routed experts in one
+ *                   call, expert outputs combined with router weights; one
+ *                   token or a batch of tokens ("Fused FFN Kernels" and
+ *                   "Token-Batch Fused FFN"; all experts of a group go out in
+ *                   one submission as in "Grouped Expert Dispatch").
+ *  - matvec_bf16    y = W x with bf16 W and f32 x ("Coalesced Dense Matvec --
+ *                   the Same Contract for bf16").
+ *
+ * Weight format (the "Layout assumptions the kernels rely on" contract):
+ *   A quantised matrix of rows x cols is a smoe_qmat:
+ *     codes  : rows * (cols*bits/8) bytes, row-major, row stride cols*bits/8.
+ *              4-bit codes: byte k of a row holds column 2k in the low nibble
+ *              and column 2k+1 in the high nibble.  2-bit codes: byte k holds
+ *              columns 4k..4k+3 from the least significant bit pair up.
+ *              Base address 16-byte aligned; the row stride is then a
+ *              multiple of 16 because cols is a multiple of 32 (4-bit) or 64
+ *              (2-bit).
+ *     scales : rows * (cols/group) f32, row-major; scale g of a row covers
+ *              columns g*group .. g*group+group-1.  4-byte aligned.
+ *   The weight at (r, j) is (code - Z) / Z * scale, Z = 7.5 at 4 bits and 1.5
+ *   at 2 bits.  group must be a multiple of 32 (4-bit) or 64 (2-bit) and
+ *   divide cols, so no 16-byte chunk of codes straddles two groups.
+ *
+ * Activations are f32 throughout (x, hidden, out, y, router weights).
+ *
+ * Memory and streams: every data pointer is a DEVICE pointer owned by the
+ * caller; the library never allocates, frees or copies device memory inside a
+ * call.  `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ * enqueue work and return; results are ready when the stream reaches them.
+ * Scratch memory comes from the caller's workspace, sized by the matching
+ * *_workspace() function.  Structures passed by host pointer (smoe_qmat,
+ * smoe_expert) are read during the call and may be reused afterwards.
+ *
+ * Errors: every call checks all of its arguments on the host before it
+ * enqueues anything and returns a negative SMOE_ERR_* code when an argument
+ * is outside the contract; in that case nothing was launched.  There is no
+ * fallback kernel.  smoe_status_str() gives a message for each code.
+ */
+#ifndef SMOE_H
+#define SMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SMOE_OK = 0,
+    SMOE_ERR_NULL = -1,      /* a required pointer is NULL */
+    SMOE_ERR_BITS = -2,      /* bits is not 2 or 4 */
+    SMOE_ERR_GROUP = -3,     /* group not a multiple of 32 (4-bit) / 64 (2-bit), or does not divide cols */
+    SMOE_ERR_SHAPE = -4,     /* a size is <= 0, not a multiple of the chunk width, or above the kernel limits */
+    SMOE_ERR_ALIGN = -5,     /* codes / W not 16-byte aligned, or f32 data not 4-byte aligned */
+    SMOE_ERR_WORKSPACE = -6, /* workspace NULL or smaller than *_workspace() asks for */
+    SMOE_ERR_ALIAS = -7,     /* an output range overlaps an input or the workspace */
+    SMOE_ERR_DEVICE = -8,    /* current device is not gfx950, or a device query failed */
+    SMOE_ERR_LAUNCH = -9,    /* the HIP runtime refused a launch */
+};
+
+/* Largest n_experts accepted by smoe_expert_ffn in one call. */
+#define SMOE_MAX_EXPERTS 16
+/* Largest cols of a quantised matrix (d_model for gate/up, d_ff for down). */
+#define SMOE_MAX_QCOLS 16384
+/* Largest cols of a bf16 matrix. */
+#define SMOE_MAX_BF16_COLS 16384
+
+typedef struct smoe_qmat {
+    const uint8_t *codes;
+    const float *scales;
+} smoe_qmat;
+
+typedef struct smoe_expert {
+    smoe_qmat gate;   /* [d_ff x d_model] */
+    smoe_qmat up;     /* [d_ff x d_model] */
+    smoe_qmat down;   /* [d_model x d_ff] */
+} smoe_expert;
+
+/*
+ * hidden[i] = SiLU((G x)[i]) * (U x)[i],  i < d_ff, for one expert.
+ *   gate, up : [d_ff x d_model] quantised matrices (host structs, device data)
+ *   x        : f32 [d_model]
+ *   hidden   : f32 [d_ff], must not overlap x or the weights
+ * SiLU(t) = t / (1 + exp(-t)).
+ */
+int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group,
+                 int d_ff, int d_model, const float *x, float *hidden, void *stream);
+
+/*
+ * out[j] = (D hidden)[j],  j < d_model, for one expert.
+ *   down   : [d_model x d_ff] quantised matrix
+ *   hidden : f32 [d_ff]
+ *   out    : f32 [d_model], must not overlap hidden or the weights
+ */
+int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
+              const float *hidden, float *out, void *stream);
+
+/*
+ * Routed experts over T tokens:
+ *   out[t][:] = sum_e route_w[t][e] * down_e( SiLU(gate_e x[t]) * (up_e x[t]) )
+ *   experts   : host array of n_experts expert descriptors (1..SMOE_MAX_EXPERTS)
+ *   route_w   : f32 [T][n_experts] device array, or NULL for weight 1 everywhere
+ *   x         : f32 [T][d_model]
+ *   out       : f32 [T][d_model], must not overlap x, route_w, workspace or weights
+ *   workspace : device scratch of at least smoe_expert_ffn_workspace(...) bytes,
+ *               256-byte aligned; its contents need not be initialised and are
+ *               clobbered.  Calls that share a workspace must be ordered (one
+ *               stream), or they race.
+ * T == 1 runs the decode kernels (two launches); T > 1 runs the token-batch
+ * kernels, in which every expert processes every token.
+ */
+size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T);
+int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w,
+                    int bits, int group, int d_model, int d_ff, int T,
+                    const float *x, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * y[r] = sum_j float(W[r][j]) * x[j],  r < rows.
+ *   W : bf16 bit patterns [rows x cols], 16-byte aligned, cols % 8 == 0
+ *   x : f32 [cols]
+ *   y : f32 [rows], must not overlap W or x
+ *   workspace : may be NULL when matvec_bf16_workspace() returns 0
+ */
+size_t matvec_bf16_workspace(int rows, int cols);
+int matvec_bf16(const uint16_t *W, int rows, int cols, const float *x, float *y,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message for a status code (static string). */
+const char *smoe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

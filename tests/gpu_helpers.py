@@ -1,0 +1,76 @@
+"""Moving the seeded host workloads onto the GPU, and the parity bar.
+
+The bar (f32 GPU output against the f64 oracle): max |gpu - oracle| <=
+1e-4 * max(1, max |oracle|), the agreement level for this path; the pages
+report ~1e-6 for a reassociated f32 reduction, so results are also expected
+to sit far below the bar.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+TOL = 1e-4
+
+
+def parity(got, want, tol=TOL):
+    """(max abs error, bound); the bound is tol * max(1, max|want|)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    bound = tol * max(1.0, float(np.max(np.abs(want))) if want.size else 1.0)
+    return err, bound
+
+
+def assert_parity(got, want, what, tol=TOL):
+    err, bound = parity(got, want, tol)
+    print(f"[parity] {what}: max|diff| = {err:.3e} (bound {bound:.3e})", flush=True)
+    assert err <= bound, f"{what}: max|diff| {err:.3e} > {bound:.3e}"
+    return err
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+@dataclass
+class DevQ:
+    codes: object
+    scales: object
+
+
+@dataclass
+class DevExpert:
+    gate: DevQ
+    up: DevQ
+    down: DevQ
+
+
+def dev_experts(group):
+    return [DevExpert(*[DevQ(dev(m.codes), dev(m.scales)) for m in (e.gate, e.up, e.down)])
+            for e in group.experts]
+
+
+def run_ffn(gq, dexp, bits, group_size, x, route=None, T=None):
+    """smoe_expert_ffn through the C ABI; returns the f32 output as numpy."""
+    import torch
+    d_model = dexp[0].gate.codes.shape[1] * 8 // bits
+    d_ff = dexp[0].gate.codes.shape[0]
+    xd = x if isinstance(x, torch.Tensor) else dev(np.asarray(x, np.float32))
+    T = xd.numel() // d_model
+    out = torch.empty(T * d_model, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gq.smoe_expert_ffn_workspace(len(dexp), d_model, d_ff, T), dtype=torch.uint8,
+                     device="cuda")
+    rd = None
+    if route is not None:
+        rd = route if isinstance(route, torch.Tensor) else dev(np.asarray(route, np.float32))
+    gq.smoe_expert_ffn(dexp, bits, group_size, xd, out, route_w=rd, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(T, d_model) if T > 1 else out.cpu().numpy()

@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/smoe.h declares, and refuses every out-of-contract argument with the
+documented status before it touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smoe.h")
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import group_quantized_moe_amd as gq
+    if not os.path.exists(gq.LIB_PATH):
+        from group_quantized_moe_amd import build
+        build.build()
+    gq.lib()
+    return gq
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert set(declared_functions()) == {
+        "smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
+        "matvec_bf16_workspace", "matvec_bf16", "smoe_status_str"}
+
+
+def test_library_exports_every_declared_symbol(gq):
+    L = ctypes.CDLL(gq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(gq.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(gq):
+    for s in range(0, -10, -1):
+        assert gq.smoe_status_str(s) not in ("", "unknown status")
+    assert gq.smoe_status_str(-99) == "unknown status"
+
+
+# Fake, well-aligned device addresses: every call below must be refused (or
+# reach the device check) before anything dereferences them.
+A = 0x10000000
+QM = lambda base: ctypes.byref(__import__("group_quantized_moe_amd").QMat(base, base + 0x1000000))
+
+
+def gate_up(L, bits=4, group=64, d_ff=512, d_model=256, x=A + 0x8000000, h=A + 0x9000000, g=A, u=A + 0x4000000):
+    import group_quantized_moe_amd as gq
+    return L.smoe_gate_up(ctypes.byref(gq.QMat(g, g + 0x1000000)), ctypes.byref(gq.QMat(u, u + 0x1000000)),
+                          bits, group, d_ff, d_model, x, h, None)
+
+
+def test_gate_up_refusals(gq):
+    L = gq.lib()
+    assert gate_up(L, bits=3) == -2
+    assert gate_up(L, bits=8) == -2
+    assert gate_up(L, group=48) == -3              # not a multiple of 32
+    assert gate_up(L, bits=2, group=32) == -3      # 2-bit needs multiples of 64
+    assert gate_up(L, group=512) == -3             # does not divide d_model = 256
+    assert gate_up(L, d_model=80) == -4            # not a multiple of 32
+    assert gate_up(L, d_ff=0) == -4
+    assert gate_up(L, d_model=32768) == -4         # above SMOE_MAX_QCOLS
+    assert gate_up(L, x=0) == -1
+    assert gate_up(L, g=A + 8) == -5               # codes not 16-byte aligned
+    assert gate_up(L, x=A + 0x8000004) == -5       # x not 16-byte aligned
+    assert gate_up(L, h=A + 0x100) == -7           # hidden inside the gate codes
+    assert gate_up(L, h=A + 0x8000000 + 512) == -7 # hidden inside x
+    assert gate_up(L) == -8                        # all valid: no gfx950 device here
+
+
+def test_down_and_bf16_refusals(gq):
+    L = gq.lib()
+    D = gq.QMat(A, A + 0x1000000)
+    assert L.smoe_down(ctypes.byref(D), 4, 64, 256, 512, A + 0x8000000, A + 0x8000000, None) == -7
+    assert L.smoe_down(ctypes.byref(D), 4, 64, 256, 500, A + 0x8000000, A + 0x9000000, None) == -4
+    assert L.smoe_down(ctypes.byref(D), 4, 64, 256, 512, A + 0x8000000, A + 0x9000000, None) == -8
+    assert L.matvec_bf16(A, 16, 12, A + 0x8000000, A + 0x9000000, None, 0, None) == -4
+    assert L.matvec_bf16(A + 2, 16, 16, A + 0x8000000, A + 0x9000000, None, 0, None) == -5
+    assert L.matvec_bf16(A, 16, 16, A + 0x8000000, A + 16, None, 0, None) == -7
+    assert L.matvec_bf16(A, 16, 16, A + 0x8000000, A + 0x9000000, None, 0, None) == -8
+    assert L.matvec_bf16_workspace(512, 4096) == 0
+
+
+def test_expert_ffn_refusals(gq):
+    L = gq.lib()
+    n = 2
+    arr = (gq.Expert * n)()
+    for k in range(n):
+        b = A + k * 0x10000000
+        arr[k] = gq.Expert(gq.QMat(b, b + 0x1000000), gq.QMat(b + 0x2000000, b + 0x3000000),
+                           gq.QMat(b + 0x4000000, b + 0x5000000))
+    X, OUT, WS = 0x80000000, 0x90000000, 0xA0000000
+    need = L.smoe_expert_ffn_workspace(n, 256, 512, 1)
+    assert need >= 4 * n * 512
+    call = lambda **kw: L.smoe_expert_ffn(
+        arr, kw.get("n", n), kw.get("route", None), 4, 64, 256, 512, kw.get("T", 1), X,
+        kw.get("out", OUT), kw.get("ws", WS), kw.get("wsb", need), None)
+    assert call(n=0) == -4
+    assert call(n=17) == -4
+    assert call(T=0) == -4
+    assert call(ws=0) == -6
+    assert call(wsb=need - 1) == -6
+    assert call(ws=WS + 64) == -5                  # workspace must be 256-byte aligned
+    assert call(out=WS + 256) == -7                # out inside the workspace
+    assert call(out=A + 0x100) == -7               # out inside expert 0's gate codes
+    assert call() == -8
