@@ -246,21 +246,27 @@ __global__ __launch_bounds__(512) void k_down(const DownArgs a)
     }
 
     // Several experts: publish this expert's weighted rows, then the last block
-    // of the row tile adds the experts in ascending order.
+    // of the row tile adds the experts in ascending order.  The partial rows
+    // are written and read with agent-scope atomic accesses, which go through
+    // to the device-wide point of coherence instead of staying in one XCD's
+    // L2, so no cache-wide write-back or invalidate is needed: each wave waits
+    // for its stores to complete before the barrier, and only then does one
+    // thread bump the tile's counter.
     for (int t = tid; t < RB; t += blockDim.x) {
         const int r = row0 + t;
         if (r < a.d_model) {
             float y = 0.0f;
             for (int w = 0; w < nw; ++w) y += red[w * RB + t];
-            a.partial[(size_t)e * a.d_model + r] = y * rw;
+            __hip_atomic_store(a.partial + (size_t)e * a.d_model + r, y * rw, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.counters[rb], 1) == E - 1;
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(&a.counters[rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == E - 1;
     __syncthreads();
     if (s_last) {
-        __threadfence();
         for (int t = tid; t < RB; t += blockDim.x) {
             const int r = row0 + t;
             if (r < a.d_model) {
