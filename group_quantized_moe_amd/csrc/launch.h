@@ -11,7 +11,7 @@ namespace smoe {
 // (16-byte pieces of a packed row) of one row are split into nw contiguous
 // slices, one per wave; within a wave, `lpr` lanes share a row and each lane
 // owns `nch` chunks of the slice, so 64/lpr rows are in flight per wave step;
-// `iter` steps are unrolled, so a block covers (64/lpr)*iter rows.
+// a tile is `iter` such steps, (64/lpr)*iter rows.
 struct MapConfig {
     int nw, lpr, nch, iter;
     int rows_per_block() const { return (64 / lpr) * iter; }
@@ -24,8 +24,8 @@ struct GateUpArgs {
     float *hidden;         // [n_experts][d_ff]
     int *counters;         // zeroed for a following combined down launch (may be null)
     int n_counters;
-    int d_model, d_ff, group;
-    int blocks_per_expert;
+    int d_model, d_ff, group, n_experts;
+    int blocks_per_expert; // row tiles per expert
 };
 
 struct DownArgs {
@@ -51,9 +51,10 @@ struct Bf16Args {
 bool choose_qmap(int bits, int chunks, int rows, int n_experts, MapConfig *cfg);
 bool choose_bf16map(int chunks, int rows, MapConfig *cfg);
 
-hipError_t launch_gate_up(int bits, const MapConfig &cfg, const GateUpArgs &a, int n_experts,
-                          hipStream_t stream);
-hipError_t launch_down(int bits, const MapConfig &cfg, const DownArgs &a, hipStream_t stream);
+// `cus` is the device's compute-unit count; the decode kernels size their
+// persistent grids from it.
+hipError_t launch_gate_up(int bits, const MapConfig &cfg, const GateUpArgs &a, int cus, hipStream_t stream);
+hipError_t launch_down(int bits, const MapConfig &cfg, const DownArgs &a, int cus, hipStream_t stream);
 hipError_t launch_matvec_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream_t stream);
 
 }  // namespace smoe

@@ -142,7 +142,8 @@ int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group
         return SMOE_ERR_ALIAS;
     MapConfig cfg;
     if (!smoe::choose_qmap(bits, d_model * bits / 128, d_ff, 1, &cfg)) return SMOE_ERR_SHAPE;
-    if ((rc = check_device(nullptr))) return rc;
+    DeviceInfo dev;
+    if ((rc = check_device(&dev))) return rc;
 
     smoe::GateUpArgs a{};
     a.gate[0] = {gate->codes, gate->scales};
@@ -154,8 +155,9 @@ int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;
+    a.n_experts = 1;
     a.blocks_per_expert = (d_ff + cfg.rows_per_block() - 1) / cfg.rows_per_block();
-    return launch_status(smoe::launch_gate_up(bits, cfg, a, 1, (hipStream_t)stream));
+    return launch_status(smoe::launch_gate_up(bits, cfg, a, dev.cus, (hipStream_t)stream));
 }
 
 int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff, const float *hidden,
@@ -172,7 +174,8 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
         return SMOE_ERR_ALIAS;
     MapConfig cfg;
     if (!smoe::choose_qmap(bits, d_ff * bits / 128, d_model, 1, &cfg)) return SMOE_ERR_SHAPE;
-    if ((rc = check_device(nullptr))) return rc;
+    DeviceInfo dev;
+    if ((rc = check_device(&dev))) return rc;
 
     smoe::DownArgs a{};
     a.down[0] = {down->codes, down->scales};
@@ -186,7 +189,7 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
     a.group = group;
     a.n_experts = 1;
     a.row_blocks = (d_model + cfg.rows_per_block() - 1) / cfg.rows_per_block();
-    return launch_status(smoe::launch_down(bits, cfg, a, (hipStream_t)stream));
+    return launch_status(smoe::launch_down(bits, cfg, a, dev.cus, (hipStream_t)stream));
 }
 
 size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
@@ -235,7 +238,8 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     MapConfig gu, dn;
     if (!smoe::choose_qmap(bits, d_model * bits / 128, d_ff, n_experts, &gu)) return SMOE_ERR_SHAPE;
     if (!smoe::choose_qmap(bits, d_ff * bits / 128, d_model, n_experts, &dn)) return SMOE_ERR_SHAPE;
-    if ((rc = check_device(nullptr))) return rc;
+    DeviceInfo dev;
+    if ((rc = check_device(&dev))) return rc;
 
     const DecodeWorkspace w = decode_workspace(n_experts, d_model, d_ff);
     char *ws = static_cast<char *>(workspace);
@@ -259,8 +263,9 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     g.d_model = d_model;
     g.d_ff = d_ff;
     g.group = group;
+    g.n_experts = n_experts;
     g.blocks_per_expert = (d_ff + gu.rows_per_block() - 1) / gu.rows_per_block();
-    if ((rc = launch_status(smoe::launch_gate_up(bits, gu, g, n_experts, st)))) return rc;
+    if ((rc = launch_status(smoe::launch_gate_up(bits, gu, g, dev.cus, st)))) return rc;
 
     d.hidden = hidden;
     d.route_w = route_w;
@@ -272,7 +277,7 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     d.group = group;
     d.n_experts = n_experts;
     d.row_blocks = row_blocks;
-    return launch_status(smoe::launch_down(bits, dn, d, st));
+    return launch_status(smoe::launch_down(bits, dn, d, dev.cus, st));
 }
 
 size_t matvec_bf16_workspace(int rows, int cols)
