@@ -49,14 +49,17 @@ __global__ __launch_bounds__(512) void k_matvec_bf16(const Bf16Args a)
         valid[k] = cs < sl && c[k] < cpr;
     }
 
+    // Loads are unconditional from clamped, in-bounds addresses (a divergent
+    // "load, else zero" would serialise them); lanes outside the matrix get a
+    // zero x slice below, and rows past the end are never stored.
     uint4 q[ITER][NCH];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int r = row0 + slot + RS * it;
+        const int rc = r < a.rows ? r : a.rows - 1;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
-            q[it][k] = (valid[k] && r < a.rows) ? load16(W + (size_t)r * row_bytes + (size_t)c[k] * 16)
-                                                : make_uint4(0, 0, 0, 0);
+            q[it][k] = load16(W + (size_t)rc * row_bytes + (size_t)(valid[k] ? c[k] : 0) * 16);
     }
 
     float xv[NCH][8];

@@ -7,36 +7,54 @@
 
 namespace smoe {
 
-// Lane mapping of one matvec launch.  A block has `nw` waves; the chunks
-// (16-byte pieces of a packed row) of one row are split into nw contiguous
-// slices, one per wave; within a wave, `lpr` lanes share a row and each lane
-// owns `nch` chunks of the slice, so 64/lpr rows are in flight per wave step;
-// a tile is `iter` such steps, (64/lpr)*iter rows.
+// ---------------------------------------------------------------------------
+// Decode (one token) launches of the quantised expert FFN
+// ---------------------------------------------------------------------------
+
+// Which passes a plan covers: gate_up only, down only, or both (the expert FFN).
+enum DecodeMode : int { kGateUpOnly = 0, kDownOnly = 1, kBoth = 2 };
+
+// Lane mapping of the decode launches.  A block has `nw` waves; every wave owns
+// whole rows: `lpr` lanes share a row and each owns `nch` of its 16-byte
+// chunks (lane lr owns chunks lr, lr + lpr, ...), so a wave covers 64/lpr
+// rows per step.  gate_up (cols = d_model) and down (cols = d_ff) each have
+// their own lpr / nch.
+struct DecodePlan {
+    int mode, nw;
+    int lpr_g, nch_g;
+    int lpr_d, nch_d;
+    int d_model, d_ff;
+};
+
+struct DecodeArgs {
+    QPtr gate[kMaxExperts];
+    QPtr up[kMaxExperts];
+    QPtr down[kMaxExperts];
+    const float *x;          // [d_model]
+    float *hidden;           // [n_experts][d_ff]
+    const float *route_w;    // [n_experts] or null (weight 1)
+    float *out;              // [d_model]
+    unsigned long long *row_acc;  // [d_model] exact expert sums, zero on entry and exit (n_experts > 1)
+    int d_model, d_ff, group, n_experts;
+    int lpr_g, lpr_d;
+    int dn_rows_per_wave;    // set by the down launcher
+};
+
+bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, DecodePlan *plan);
+// `cus` is the device's compute-unit count; the persistent grids are sized from it.
+hipError_t launch_gate_up(int bits, const DecodePlan &plan, const DecodeArgs &args, int cus, hipStream_t stream);
+hipError_t launch_down(int bits, const DecodePlan &plan, const DecodeArgs &args, int cus, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Dense bf16 matvec
+// ---------------------------------------------------------------------------
+
+// Lane mapping of a bf16 matvec launch: nw waves split a row's chunks into
+// slices, lpr lanes share a row, each lane owns nch chunks; a block covers
+// (64/lpr)*iter rows.
 struct MapConfig {
     int nw, lpr, nch, iter;
     int rows_per_block() const { return (64 / lpr) * iter; }
-};
-
-struct GateUpArgs {
-    QPtr gate[kMaxExperts];
-    QPtr up[kMaxExperts];
-    const float *x;        // [d_model]
-    float *hidden;         // [n_experts][d_ff]
-    int *counters;         // zeroed for a following combined down launch (may be null)
-    int n_counters;
-    int d_model, d_ff, group, n_experts;
-    int blocks_per_expert; // row tiles per expert
-};
-
-struct DownArgs {
-    QPtr down[kMaxExperts];
-    const float *hidden;   // [n_experts][d_ff]
-    const float *route_w;  // [n_experts] or null (weight 1)
-    float *out;            // [d_model]
-    float *partial;        // [n_experts][d_model], when n_experts > 1
-    int *counters;         // [row_blocks], zero on entry, when n_experts > 1
-    int d_model, d_ff, group, n_experts;
-    int row_blocks;
 };
 
 struct Bf16Args {
@@ -46,15 +64,7 @@ struct Bf16Args {
     int rows, cols;
 };
 
-// Picks a lane mapping for rows of `chunks` 16-byte chunks; returns false when
-// no supported mapping covers the row.
-bool choose_qmap(int bits, int chunks, int rows, int n_experts, MapConfig *cfg);
 bool choose_bf16map(int chunks, int rows, MapConfig *cfg);
-
-// `cus` is the device's compute-unit count; the decode kernels size their
-// persistent grids from it.
-hipError_t launch_gate_up(int bits, const MapConfig &cfg, const GateUpArgs &a, int cus, hipStream_t stream);
-hipError_t launch_down(int bits, const MapConfig &cfg, const DownArgs &a, int cus, hipStream_t stream);
 hipError_t launch_matvec_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream_t stream);
 
 }  // namespace smoe

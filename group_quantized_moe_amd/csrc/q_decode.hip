@@ -44,6 +44,7 @@
 //    tile (an agent-scope counter) adds the experts in ascending order.
 #include "launch.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <map>
@@ -109,40 +110,72 @@ __device__ __forceinline__ int make_planes(const float *v, int k, uint32_t *word
     return sum;
 }
 
-// Block-wide: digit planes of a vector of n columns into LDS.
-//   cmax   : [n / cols_per_chunk] largest |v| per chunk
-//   dwsum  : [n / cols_per_dw]    sum of X per code dword
-//   planes : [n / cols_per_dw][words_per_dw]
-template <int BITS>
-__device__ void build_planes(const float *vec, int n, uint32_t *planes, float *cmax, int *dwsum)
+// The input vector of a block, one code dword's worth of columns (8 at 4 bits,
+// 16 at 2 bits) per thread and group slot: thread t holds dword groups
+// t, t + blockDim, ...  Loaded straight into registers at kernel start,
+// before any code load is issued, so that waiting for it never waits for the
+// (much slower) stream of code loads behind it.
+template <int BITS, int GPT>
+struct VecRegs {
+    float v[GPT][DigitLayout<BITS>::kColsPerDw];
+    bool ok[GPT];
+};
+
+template <int BITS, int GPT>
+__device__ __forceinline__ void load_vec_regs(const float *vec, int n, VecRegs<BITS, GPT> &r)
 {
     using DL = DigitLayout<BITS>;
-    constexpr int kColsPerChunk = 4 * DL::kColsPerDw;
-    const int nch = n / kColsPerChunk, ndw = n / DL::kColsPerDw;
-    for (int c = threadIdx.x; c < nch; c += blockDim.x) {
-        const float4 *src = reinterpret_cast<const float4 *>(vec + (size_t)c * kColsPerChunk);
-        float m = 0.0f;
+    const int ndw = n / DL::kColsPerDw;
 #pragma unroll
-        for (int i = 0; i < kColsPerChunk / 4; ++i) {
-            const float4 t = src[i];
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))));
-        }
-        cmax[c] = m;
-    }
-    __syncthreads();
-    for (int q = threadIdx.x; q < ndw; q += blockDim.x) {
-        const int k = chunk_shift(cmax[q >> 2]);
-        float v[DL::kColsPerDw];
-        const float4 *src = reinterpret_cast<const float4 *>(vec + (size_t)q * DL::kColsPerDw);
+    for (int g = 0; g < GPT; ++g) {
+        const int q = threadIdx.x + g * blockDim.x;
+        r.ok[g] = q < ndw;
+        const float4 *src = reinterpret_cast<const float4 *>(vec + (size_t)(q < ndw ? q : ndw - 1) * DL::kColsPerDw);
 #pragma unroll
         for (int i = 0; i < DL::kColsPerDw / 4; ++i) {
             const float4 t = src[i];
-            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+            r.v[g][4 * i] = t.x; r.v[g][4 * i + 1] = t.y; r.v[g][4 * i + 2] = t.z; r.v[g][4 * i + 3] = t.w;
         }
-        uint32_t w[DL::kWordsPerDw];
-        dwsum[q] = make_planes<BITS>(v, k, w);
+    }
+}
+
+// Largest value over the 4 lanes of an aligned quad (every lane gets it).
+__device__ __forceinline__ float quad_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));  // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));  // quad_perm [2,3,0,1]
+    return v;
+}
+
+// Block-wide: digit planes of the vector held in VecRegs, into LDS.  The four
+// code dwords of a chunk belong to four consecutive threads of one wave, so the
+// chunk's largest |v| is a quad reduction and one barrier suffices.
+//   cmax   : [chunks] largest |v| per chunk
+//   dwsum  : [ndw]    sum of X per code dword
+//   planes : word w of chunk c at ((w / 4) * chunks + c) * 4 + w % 4, so that
+//            consecutive lanes reading consecutive chunks with 16-byte loads hit
+//            consecutive LDS addresses (no bank conflicts).
+template <int BITS, int GPT>
+__device__ void build_planes(const VecRegs<BITS, GPT> &r, int chunks, uint32_t *planes, float *cmax, int *dwsum)
+{
+    using DL = DigitLayout<BITS>;
 #pragma unroll
-        for (int i = 0; i < DL::kWordsPerDw; ++i) planes[(size_t)q * DL::kWordsPerDw + i] = w[i];
+    for (int g = 0; g < GPT; ++g) {
+        const int q = threadIdx.x + g * blockDim.x;
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DL::kColsPerDw; ++i) m = fmaxf(m, fabsf(r.v[g][i]));
+        m = quad_max(m);  // blockDim and the group stride are multiples of 4
+        if (!r.ok[g]) continue;
+        const int c = q >> 2, dw = q & 3;
+        if (dw == 0) cmax[c] = m;
+        uint32_t w[DL::kWordsPerDw];
+        dwsum[q] = make_planes<BITS>(r.v[g], chunk_shift(m), w);
+#pragma unroll
+        for (int i = 0; i < DL::kWordsPerDw; ++i) {
+            const int word = dw * DL::kWordsPerDw + i;
+            planes[((size_t)(word >> 2) * chunks + c) * 4 + (word & 3)] = w[i];
+        }
     }
     __syncthreads();
 }
@@ -156,17 +189,16 @@ struct ChunkVec {
 };
 
 template <int BITS>
-__device__ __forceinline__ void load_chunk_vec(const uint32_t *planes, const float *cmax,
-                                               const int *dwsum, int c, bool valid, ChunkVec<BITS> &cv)
+__device__ __forceinline__ void load_chunk_vec(const uint32_t *planes, const float *cmax, const int *dwsum,
+                                               int chunks, int c, bool valid, ChunkVec<BITS> &cv)
 {
     // Branch-free: an invalid chunk reads chunk 0 and is zeroed by selects (an
     // early return here makes the compiler spill the struct to scratch).
     using DL = DigitLayout<BITS>;
     const int cc = valid ? c : 0;
-    const uint4 *src = reinterpret_cast<const uint4 *>(planes + (size_t)cc * DL::kWordsPerChunk);
 #pragma unroll
     for (int i = 0; i < DL::kWordsPerChunk / 4; ++i) {
-        const uint4 t = src[i];
+        const uint4 t = *reinterpret_cast<const uint4 *>(planes + ((size_t)i * chunks + cc) * 4);
         cv.w[4 * i] = valid ? t.x : 0u;
         cv.w[4 * i + 1] = valid ? t.y : 0u;
         cv.w[4 * i + 2] = valid ? t.z : 0u;
@@ -220,290 +252,316 @@ __device__ __forceinline__ float chunk_contrib(const uint4 q, float s, const Chu
     return s * fmaf((float)chunk_idot<BITS>(q, cv), cv.alpha, cv.beta);
 }
 
-// Lane -> chunk mapping shared by both kernels.
-template <int LPR, int NCH>
-struct LaneMap {
-    int lr, slot, c[NCH];
+// Lane -> chunk mapping of a wave that owns whole rows: lpr lanes (a power of
+// two, 8..64, uniform over the launch) share a row, so a wave covers 64/lpr rows
+// per step; lane lr owns chunks lr, lr + lpr, ..., lr + (NCH-1)*lpr.
+template <int NCH>
+struct RowLanes {
+    int lr, slot, rs, c[NCH];
     bool valid[NCH];
-    __device__ __forceinline__ explicit LaneMap(int cpr)
+    __device__ __forceinline__ RowLanes(int cpr, int lpr)
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-        const int sl = (cpr + nw - 1) / nw;
-        lr = lane % LPR;
-        slot = lane / LPR;
+        const int lane = threadIdx.x & 63;
+        const int sh = __builtin_ctz(lpr);
+        lr = lane & (lpr - 1);
+        slot = lane >> sh;
+        rs = 64 >> sh;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const int cs = lr + LPR * k;
-            c[k] = wave * sl + cs;
-            valid[k] = cs < sl && c[k] < cpr;
+            c[k] = lr + lpr * k;
+            valid[k] = c[k] < cpr;
         }
     }
 };
 
-// Code and scale registers of one tile of ITER row steps for M matrices.
-template <int ITER, int NCH, int M>
-struct TileRegs {
-    uint4 q[ITER][NCH][M];
-    float s[ITER][NCH][M];
+// Sum over aligned groups of lpr lanes (lpr uniform): DPP inside 16-lane rows,
+// lane shuffles across rows.
+__device__ __forceinline__ float lane_group_sum_rt(float v, int lpr)
+{
+    if (lpr >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (lpr >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (lpr >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if (lpr >= 16) v += dpp<0x140>(v);  // row_mirror
+    if (lpr >= 32) v += __shfl_xor(v, 16);
+    if (lpr >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Code and scale registers of one wave step (one row per lane group) for M
+// matrices.  Loads are issued unconditionally from clamped, always in-bounds
+// addresses; `ok` marks the lanes whose load is real, and the scale of any
+// other lane is replaced by zero when the step is computed.  (A divergent
+// "load, else zero the registers" would make the compiler wait for the load
+// before the zeroing write, which serialises the prefetch.)
+template <int NCH, int M>
+struct StepRegs {
+    uint4 q[NCH][M];
+    float s[NCH][M];
+    bool ok[NCH];
 };
 
-// Dynamic LDS of both kernels:
-//   red    f32 [2][nw][RB][M]   cross-wave partial rows, double-buffered by tile
-//   cmax   f32 [nch4]           nch4 = chunks per row rounded up to 4
+// Dynamic LDS: the input vector's digit planes,
+//   cmax   f32 [chunks4]        chunks rounded up to 4
 //   dwsum  i32 [ndw]            ndw = code dwords per row = 4 * chunks
-//   planes u32 [ndw][words_per_dw]
+//   planes u32 [ndw * words_per_dw]
 template <int BITS>
-__host__ __device__ size_t smem_bytes(int nw, int rb, int m, int cols)
+__host__ __device__ size_t plane_lds_bytes(int cols)
 {
     const size_t ndw = (size_t)cols / DigitLayout<BITS>::kColsPerDw;
-    const size_t nch4 = ((ndw / 4) + 3) & ~size_t(3);
-    return sizeof(float) * (2 * (size_t)nw * rb * m) + sizeof(float) * nch4 + sizeof(int) * ndw +
-           sizeof(uint32_t) * ndw * DigitLayout<BITS>::kWordsPerDw;
+    const size_t chunks4 = ((ndw / 4) + 3) & ~size_t(3);
+    return sizeof(float) * chunks4 + sizeof(int) * ndw + sizeof(uint32_t) * ndw * DigitLayout<BITS>::kWordsPerDw;
 }
 
 template <int BITS>
-struct SmemView {
-    float *red;
+struct PlaneLds {
     float *cmax;
     int *dwsum;
     uint32_t *planes;
-    __device__ SmemView(unsigned char *base, int nw, int rb, int m, int cols)
+    int chunks;
+    __device__ PlaneLds(unsigned char *base, int cols)
     {
         const size_t ndw = (size_t)cols / DigitLayout<BITS>::kColsPerDw;
-        const size_t nch4 = ((ndw / 4) + 3) & ~size_t(3);
-        red = reinterpret_cast<float *>(base);
-        cmax = red + 2 * (size_t)nw * rb * m;
-        dwsum = reinterpret_cast<int *>(cmax + nch4);
+        const size_t chunks4 = ((ndw / 4) + 3) & ~size_t(3);
+        chunks = (int)(ndw / 4);
+        cmax = reinterpret_cast<float *>(base);
+        dwsum = reinterpret_cast<int *>(cmax + chunks4);
         planes = reinterpret_cast<uint32_t *>(dwsum + ndw);
     }
 };
 
-template <int BITS, int LPR, int NCH, int ITER>
-__global__ __launch_bounds__(512) void k_gate_up(const GateUpArgs a)
+// Code dwords of a vector of up to kMaxQCols columns per thread of a 512-thread block.
+constexpr int kBlockThreads = 512;
+constexpr int kMaxQCols = 8192;
+template <int BITS>
+constexpr int kGroupsPerThread = (kMaxQCols / DigitLayout<BITS>::kColsPerDw + kBlockThreads - 1) / kBlockThreads;
+
+// gate_up: hidden[e][i] = SiLU(G_e x)[i] * (U_e x)[i] for every expert.
+//
+// Blocks are persistent; each block builds the digit planes of x in LDS once,
+// every lane copies the planes of its chunks into registers, and from then on
+// each wave streams whole rows on its own: no LDS and no barrier in the row
+// loop, the codes and scales of the next step are in flight while a step is
+// reduced.  Wave steps are numbered expert by expert; global wave w takes steps
+// w, w + W, w + 2W, ... of the E * ceil(d_ff / rs) steps.
+template <int BITS, int NCH>
+__global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
-    constexpr int RS = 64 / LPR;
-    constexpr int RB = RS * ITER;
     extern __shared__ __align__(16) unsigned char smem[];
-
-    const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int nw = blockDim.x >> 6;
     const int cpr = a.d_model / CPC;
-    const SmemView<BITS> sm(smem, nw, RB, 2, a.d_model);
+    const RowLanes<NCH> rl(cpr, a.lpr_g);
+    const PlaneLds<BITS> lds(smem, a.d_model);
     const size_t row_bytes = (size_t)a.d_model * BITS / 8;
     const int gpr = a.d_model / a.group;
-    const int ntiles = a.n_experts * a.blocks_per_expert;
-    const LaneMap<LPR, NCH> lm(cpr);
+    const int spe = (a.d_ff + rl.rs - 1) / rl.rs;  // wave steps per expert
+    const int nsteps = a.n_experts * spe;
+    const int W = gridDim.x * nw;
     int gi[NCH];
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) gi[k] = lm.valid[k] ? lm.c[k] * CPC / a.group : 0;
+    for (int k = 0; k < NCH; ++k) gi[k] = rl.valid[k] ? rl.c[k] * CPC / a.group : 0;
 
-    if (blockIdx.x == 0)
-        for (int i = tid; i < a.n_counters; i += blockDim.x) a.counters[i] = 0;
-
-    auto load_tile = [&](TileRegs<ITER, NCH, 2> &t, int tile) {
-        const int e = tile / a.blocks_per_expert;
-        const int row0 = (tile - e * a.blocks_per_expert) * RB;
+    auto load_step = [&](StepRegs<NCH, 2> &t, int step) {
+        const int e = step / spe;
+        const int r = (step - e * spe) * rl.rs + rl.slot;
+        const int rc = r < a.d_ff ? r : a.d_ff - 1;
         const QPtr G = a.gate[e], U = a.up[e];
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            const int r = row0 + lm.slot + RS * it;
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                if (lm.valid[k] && r < a.d_ff) {
-                    const size_t off = (size_t)r * row_bytes + (size_t)lm.c[k] * 16;
-                    t.q[it][k][0] = load16(G.codes + off);
-                    t.q[it][k][1] = load16(U.codes + off);
-                    t.s[it][k][0] = G.scales[(size_t)r * gpr + gi[k]];
-                    t.s[it][k][1] = U.scales[(size_t)r * gpr + gi[k]];
-                } else {
-                    t.q[it][k][0] = t.q[it][k][1] = make_uint4(0, 0, 0, 0);
-                    t.s[it][k][0] = t.s[it][k][1] = 0.0f;
-                }
-            }
+        for (int k = 0; k < NCH; ++k) {
+            const int cc = rl.valid[k] ? rl.c[k] : 0;
+            const size_t off = (size_t)rc * row_bytes + (size_t)cc * 16;
+            t.q[k][0] = load16(G.codes + off);
+            t.q[k][1] = load16(U.codes + off);
+            t.s[k][0] = G.scales[(size_t)rc * gpr + gi[k]];
+            t.s[k][1] = U.scales[(size_t)rc * gpr + gi[k]];
+            t.ok[k] = rl.valid[k] && r < a.d_ff;
         }
     };
 
-    int tile = blockIdx.x;
-    TileRegs<ITER, NCH, 2> A, B;
-    if (tile < ntiles) load_tile(A, tile);
+    // Order of the prologue: the input vector's loads, then the first two steps'
+    // code loads, then the digit planes (which wait only for the vector).  The
+    // wave index is made explicitly scalar, so that the step, the expert and the
+    // expert's matrix pointers live in SGPRs (scalar loads from the kernel
+    // arguments) rather than behind a vector load in front of every step.
+    VecRegs<BITS, kGroupsPerThread<BITS>> xr;
+    load_vec_regs<BITS>(a.x, a.d_model, xr);
+    int step = blockIdx.x * nw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    StepRegs<NCH, 2> A, B;
+    if (step < nsteps) load_step(A, step);
+    if (step + W < nsteps) load_step(B, step + W);
 
-    build_planes<BITS>(a.x, a.d_model, sm.planes, sm.cmax, sm.dwsum);
+    build_planes<BITS>(xr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k)
-        load_chunk_vec<BITS>(sm.planes, sm.cmax, sm.dwsum, lm.c[k], lm.valid[k], cv[k]);
+        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, rl.c[k], rl.valid[k], cv[k]);
 
-    auto compute_tile = [&](const TileRegs<ITER, NCH, 2> &t, int tile, int buf) {
-        float *rb = sm.red + buf * (nw * RB * 2);
+    auto compute_step = [&](const StepRegs<NCH, 2> &t, int step) {
+        float g = 0.0f, u = 0.0f;
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            float pg = 0.0f, pu = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                pg += chunk_contrib<BITS>(t.q[it][k][0], t.s[it][k][0], cv[k]);
-                pu += chunk_contrib<BITS>(t.q[it][k][1], t.s[it][k][1], cv[k]);
-            }
-            pg = lane_group_sum<LPR>(pg);
-            pu = lane_group_sum<LPR>(pu);
-            if (lm.lr == 0) {
-                const int i = wave * RB + lm.slot + RS * it;
-                rb[2 * i] = pg;
-                rb[2 * i + 1] = pu;
-            }
+        for (int k = 0; k < NCH; ++k) {
+            g += chunk_contrib<BITS>(t.q[k][0], t.ok[k] ? t.s[k][0] : 0.0f, cv[k]);
+            u += chunk_contrib<BITS>(t.q[k][1], t.ok[k] ? t.s[k][1] : 0.0f, cv[k]);
         }
-        __syncthreads();
-        const int e = tile / a.blocks_per_expert;
-        const int row0 = (tile - e * a.blocks_per_expert) * RB;
-        for (int i = tid; i < RB; i += blockDim.x) {
-            const int r = row0 + i;
-            if (r < a.d_ff) {
-                float g = 0.0f, u = 0.0f;
-                for (int w = 0; w < nw; ++w) {
-                    g += rb[2 * (w * RB + i)];
-                    u += rb[2 * (w * RB + i) + 1];
-                }
-                a.hidden[(size_t)e * a.d_ff + r] = silu(g) * u;
-            }
-        }
+        g = lane_group_sum_rt(g, a.lpr_g);
+        u = lane_group_sum_rt(u, a.lpr_g);
+        const int e = step / spe;
+        const int r = (step - e * spe) * rl.rs + rl.slot;
+        if (rl.lr == 0 && r < a.d_ff) a.hidden[(size_t)e * a.d_ff + r] = silu(g) * u;
     };
 
-    // Two-stage pipeline: the next tile's loads are in flight while this one is
-    // reduced.  The partial-row buffer alternates, so one barrier per tile
-    // suffices (a buffer is rewritten only after the following tile's barrier).
-    while (tile < ntiles) {
-        const int t1 = tile + gridDim.x;
-        if (t1 < ntiles) load_tile(B, t1);
-        compute_tile(A, tile, 0);
-        if (t1 >= ntiles) break;
-        const int t2 = t1 + gridDim.x;
-        if (t2 < ntiles) load_tile(A, t2);
-        compute_tile(B, t1, 1);
-        tile = t2;
+    while (step < nsteps) {
+        const int s1 = step + W;
+        compute_step(A, step);
+        if (s1 >= nsteps) break;
+        const int s2 = s1 + W;
+        if (s2 < nsteps) load_step(A, s2);
+        compute_step(B, s1);
+        const int s3 = s2 + W;
+        if (s3 < nsteps) load_step(B, s3);
+        step = s2;
     }
 }
 
-template <int BITS, int LPR, int NCH, int ITER>
-__global__ __launch_bounds__(512) void k_down(const DownArgs a)
+// down: out = sum_e r_e * (D_e hidden_e).
+//
+// Blocks are bound to one expert (block b serves expert b % E) and build that
+// expert's hidden digit planes in LDS once; waves then stream whole rows on
+// their own as in gate_up.  With one expert the rows go straight to out.  With
+// several, the experts' router-weighted rows are summed exactly: each
+// contribution is rounded to a multiple of 2^-32 (an error of at most 2^-33 per
+// term, far below f32 resolution for outputs of order one, and at most
+// E * 2^-33 in absolute terms) and added as a 64-bit integer to a per-row
+// accumulator whose top five bits count the experts in.  Integer addition is
+// associative, so the sum does not depend on the order in which experts
+// arrive: the result is bitwise reproducible.  The expert whose addition
+// completes the count converts the exact sum to f32 once, writes out, and
+// re-zeroes the accumulator for the next call.  One atomic per row and
+// expert, deferred to the end of the wave, is the only cross-block traffic.
+// A contribution of magnitude 2^20 or more does not fit the accumulator; it is
+// added as a NaN marker so that the row comes out NaN rather than wrong.
+constexpr int kAccFracBits = 32;
+constexpr int kAccCountShift = 59;
+constexpr unsigned long long kAccBias = 1ull << 52;    // keeps every term non-negative
+constexpr unsigned long long kAccNan = 1ull << 58;     // set in the sum when a term overflowed
+
+__device__ __forceinline__ unsigned long long acc_term(float v)
+{
+    const double t = (double)v * 4294967296.0;  // v * 2^32
+    if (!(fabs(t) < 4503599627370496.0))        // |v| < 2^20 (also false for NaN)
+        return (1ull << kAccCountShift) | kAccNan;
+    return (1ull << kAccCountShift) + kAccBias + (unsigned long long)(long long)__builtin_rint(t);
+}
+
+__device__ __forceinline__ float acc_value(unsigned long long sum, int n)
+{
+    if (sum & kAccNan) return __builtin_nanf("");
+    const unsigned long long mag = sum & ((1ull << kAccCountShift) - 1);
+    const long long fixed = (long long)(mag - (unsigned long long)n * kAccBias);
+    return (float)((double)fixed * (1.0 / 4294967296.0));
+}
+
+template <int BITS, int NCH>
+__global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
-    constexpr int RS = 64 / LPR;
-    constexpr int RB = RS * ITER;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_last;
-
-    const int tid = threadIdx.x, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
     const int E = a.n_experts;
     const int cpr = a.d_ff / CPC;
-    const SmemView<BITS> sm(smem, nw, RB, 1, a.d_ff);
-
-    // Blocks are bound to one expert: block b serves expert b % E and walks that
-    // expert's row tiles with a stride of gridDim.x / E.
-    const int e = blockIdx.x % E;
-    const int bpe = gridDim.x / E;
+    const RowLanes<NCH> rl(cpr, a.lpr_d);
+    const PlaneLds<BITS> lds(smem, a.d_ff);
     const size_t row_bytes = (size_t)a.d_ff * BITS / 8;
     const int gpr = a.d_ff / a.group;
+    const int e = blockIdx.x % E;
+    const int bpe = gridDim.x / E;                 // blocks per expert
+    const int We = bpe * nw;                       // waves per expert
+    const int nsteps = (a.d_model + rl.rs - 1) / rl.rs;
+    const int w0 = (blockIdx.x / E) * nw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const QPtr D = a.down[e];
     const float rw = a.route_w ? a.route_w[e] : 1.0f;
-    const LaneMap<LPR, NCH> lm(cpr);
+    // This wave's router-weighted rows, kept until the deferred combine.
+    float *mine = reinterpret_cast<float *>(smem + plane_lds_bytes<BITS>(a.d_ff)) +
+                  (threadIdx.x >> 6) * a.dn_rows_per_wave;
     int gi[NCH];
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) gi[k] = lm.valid[k] ? lm.c[k] * CPC / a.group : 0;
+    for (int k = 0; k < NCH; ++k) gi[k] = rl.valid[k] ? rl.c[k] * CPC / a.group : 0;
 
-    auto load_tile = [&](TileRegs<ITER, NCH, 1> &t, int rb) {
-        const int row0 = rb * RB;
+    auto load_step = [&](StepRegs<NCH, 1> &t, int step) {
+        const int r = step * rl.rs + rl.slot;
+        const int rc = r < a.d_model ? r : a.d_model - 1;
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            const int r = row0 + lm.slot + RS * it;
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                if (lm.valid[k] && r < a.d_model) {
-                    t.q[it][k][0] = load16(D.codes + (size_t)r * row_bytes + (size_t)lm.c[k] * 16);
-                    t.s[it][k][0] = D.scales[(size_t)r * gpr + gi[k]];
-                } else {
-                    t.q[it][k][0] = make_uint4(0, 0, 0, 0);
-                    t.s[it][k][0] = 0.0f;
-                }
-            }
+        for (int k = 0; k < NCH; ++k) {
+            const int cc = rl.valid[k] ? rl.c[k] : 0;
+            t.q[k][0] = load16(D.codes + (size_t)rc * row_bytes + (size_t)cc * 16);
+            t.s[k][0] = D.scales[(size_t)rc * gpr + gi[k]];
+            t.ok[k] = rl.valid[k] && r < a.d_model;
         }
     };
 
-    int rb = blockIdx.x / E;
-    TileRegs<ITER, NCH, 1> A, B;
-    if (rb < a.row_blocks) load_tile(A, rb);
+    if ((int)blockIdx.x >= bpe * E) return;  // whole block idle: no barrier follows for it
+    VecRegs<BITS, kGroupsPerThread<BITS>> hr;
+    load_vec_regs<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, hr);
+    int step = w0;
+    StepRegs<NCH, 1> A, B;
+    if (step < nsteps) load_step(A, step);
+    if (step + We < nsteps) load_step(B, step + We);
 
-    build_planes<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, sm.planes, sm.cmax, sm.dwsum);
+    build_planes<BITS>(hr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k)
-        load_chunk_vec<BITS>(sm.planes, sm.cmax, sm.dwsum, lm.c[k], lm.valid[k], cv[k]);
+        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, rl.c[k], rl.valid[k], cv[k]);
 
-    auto compute_tile = [&](const TileRegs<ITER, NCH, 1> &t, int rb, int buf) {
-        float *rbuf = sm.red + buf * (nw * RB);
+    auto compute_step = [&](const StepRegs<NCH, 1> &t, int step) {
+        float y = 0.0f;
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            float py = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) py += chunk_contrib<BITS>(t.q[it][k][0], t.s[it][k][0], cv[k]);
-            py = lane_group_sum<LPR>(py);
-            if (lm.lr == 0) rbuf[wave * RB + lm.slot + RS * it] = py;
-        }
-        __syncthreads();
-        const int row0 = rb * RB;
-        if (E == 1) {
-            for (int i = tid; i < RB; i += blockDim.x) {
-                const int r = row0 + i;
-                if (r < a.d_model) {
-                    float y = 0.0f;
-                    for (int w = 0; w < nw; ++w) y += rbuf[w * RB + i];
-                    a.out[r] = y * rw;
-                }
-            }
-            return;
-        }
-        // Publish this expert's weighted rows with agent-scope stores (they go
-        // through to the device-wide point of coherence, so no cache-wide
-        // write-back is needed), wait for them, then count the expert in; the
-        // last expert of the tile adds all experts in ascending order, reading
-        // with agent-scope loads.
-        for (int i = tid; i < RB; i += blockDim.x) {
-            const int r = row0 + i;
-            if (r < a.d_model) {
-                float y = 0.0f;
-                for (int w = 0; w < nw; ++w) y += rbuf[w * RB + i];
-                __hip_atomic_store(a.partial + (size_t)e * a.d_model + r, y * rw, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0)
-            s_last = __hip_atomic_fetch_add(&a.counters[rb], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) == E - 1;
-        __syncthreads();
-        if (s_last) {
-            for (int i = tid; i < RB; i += blockDim.x) {
-                const int r = row0 + i;
-                if (r < a.d_model) {
-                    float acc = 0.0f;
-                    for (int x = 0; x < E; ++x)
-                        acc += __hip_atomic_load(a.partial + (size_t)x * a.d_model + r, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                    a.out[r] = acc;
-                }
-            }
-            if (tid == 0) a.counters[rb] = 0;
+        for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][0], t.ok[k] ? t.s[k][0] : 0.0f, cv[k]);
+        y = lane_group_sum_rt(y, a.lpr_d);
+        const int r = step * rl.rs + rl.slot;
+        if (rl.lr == 0 && r < a.d_model) {
+            if (E == 1)
+                a.out[r] = y * rw;
+            else
+                mine[((step - w0) / We) * rl.rs + rl.slot] = y * rw;
         }
     };
 
-    while (rb < a.row_blocks) {
-        const int r1 = rb + bpe;
-        if (r1 < a.row_blocks) load_tile(B, r1);
-        compute_tile(A, rb, 0);
-        if (r1 >= a.row_blocks) break;
-        const int r2 = r1 + bpe;
-        if (r2 < a.row_blocks) load_tile(A, r2);
-        compute_tile(B, r1, 1);
-        rb = r2;
+    while (step < nsteps) {
+        const int s1 = step + We;
+        compute_step(A, step);
+        if (s1 >= nsteps) break;
+        const int s2 = s1 + We;
+        if (s2 < nsteps) load_step(A, s2);
+        compute_step(B, s1);
+        const int s3 = s2 + We;
+        if (s3 < nsteps) load_step(B, s3);
+        step = s2;
+    }
+
+    if (E > 1) {
+        // One 64-bit addition per row of this wave, all rows at once (lane j
+        // takes the wave's j-th row); the lane that completes a row writes it.
+        // The rows were stored to LDS by lanes of this same wave, whose LDS
+        // accesses complete in order.
+        __builtin_amdgcn_wave_barrier();
+        const int my_steps = w0 < nsteps ? (nsteps - 1 - w0) / We + 1 : 0;
+        const int my_rows = my_steps * rl.rs;
+        for (int j0 = 0; j0 < my_rows; j0 += 64) {
+            const int j = j0 + lane;
+            if (j < my_rows) {
+                const int r = (w0 + (j / rl.rs) * We) * rl.rs + (j % rl.rs);
+                if (r < a.d_model) {
+                    const unsigned long long term = acc_term(mine[j]);
+                    const unsigned long long sum =
+                        __hip_atomic_fetch_add(a.row_acc + r, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + term;
+                    if ((int)(sum >> kAccCountShift) == E) {
+                        a.out[r] = acc_value(sum, E);
+                        __hip_atomic_store(a.row_acc + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -518,117 +576,97 @@ int blocks_per_cu(const void *fn, int block, size_t lds)
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block, lds) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block, lds) != hipSuccess || n < 1) n = 0;
     cache[key] = n;
     return n;
 }
 
-// Fewest rounds over the resident capacity, with the tiles spread evenly.
-long balanced_grid(long tiles, long capacity)
+template <int BITS, int NCH>
+hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-    if (capacity < 1) capacity = 1;
-    const long rounds = (tiles + capacity - 1) / capacity;
-    return (tiles + rounds - 1) / rounds;
-}
-
-template <int BITS, int LPR, int NCH, int ITER>
-hipError_t run_gate_up(const MapConfig &cfg, const GateUpArgs &a, int cus, hipStream_t st)
-{
-    constexpr int RB = (64 / LPR) * ITER;
-    const int block = 64 * cfg.nw;
-    const size_t lds = smem_bytes<BITS>(cfg.nw, RB, 2, a.d_model);
-    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, LPR, NCH, ITER>);
-    const long tiles = (long)a.n_experts * a.blocks_per_expert;
-    const long grid = balanced_grid(tiles, (long)cus * blocks_per_cu(fn, block, lds));
-    hipLaunchKernelGGL((k_gate_up<BITS, LPR, NCH, ITER>), dim3((unsigned)grid), dim3(block), lds, st, a);
-    return hipGetLastError();
-}
-
-template <int BITS, int LPR, int NCH, int ITER>
-hipError_t run_down(const MapConfig &cfg, const DownArgs &a, int cus, hipStream_t st)
-{
-    constexpr int RB = (64 / LPR) * ITER;
-    const int block = 64 * cfg.nw;
-    const size_t lds = smem_bytes<BITS>(cfg.nw, RB, 1, a.d_ff);
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, LPR, NCH, ITER>);
+    const int block = 64 * p.nw;
+    const size_t lds = plane_lds_bytes<BITS>(a.d_model);
+    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH>);
     const long cap = (long)cus * blocks_per_cu(fn, block, lds);
-    const long per_expert = balanced_grid(a.row_blocks, cap / a.n_experts > 0 ? cap / a.n_experts : 1);
-    hipLaunchKernelGGL((k_down<BITS, LPR, NCH, ITER>), dim3((unsigned)(per_expert * a.n_experts)),
-                       dim3(block), lds, st, a);
+    if (cap < 1) return hipErrorInvalidConfiguration;
+    const long steps = (long)a.n_experts * ((a.d_ff + 64 / p.lpr_g - 1) / (64 / p.lpr_g));
+    const long grid = std::max(1L, std::min(cap, (steps + p.nw - 1) / p.nw));
+    hipLaunchKernelGGL((k_gate_up<BITS, NCH>), dim3((unsigned)grid), dim3(block), lds, st, a);
     return hipGetLastError();
+}
+
+template <int BITS, int NCH>
+hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
+{
+    const int block = 64 * p.nw;
+    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH>);
+    const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
+    // Resident blocks: the occupancy query's answer, but at most two blocks of
+    // this size per CU (more were measured not to be co-resident, which puts a
+    // second round of blocks after the first).
+    const long cap = (long)cus * std::min(2, blocks_per_cu(fn, block, planes + 4096));
+    if (cap < a.n_experts) return hipErrorInvalidConfiguration;
+    const int rs = 64 / p.lpr_d;
+    const long steps = (a.d_model + rs - 1) / rs;
+    const long per_expert = std::max(1L, std::min(cap / a.n_experts, (steps + p.nw - 1) / p.nw));
+    const long waves = per_expert * p.nw;
+    a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
+    const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
+    hipLaunchKernelGGL((k_down<BITS, NCH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st, a);
+    return hipGetLastError();
+}
+
+// Lanes per row and chunks per lane for whole-row waves over `cpr` chunks:
+// as few idle lanes as possible, then as few plane registers as possible.
+bool row_map(int bits, int cpr, int *lpr_out, int *nch_out)
+{
+    const int max_nch = bits == 4 ? 4 : 2;
+    double best = 1e30;
+    int bl = 0, bn = 0;
+    for (int nch = 1; nch <= max_nch; ++nch)
+        for (int lpr = 8; lpr <= 64; lpr *= 2) {
+            if (lpr * nch < cpr) continue;
+            const double waste = 1.0 - (double)cpr / ((double)lpr * nch);
+            const double pen = 4.0 * waste + 0.5 * (nch - 1) * (bits == 4 ? 1.0 : 2.0);
+            if (pen < best) {
+                best = pen;
+                bl = lpr;
+                bn = nch;
+            }
+        }
+    if (!bl) return false;
+    *lpr_out = bl;
+    *nch_out = bn;
+    return true;
 }
 
 }  // namespace
 
-// Instantiated mappings (blocks of at most 8 waves): lanes per row 2..32; one or
-// two chunks per lane at 4 bits, one at 2 bits (a 2-bit chunk is already 64
-// codes); 1 or 2 row steps per tile.
-#define SMOE_QMAP_ITERS(F, B, L, N) F(B, L, N, 1) F(B, L, N, 2)
-#define SMOE_QMAP_LPRS(F, B, N)                                                                \
-    SMOE_QMAP_ITERS(F, B, 2, N) SMOE_QMAP_ITERS(F, B, 4, N) SMOE_QMAP_ITERS(F, B, 8, N)         \
-    SMOE_QMAP_ITERS(F, B, 16, N) SMOE_QMAP_ITERS(F, B, 32, N)
-#define SMOE_QMAP_ALL(F) SMOE_QMAP_LPRS(F, 4, 1) SMOE_QMAP_LPRS(F, 4, 2) SMOE_QMAP_LPRS(F, 2, 1)
-
-static bool qmap_instantiated(int bits, int lpr, int nch, int iter)
+bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, DecodePlan *p)
 {
-#define SMOE_HAS(B, L, N, I) if (bits == B && lpr == L && nch == N && iter == I) return true;
-    SMOE_QMAP_ALL(SMOE_HAS)
-#undef SMOE_HAS
-    return false;
-}
-
-bool choose_qmap(int bits, int chunks, int rows, int n_experts, MapConfig *cfg)
-{
-    // Cover the row with nw * lpr * nch lane-chunks, wasting as few lanes as
-    // possible, preferring one chunk per lane and blocks of about 8 waves.
-    static const int kNw[] = {8, 6, 4, 7, 5, 3, 2, 1};
-    static const int kLpr[] = {16, 8, 4, 2, 32};
-    double best = 1e30;
-    MapConfig pick{0, 0, 0, 0};
-    for (int nch = 1; nch <= (bits == 4 ? 2 : 1); ++nch)
-        for (int lpr : kLpr)
-            for (int nw : kNw) {
-                const int sl = (chunks + nw - 1) / nw;
-                if (sl > lpr * nch) continue;
-                const double waste = 1.0 - (double)chunks / (nw * lpr * nch);
-                const double pen = 10.0 * waste + 0.7 * (nch - 1) +
-                                   0.25 * std::abs(std::log2((double)nw / 8.0));
-                if (pen < best) {
-                    best = pen;
-                    pick = MapConfig{nw, lpr, nch, 1};
-                }
-            }
-    if (!pick.nw) return false;
-    // Two row steps per tile unless the matrix is too small to give a few
-    // thousand waves work.
-    const int rs = 64 / pick.lpr;
-    const long tiles2 = (long)n_experts * ((rows + 2 * rs - 1) / (2 * rs));
-    pick.iter = tiles2 * pick.nw >= 4096 ? 2 : 1;
-    if (!qmap_instantiated(bits, pick.lpr, pick.nch, pick.iter)) return false;
-    *cfg = pick;
+    (void)n_experts;
+    const int cpc = 128 / bits;
+    DecodePlan q{mode, 8, 64, 1, 64, 1, d_model, d_ff};
+    if (mode != kDownOnly && !row_map(bits, d_model / cpc, &q.lpr_g, &q.nch_g)) return false;
+    if (mode != kGateUpOnly && !row_map(bits, d_ff / cpc, &q.lpr_d, &q.nch_d)) return false;
+    *p = q;
     return true;
 }
 
-size_t qmap_lds_bytes(int bits, const MapConfig &cfg, int cols, int m)
-{
-    return bits == 4 ? smem_bytes<4>(cfg.nw, cfg.rows_per_block(), m, cols)
-                     : smem_bytes<2>(cfg.nw, cfg.rows_per_block(), m, cols);
-}
+int decode_rows_per_tile(int lpr) { return 64 / lpr; }
 
-hipError_t launch_gate_up(int bits, const MapConfig &cfg, const GateUpArgs &a, int cus, hipStream_t st)
+hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, L, N, I) \
-    if (bits == B && cfg.lpr == L && cfg.nch == N && cfg.iter == I) return run_gate_up<B, L, N, I>(cfg, a, cus, st);
-    SMOE_QMAP_ALL(SMOE_RUN)
+#define SMOE_RUN(B, N) if (bits == B && p.nch_g == N) return run_gate_up<B, N>(p, a, cus, st);
+    SMOE_RUN(4, 1) SMOE_RUN(4, 2) SMOE_RUN(4, 3) SMOE_RUN(4, 4) SMOE_RUN(2, 1) SMOE_RUN(2, 2)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
 }
 
-hipError_t launch_down(int bits, const MapConfig &cfg, const DownArgs &a, int cus, hipStream_t st)
+hipError_t launch_down(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, L, N, I) \
-    if (bits == B && cfg.lpr == L && cfg.nch == N && cfg.iter == I) return run_down<B, L, N, I>(cfg, a, cus, st);
-    SMOE_QMAP_ALL(SMOE_RUN)
+#define SMOE_RUN(B, N) if (bits == B && p.nch_d == N) return run_down<B, N>(p, a, cus, st);
+    SMOE_RUN(4, 1) SMOE_RUN(4, 2) SMOE_RUN(4, 3) SMOE_RUN(4, 4) SMOE_RUN(2, 1) SMOE_RUN(2, 2)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
 }

@@ -10,6 +10,7 @@
 #include "../../include/smoe.h"
 #include "launch.h"
 
+using smoe::DecodePlan;
 using smoe::MapConfig;
 
 namespace {
@@ -87,22 +88,30 @@ bool overlaps_qmat(const void *out, size_t nout, const smoe_qmat *m, int bits, i
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SMOE_OK : SMOE_ERR_LAUNCH; }
 
-// Workspace layout of the decode path (T == 1):
-//   hidden   f32 [n_experts][d_ff]
-//   partial  f32 [n_experts][d_model]
-//   counters i32 [d_model]    (one per row tile of the down pass; d_model bounds it)
+// Workspace layout of the decode path (T == 1), every piece 256-byte aligned:
+//   hidden    f32 [n_experts][d_ff]
+//   row_acc   u64 [d_model]          exact per-row sums of the experts' outputs
+// row_acc must be zero before the first call; every call leaves it zero.
 struct DecodeWorkspace {
-    size_t hidden, partial, counters, total;
+    size_t hidden, row_acc, total;
 };
 
 DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
 {
     DecodeWorkspace w;
     w.hidden = 0;
-    w.partial = w.hidden + align256((size_t)n_experts * d_ff * 4);
-    w.counters = w.partial + align256((size_t)n_experts * d_model * 4);
-    w.total = w.counters + align256((size_t)d_model * 4);
+    w.row_acc = w.hidden + align256((size_t)n_experts * d_ff * 4);
+    w.total = w.row_acc + align256((size_t)d_model * 8);
     return w;
+}
+
+void fill_experts(smoe::DecodeArgs &a, const smoe_expert *experts, int n)
+{
+    for (int e = 0; e < n; ++e) {
+        a.gate[e] = {experts[e].gate.codes, experts[e].gate.scales};
+        a.up[e] = {experts[e].up.codes, experts[e].up.scales};
+        a.down[e] = {experts[e].down.codes, experts[e].down.scales};
+    }
 }
 
 }  // namespace
@@ -140,24 +149,23 @@ int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group
         overlaps_qmat(hidden, nh, gate, bits, group, d_ff, d_model) ||
         overlaps_qmat(hidden, nh, up, bits, group, d_ff, d_model))
         return SMOE_ERR_ALIAS;
-    MapConfig cfg;
-    if (!smoe::choose_qmap(bits, d_model * bits / 128, d_ff, 1, &cfg)) return SMOE_ERR_SHAPE;
+    DecodePlan plan;
+    if (!smoe::plan_decode(smoe::kGateUpOnly, bits, d_model, d_ff, 1, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
-    smoe::GateUpArgs a{};
+    smoe::DecodeArgs a{};
     a.gate[0] = {gate->codes, gate->scales};
     a.up[0] = {up->codes, up->scales};
     a.x = x;
     a.hidden = hidden;
-    a.counters = nullptr;
-    a.n_counters = 0;
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;
     a.n_experts = 1;
-    a.blocks_per_expert = (d_ff + cfg.rows_per_block() - 1) / cfg.rows_per_block();
-    return launch_status(smoe::launch_gate_up(bits, cfg, a, dev.cus, (hipStream_t)stream));
+    a.lpr_g = plan.lpr_g;
+    a.lpr_d = plan.lpr_d;
+    return launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, (hipStream_t)stream));
 }
 
 int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff, const float *hidden,
@@ -172,24 +180,22 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
     if (overlap(out, no, hidden, (size_t)d_ff * 4) ||
         overlaps_qmat(out, no, down, bits, group, d_model, d_ff))
         return SMOE_ERR_ALIAS;
-    MapConfig cfg;
-    if (!smoe::choose_qmap(bits, d_ff * bits / 128, d_model, 1, &cfg)) return SMOE_ERR_SHAPE;
+    DecodePlan plan;
+    if (!smoe::plan_decode(smoe::kDownOnly, bits, d_model, d_ff, 1, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
-    smoe::DownArgs a{};
+    smoe::DecodeArgs a{};
     a.down[0] = {down->codes, down->scales};
-    a.hidden = hidden;
-    a.route_w = nullptr;
+    a.hidden = const_cast<float *>(hidden);
     a.out = out;
-    a.partial = nullptr;
-    a.counters = nullptr;
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;
     a.n_experts = 1;
-    a.row_blocks = (d_model + cfg.rows_per_block() - 1) / cfg.rows_per_block();
-    return launch_status(smoe::launch_down(bits, cfg, a, dev.cus, (hipStream_t)stream));
+    a.lpr_g = plan.lpr_g;
+    a.lpr_d = plan.lpr_d;
+    return launch_status(smoe::launch_down(bits, plan, a, dev.cus, (hipStream_t)stream));
 }
 
 size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
@@ -235,49 +241,29 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
             overlaps_qmat(workspace, need, &ex.down, bits, group, d_model, d_ff))
             return SMOE_ERR_ALIAS;
     }
-    MapConfig gu, dn;
-    if (!smoe::choose_qmap(bits, d_model * bits / 128, d_ff, n_experts, &gu)) return SMOE_ERR_SHAPE;
-    if (!smoe::choose_qmap(bits, d_ff * bits / 128, d_model, n_experts, &dn)) return SMOE_ERR_SHAPE;
+    DecodePlan plan;
+    if (!smoe::plan_decode(smoe::kBoth, bits, d_model, d_ff, n_experts, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
     const DecodeWorkspace w = decode_workspace(n_experts, d_model, d_ff);
     char *ws = static_cast<char *>(workspace);
-    float *hidden = reinterpret_cast<float *>(ws + w.hidden);
-    float *partial = reinterpret_cast<float *>(ws + w.partial);
-    int *counters = reinterpret_cast<int *>(ws + w.counters);
-    const int row_blocks = (d_model + dn.rows_per_block() - 1) / dn.rows_per_block();
+    smoe::DecodeArgs a{};
+    fill_experts(a, experts, n_experts);
+    a.x = x;
+    a.hidden = reinterpret_cast<float *>(ws + w.hidden);
+    a.route_w = route_w;
+    a.out = out;
+    a.row_acc = reinterpret_cast<unsigned long long *>(ws + w.row_acc);
+    a.d_model = d_model;
+    a.d_ff = d_ff;
+    a.group = group;
+    a.n_experts = n_experts;
+    a.lpr_g = plan.lpr_g;
+    a.lpr_d = plan.lpr_d;
     hipStream_t st = (hipStream_t)stream;
-
-    smoe::GateUpArgs g{};
-    smoe::DownArgs d{};
-    for (int e = 0; e < n_experts; ++e) {
-        g.gate[e] = {experts[e].gate.codes, experts[e].gate.scales};
-        g.up[e] = {experts[e].up.codes, experts[e].up.scales};
-        d.down[e] = {experts[e].down.codes, experts[e].down.scales};
-    }
-    g.x = x;
-    g.hidden = hidden;
-    g.counters = n_experts > 1 ? counters : nullptr;
-    g.n_counters = n_experts > 1 ? row_blocks : 0;
-    g.d_model = d_model;
-    g.d_ff = d_ff;
-    g.group = group;
-    g.n_experts = n_experts;
-    g.blocks_per_expert = (d_ff + gu.rows_per_block() - 1) / gu.rows_per_block();
-    if ((rc = launch_status(smoe::launch_gate_up(bits, gu, g, dev.cus, st)))) return rc;
-
-    d.hidden = hidden;
-    d.route_w = route_w;
-    d.out = out;
-    d.partial = partial;
-    d.counters = counters;
-    d.d_model = d_model;
-    d.d_ff = d_ff;
-    d.group = group;
-    d.n_experts = n_experts;
-    d.row_blocks = row_blocks;
-    return launch_status(smoe::launch_down(bits, dn, d, dev.cus, st));
+    if ((rc = launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, st)))) return rc;
+    return launch_status(smoe::launch_down(bits, plan, a, dev.cus, st));
 }
 
 size_t matvec_bf16_workspace(int rows, int cols)

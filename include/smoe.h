@@ -72,7 +72,7 @@ enum {
 /* Largest n_experts accepted by smoe_expert_ffn in one call. */
 #define SMOE_MAX_EXPERTS 16
 /* Largest cols of a quantised matrix (d_model for gate/up, d_ff for down). */
-#define SMOE_MAX_QCOLS 16384
+#define SMOE_MAX_QCOLS 8192
 /* Largest cols of a bf16 matrix. */
 #define SMOE_MAX_BF16_COLS 16384
 
@@ -114,11 +114,17 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  *   x         : f32 [T][d_model]
  *   out       : f32 [T][d_model], must not overlap x, route_w, workspace or weights
  *   workspace : device scratch of at least smoe_expert_ffn_workspace(...) bytes,
- *               256-byte aligned; its contents need not be initialised and are
- *               clobbered.  Calls that share a workspace must be ordered (one
- *               stream), or they race.
- * T == 1 runs the decode kernels (two launches); T > 1 runs the token-batch
- * kernels, in which every expert processes every token.
+ *               256-byte aligned.  It must be ZERO-FILLED before its first use
+ *               (e.g. allocated with torch.zeros or cleared once with
+ *               hipMemset): part of it holds per-row counters through which
+ *               the experts' outputs are combined, and every completed call
+ *               leaves those counters zero again.  The rest is scratch that
+ *               each call overwrites.  Calls that share a workspace must be
+ *               ordered (one stream), or they race.
+ * T == 1 runs the decode kernels (a gate_up launch and a down launch that also
+ * combines the experts, deterministically: the sum over experts is taken in
+ * ascending expert order); T > 1 runs the token-batch kernels, in which every
+ * expert processes every token.
  */
 size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T);
 int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w,

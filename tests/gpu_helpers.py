@@ -66,7 +66,7 @@ def run_ffn(gq, dexp, bits, group_size, x, route=None, T=None):
     xd = x if isinstance(x, torch.Tensor) else dev(np.asarray(x, np.float32))
     T = xd.numel() // d_model
     out = torch.empty(T * d_model, dtype=torch.float32, device="cuda")
-    ws = torch.empty(gq.smoe_expert_ffn_workspace(len(dexp), d_model, d_ff, T), dtype=torch.uint8,
+    ws = torch.zeros(gq.smoe_expert_ffn_workspace(len(dexp), d_model, d_ff, T), dtype=torch.uint8,
                      device="cuda")
     rd = None
     if route is not None:

@@ -66,7 +66,7 @@ def test_gate_up_refusals(gq):
     assert gate_up(L, group=512) == -3             # does not divide d_model = 256
     assert gate_up(L, d_model=80) == -4            # not a multiple of 32
     assert gate_up(L, d_ff=0) == -4
-    assert gate_up(L, d_model=32768) == -4         # above SMOE_MAX_QCOLS
+    assert gate_up(L, d_model=16384) == -4         # above SMOE_MAX_QCOLS
     assert gate_up(L, x=0) == -1
     assert gate_up(L, g=A + 8) == -5               # codes not 16-byte aligned
     assert gate_up(L, x=A + 0x8000004) == -5       # x not 16-byte aligned
