@@ -46,6 +46,46 @@ hipError_t launch_gate_up(int bits, const DecodePlan &plan, const DecodeArgs &ar
 hipError_t launch_down(int bits, const DecodePlan &plan, const DecodeArgs &args, int cus, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
+// Token-batch (T > 1) launches of the quantised expert FFN (matrix cores)
+// ---------------------------------------------------------------------------
+
+// Activations in the workspace are f16 hi/lo halves in sigma order (element
+// 8b + i of a row holds column 8b + sigma(i), sigma = 0,4,1,5,2,6,3,7) with one
+// power-of-two exponent per (row, quantisation group).
+struct TbArgs {
+    QPtr gate[kMaxExperts];
+    QPtr up[kMaxExperts];
+    QPtr down[kMaxExperts];
+    const float *x;          // [T][d_model]
+    const float *route_w;    // [T][n_experts] or null (weight 1)
+    float *out;              // [T][d_model]
+    _Float16 *xh, *xl;       // [T][d_model]
+    int *xe;                 // [T][d_model / group]
+    _Float16 *hh, *hl;       // [n_experts][T][d_ff]
+    int *he;                 // [n_experts][T][d_ff / group]
+    int T, d_model, d_ff, group, n_experts;
+    int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
+    int ks_dn, rw_dn;        // down waves per block: rw_dn row slices x ks_dn (expert, group) slices
+};
+
+// Tiling of the three token-batch launches: 16*ntt tokens per block; waves per
+// block, block counts and dynamic LDS bytes of gate_up and down.
+struct TbPlan {
+    int ntt;
+    int rw_gu, ks_gu, gu_waves;
+    long gu_blocks;
+    size_t gu_lds;
+    int rw_dn, ks_dn, dn_waves;
+    long dn_blocks;
+    size_t dn_lds;
+};
+
+// False if the shape is outside what the token-batch kernels cover (group
+// must be 32, 64, 96 or 128 columns at 4 bits, 64 or 128 at 2 bits).
+bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T, TbPlan *plan);
+hipError_t launch_batch(int bits, const TbPlan &plan, const TbArgs &args, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // Dense bf16 matvec
 // ---------------------------------------------------------------------------
 

@@ -105,7 +105,36 @@ DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
     return w;
 }
 
-void fill_experts(smoe::DecodeArgs &a, const smoe_expert *experts, int n)
+// Workspace layout of the token-batch path (T > 1), every piece 256-byte aligned:
+//   xh, xl  f16 [T][d_model]            hi/lo halves of the scaled activations
+//   xe      i32 [T][d_model/group]      their power-of-two exponents
+//   hh, hl  f16 [n_experts][T][d_ff]    hi/lo halves of the scaled hidden rows
+//   he      i32 [n_experts][T][d_ff/group]
+// Everything is rewritten by each call before it is read.
+struct BatchWorkspace {
+    size_t xh, xl, xe, hh, hl, he, total;
+};
+
+BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int group)
+{
+    BatchWorkspace w;
+    const size_t nx = (size_t)T * d_model, nh = (size_t)n_experts * T * d_ff;
+    w.xh = 0;
+    w.xl = w.xh + align256(nx * 2);
+    w.xe = w.xl + align256(nx * 2);
+    w.hh = w.xe + align256((size_t)T * (d_model / group) * 4);
+    w.hl = w.hh + align256(nh * 2);
+    w.he = w.hl + align256(nh * 2);
+    w.total = w.he + align256((size_t)n_experts * T * (d_ff / group) * 4);
+    return w;
+}
+
+// The smallest group the token-batch layout can need (32 columns) gives the
+// largest exponent arrays; the workspace size does not depend on the group.
+constexpr int kMinBatchGroup = 32;
+
+template <class Args>
+void fill_experts(Args &a, const smoe_expert *experts, int n)
 {
     for (int e = 0; e < n; ++e) {
         a.gate[e] = {experts[e].gate.codes, experts[e].gate.scales};
@@ -113,6 +142,7 @@ void fill_experts(smoe::DecodeArgs &a, const smoe_expert *experts, int n)
         a.down[e] = {experts[e].down.codes, experts[e].down.scales};
     }
 }
+
 
 }  // namespace
 
@@ -202,7 +232,8 @@ size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
 {
     if (n_experts <= 0 || d_model <= 0 || d_ff <= 0 || T <= 0) return 0;
     if (T == 1) return decode_workspace(n_experts, d_model, d_ff).total;
-    return 0;  // token batch: not available in this build
+    if (T > SMOE_MAX_TOKENS) return 0;
+    return batch_workspace(n_experts, d_model, d_ff, T, kMinBatchGroup).total;
 }
 
 int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int bits,
@@ -212,7 +243,8 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     int rc = check_format(bits, group);
     if (rc) return rc;
     if (!experts || !x || !out) return SMOE_ERR_NULL;
-    if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS || T < 1) return SMOE_ERR_SHAPE;
+    if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS || T < 1 || T > SMOE_MAX_TOKENS)
+        return SMOE_ERR_SHAPE;
     for (int e = 0; e < n_experts; ++e) {
         if ((rc = check_qmat(&experts[e].gate, bits, group, d_ff, d_model))) return rc;
         if ((rc = check_qmat(&experts[e].up, bits, group, d_ff, d_model))) return rc;
@@ -220,7 +252,9 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     }
     if (!aligned(x, 16) || !aligned(out, 4) || (route_w && !aligned(route_w, 4)))
         return SMOE_ERR_ALIGN;
-    if (T != 1) return SMOE_ERR_SHAPE;  // token batch: not available in this build
+    smoe::TbPlan tplan{};
+    if (T > 1 && !smoe::plan_batch(bits, group, d_model, d_ff, n_experts, T, &tplan))
+        return SMOE_ERR_GROUP;
 
     const size_t need = smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T);
     if (!workspace || workspace_bytes < need) return SMOE_ERR_WORKSPACE;
@@ -241,6 +275,35 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
             overlaps_qmat(workspace, need, &ex.down, bits, group, d_model, d_ff))
             return SMOE_ERR_ALIAS;
     }
+    hipStream_t st = (hipStream_t)stream;
+    if (T > 1) {
+        DeviceInfo dev;
+        if ((rc = check_device(&dev))) return rc;
+        const BatchWorkspace w = batch_workspace(n_experts, d_model, d_ff, T, group);
+        char *ws = static_cast<char *>(workspace);
+        smoe::TbArgs a{};
+        fill_experts(a, experts, n_experts);
+        a.x = x;
+        a.route_w = route_w;
+        a.out = out;
+        a.xh = reinterpret_cast<_Float16 *>(ws + w.xh);
+        a.xl = reinterpret_cast<_Float16 *>(ws + w.xl);
+        a.xe = reinterpret_cast<int *>(ws + w.xe);
+        a.hh = reinterpret_cast<_Float16 *>(ws + w.hh);
+        a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
+        a.he = reinterpret_cast<int *>(ws + w.he);
+        a.T = T;
+        a.d_model = d_model;
+        a.d_ff = d_ff;
+        a.group = group;
+        a.n_experts = n_experts;
+        a.ks_gu = tplan.ks_gu;
+        a.rw_gu = tplan.rw_gu;
+        a.ks_dn = tplan.ks_dn;
+        a.rw_dn = tplan.rw_dn;
+        return launch_status(smoe::launch_batch(bits, tplan, a, st));
+    }
+
     DecodePlan plan;
     if (!smoe::plan_decode(smoe::kBoth, bits, d_model, d_ff, n_experts, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
@@ -261,7 +324,6 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     a.n_experts = n_experts;
     a.lpr_g = plan.lpr_g;
     a.lpr_d = plan.lpr_d;
-    hipStream_t st = (hipStream_t)stream;
     if ((rc = launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, st)))) return rc;
     return launch_status(smoe::launch_down(bits, plan, a, dev.cus, st));
 }

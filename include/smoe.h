@@ -75,6 +75,8 @@ enum {
 #define SMOE_MAX_QCOLS 8192
 /* Largest cols of a bf16 matrix. */
 #define SMOE_MAX_BF16_COLS 16384
+/* Largest token count T of smoe_expert_ffn. */
+#define SMOE_MAX_TOKENS 65536
 
 typedef struct smoe_qmat {
     const uint8_t *codes;
@@ -123,8 +125,16 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  *               ordered (one stream), or they race.
  * T == 1 runs the decode kernels (a gate_up launch and a down launch that also
  * combines the experts, deterministically: the sum over experts is taken in
- * ascending expert order); T > 1 runs the token-batch kernels, in which every
- * expert processes every token.
+ * ascending expert order).
+ * 2 <= T <= SMOE_MAX_TOKENS runs the token-batch kernels on the matrix cores,
+ * in which every expert processes every token: an activation pass, a gate_up
+ * pass and a down pass that sums the experts in a fixed order (deterministic,
+ * no atomics).  They need group = 32, 64, 96 or 128 at 4 bits and 64 or 128 at
+ * 2 bits, else SMOE_ERR_GROUP.  Activations are carried to the matrix cores
+ * as two f16 halves scaled by a power of two per group, about 22 significant
+ * bits; non-finite inputs give non-finite outputs.
+ * The workspace size depends on (n_experts, d_model, d_ff, T) only; for T > 1
+ * nothing in it needs to be zero and every call rewrites it.
  */
 size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T);
 int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w,

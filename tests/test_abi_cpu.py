@@ -111,3 +111,30 @@ def test_expert_ffn_refusals(gq):
     assert call(out=WS + 256) == -7                # out inside the workspace
     assert call(out=A + 0x100) == -7               # out inside expert 0's gate codes
     assert call() == -8
+
+
+def test_expert_ffn_batch_refusals(gq):
+    """T > 1: workspace sizing and the token-batch refusals (group outside the
+    batch tiling, T above the limit), all decided before the device query."""
+    L = gq.lib()
+    n, T = 2, 40
+    arr = (gq.Expert * n)()
+    for k in range(n):
+        b = A + k * 0x10000000
+        arr[k] = gq.Expert(gq.QMat(b, b + 0x1000000), gq.QMat(b + 0x2000000, b + 0x3000000),
+                           gq.QMat(b + 0x4000000, b + 0x5000000))
+    X, OUT, WS = 0x80000000, 0x90000000, 0xA0000000
+    need = L.smoe_expert_ffn_workspace(n, 320, 640, T)
+    # hi/lo halves of X and H plus one exponent per 32 columns at least.
+    assert need >= 4 * T * 320 + 4 * n * T * 640 + 4 * T * 10 + 4 * n * T * 20
+    assert L.smoe_expert_ffn_workspace(n, 320, 640, 65537) == 0
+    call = lambda **kw: L.smoe_expert_ffn(
+        arr, n, None, kw.get("bits", 4), kw.get("group", 64), 320, 640, kw.get("T", T), X, OUT, WS,
+        kw.get("wsb", need), None)
+    assert call(group=160) == -3                   # valid for decode, not for the batch tiling
+    assert call(bits=2, group=32) == -3
+    assert call(T=65537) == -4
+    assert call(wsb=need - 1) == -6
+    assert call() == -8
+    assert call(group=32) == -8
+    assert call(bits=2, group=64) == -8

@@ -1,0 +1,139 @@
+"""GPU parity of the token-batch path (T > 1, matrix cores) against the f64
+oracle, through the C ABI: the prefill workload (8 Q4 experts at d_model 4096 /
+d_ff 1536, T = 16, 64, 256), ragged and edge shapes, and the per-token
+invariants of the batch (a row equals the one-token result, duplicated tokens
+give identical rows)."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import assert_parity, dev, dev_experts, run_ffn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import torch
+    import group_quantized_moe_amd as gq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gq.lib()
+    return gq
+
+
+@pytest.fixture(scope="module")
+def q4_group8():
+    g = workloads.make_group(workloads.Q4_GROUP8)
+    return g, dev_experts(g)
+
+
+def sample_tokens(T, k=12):
+    """First, last, the tile edges around 16 and 64, and a seeded spread."""
+    picks = {0, T - 1, min(15, T - 1), min(16, T - 1), min(63, T - 1), min(64, T - 1)}
+    rng = np.random.default_rng(T)
+    picks |= set(int(v) for v in rng.choice(T, size=min(k, T), replace=False))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("T", sorted(workloads.BATCH_TOKENS))
+def test_prefill_workload(gq, oracle_lib, q4_group8, T):
+    """All T tokens through all 8 experts, router-weighted sum; the oracle
+    checks every token at T = 16 and a sample (with the tile edges) above."""
+    g, de = q4_group8
+    X, R = workloads.make_batch_inputs(T)
+    got = run_ffn(gq, de, 4, 64, X, route=R)
+    rows = list(range(T)) if T <= 16 else sample_tokens(T)
+    want = oracle_lib.expert_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X[rows], R[rows])
+    assert_parity(got[rows], want, f"prefill T={T} ({len(rows)} tokens checked)")
+
+
+@pytest.mark.parametrize("k", [0, 7])
+def test_prefill_single_expert(gq, oracle_lib, q4_group8, k):
+    """One expert of the workload on its own (route weights absent = 1)."""
+    g, de = q4_group8
+    X, _ = workloads.make_batch_inputs(16)
+    got = run_ffn(gq, [de[k]], 4, 64, X)
+    want = oracle_lib.expert_ffn([g.experts[k]], 4, 64, g.d_model, g.d_ff, X)
+    assert_parity(got, want, f"prefill T=16 expert {k} alone")
+
+
+def test_batch_rows_match_decode_and_duplicates(gq, q4_group8):
+    """Row t of a batch equals the decode result for X[t] (within the bar: a
+    different kernel); identical tokens in different tiles give identical rows."""
+    g, de = q4_group8
+    X, R = workloads.make_batch_inputs(16)
+    Xd = np.concatenate([X, X[::-1], X[:5]])          # T = 37: three token tiles, ragged
+    Rd = np.concatenate([R, R[::-1], R[:5]])
+    got = run_ffn(gq, de, 4, 64, Xd, route=Rd)
+    for t in range(16):
+        assert np.array_equal(got[t], got[31 - t]), f"token {t} and its duplicate differ"
+    for t in range(5):
+        assert np.array_equal(got[t], got[32 + t]), f"token {t} and its duplicate differ"
+    for t in (0, 9, 15):
+        one = run_ffn(gq, de, 4, 64, X[t], route=R[t])
+        assert_parity(got[t], one, f"batch row {t} vs decode")
+
+
+def test_batch_deterministic(gq, q4_group8):
+    g, de = q4_group8
+    X, R = workloads.make_batch_inputs(64)
+    a = run_ffn(gq, de, 4, 64, X, route=R)
+    b = run_ffn(gq, de, 4, 64, X, route=R)
+    assert np.array_equal(a, b)
+
+
+BATCH_EDGE = [  # bits, group, d_model, d_ff, n_experts, T
+    (4, 64, 256, 512, 2, 2),
+    (4, 64, 256, 512, 1, 17),
+    (4, 32, 96, 160, 3, 5),
+    (4, 32, 96, 160, 3, 33),
+    (4, 96, 192, 288, 2, 20),
+    (4, 128, 512, 384, 2, 70),
+    (4, 64, 8192, 128, 1, 3),
+    (4, 64, 64, 8192, 2, 18),
+    (4, 64, 256, 64, 16, 4),
+    (2, 64, 256, 384, 3, 20),
+    (2, 128, 512, 256, 2, 9),
+    (2, 64, 192, 128, 1, 65),
+]
+
+
+@pytest.mark.parametrize("bits,group,d_model,d_ff,n,T", BATCH_EDGE,
+                         ids=lambda v: str(v))
+def test_batch_edge_shapes(gq, oracle_lib, bits, group, d_model, d_ff, n, T):
+    g = workloads.expert_group(100 + d_model + d_ff + T, n, d_model, d_ff, bits, group)
+    X = workloads.activation_batch(200 + T, T, d_model)
+    R = workloads.router_weights(300 + T, n, T)
+    got = run_ffn(gq, dev_experts(g), bits, group, X, route=R)
+    want = oracle_lib.expert_ffn(g.experts, bits, group, d_model, d_ff, X, R)
+    assert_parity(got, want, f"batch Q{bits} g{group} {d_model}x{d_ff} E={n} T={T}")
+
+
+def test_batch_extreme_magnitudes(gq, oracle_lib):
+    """Tokens whose scale differs by 2^40 from each other, and an all-zero
+    token: the per-group power-of-two scaling keeps each row to the bar of its
+    own magnitude."""
+    g = workloads.expert_group(7, 2, 256, 512, 4, 64)
+    X = workloads.activation_batch(8, 6, 256).astype(np.float64)
+    X[1] *= 2.0 ** 20
+    X[2] *= 2.0 ** -20
+    X[3] = 0.0
+    X[4, :64] *= 2.0 ** 30   # one group of one token far above the rest
+    X = X.astype(np.float32)
+    got = run_ffn(gq, dev_experts(g), 4, 64, X)
+    want = oracle_lib.expert_ffn(g.experts, 4, 64, 256, 512, X)
+    for t in range(6):
+        assert_parity(got[t], want[t], f"extreme token {t}")
+
+
+def test_batch_refuses_unsupported_group(gq):
+    """group 160 is a valid 4-bit group for decode but not for the batch tiling."""
+    import torch
+    g = workloads.expert_group(9, 1, 320, 160, 4, 160)
+    de = dev_experts(g)
+    X = dev(workloads.activation_batch(9, 4, 320))
+    out = torch.empty(4 * 320, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(gq.smoe_expert_ffn_workspace(1, 320, 160, 4), dtype=torch.uint8, device="cuda")
+    with pytest.raises(gq.SmoeError) as ei:
+        gq.smoe_expert_ffn(de, 4, 160, X, out, workspace=ws)
+    assert ei.value.status == -3
