@@ -1,15 +1,25 @@
-"""Benchmark: effective HBM bandwidth and microseconds per Q4 8-expert FFN
-decode group on one MI355X.
+"""Benchmark of the group-quantised routed-expert FFN path on one MI355X.
 
-One step = one smoe_expert_ffn call with T = 1: the fused gate+up+SiLU pass
-and the down pass with the router-weighted sum over 8 experts at d_model 4096,
-d_ff 1536, 4-bit codes, group 64, f32 scales.  Inputs are seeded synthetic
-weights with the shapes and distributions of the Metal Compute Kernels page
-(S-MoE docs) workload; they stand in for trained vault blobs.  Weights sit in
-HBM before the timed region; to keep the 256 MB Infinity Cache from serving
-them, the step cycles through >= 1 GiB of byte-identical replicas.
+Default workload (the headline): one Q4 8-expert FFN decode group, i.e. one
+smoe_expert_ffn call with T = 1 -- the fused gate+up+SiLU pass and the down
+pass with the router-weighted sum over 8 experts at d_model 4096, d_ff 1536,
+4-bit codes, group 64, f32 scales.  Reported as effective HBM GB/s (algorithmic
+bytes / time), microseconds per group and fraction of the 8 TB/s HBM peak.
 
-Prints one JSON line (see the keys below).  `python bench.py --steps K --warmup W`.
+Other rows of the path, one JSON line each with --workload:
+  decode_q2           the same group with 2-bit codes
+  prefill             --tokens T (16, 64 or 256): every token through all 8
+                      experts on the matrix cores (bound by HBM at T = 16, by
+                      the f16 MFMA rate above)
+  bf16                --shape q_proj|o_proj|kv_proj|lm_head dense matvec
+
+Inputs are seeded synthetic weights with the shapes and distributions of the
+Metal Compute Kernels page (S-MoE docs) workloads; they stand in for trained
+weights.  Weights sit in HBM before the timed region; so that the 256 MB
+Infinity Cache cannot serve them, each step cycles through >= 1 GiB of
+byte-identical replicas.
+
+`python bench.py [--workload W] --steps K --warmup W` prints one JSON line.
 """
 from __future__ import annotations
 
@@ -26,86 +36,53 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
-KERNEL_SOURCES = ["group_quantized_moe_amd/csrc/q_decode.hip", "group_quantized_moe_amd/csrc/common.h",
-                  "group_quantized_moe_amd/csrc/launch.h", "group_quantized_moe_amd/csrc/smoe_api.cpp"]
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense f16 matrix peak, TFLOP/s
+CSRC = "group_quantized_moe_amd/csrc/"
+KERNEL_SOURCES = {
+    "decode": [CSRC + "q_decode.hip", CSRC + "common.h", CSRC + "launch.h", CSRC + "smoe_api.cpp"],
+    "prefill": [CSRC + "q_batch.hip", CSRC + "common.h", CSRC + "launch.h", CSRC + "smoe_api.cpp"],
+    "bf16": [CSRC + "bf16_matvec.hip", CSRC + "common.h", CSRC + "launch.h", CSRC + "smoe_api.cpp"],
+}
 
 
-def algorithmic_bytes(g, n_experts):
-    """Codes + scales of every matrix, x, out and the router weights, each once."""
-    weights = g.byte_count()
-    return weights + 4 * g.d_model + 4 * g.d_model + 4 * n_experts
-
-
-def kernel_source_hash():
+def kernel_source_hash(kind):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """Measured HBM bytes per step from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "decode_q4_8expert_pmc.json")
+def load_traffic(name, kind):
+    """Measured HBM bytes per step from the committed rocprofv3 counter runs
+    (profiles/<name>_pmc.json), if they were taken on the current kernel
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return d.get("traffic_bytes_per_step")
 
 
-def cpu_baseline(g, x, r, budget_s):
-    """The f64 oracle on the host: whole 8-expert groups, repeated until the
-    time budget is used (at least one group)."""
-    import oracle
-    if not os.path.exists(oracle.LIB_PATH):
-        oracle.build()
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.expert_ffn(g.experts, g.bits, g.group, g.d_model, g.d_ff, x, r[None])
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return n, dt, oracle.threads()
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle work for the CPU baseline (0 to skip)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
-
+def to_dev(a):
     import torch
-    import workloads
-    import group_quantized_moe_amd as gq
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
 
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    L = gq.lib()
-    spec = workloads.Q4_GROUP8
-    g, x, r = workloads.make_decode_inputs(spec)
-    E = spec["n_experts"]
-    nbytes = algorithmic_bytes(g, E)
 
-    def to_dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+def replica_count(nbytes):
+    return max(2, -(-(1 << 30) // nbytes))
 
+
+def expert_arrays(gq, g, E, replicas):
+    """ctypes smoe_expert arrays for `replicas` device copies of the group."""
     base = [to_dev(t) for e in g.experts for m in (e.gate, e.up, e.down) for t in (m.codes, m.scales)]
-    replicas = max(2, -(-(1 << 30) // g.byte_count()))
     reps = [base] + [[t.clone() for t in base] for _ in range(replicas - 1)]
     arrays = []
     for rep in reps:
@@ -115,6 +92,64 @@ def main():
             arr[k] = gq.Expert(gq.QMat(gc.data_ptr(), gs.data_ptr()), gq.QMat(uc.data_ptr(), us.data_ptr()),
                                gq.QMat(dc.data_ptr(), ds.data_ptr()))
         arrays.append(arr)
+    return arrays, reps
+
+
+def time_steps(step, steps, warmup, stream):
+    """Warmup, then `steps` back-to-back steps between two events on the
+    launch stream; then a median per-call duration from an event pair around
+    each of up to 100 further calls (sampled apart from the timed region)."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    us_step = e0.elapsed_time(e1) * 1e3 / steps
+    nsamp = min(100, steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsamp)]
+    for i in range(nsamp):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    return us_step, per_call, wall * 1e6 / steps
+
+
+def cpu_oracle(fn, budget_s, units_per_call):
+    """Run the f64 oracle repeatedly until budget_s has passed (at least once);
+    returns (calls, seconds, threads)."""
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return n, time.perf_counter() - t0, oracle.threads()
+
+
+def decode_bench(args, spec):
+    import torch
+    import workloads
+    import group_quantized_moe_amd as gq
+    L = gq.lib()
+    g, x, r = workloads.make_decode_inputs(spec)
+    E = spec["n_experts"]
+    # Algorithmic bytes: codes + scales of every matrix, x, out and the router weights, each once.
+    nbytes = g.byte_count() + 4 * g.d_model + 4 * g.d_model + 4 * E
+    replicas = replica_count(g.byte_count())
+    arrays, _keep = expert_arrays(gq, g, E, replicas)
     xd, rd = to_dev(x), to_dev(r)
     out = torch.empty(g.d_model, dtype=torch.float32, device="cuda")
     ws = torch.zeros(gq.smoe_expert_ffn_workspace(E, g.d_model, g.d_ff, 1), dtype=torch.uint8, device="cuda")
@@ -127,77 +162,199 @@ def main():
         if rc != 0:
             raise gq.SmoeError("smoe_expert_ffn", rc)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K back-to-back steps between two events on the launch stream.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = e0.elapsed_time(e1)
-    us_step = gpu_ms * 1e3 / args.steps
+    us_step, per_call, wall_us = time_steps(step, args.steps, args.warmup, stream)
     gbs = nbytes / (us_step * 1e-6) / 1e9
-
-    # Per-launch duration of the step's kernels, measured with an event pair
-    # around each step (sampled separately so the timed region has no extra
-    # events in it).
-    nsamp = min(100, args.steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsamp)]
-    for i in range(nsamp):
-        evs[i][0].record(stream)
-        step(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_launch_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
-
     cpu = None
     if args.cpu_budget > 0:
-        n, dt, cores = cpu_baseline(g, x, r, args.cpu_budget)
+        import oracle
+        n, dt, cores = cpu_oracle(lambda: oracle.expert_ffn(g.experts, g.bits, g.group, g.d_model, g.d_ff,
+                                                            x, r[None]), args.cpu_budget, 1)
         cpu = {"value": round(n * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"{n} whole Q4 8-expert groups (f64 oracle, {dt:.1f} s)",
+               "sample": f"{n} whole {E}-expert Q{g.bits} groups (f64 oracle, {dt:.1f} s)",
                "us_per_group": round(dt / n * 1e6, 1)}
-
-    achieved = nbytes / (us_step * 1e-6) / 1e9
-    line = {
-        "metric": "effective HBM GB/s per Q4 8-expert FFN group (decode, T=1)",
+    return {
+        "metric": f"effective HBM GB/s per Q{g.bits} {E}-expert FFN group (decode, T=1)",
         "value": round(gbs, 1),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(us_step / 1e3, 6),
         "us_per_group": round(us_step, 3),
         "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int4 codes x int4 digit planes -> int32, f32 epilogue",
-        "data": "synthetic (seeded; stands in for trained expert weights)",
+        "wall_us_per_step": round(wall_us, 3),
+        "dtype": f"u{g.bits} codes x i4 digit planes -> i32, f32 epilogue",
         "config": {"workload": spec["name"], "d_model": g.d_model, "d_ff": g.d_ff, "n_experts": E,
                    "bits": g.bits, "group": g.group, "scales": "f32", "tokens": 1,
                    "algorithmic_bytes_per_step": nbytes, "replicas_rotated": replicas,
                    "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "smoe_expert_ffn T=1 (k_gate_up + k_down)",
-            "achieved": round(achieved, 1),
+            "kernel": "one smoe_expert_ffn call = k_gate_up + k_down on one stream",
+            "achieved": round(nbytes / (per_call * 1e-6) / 1e9, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(),
-            "per_launch_us_events": round(per_launch_us, 3),
+            "frac": round(nbytes / (per_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(spec["name"], "decode"),
+            "per_call_us_events": round(per_call, 3),
         },
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+
+
+def prefill_bench(args):
+    import torch
+    import workloads
+    import group_quantized_moe_amd as gq
+    L = gq.lib()
+    T = args.tokens
+    spec = workloads.Q4_GROUP8
+    g = workloads.make_group(spec)
+    X, R = workloads.make_batch_inputs(T)
+    E = spec["n_experts"]
+    flops = 2 * T * E * 3 * g.d_model * g.d_ff
+    nbytes = g.byte_count() + T * g.d_model * 4 * 2 + T * E * 4
+    replicas = replica_count(g.byte_count())
+    arrays, _keep = expert_arrays(gq, g, E, replicas)
+    xd, rd = to_dev(X), to_dev(R)
+    out = torch.empty(T * g.d_model, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(gq.smoe_expert_ffn_workspace(E, g.d_model, g.d_ff, T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        rc = L.smoe_expert_ffn(arrays[i % replicas], E, rd.data_ptr(), 4, 64, g.d_model, g.d_ff, T,
+                               xd.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        if rc != 0:
+            raise gq.SmoeError("smoe_expert_ffn", rc)
+
+    us_step, per_call, wall_us = time_steps(step, args.steps, args.warmup, stream)
+    tflops = flops / (per_call * 1e-6) / 1e12
+    gbs = nbytes / (per_call * 1e-6) / 1e9
+    hbm_bound = T <= 16
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        ns = 4
+        n, dt, cores = cpu_oracle(lambda: oracle.expert_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X[:ns], R[:ns]),
+                                  args.cpu_budget, ns)
+        cpu = {"value": round(n * ns * 2 * E * 3 * g.d_model * g.d_ff / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": cores, "kind": "oracle",
+               "sample": f"{n} calls of {ns} tokens x {E} experts (f64 oracle, {dt:.1f} s)",
+               "us_per_token": round(dt / (n * ns) * 1e6, 1)}
+    return {
+        "metric": f"prefill tokens/s through 8 Q4 experts (T={T}), with TFLOP/s and HBM GB/s",
+        "value": round(T / (us_step * 1e-6), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(us_step / 1e3, 6),
+        "us_per_call": round(us_step, 3),
+        "tflops": round(flops / (us_step * 1e-6) / 1e12, 2),
+        "hbm_gbs": round(nbytes / (us_step * 1e-6) / 1e9, 1),
+        "wall_us_per_step": round(wall_us, 3),
+        "dtype": "f16 exact codes x f16 hi/lo activations -> f32",
+        "config": {"workload": f"prefill_q4_8expert_4096x1536_T{T}", "tokens": T, "d_model": g.d_model,
+                   "d_ff": g.d_ff, "n_experts": E, "bits": 4, "group": 64, "algorithmic_flops": flops,
+                   "algorithmic_bytes": nbytes, "replicas_rotated": replicas, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm" if hbm_bound else "mfma",
+            "kernel": "one smoe_expert_ffn call = k_tb_prep + k_tb_gate_up + k_tb_down",
+            "achieved": round(gbs if hbm_bound else tflops, 2),
+            "peak": PEAK_HBM_GBS if hbm_bound else PEAK_F16_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round((gbs / PEAK_HBM_GBS) if hbm_bound else (tflops / PEAK_F16_TFLOPS), 4),
+            "traffic": load_traffic(f"prefill_q4_T{T}", "prefill"),
+            "per_call_us_events": round(per_call, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+
+
+def bf16_bench(args):
+    import torch
+    import workloads
+    import group_quantized_moe_amd as gq
+    L = gq.lib()
+    shape = {s[2]: s for s in workloads.BF16_SHAPES}[args.shape]
+    rows, cols, role, seed = shape
+    W, x = workloads.make_bf16(rows, cols, seed)
+    nbytes = rows * cols * 2 + cols * 4 + rows * 4
+    replicas = replica_count(rows * cols * 2)
+    Wd = to_dev(W)
+    reps = [Wd] + [Wd.clone() for _ in range(replicas - 1)]
+    xd = to_dev(x)
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        rc = L.matvec_bf16(reps[i % replicas].data_ptr(), rows, cols, xd.data_ptr(), y.data_ptr(), None, 0, sp)
+        if rc != 0:
+            raise gq.SmoeError("matvec_bf16", rc)
+
+    us_step, per_call, wall_us = time_steps(step, args.steps, args.warmup, stream)
+    gbs = nbytes / (us_step * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        n, dt, cores = cpu_oracle(lambda: oracle.matvec_bf16(W, x), args.cpu_budget, 1)
+        cpu = {"value": round(n * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"{n} whole {rows}x{cols} matvecs (f64 oracle, {dt:.1f} s)"}
+    return {
+        "metric": f"effective HBM GB/s of the bf16 matvec {rows}x{cols} ({role})",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(us_step / 1e3, 6),
+        "us_per_call": round(us_step, 3),
+        "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "wall_us_per_step": round(wall_us, 3),
+        "dtype": "bf16 x f32 -> f32",
+        "config": {"workload": f"bf16_{role}_{rows}x{cols}", "rows": rows, "cols": cols,
+                   "algorithmic_bytes_per_step": nbytes, "replicas_rotated": replicas,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_matvec_bf16 (one launch per call)",
+            "achieved": round(nbytes / (per_call * 1e-6) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (per_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(f"bf16_{role}", "bf16"),
+            "per_call_us_events": round(per_call, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "prefill", "bf16"])
+    ap.add_argument("--tokens", type=int, default=16, help="prefill: tokens per call")
+    ap.add_argument("--shape", default="q_proj", help="bf16: q_proj, o_proj, kv_proj or lm_head")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU code: it runs on one device)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "decode_q4":
+        line = decode_bench(args, workloads.Q4_GROUP8)
+    elif args.workload == "decode_q2":
+        line = decode_bench(args, workloads.Q2_GROUP8)
+    elif args.workload == "prefill":
+        line = prefill_bench(args)
+    else:
+        line = bf16_bench(args)
+    head = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded; stands in for trained weights)"}
+    print(json.dumps({**{k: line[k] for k in ("metric", "value", "unit")}, **head,
+                      **{k: v for k, v in line.items() if k not in ("metric", "value", "unit")}}), flush=True)
 
 
 if __name__ == "__main__":

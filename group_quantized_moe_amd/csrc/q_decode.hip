@@ -26,22 +26,25 @@
 //    contribution is s * (float(I) * 2^-k / Z + beta), where beta restores the
 //    code offset from the exact digit sum of the chunk.
 //
-//  * Registers instead of LDS for the vector.  A block of nw waves covers a
-//    tile of rows; the chunks of a row are split into nw contiguous slices,
-//    one per wave, and inside a wave LPR lanes share a row, so each lane always
-//    reads the same column chunk(s) and keeps that chunk's digit planes in
-//    registers for the whole kernel.  The row loop touches no LDS except the
-//    final cross-wave reduction.
+//  * Whole rows per wave.  lpr lanes (8..64, chosen per shape) share a row
+//    and lane lr owns chunks lr, lr + lpr, ... of it, so a wave covers 64/lpr
+//    rows per step; the row sum is a DPP / lane-shuffle reduction.  A lane
+//    always reads the same column chunks, so it copies those chunks' digit
+//    planes from LDS into registers once and the row loop touches no LDS and
+//    has no barrier.
 //
-//  * Persistent, pipelined blocks.  The grid is sized to what is resident on
-//    the device; each block walks its tiles in a grid stride and issues the
-//    16-byte code loads and scale loads of the next tile before it computes the
-//    current one, so HBM traffic and integer math overlap.
+//  * Persistent, pipelined waves.  Each block first builds the digit planes of
+//    the vector in LDS (one barrier); its waves then walk their row steps in a
+//    grid stride, two steps of 16-byte code loads and scale loads always in
+//    flight ahead of the step being reduced.  Loads are issued from clamped,
+//    always valid addresses so that no lane's load is conditional.
 //
-//  * Deterministic expert combine.  The down kernel runs blocks bound to one
-//    expert; for each row tile, every expert's router-weighted rows are written
-//    with agent-scope stores, and the last of the experts' blocks to finish the
-//    tile (an agent-scope counter) adds the experts in ascending order.
+//  * Deterministic expert combine.  down blocks are bound to one expert each.
+//    A wave keeps its router-weighted rows in LDS and, at its end, adds each
+//    row to a per-row 64-bit accumulator as an exact fixed-point term (2^-32
+//    resolution) together with a count; integer addition does not depend on
+//    the order of arrival, so the result is bitwise reproducible, and the
+//    expert that completes a row's count writes the row and clears the word.
 #include "launch.h"
 
 #include <algorithm>
@@ -440,7 +443,6 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 // expert, deferred to the end of the wave, is the only cross-block traffic.
 // A contribution of magnitude 2^20 or more does not fit the accumulator; it is
 // added as a NaN marker so that the row comes out NaN rather than wrong.
-constexpr int kAccFracBits = 32;
 constexpr int kAccCountShift = 59;
 constexpr unsigned long long kAccBias = 1ull << 52;    // keeps every term non-negative
 constexpr unsigned long long kAccNan = 1ull << 58;     // set in the sum when a term overflowed
