@@ -255,54 +255,6 @@ __device__ __forceinline__ float chunk_contrib(const uint4 q, float s, const Chu
     return s * fmaf((float)chunk_idot<BITS>(q, cv), cv.alpha, cv.beta);
 }
 
-// Lane -> chunk mapping of a wave that owns whole rows: lpr lanes (a power of
-// two, 8..64, uniform over the launch) share a row, so a wave covers 64/lpr rows
-// per step; lane lr owns chunks lr, lr + lpr, ..., lr + (NCH-1)*lpr.
-template <int NCH>
-struct RowLanes {
-    int lr, slot, rs, c[NCH];
-    bool valid[NCH];
-    __device__ __forceinline__ RowLanes(int cpr, int lpr)
-    {
-        const int lane = threadIdx.x & 63;
-        const int sh = __builtin_ctz(lpr);
-        lr = lane & (lpr - 1);
-        slot = lane >> sh;
-        rs = 64 >> sh;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            c[k] = lr + lpr * k;
-            valid[k] = c[k] < cpr;
-        }
-    }
-};
-
-// Sum over aligned groups of lpr lanes (lpr uniform): DPP inside 16-lane rows,
-// lane shuffles across rows.
-__device__ __forceinline__ float lane_group_sum_rt(float v, int lpr)
-{
-    if (lpr >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-    if (lpr >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-    if (lpr >= 8) v += dpp<0x141>(v);   // row_half_mirror
-    if (lpr >= 16) v += dpp<0x140>(v);  // row_mirror
-    if (lpr >= 32) v += __shfl_xor(v, 16);
-    if (lpr >= 64) v += __shfl_xor(v, 32);
-    return v;
-}
-
-// Code and scale registers of one wave step (one row per lane group) for M
-// matrices.  Loads are issued unconditionally from clamped, always in-bounds
-// addresses; `ok` marks the lanes whose load is real, and the scale of any
-// other lane is replaced by zero when the step is computed.  (A divergent
-// "load, else zero the registers" would make the compiler wait for the load
-// before the zeroing write, which serialises the prefetch.)
-template <int NCH, int M>
-struct StepRegs {
-    uint4 q[NCH][M];
-    float s[NCH][M];
-    bool ok[NCH];
-};
-
 // Dynamic LDS: the input vector's digit planes,
 //   cmax   f32 [chunks4]        chunks rounded up to 4
 //   dwsum  i32 [ndw]            ndw = code dwords per row = 4 * chunks
@@ -338,91 +290,210 @@ constexpr int kMaxQCols = 8192;
 template <int BITS>
 constexpr int kGroupsPerThread = (kMaxQCols / DigitLayout<BITS>::kColsPerDw + kBlockThreads - 1) / kBlockThreads;
 
+// Lanes of a whole-row wave with adjacent chunks: lpr lanes share a row and
+// lane lr owns chunks lr*NCH .. lr*NCH + NCH - 1 of it, so a lane's chunks are
+// one contiguous run of its row (and, when NCH chunks fit in one quantisation
+// group, share one scale).  Chunks past the row end are idle: their digit
+// planes and epilogue constants are zero and their loads read a valid chunk.
+// Offsets are per lane and constant for the whole kernel: code bytes from the
+// start of the step's first row, scale bytes from the start of its scale row.
+template <int NCH>
+struct AdjLanes {
+    int lr, slot, rs;
+    int c[NCH];
+    bool valid[NCH];
+    unsigned coff[NCH];   // slot * row_bytes + 16 * chunk
+    unsigned soff[NCH];   // 4 * (slot * gpr + group of chunk)
+    __device__ __forceinline__ AdjLanes(int cpr, int lpr, int cpc, int group, size_t row_bytes, int gpr)
+    {
+        const int lane = threadIdx.x & 63;
+        const int sh = __builtin_ctz(lpr);
+        lr = lane & (lpr - 1);
+        slot = lane >> sh;
+        rs = 64 >> sh;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            c[k] = lr * NCH + k;
+            valid[k] = c[k] < cpr;
+            const int cc = valid[k] ? c[k] : cpr - 1;
+            coff[k] = (unsigned)(slot * row_bytes + 16u * cc);
+            soff[k] = 4u * (unsigned)(slot * gpr + cc * cpc / group);
+        }
+    }
+    // Lane that holds the row sum after group_sum.
+    __device__ __forceinline__ bool writer(int lpr) const { return lpr >= 32 ? lr == lpr - 1 : lr == 0; }
+};
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over aligned groups of lpr lanes, all in DPP (no LDS).  For lpr <= 16
+// every lane of a group gets the sum; for 32 and 64 it lands in the group's
+// last lane (row_bcast:15 adds row 0 into row 1 and row 2 into row 3,
+// row_bcast:31 adds lane 31 into rows 2 and 3).
+__device__ __forceinline__ float group_sum(float v, int lpr)
+{
+    if (lpr >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (lpr >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (lpr >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if (lpr >= 16) v += dpp<0x140>(v);  // row_mirror
+    if (lpr >= 32) v += dpp_rows<0x142, 0xA>(v);
+    if (lpr >= 64) v += dpp_rows<0x143, 0xC>(v);
+    return v;
+}
+
+// SiLU(t) = t / (1 + e^-t) with the hardware base-2 exponential and
+// reciprocal (each within about one ulp): a few ulp overall, and the right
+// limits (t for large t, -0 for very negative t, NaN for NaN).
+__device__ __forceinline__ float silu_hw(float t)
+{
+    const float e = __builtin_amdgcn_exp2f(t * -1.44269504088896341f);
+    return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Code and scale registers of one step: NCH chunks of M matrices for the
+// lane's row.  With one_scale, scale 0 stands for all of the lane's chunks.
+template <int NCH, int M>
+struct Stage {
+    uint4 q[NCH][M];
+    float s[NCH][M];
+};
+
+template <int NCH, int M>
+__device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *const *codes, const float *const *scales,
+                                           size_t code_row, size_t scale_row, const AdjLanes<NCH> &ln,
+                                           bool one_scale, bool clamp, int row0, int rows, size_t row_bytes, int gpr)
+{
+    if (!clamp) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint8_t *cb = codes[m] + code_row;
+            const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]) + scale_row;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                t.q[k][m] = *reinterpret_cast<const uint4 *>(cb + ln.coff[k]);
+                if (k == 0 || !one_scale) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
+            }
+        }
+    } else {
+        // Last, partial step of a matrix: rows past the end read the last row.
+        const int r = min(row0 + ln.slot, rows - 1);
+        const int dr = r - row0 - ln.slot;  // <= 0
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint8_t *cb = codes[m] + code_row + (ptrdiff_t)dr * (ptrdiff_t)row_bytes;
+            const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]) + scale_row + (ptrdiff_t)dr * gpr * 4;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                t.q[k][m] = *reinterpret_cast<const uint4 *>(cb + ln.coff[k]);
+                if (k == 0 || !one_scale) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
+            }
+        }
+    }
+}
+
+// Row sums of matrix m for the lane's chunks (before the cross-lane sum).
+template <int BITS, int NCH, int M>
+__device__ __forceinline__ float stage_dot(const Stage<NCH, M> &t, int m, const ChunkVec<BITS> *cv, bool one_scale)
+{
+    if (one_scale) {
+        float p = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) p += fmaf((float)chunk_idot<BITS>(t.q[k][m], cv[k]), cv[k].alpha, cv[k].beta);
+        return t.s[0][m] * p;
+    }
+    float y = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][m], t.s[k][m], cv[k]);
+    return y;
+}
+
+// Step cursor over the steps of consecutive matrices: `spm` steps of `rs`
+// rows per matrix; tracks the matrix index and first row without division.
+struct Cursor {
+    int m, s;   // matrix, step within it
+    __device__ __forceinline__ void init(int step, int spm) { m = step / spm; s = step - m * spm; }
+    __device__ __forceinline__ void next(int spm) { if (++s == spm) { s = 0; ++m; } }
+};
+
 // gate_up: hidden[e][i] = SiLU(G_e x)[i] * (U_e x)[i] for every expert.
 //
-// Blocks are persistent; each block builds the digit planes of x in LDS once,
-// every lane copies the planes of its chunks into registers, and from then on
-// each wave streams whole rows on its own: no LDS and no barrier in the row
-// loop, the codes and scales of the next step are in flight while a step is
-// reduced.  Wave steps are numbered expert by expert; global wave w takes steps
-// w, w + W, w + 2W, ... of the E * ceil(d_ff / rs) steps.
-template <int BITS, int NCH>
+// Blocks are persistent.  Each builds the digit planes of x in LDS once (one
+// barrier), every lane copies the planes of its chunks into registers, and
+// from then on each wave streams whole rows on its own.  Wave w takes a
+// contiguous range of the E * ceil(d_ff / rs) row steps (experts in order),
+// with DEPTH steps of code and scale loads in flight ahead of the step being
+// reduced; the first DEPTH steps are issued before the planes are built.
+template <int BITS, int NCH, int DEPTH>
 __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
     extern __shared__ __align__(16) unsigned char smem[];
     const int nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int cpr = a.d_model / CPC;
-    const RowLanes<NCH> rl(cpr, a.lpr_g);
-    const PlaneLds<BITS> lds(smem, a.d_model);
     const size_t row_bytes = (size_t)a.d_model * BITS / 8;
     const int gpr = a.d_model / a.group;
-    const int spe = (a.d_ff + rl.rs - 1) / rl.rs;  // wave steps per expert
+    const AdjLanes<NCH> ln(cpr, a.lpr_g, CPC, a.group, row_bytes, gpr);
+    const bool one_scale = a.group % (NCH * CPC) == 0;
+    const PlaneLds<BITS> lds(smem, a.d_model);
+    const int rs = ln.rs;
+    const int spe = (a.d_ff + rs - 1) / rs;
     const int nsteps = a.n_experts * spe;
     const int W = gridDim.x * nw;
-    int gi[NCH];
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) gi[k] = rl.valid[k] ? rl.c[k] * CPC / a.group : 0;
+    const int wg = blockIdx.x * nw + wave;
+    const int sb = (int)((long)wg * nsteps / W), se = (int)((long)(wg + 1) * nsteps / W);
 
-    auto load_step = [&](StepRegs<NCH, 2> &t, int step) {
-        const int e = step / spe;
-        const int r = (step - e * spe) * rl.rs + rl.slot;
-        const int rc = r < a.d_ff ? r : a.d_ff - 1;
-        const QPtr G = a.gate[e], U = a.up[e];
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int cc = rl.valid[k] ? rl.c[k] : 0;
-            const size_t off = (size_t)rc * row_bytes + (size_t)cc * 16;
-            t.q[k][0] = load16(G.codes + off);
-            t.q[k][1] = load16(U.codes + off);
-            t.s[k][0] = G.scales[(size_t)rc * gpr + gi[k]];
-            t.s[k][1] = U.scales[(size_t)rc * gpr + gi[k]];
-            t.ok[k] = rl.valid[k] && r < a.d_ff;
-        }
+    auto load = [&](Stage<NCH, 2> &t, const Cursor &c) {
+        const int row0 = c.s * rs;
+        const uint8_t *codes[2] = {a.gate[c.m].codes, a.up[c.m].codes};
+        const float *scales[2] = {a.gate[c.m].scales, a.up[c.m].scales};
+        load_stage<NCH, 2>(t, codes, scales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln, one_scale,
+                           row0 + rs > a.d_ff, row0, a.d_ff, row_bytes, gpr);
     };
 
-    // Order of the prologue: the input vector's loads, then the first two steps'
-    // code loads, then the digit planes (which wait only for the vector).  The
-    // wave index is made explicitly scalar, so that the step, the expert and the
-    // expert's matrix pointers live in SGPRs (scalar loads from the kernel
-    // arguments) rather than behind a vector load in front of every step.
+    // The vector's loads go first, then the first steps' code loads, then the
+    // digit planes (which wait only for the vector).
     VecRegs<BITS, kGroupsPerThread<BITS>> xr;
     load_vec_regs<BITS>(a.x, a.d_model, xr);
-    int step = blockIdx.x * nw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    StepRegs<NCH, 2> A, B;
-    if (step < nsteps) load_step(A, step);
-    if (step + W < nsteps) load_step(B, step + W);
+    Stage<NCH, 2> S[DEPTH];
+    Cursor cl;
+    cl.init(sb, spe);
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+        if (sb + i < se) {
+            load(S[i], cl);
+            cl.next(spe);
+        }
 
     build_planes<BITS>(xr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k)
-        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, rl.c[k], rl.valid[k], cv[k]);
+        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
 
-    auto compute_step = [&](const StepRegs<NCH, 2> &t, int step) {
-        float g = 0.0f, u = 0.0f;
+    Cursor cc;
+    cc.init(sb, spe);
+    for (int base = sb; base < se; base += DEPTH) {
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            g += chunk_contrib<BITS>(t.q[k][0], t.ok[k] ? t.s[k][0] : 0.0f, cv[k]);
-            u += chunk_contrib<BITS>(t.q[k][1], t.ok[k] ? t.s[k][1] : 0.0f, cv[k]);
+        for (int i = 0; i < DEPTH; ++i) {
+            if (base + i < se) {
+                float g = stage_dot<BITS, NCH, 2>(S[i], 0, cv, one_scale);
+                float u = stage_dot<BITS, NCH, 2>(S[i], 1, cv, one_scale);
+                g = group_sum(g, a.lpr_g);
+                u = group_sum(u, a.lpr_g);
+                const int r = cc.s * rs + ln.slot;
+                if (ln.writer(a.lpr_g) && r < a.d_ff) a.hidden[(size_t)cc.m * a.d_ff + r] = silu_hw(g) * u;
+                cc.next(spe);
+                if (base + i + DEPTH < se) {
+                    load(S[i], cl);
+                    cl.next(spe);
+                }
+            }
         }
-        g = lane_group_sum_rt(g, a.lpr_g);
-        u = lane_group_sum_rt(u, a.lpr_g);
-        const int e = step / spe;
-        const int r = (step - e * spe) * rl.rs + rl.slot;
-        if (rl.lr == 0 && r < a.d_ff) a.hidden[(size_t)e * a.d_ff + r] = silu(g) * u;
-    };
-
-    while (step < nsteps) {
-        const int s1 = step + W;
-        compute_step(A, step);
-        if (s1 >= nsteps) break;
-        const int s2 = s1 + W;
-        if (s2 < nsteps) load_step(A, s2);
-        compute_step(B, s1);
-        const int s3 = s2 + W;
-        if (s3 < nsteps) load_step(B, s3);
-        step = s2;
     }
 }
 
@@ -463,104 +534,89 @@ __device__ __forceinline__ float acc_value(unsigned long long sum, int n)
     return (float)((double)fixed * (1.0 / 4294967296.0));
 }
 
-template <int BITS, int NCH>
+template <int BITS, int NCH, int DEPTH>
 __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
     extern __shared__ __align__(16) unsigned char smem[];
     const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int E = a.n_experts;
     const int cpr = a.d_ff / CPC;
-    const RowLanes<NCH> rl(cpr, a.lpr_d);
-    const PlaneLds<BITS> lds(smem, a.d_ff);
     const size_t row_bytes = (size_t)a.d_ff * BITS / 8;
     const int gpr = a.d_ff / a.group;
+    const AdjLanes<NCH> ln(cpr, a.lpr_d, CPC, a.group, row_bytes, gpr);
+    const bool one_scale = a.group % (NCH * CPC) == 0;
+    const PlaneLds<BITS> lds(smem, a.d_ff);
+    const int rs = ln.rs;
     const int e = blockIdx.x % E;
     const int bpe = gridDim.x / E;                 // blocks per expert
     const int We = bpe * nw;                       // waves per expert
-    const int nsteps = (a.d_model + rl.rs - 1) / rl.rs;
-    const int w0 = (blockIdx.x / E) * nw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const QPtr D = a.down[e];
+    const int nsteps = (a.d_model + rs - 1) / rs;
+    const int iw = (blockIdx.x / E) * nw + wave;   // this wave among its expert's waves
+    const int sb = (int)((long)iw * nsteps / We), se = (int)((long)(iw + 1) * nsteps / We);
+    const uint8_t *dcodes[1] = {a.down[e].codes};
+    const float *dscales[1] = {a.down[e].scales};
     const float rw = a.route_w ? a.route_w[e] : 1.0f;
     // This wave's router-weighted rows, kept until the deferred combine.
-    float *mine = reinterpret_cast<float *>(smem + plane_lds_bytes<BITS>(a.d_ff)) +
-                  (threadIdx.x >> 6) * a.dn_rows_per_wave;
-    int gi[NCH];
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) gi[k] = rl.valid[k] ? rl.c[k] * CPC / a.group : 0;
-
-    auto load_step = [&](StepRegs<NCH, 1> &t, int step) {
-        const int r = step * rl.rs + rl.slot;
-        const int rc = r < a.d_model ? r : a.d_model - 1;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const int cc = rl.valid[k] ? rl.c[k] : 0;
-            t.q[k][0] = load16(D.codes + (size_t)rc * row_bytes + (size_t)cc * 16);
-            t.s[k][0] = D.scales[(size_t)rc * gpr + gi[k]];
-            t.ok[k] = rl.valid[k] && r < a.d_model;
-        }
+    float *mine = reinterpret_cast<float *>(smem + ((plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15))) +
+                  wave * a.dn_rows_per_wave;
+    auto load = [&](Stage<NCH, 1> &t, int step) {
+        const int row0 = step * rs;
+        load_stage<NCH, 1>(t, dcodes, dscales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln, one_scale,
+                           row0 + rs > a.d_model, row0, a.d_model, row_bytes, gpr);
     };
 
     if ((int)blockIdx.x >= bpe * E) return;  // whole block idle: no barrier follows for it
     VecRegs<BITS, kGroupsPerThread<BITS>> hr;
     load_vec_regs<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, hr);
-    int step = w0;
-    StepRegs<NCH, 1> A, B;
-    if (step < nsteps) load_step(A, step);
-    if (step + We < nsteps) load_step(B, step + We);
+    Stage<NCH, 1> S[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+        if (sb + i < se) load(S[i], sb + i);
 
     build_planes<BITS>(hr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k)
-        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, rl.c[k], rl.valid[k], cv[k]);
+        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
 
-    auto compute_step = [&](const StepRegs<NCH, 1> &t, int step) {
-        float y = 0.0f;
+    for (int base = sb; base < se; base += DEPTH) {
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][0], t.ok[k] ? t.s[k][0] : 0.0f, cv[k]);
-        y = lane_group_sum_rt(y, a.lpr_d);
-        const int r = step * rl.rs + rl.slot;
-        if (rl.lr == 0 && r < a.d_model) {
-            if (E == 1)
-                a.out[r] = y * rw;
-            else
-                mine[((step - w0) / We) * rl.rs + rl.slot] = y * rw;
+        for (int i = 0; i < DEPTH; ++i) {
+            const int st = base + i;
+            if (st < se) {
+                float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv, one_scale);
+                y = group_sum(y, a.lpr_d);
+                const int r = st * rs + ln.slot;
+                if (ln.writer(a.lpr_d) && r < a.d_model) {
+                    if (E == 1)
+                        a.out[r] = y * rw;
+                    else
+                        mine[(st - sb) * rs + ln.slot] = y * rw;
+                }
+                if (st + DEPTH < se) load(S[i], st + DEPTH);
+            }
         }
-    };
-
-    while (step < nsteps) {
-        const int s1 = step + We;
-        compute_step(A, step);
-        if (s1 >= nsteps) break;
-        const int s2 = s1 + We;
-        if (s2 < nsteps) load_step(A, s2);
-        compute_step(B, s1);
-        const int s3 = s2 + We;
-        if (s3 < nsteps) load_step(B, s3);
-        step = s2;
     }
 
     if (E > 1) {
-        // One 64-bit addition per row of this wave, all rows at once (lane j
-        // takes the wave's j-th row); the lane that completes a row writes it.
-        // The rows were stored to LDS by lanes of this same wave, whose LDS
+        // One 64-bit addition per row of this wave (lane j takes its j-th row);
+        // the rows were written to LDS by lanes of this same wave, whose LDS
         // accesses complete in order.
         __builtin_amdgcn_wave_barrier();
-        const int my_steps = w0 < nsteps ? (nsteps - 1 - w0) / We + 1 : 0;
-        const int my_rows = my_steps * rl.rs;
+        const int r0 = sb * rs;
+        const int my_rows = min(se * rs, a.d_model) - r0;
         for (int j0 = 0; j0 < my_rows; j0 += 64) {
             const int j = j0 + lane;
             if (j < my_rows) {
-                const int r = (w0 + (j / rl.rs) * We) * rl.rs + (j % rl.rs);
-                if (r < a.d_model) {
-                    const unsigned long long term = acc_term(mine[j]);
-                    const unsigned long long sum =
-                        __hip_atomic_fetch_add(a.row_acc + r, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + term;
-                    if ((int)(sum >> kAccCountShift) == E) {
-                        a.out[r] = acc_value(sum, E);
-                        __hip_atomic_store(a.row_acc + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                const int r = r0 + j;
+                const unsigned long long term = acc_term(mine[j]);
+                const unsigned long long sum =
+                    __hip_atomic_fetch_add(a.row_acc + r, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + term;
+                if ((int)(sum >> kAccCountShift) == E) {
+                    a.out[r] = acc_value(sum, E);
+                    __hip_atomic_store(a.row_acc + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
@@ -583,25 +639,25 @@ int blocks_per_cu(const void *fn, int block, size_t lds)
     return n;
 }
 
-template <int BITS, int NCH>
+template <int BITS, int NCH, int DEPTH>
 hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
     const size_t lds = plane_lds_bytes<BITS>(a.d_model);
-    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH>);
+    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, DEPTH>);
     const long cap = (long)cus * blocks_per_cu(fn, block, lds);
     if (cap < 1) return hipErrorInvalidConfiguration;
     const long steps = (long)a.n_experts * ((a.d_ff + 64 / p.lpr_g - 1) / (64 / p.lpr_g));
     const long grid = std::max(1L, std::min(cap, (steps + p.nw - 1) / p.nw));
-    hipLaunchKernelGGL((k_gate_up<BITS, NCH>), dim3((unsigned)grid), dim3(block), lds, st, a);
+    hipLaunchKernelGGL((k_gate_up<BITS, NCH, DEPTH>), dim3((unsigned)grid), dim3(block), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BITS, int NCH>
+template <int BITS, int NCH, int DEPTH>
 hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH>);
+    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, DEPTH>);
     const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
     // Resident blocks: the occupancy query's answer, but at most two blocks of
     // this size per CU (more were measured not to be co-resident, which puts a
@@ -614,7 +670,8 @@ hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
     const long waves = per_expert * p.nw;
     a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
     const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
-    hipLaunchKernelGGL((k_down<BITS, NCH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st, a);
+    hipLaunchKernelGGL((k_down<BITS, NCH, DEPTH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
+                       a);
     return hipGetLastError();
 }
 
@@ -642,6 +699,30 @@ bool row_map(int bits, int cpr, int *lpr_out, int *nch_out)
     return true;
 }
 
+// Among the mappings with the fewest idle lanes, the one with the most chunks
+// per lane (the most bytes per step).  down rows are short (d_ff columns), so a
+// wave covers several rows per step this way and keeps more bytes in flight.
+bool row_map_wide(int bits, int cpr, int *lpr_out, int *nch_out)
+{
+    const int max_nch = bits == 4 ? 4 : 2;
+    double best_waste = 2.0;
+    int bl = 0, bn = 0;
+    for (int nch = 1; nch <= max_nch; ++nch)
+        for (int lpr = 8; lpr <= 64; lpr *= 2) {
+            if (lpr * nch < cpr) continue;
+            const double waste = 1.0 - (double)cpr / ((double)lpr * nch);
+            if (waste < best_waste - 1e-9 || (waste < best_waste + 1e-9 && nch > bn)) {
+                best_waste = waste;
+                bl = lpr;
+                bn = nch;
+            }
+        }
+    if (!bl) return false;
+    *lpr_out = bl;
+    *nch_out = bn;
+    return true;
+}
+
 }  // namespace
 
 bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, DecodePlan *p)
@@ -650,16 +731,20 @@ bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, Decod
     const int cpc = 128 / bits;
     DecodePlan q{mode, 8, 64, 1, 64, 1, d_model, d_ff};
     if (mode != kDownOnly && !row_map(bits, d_model / cpc, &q.lpr_g, &q.nch_g)) return false;
-    if (mode != kGateUpOnly && !row_map(bits, d_ff / cpc, &q.lpr_d, &q.nch_d)) return false;
+    if (mode != kGateUpOnly && !row_map_wide(bits, d_ff / cpc, &q.lpr_d, &q.nch_d)) return false;
     *p = q;
     return true;
 }
 
 int decode_rows_per_tile(int lpr) { return 64 / lpr; }
 
+// Steps in flight per wave (the register ring of code and scale loads).
+constexpr int kGateUpDepth = 2;
+constexpr int kDownDepth = 2;
+
 hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, N) if (bits == B && p.nch_g == N) return run_gate_up<B, N>(p, a, cus, st);
+#define SMOE_RUN(B, N) if (bits == B && p.nch_g == N) return run_gate_up<B, N, kGateUpDepth>(p, a, cus, st);
     SMOE_RUN(4, 1) SMOE_RUN(4, 2) SMOE_RUN(4, 3) SMOE_RUN(4, 4) SMOE_RUN(2, 1) SMOE_RUN(2, 2)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
@@ -667,7 +752,7 @@ hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, in
 
 hipError_t launch_down(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, N) if (bits == B && p.nch_d == N) return run_down<B, N>(p, a, cus, st);
+#define SMOE_RUN(B, N) if (bits == B && p.nch_d == N) return run_down<B, N, kDownDepth>(p, a, cus, st);
     SMOE_RUN(4, 1) SMOE_RUN(4, 2) SMOE_RUN(4, 3) SMOE_RUN(4, 4) SMOE_RUN(2, 1) SMOE_RUN(2, 2)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;

@@ -17,8 +17,8 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// Device properties, queried once per device ("device limits are queried,
-// never guessed").
+// Device properties, queried once per device (limits come from the device,
+// never from constants).
 struct DeviceInfo {
     bool ok;
     int cus;
