@@ -322,12 +322,28 @@ def bf16_bench(args):
     }
 
 
+def copy_calibration(args):
+    """A plain device-to-device copy of 256 MiB (torch's copy kernel): the
+    counter runs divide FETCH_SIZE / WRITE_SIZE of a kernel by what the same
+    counters read for this copy of known size."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    us_step, per_call, wall_us = time_steps(lambda i: dst.copy_(src), args.steps, args.warmup, stream)
+    return {"metric": "device-to-device copy of 256 MiB (counter calibration)",
+            "value": round(2 * n / (us_step * 1e-6) / 1e9, 1), "unit": "GB/s (read + write)",
+            "ms_per_step": round(us_step / 1e3, 6), "bytes_read": n, "bytes_written": n,
+            "dtype": "u8", "config": {"workload": "copy_256MiB"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "prefill", "bf16"])
+    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "prefill", "bf16", "copy"])
     ap.add_argument("--tokens", type=int, default=16, help="prefill: tokens per call")
     ap.add_argument("--shape", default="q_proj", help="bf16: q_proj, o_proj, kv_proj or lm_head")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -349,6 +365,8 @@ def main():
         line = decode_bench(args, workloads.Q2_GROUP8)
     elif args.workload == "prefill":
         line = prefill_bench(args)
+    elif args.workload == "copy":
+        line = copy_calibration(args)
     else:
         line = bf16_bench(args)
     head = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,

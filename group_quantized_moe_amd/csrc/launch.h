@@ -36,7 +36,6 @@ struct DecodeArgs {
     float *out;              // [d_model]
     unsigned long long *row_acc;  // [d_model] exact expert sums, zero on entry and exit (n_experts > 1)
     int d_model, d_ff, group, n_experts;
-    int lpr_g, lpr_d;
     int dn_rows_per_wave;    // set by the down launcher
 };
 

@@ -222,30 +222,43 @@ __device__ __forceinline__ void load_chunk_vec(const uint32_t *planes, const flo
 // I = sum over the chunk of c_j * X_j, exact (|I| <= 2^30).  c_j = code - 8 at
 // 4 bits, code at 2 bits.  Digit partial sums are combined mod 2^32, which is
 // exact because the true I fits in int32.
+// Signed 4-bit dot of 8 lanes' nibbles without an accumulator input (the
+// non-accumulating form, so that no register has to be zeroed first).
+__device__ __forceinline__ int dot8_first(int a, int b)
+{
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 template <int BITS>
 __device__ __forceinline__ int chunk_idot(const uint4 q, const ChunkVec<BITS> &cv)
 {
     const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-    int acc[6] = {0, 0, 0, 0, 0, 0};
+    int acc[6];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         if constexpr (BITS == 4) {
             const int c = (int)(d[m] ^ 0x88888888u);
 #pragma unroll
-            for (int p = 0; p < 6; ++p) acc[p] = __builtin_amdgcn_sdot8(c, (int)cv.w[6 * m + p], acc[p], false);
+            for (int p = 0; p < 6; ++p)
+                acc[p] = m == 0 ? dot8_first(c, (int)cv.w[p])
+                                : __builtin_amdgcn_sdot8(c, (int)cv.w[6 * m + p], acc[p], false);
         } else {
             const int lo = (int)(d[m] & 0x33333333u);
             const int hi = (int)((d[m] >> 2) & 0x33333333u);
 #pragma unroll
             for (int p = 0; p < 6; ++p) {
-                acc[p] = __builtin_amdgcn_sdot8(lo, (int)cv.w[12 * m + p], acc[p], false);
+                acc[p] = m == 0 ? dot8_first(lo, (int)cv.w[p])
+                                : __builtin_amdgcn_sdot8(lo, (int)cv.w[12 * m + p], acc[p], false);
                 acc[p] = __builtin_amdgcn_sdot8(hi, (int)cv.w[12 * m + 6 + p], acc[p], false);
             }
         }
     }
-    uint32_t u = (uint32_t)acc[0];
+    // I = sum_p 16^p acc_p, by Horner (one shift-add per digit).
+    uint32_t u = (uint32_t)acc[5];
 #pragma unroll
-    for (int p = 1; p < 6; ++p) u += (uint32_t)acc[p] << (4 * p);
+    for (int p = 4; p >= 0; --p) u = (u << 4) + (uint32_t)acc[p];
     return (int)u;
 }
 
@@ -297,20 +310,19 @@ constexpr int kGroupsPerThread = (kMaxQCols / DigitLayout<BITS>::kColsPerDw + kB
 // planes and epilogue constants are zero and their loads read a valid chunk.
 // Offsets are per lane and constant for the whole kernel: code bytes from the
 // start of the step's first row, scale bytes from the start of its scale row.
-template <int NCH>
+template <int NCH, int LPR>
 struct AdjLanes {
-    int lr, slot, rs;
+    static constexpr int kRows = 64 / LPR;   // rows per step
+    int lr, slot;
     int c[NCH];
     bool valid[NCH];
     unsigned coff[NCH];   // slot * row_bytes + 16 * chunk
     unsigned soff[NCH];   // 4 * (slot * gpr + group of chunk)
-    __device__ __forceinline__ AdjLanes(int cpr, int lpr, int cpc, int group, size_t row_bytes, int gpr)
+    __device__ __forceinline__ AdjLanes(int cpr, int cpc, int group, size_t row_bytes, int gpr)
     {
         const int lane = threadIdx.x & 63;
-        const int sh = __builtin_ctz(lpr);
-        lr = lane & (lpr - 1);
-        slot = lane >> sh;
-        rs = 64 >> sh;
+        lr = lane & (LPR - 1);
+        slot = lane / LPR;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             c[k] = lr * NCH + k;
@@ -320,8 +332,8 @@ struct AdjLanes {
             soff[k] = 4u * (unsigned)(slot * gpr + cc * cpc / group);
         }
     }
-    // Lane that holds the row sum after group_sum.
-    __device__ __forceinline__ bool writer(int lpr) const { return lpr >= 32 ? lr == lpr - 1 : lr == 0; }
+    // Lane that holds the row sum after group_sum<LPR>.
+    __device__ __forceinline__ bool writer() const { return LPR >= 32 ? lr == LPR - 1 : lr == 0; }
 };
 
 template <int CTRL, int ROW_MASK>
@@ -330,18 +342,19 @@ __device__ __forceinline__ float dpp_rows(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Sum over aligned groups of lpr lanes, all in DPP (no LDS).  For lpr <= 16
+// Sum over aligned groups of LPR lanes, all in DPP (no LDS).  For LPR <= 16
 // every lane of a group gets the sum; for 32 and 64 it lands in the group's
 // last lane (row_bcast:15 adds row 0 into row 1 and row 2 into row 3,
 // row_bcast:31 adds lane 31 into rows 2 and 3).
-__device__ __forceinline__ float group_sum(float v, int lpr)
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v)
 {
-    if (lpr >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-    if (lpr >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-    if (lpr >= 8) v += dpp<0x141>(v);   // row_half_mirror
-    if (lpr >= 16) v += dpp<0x140>(v);  // row_mirror
-    if (lpr >= 32) v += dpp_rows<0x142, 0xA>(v);
-    if (lpr >= 64) v += dpp_rows<0x143, 0xC>(v);
+    if constexpr (LPR >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (LPR >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v += dpp<0x141>(v);   // row_half_mirror
+    if constexpr (LPR >= 16) v += dpp<0x140>(v);  // row_mirror
+    if constexpr (LPR >= 32) v += dpp_rows<0x142, 0xA>(v);
+    if constexpr (LPR >= 64) v += dpp_rows<0x143, 0xC>(v);
     return v;
 }
 
@@ -355,17 +368,17 @@ __device__ __forceinline__ float silu_hw(float t)
 }
 
 // Code and scale registers of one step: NCH chunks of M matrices for the
-// lane's row.  With one_scale, scale 0 stands for all of the lane's chunks.
+// lane's row.  With ONE, scale 0 stands for all of the lane's chunks.
 template <int NCH, int M>
 struct Stage {
     uint4 q[NCH][M];
     float s[NCH][M];
 };
 
-template <int NCH, int M>
+template <int NCH, int LPR, int M, bool ONE>
 __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *const *codes, const float *const *scales,
-                                           size_t code_row, size_t scale_row, const AdjLanes<NCH> &ln,
-                                           bool one_scale, bool clamp, int row0, int rows, size_t row_bytes, int gpr)
+                                           size_t code_row, size_t scale_row, const AdjLanes<NCH, LPR> &ln,
+                                           bool clamp, int row0, int rows, size_t row_bytes, int gpr)
 {
     if (!clamp) {
 #pragma unroll
@@ -375,7 +388,7 @@ __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *cons
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
                 t.q[k][m] = *reinterpret_cast<const uint4 *>(cb + ln.coff[k]);
-                if (k == 0 || !one_scale) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
+                if (k == 0 || !ONE) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
             }
         }
     } else {
@@ -389,17 +402,17 @@ __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *cons
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
                 t.q[k][m] = *reinterpret_cast<const uint4 *>(cb + ln.coff[k]);
-                if (k == 0 || !one_scale) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
+                if (k == 0 || !ONE) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
             }
         }
     }
 }
 
 // Row sums of matrix m for the lane's chunks (before the cross-lane sum).
-template <int BITS, int NCH, int M>
-__device__ __forceinline__ float stage_dot(const Stage<NCH, M> &t, int m, const ChunkVec<BITS> *cv, bool one_scale)
+template <int BITS, int NCH, int M, bool ONE>
+__device__ __forceinline__ float stage_dot(const Stage<NCH, M> &t, int m, const ChunkVec<BITS> *cv)
 {
-    if (one_scale) {
+    if constexpr (ONE) {
         float p = 0.0f;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) p += fmaf((float)chunk_idot<BITS>(t.q[k][m], cv[k]), cv[k].alpha, cv[k].beta);
@@ -427,7 +440,7 @@ struct Cursor {
 // contiguous range of the E * ceil(d_ff / rs) row steps (experts in order),
 // with DEPTH steps of code and scale loads in flight ahead of the step being
 // reduced; the first DEPTH steps are issued before the planes are built.
-template <int BITS, int NCH, int DEPTH>
+template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
 __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -437,10 +450,9 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     const int cpr = a.d_model / CPC;
     const size_t row_bytes = (size_t)a.d_model * BITS / 8;
     const int gpr = a.d_model / a.group;
-    const AdjLanes<NCH> ln(cpr, a.lpr_g, CPC, a.group, row_bytes, gpr);
-    const bool one_scale = a.group % (NCH * CPC) == 0;
+    const AdjLanes<NCH, LPR> ln(cpr, CPC, a.group, row_bytes, gpr);
     const PlaneLds<BITS> lds(smem, a.d_model);
-    const int rs = ln.rs;
+    constexpr int rs = AdjLanes<NCH, LPR>::kRows;
     const int spe = (a.d_ff + rs - 1) / rs;
     const int nsteps = a.n_experts * spe;
     const int W = gridDim.x * nw;
@@ -451,8 +463,8 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
         const int row0 = c.s * rs;
         const uint8_t *codes[2] = {a.gate[c.m].codes, a.up[c.m].codes};
         const float *scales[2] = {a.gate[c.m].scales, a.up[c.m].scales};
-        load_stage<NCH, 2>(t, codes, scales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln, one_scale,
-                           row0 + rs > a.d_ff, row0, a.d_ff, row_bytes, gpr);
+        load_stage<NCH, LPR, 2, ONE>(t, codes, scales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln,
+                                     row0 + rs > a.d_ff, row0, a.d_ff, row_bytes, gpr);
     };
 
     // The vector's loads go first, then the first steps' code loads, then the
@@ -481,12 +493,12 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
             if (base + i < se) {
-                float g = stage_dot<BITS, NCH, 2>(S[i], 0, cv, one_scale);
-                float u = stage_dot<BITS, NCH, 2>(S[i], 1, cv, one_scale);
-                g = group_sum(g, a.lpr_g);
-                u = group_sum(u, a.lpr_g);
+                float g = stage_dot<BITS, NCH, 2, ONE>(S[i], 0, cv);
+                float u = stage_dot<BITS, NCH, 2, ONE>(S[i], 1, cv);
+                g = group_sum<LPR>(g);
+                u = group_sum<LPR>(u);
                 const int r = cc.s * rs + ln.slot;
-                if (ln.writer(a.lpr_g) && r < a.d_ff) a.hidden[(size_t)cc.m * a.d_ff + r] = silu_hw(g) * u;
+                if (ln.writer() && r < a.d_ff) a.hidden[(size_t)cc.m * a.d_ff + r] = silu_hw(g) * u;
                 cc.next(spe);
                 if (base + i + DEPTH < se) {
                     load(S[i], cl);
@@ -534,7 +546,7 @@ __device__ __forceinline__ float acc_value(unsigned long long sum, int n)
     return (float)((double)fixed * (1.0 / 4294967296.0));
 }
 
-template <int BITS, int NCH, int DEPTH>
+template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
 __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -545,10 +557,9 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     const int cpr = a.d_ff / CPC;
     const size_t row_bytes = (size_t)a.d_ff * BITS / 8;
     const int gpr = a.d_ff / a.group;
-    const AdjLanes<NCH> ln(cpr, a.lpr_d, CPC, a.group, row_bytes, gpr);
-    const bool one_scale = a.group % (NCH * CPC) == 0;
+    const AdjLanes<NCH, LPR> ln(cpr, CPC, a.group, row_bytes, gpr);
     const PlaneLds<BITS> lds(smem, a.d_ff);
-    const int rs = ln.rs;
+    constexpr int rs = AdjLanes<NCH, LPR>::kRows;
     const int e = blockIdx.x % E;
     const int bpe = gridDim.x / E;                 // blocks per expert
     const int We = bpe * nw;                       // waves per expert
@@ -563,8 +574,8 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
                   wave * a.dn_rows_per_wave;
     auto load = [&](Stage<NCH, 1> &t, int step) {
         const int row0 = step * rs;
-        load_stage<NCH, 1>(t, dcodes, dscales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln, one_scale,
-                           row0 + rs > a.d_model, row0, a.d_model, row_bytes, gpr);
+        load_stage<NCH, LPR, 1, ONE>(t, dcodes, dscales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln,
+                                     row0 + rs > a.d_model, row0, a.d_model, row_bytes, gpr);
     };
 
     if ((int)blockIdx.x >= bpe * E) return;  // whole block idle: no barrier follows for it
@@ -586,10 +597,10 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
         for (int i = 0; i < DEPTH; ++i) {
             const int st = base + i;
             if (st < se) {
-                float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv, one_scale);
-                y = group_sum(y, a.lpr_d);
+                float y = stage_dot<BITS, NCH, 1, ONE>(S[i], 0, cv);
+                y = group_sum<LPR>(y);
                 const int r = st * rs + ln.slot;
-                if (ln.writer(a.lpr_d) && r < a.d_model) {
+                if (ln.writer() && r < a.d_model) {
                     if (E == 1)
                         a.out[r] = y * rw;
                     else
@@ -639,25 +650,25 @@ int blocks_per_cu(const void *fn, int block, size_t lds)
     return n;
 }
 
-template <int BITS, int NCH, int DEPTH>
+template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
 hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
     const size_t lds = plane_lds_bytes<BITS>(a.d_model);
-    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, DEPTH>);
+    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, LPR, ONE, DEPTH>);
     const long cap = (long)cus * blocks_per_cu(fn, block, lds);
     if (cap < 1) return hipErrorInvalidConfiguration;
     const long steps = (long)a.n_experts * ((a.d_ff + 64 / p.lpr_g - 1) / (64 / p.lpr_g));
     const long grid = std::max(1L, std::min(cap, (steps + p.nw - 1) / p.nw));
-    hipLaunchKernelGGL((k_gate_up<BITS, NCH, DEPTH>), dim3((unsigned)grid), dim3(block), lds, st, a);
+    hipLaunchKernelGGL((k_gate_up<BITS, NCH, LPR, ONE, DEPTH>), dim3((unsigned)grid), dim3(block), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BITS, int NCH, int DEPTH>
+template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
 hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, DEPTH>);
+    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, ONE, DEPTH>);
     const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
     // Resident blocks: the occupancy query's answer, but at most two blocks of
     // this size per CU (more were measured not to be co-resident, which puts a
@@ -670,7 +681,7 @@ hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
     const long waves = per_expert * p.nw;
     a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
     const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
-    hipLaunchKernelGGL((k_down<BITS, NCH, DEPTH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
+    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, ONE, DEPTH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
                        a);
     return hipGetLastError();
 }
@@ -683,7 +694,7 @@ bool row_map(int bits, int cpr, int *lpr_out, int *nch_out)
     double best = 1e30;
     int bl = 0, bn = 0;
     for (int nch = 1; nch <= max_nch; ++nch)
-        for (int lpr = 8; lpr <= 64; lpr *= 2) {
+        for (int lpr = 16; lpr <= 64; lpr *= 2) {
             if (lpr * nch < cpr) continue;
             const double waste = 1.0 - (double)cpr / ((double)lpr * nch);
             const double pen = 4.0 * waste + 0.5 * (nch - 1) * (bits == 4 ? 1.0 : 2.0);
@@ -708,7 +719,7 @@ bool row_map_wide(int bits, int cpr, int *lpr_out, int *nch_out)
     double best_waste = 2.0;
     int bl = 0, bn = 0;
     for (int nch = 1; nch <= max_nch; ++nch)
-        for (int lpr = 8; lpr <= 64; lpr *= 2) {
+        for (int lpr = 16; lpr <= 64; lpr *= 2) {
             if (lpr * nch < cpr) continue;
             const double waste = 1.0 - (double)cpr / ((double)lpr * nch);
             if (waste < best_waste - 1e-9 || (waste < best_waste + 1e-9 && nch > bn)) {
@@ -736,24 +747,39 @@ bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, Decod
     return true;
 }
 
-int decode_rows_per_tile(int lpr) { return 64 / lpr; }
-
 // Steps in flight per wave (the register ring of code and scale loads).
 constexpr int kGateUpDepth = 2;
 constexpr int kDownDepth = 2;
 
+// Kernels are compiled per (bits, chunks per lane, lanes per row, one scale per
+// lane): lanes per row 16, 32 or 64; chunks per lane 1..4 (4-bit) or 1..2 (2-bit).
+#define SMOE_FOR_LPR(X, B, N)                                                  \
+    X(B, N, 16, true) X(B, N, 16, false) X(B, N, 32, true) X(B, N, 32, false) \
+    X(B, N, 64, true) X(B, N, 64, false)
+#define SMOE_FOR_ALL(X)                                                        \
+    SMOE_FOR_LPR(X, 4, 1) SMOE_FOR_LPR(X, 4, 2) SMOE_FOR_LPR(X, 4, 3) SMOE_FOR_LPR(X, 4, 4) \
+    SMOE_FOR_LPR(X, 2, 1) SMOE_FOR_LPR(X, 2, 2)
+
+static bool one_scale(int bits, int nch, int group) { return group % (nch * (128 / bits)) == 0; }
+
 hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, N) if (bits == B && p.nch_g == N) return run_gate_up<B, N, kGateUpDepth>(p, a, cus, st);
-    SMOE_RUN(4, 1) SMOE_RUN(4, 2) SMOE_RUN(4, 3) SMOE_RUN(4, 4) SMOE_RUN(2, 1) SMOE_RUN(2, 2)
+    const bool one = one_scale(bits, p.nch_g, a.group);
+#define SMOE_RUN(B, N, L, O)                                                   \
+    if (bits == B && p.nch_g == N && p.lpr_g == L && one == O)               \
+        return run_gate_up<B, N, L, O, kGateUpDepth>(p, a, cus, st);
+    SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
 }
 
 hipError_t launch_down(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, N) if (bits == B && p.nch_d == N) return run_down<B, N, kDownDepth>(p, a, cus, st);
-    SMOE_RUN(4, 1) SMOE_RUN(4, 2) SMOE_RUN(4, 3) SMOE_RUN(4, 4) SMOE_RUN(2, 1) SMOE_RUN(2, 2)
+    const bool one = one_scale(bits, p.nch_d, a.group);
+#define SMOE_RUN(B, N, L, O)                                                   \
+    if (bits == B && p.nch_d == N && p.lpr_d == L && one == O)               \
+        return run_down<B, N, L, O, kDownDepth>(p, a, cus, st);
+    SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
 }

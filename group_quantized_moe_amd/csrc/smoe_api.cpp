@@ -193,8 +193,6 @@ int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group
     a.d_ff = d_ff;
     a.group = group;
     a.n_experts = 1;
-    a.lpr_g = plan.lpr_g;
-    a.lpr_d = plan.lpr_d;
     return launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, (hipStream_t)stream));
 }
 
@@ -223,8 +221,6 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
     a.d_ff = d_ff;
     a.group = group;
     a.n_experts = 1;
-    a.lpr_g = plan.lpr_g;
-    a.lpr_d = plan.lpr_d;
     return launch_status(smoe::launch_down(bits, plan, a, dev.cus, (hipStream_t)stream));
 }
 
@@ -322,8 +318,6 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     a.d_ff = d_ff;
     a.group = group;
     a.n_experts = n_experts;
-    a.lpr_g = plan.lpr_g;
-    a.lpr_d = plan.lpr_d;
     if ((rc = launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, st)))) return rc;
     return launch_status(smoe::launch_down(bits, plan, a, dev.cus, st));
 }
