@@ -39,10 +39,12 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense f16 matrix peak, TFLOP/s
 CSRC = "group_quantized_moe_amd/csrc/"
+# The kernel sources (device code, tiling and launch plan) behind each workload:
+# the counter-based traffic figures are only used while these are unchanged.
 KERNEL_SOURCES = {
-    "decode": [CSRC + "q_decode.hip", CSRC + "common.h", CSRC + "launch.h", CSRC + "smoe_api.cpp"],
-    "prefill": [CSRC + "q_batch.hip", CSRC + "common.h", CSRC + "launch.h", CSRC + "smoe_api.cpp"],
-    "bf16": [CSRC + "bf16_matvec.hip", CSRC + "common.h", CSRC + "launch.h", CSRC + "smoe_api.cpp"],
+    "decode": [CSRC + "q_decode.hip", CSRC + "common.h"],
+    "prefill": [CSRC + "q_batch.hip", CSRC + "common.h"],
+    "bf16": [CSRC + "bf16_matvec.hip", CSRC + "common.h"],
 }
 
 
@@ -139,7 +141,7 @@ def cpu_oracle(fn, budget_s, units_per_call):
     return n, time.perf_counter() - t0, oracle.threads()
 
 
-def decode_bench(args, spec):
+def decode_bench(args, spec, profile):
     import torch
     import workloads
     import group_quantized_moe_amd as gq
@@ -192,7 +194,7 @@ def decode_bench(args, spec):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(nbytes / (per_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(spec["name"], "decode"),
+            "traffic": load_traffic(profile, "decode"),
             "per_call_us_events": round(per_call, 3),
         },
         "cpu_baseline": cpu,
@@ -259,7 +261,7 @@ def prefill_bench(args):
             "peak": PEAK_HBM_GBS if hbm_bound else PEAK_F16_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": round((gbs / PEAK_HBM_GBS) if hbm_bound else (tflops / PEAK_F16_TFLOPS), 4),
-            "traffic": load_traffic(f"prefill_q4_T{T}", "prefill"),
+            "traffic": load_traffic(f"prefill_t{T}", "prefill"),
             "per_call_us_events": round(per_call, 3),
         },
         "cpu_baseline": cpu,
@@ -360,9 +362,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     if args.workload == "decode_q4":
-        line = decode_bench(args, workloads.Q4_GROUP8)
+        line = decode_bench(args, workloads.Q4_GROUP8, "decode_q4")
     elif args.workload == "decode_q2":
-        line = decode_bench(args, workloads.Q2_GROUP8)
+        line = decode_bench(args, workloads.Q2_GROUP8, "decode_q2")
     elif args.workload == "prefill":
         line = prefill_bench(args)
     elif args.workload == "copy":
