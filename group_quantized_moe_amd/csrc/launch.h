@@ -49,8 +49,10 @@ hipError_t launch_down(int bits, const DecodePlan &plan, const DecodeArgs &args,
 // ---------------------------------------------------------------------------
 
 // Activations in the workspace are f16 hi/lo halves in sigma order (element
-// 8b + i of a row holds column 8b + sigma(i), sigma = 0,4,1,5,2,6,3,7) with one
-// power-of-two exponent per (row, quantisation group).
+// 8b + i of a row holds column 8b + sigma(i), sigma = 0,4,1,5,2,6,3,7), scaled
+// by a power of two: one exponent per token for X, one per (token, group of
+// d_ff columns) for the hidden rows, kept as a factor that also holds the
+// router weight.
 struct TbArgs {
     QPtr gate[kMaxExperts];
     QPtr up[kMaxExperts];
@@ -59,18 +61,19 @@ struct TbArgs {
     const float *route_w;    // [T][n_experts] or null (weight 1)
     float *out;              // [T][d_model]
     _Float16 *xh, *xl;       // [T][d_model]
-    int *xe;                 // [T][d_model / group]
+    int *xe;                 // [T]
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
-    int *he;                 // [n_experts][T][d_ff / group]
-    int T, d_model, d_ff, group, n_experts;
+    float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
+    int T, t_pad, d_model, d_ff, group, n_experts;
     int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
     int ks_dn, rw_dn;        // down waves per block: rw_dn row slices x ks_dn (expert, group) slices
 };
 
-// Tiling of the three token-batch launches: 16*ntt tokens per block; waves per
-// block, block counts and dynamic LDS bytes of gate_up and down.
+// Tiling of the three token-batch launches: 16*ntt tokens per block, rt_gu row
+// tiles per gate_up wave; waves per block, block counts and dynamic LDS bytes
+// of gate_up and down.
 struct TbPlan {
-    int ntt;
+    int ntt, rt_gu;
     int rw_gu, ks_gu, gu_waves;
     long gu_blocks;
     size_t gu_lds;
@@ -78,6 +81,9 @@ struct TbPlan {
     long dn_blocks;
     size_t dn_lds;
 };
+
+// Token rows of the hidden-row factors are padded to a multiple of this.
+constexpr int kTokenPad = 32;
 
 // False if the shape is outside what the token-batch kernels cover (group
 // must be 32, 64, 96 or 128 columns at 4 bits, 64 or 128 at 2 bits).

@@ -11,28 +11,32 @@
 // Why the contraction can run on f16 MFMA without losing f32 accuracy:
 //  * a code c enters the matrix core as the f16 value c - Z (Z = 7.5 or 1.5),
 //    which is exact; the scale s/Z is applied per quantisation group afterwards;
-//  * an activation row is cut into quantisation groups; each group is scaled by
-//    a power of two 2^-e chosen so every scaled value is below 1 in magnitude,
-//    then written as hi + lo with hi = f16(v), lo = f16(v - hi): 22 significant
-//    bits, no overflow, and the scaling is undone exactly by ldexp;
+//  * activations are scaled by a power of two 2^-e so that every scaled value
+//    is below 1 in magnitude (one e per token for X, one per token and group of
+//    d_ff columns for the hidden rows), then written as hi + lo with
+//    hi = f16(v), lo = f16(v - hi): 22 significant bits, no overflow, and the
+//    scaling is undone exactly;
 //  * v_mfma_f32_16x16x32_f16 multiplies exactly and accumulates in f32; hi and
 //    lo go through two MFMAs into one accumulator per group, and the group's
-//    f32 result is multiplied by ldexp(s/Z, e) into the running output.
+//    f32 result is multiplied by its scale into the running output.
 //
-// Launch sequence (one stream): k_tb_prep (X -> hi/lo + exponents),
-// k_tb_gate_up (both projections, SiLU, H -> hi/lo + exponents per group of
-// d_ff columns), k_tb_down (all experts summed with the router weights in a
-// fixed order, so the result is deterministic; no atomics).
+// Launch sequence (one stream): k_tb_prep (X -> hi/lo halves + per-token
+// exponent), k_tb_gate_up (both projections, SiLU, hidden rows -> hi/lo halves
+// + one factor per (expert, group, token) that folds the group's power of two
+// and the router weight), k_tb_down (all experts summed in a fixed order, so
+// the result is deterministic; no atomics).
 //
-// Fragment layout of v_mfma_f32_16x16x32_f16 (lane l, q = l / 16, n = l % 16):
-//   A (16 x 32):  row n, k = 8q + i for element i = 0..7      <- weight codes
-//   B (32 x 16):  column n, k = 8q + i                          <- activations
-//   D (16 x 16):  rows 4q + i (i = 0..3), column n              -> outputs
-// Within one quantisation group of 32*KB columns, lane group q owns the 8*KB
-// columns [q*8KB, (q+1)*8KB), so its codes are one contiguous load; K-block j
-// uses columns q*8KB + 8j + sigma(i), sigma = (0,4,1,5,2,6,3,7).  sigma is the
-// order in which the nibble unpacking below yields codes; activations are
-// stored in the same order (element 8b + i holds column 8b + sigma(i)).
+// Orientation: tokens are the MFMA's M side, weight rows its N side.  For
+// v_mfma_f32_16x16x32_f16 (lane l, q = l / 16, n = l % 16):
+//   A (16 x 32):  token n, k = 8q + i for element i = 0..7   <- activations
+//   B (32 x 16):  row n,   k = 8q + i                         <- weight codes
+//   D (16 x 16):  tokens 4q + i (i = 0..3), row n             -> outputs
+// so a lane needs one scale per row tile and group.  Within one quantisation
+// group of 32*KB columns, lane group q owns the 8*KB columns [q*8KB,
+// (q+1)*8KB): its codes are one contiguous load, and K-block j uses columns
+// q*8KB + 8j + sigma(i), sigma = (0,4,1,5,2,6,3,7), the order in which the
+// nibble unpacking yields codes.  Activations are stored in the same order
+// (element 8b + i holds column 8b + sigma(i)).
 #include "common.h"
 #include "launch.h"
 
@@ -91,7 +95,7 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, CodeWords<BITS, KB>
     }
 }
 
-// A fragment of K-block j: the lane's 8 codes in sigma order as f16 (c - Z).
+// B fragment of K-block j: the lane's 8 codes in sigma order as f16 (c - Z).
 template <int BITS, int KB>
 __device__ __forceinline__ half8 code_frag(const CodeWords<BITS, KB> &c, int j)
 {
@@ -124,13 +128,6 @@ __device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
-    return v;
-}
-
 // Exponent e with |m| = f * 2^e, f in [0.5, 1) (0 for m == 0): v * 2^-e < 1.
 __device__ __forceinline__ int norm_exponent(float m)
 {
@@ -139,50 +136,85 @@ __device__ __forceinline__ int norm_exponent(float m)
     return e;
 }
 
+// Largest value over the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));  // row_mirror
+    return v;
+}
+
 // -------------------------------------------------------------------------
-// X -> hi/lo halves in sigma order + one exponent per (token, group).
-// One wave per (token, group).
-__global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, int rows, int cols,
-                                                 int group, _Float16 *__restrict__ xh,
+// X -> hi/lo halves in sigma order + one exponent per token.  One block per
+// token.
+__global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, int cols, _Float16 *__restrict__ xh,
                                                  _Float16 *__restrict__ xl, int *__restrict__ xe)
 {
-    const int lane = threadIdx.x & 63;
-    const int G = cols / group;
-    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= (long)rows * G) return;
-    const long t = pair / G;
-    const int g = (int)(pair % G);
-    const size_t base = (size_t)t * cols + (size_t)g * group;
+    __shared__ float s_max[4];
+    const size_t base = (size_t)blockIdx.x * cols;
     float m = 0.0f;
-    for (int c = lane; c < group; c += 64) m = fmaxf(m, fabsf(x[base + c]));
-    const int e = norm_exponent(wave_max(m));
-    for (int c = lane; c < group; c += 64) {
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) m = fmaxf(m, fabsf(x[base + c]));
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    const int e = norm_exponent(m);
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) {
         const float v = ldexpf(x[base + c], -e);
         const _Float16 h = (_Float16)v;
         const size_t pos = base + (c & ~7) + sigma_pos(c & 7);
         xh[pos] = h;
         xl[pos] = (_Float16)(v - (float)h);
     }
-    if (lane == 0) xe[pair] = e;
+    if (threadIdx.x == 0) xe[blockIdx.x] = e;
+}
+
+// One step of the K loop: the activation fragments of NTT token tiles and
+// the codes and scales of NB row tiles, for one quantisation group.
+template <int BITS, int KB, int NTT, int NB>
+struct TbStage {
+    half8 ah[NTT][KB], al[NTT][KB];
+    CodeWords<BITS, KB> cw[NB];
+    float s[NB];
+};
+
+// sum over the step's K-blocks of (hi + lo) x codes, for token tile tt and
+// row tile b: one f32 accumulator per quantisation group.
+template <int BITS, int KB, int NTT, int NB>
+__device__ __forceinline__ f32x4 group_mfma(const TbStage<BITS, KB, NTT, NB> &st, const half8 *bf, int tt)
+{
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        acc = mfma(st.ah[tt][j], bf[j], acc);
+        acc = mfma(st.al[tt][j], bf[j], acc);
+    }
+    return acc;
 }
 
 // -------------------------------------------------------------------------
-// Gate and up for one expert, one quantisation group of d_ff rows (the block's
-// H group) and 16*NTT tokens.  Wave (rw, ks): rows rw*16*RT .. +16*RT of the
-// H group in both matrices, quantisation groups [ks*G/KS, (ks+1)*G/KS) of
-// d_model.  Partial sums over ks are added in LDS in a fixed order.
+// Gate and up for one expert, one quantisation group of d_ff rows (the
+// block's "H group") and 16*NTT tokens.  Wave (rw, ks) covers rows
+// rw*16*RT .. +16*RT of the H group in both matrices and quantisation groups
+// [ks*G/KS, (ks+1)*G/KS) of d_model; partial sums over ks are added in LDS in
+// a fixed order.  The hidden rows are normalised per (token, H group), split
+// into hi/lo halves and stored with the factor r[t][e] * 2^e for down.
 template <int BITS, int KB, int NTT, int RT>
 __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
 {
     extern __shared__ float lds[];
-    constexpr int NM = 2;  // gate, up
-    constexpr int kTiles = NM * RT * NTT;
+    constexpr int NB = 2 * RT;            // gate row tiles, then up row tiles
+    constexpr int kTot = NB * NTT * 4;    // accumulator floats per lane
+    constexpr int DEPTH = 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KS = a.ks_gu, RW = a.rw_gu;
     const int ks = wave % KS, rw = wave / KS;
     const int q = lane >> 4, n = lane & 15;
-    const int group = a.group, d_model = a.d_model, d_ff = a.d_ff, T = a.T;
+    const int group = a.group, d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
     const int G = d_model / group, HG = d_ff / group;
     const int NTB = (T + 16 * NTT - 1) / (16 * NTT);
     int b = blockIdx.x;
@@ -190,190 +222,177 @@ __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
     b /= NTB;
     const int hg = b % HG;
     const int e = b / HG;
-    const int row0 = hg * group + rw * 16 * RT;
+    const int row0 = hg * group + rw * 16 * RT;   // first d_ff row of this wave
     const int t0 = tb * 16 * NTT;
     const size_t rs = (size_t)d_model * BITS / 8;
-    const QPtr mats[NM] = {a.gate[e], a.up[e]};
-
-    int tok[NTT];
+    const uint8_t *code_base[NB];
+    const float *scale_base[NB];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) tok[tt] = min(t0 + tt * 16 + n, T - 1);
-
-    f32x4 tot[NM][RT][NTT];
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+        for (int rt = 0; rt < RT; ++rt) {
+            const QPtr M = m == 0 ? a.gate[e] : a.up[e];
+            const int row = row0 + rt * 16 + n;
+            code_base[m * RT + rt] = M.codes + (size_t)row * rs + (size_t)(q * 8 * KB) * BITS / 8;
+            scale_base[m * RT + rt] = M.scales + (size_t)row * G;
+        }
+    const _Float16 *xh_base[NTT], *xl_base[NTT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+    for (int tt = 0; tt < NTT; ++tt) {
+        const size_t off = (size_t)min(t0 + tt * 16 + n, T - 1) * d_model + q * 8 * KB;
+        xh_base[tt] = a.xh + off;
+        xl_base[tt] = a.xl + off;
+    }
+    using Stage = TbStage<BITS, KB, NTT, NB>;
+    auto load = [&](Stage &st, int g) {
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) tot[m][rt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    const int gbeg = ks * G / KS, gend = (ks + 1) * G / KS;
-    for (int g = gbeg; g < gend; ++g) {
-        CodeWords<BITS, KB> cw[NM][RT];
-        float sc[NM][RT][4];
-        const size_t cofs = (size_t)(g * group + q * 8 * KB) * BITS / 8;
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                load_codes(mats[m].codes + (size_t)(row0 + rt * 16 + n) * rs + cofs, cw[m][rt]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sc[m][rt][i] = mats[m].scales[(size_t)(row0 + rt * 16 + 4 * q + i) * G + g] *
-                                   QFormat<BITS>::kInvZ;
-            }
-        half8 bh[NTT][KB], bl[NTT][KB];
-        int ex[NTT];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            const size_t xo = (size_t)tok[tt] * d_model + g * group + q * 8 * KB;
+        for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
-                bh[tt][j] = load_half8(a.xh + xo + 8 * j);
-                bl[tt][j] = load_half8(a.xl + xo + 8 * j);
+                st.ah[tt][j] = load_half8(xh_base[tt] + (size_t)g * group + 8 * j);
+                st.al[tt][j] = load_half8(xl_base[tt] + (size_t)g * group + 8 * j);
             }
-            ex[tt] = a.xe[(size_t)tok[tt] * G + g];
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) {
+            load_codes<BITS, KB>(code_base[bt] + (size_t)g * group * BITS / 8, st.cw[bt]);
+            st.s[bt] = scale_base[bt][g];
         }
+    };
+
+    f32x4 tot[NB][NTT];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+    for (int bt = 0; bt < NB; ++bt)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                half8 af[KB];
+        for (int tt = 0; tt < NTT; ++tt) tot[bt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // Every wave has at least one group (KS <= G).  Ring loads are
+    // unconditional (past the last group they re-read it) so that waiting for
+    // one stage leaves the other in flight.
+    const int gbeg = ks * G / KS, gend = (ks + 1) * G / KS;
+    Stage S[DEPTH];
 #pragma unroll
-                for (int j = 0; j < KB; ++j) af[j] = code_frag<BITS, KB>(cw[m][rt], j);
+    for (int i = 0; i < DEPTH; ++i) load(S[i], min(gbeg + i, gend - 1));
+    for (int base = gbeg; base < gend; base += DEPTH) {
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < DEPTH; ++i) {
+            const int g = base + i;
+            if (g < gend) {
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) {
-                        acc = mfma(af[j], bh[tt][j], acc);
-                        acc = mfma(af[j], bl[tt][j], acc);
+                for (int bt = 0; bt < NB; ++bt) {
+                    half8 bf[KB];
+#pragma unroll
+                    for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw[bt], j);
+                    const float s = S[i].s[bt] * QFormat<BITS>::kInvZ;
+#pragma unroll
+                    for (int tt = 0; tt < NTT; ++tt) {
+                        const f32x4 acc = group_mfma<BITS, KB, NTT, NB>(S[i], bf, tt);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) tot[bt][tt][r] = fmaf(s, acc[r], tot[bt][tt][r]);
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        tot[m][rt][tt][i] = fmaf(ldexpf(sc[m][rt][i], ex[tt]), acc[i], tot[m][rt][tt][i]);
                 }
             }
+            load(S[i], min(g + DEPTH, gend - 1));
+        }
     }
 
     // Sum the KS partials: tot(0) + (tot(1) + (... + tot(KS-1))).
-    float *buf = lds + (size_t)rw * kTiles * 4 * 64;
+    float *buf = lds + (size_t)rw * kTot * 64;
     if (KS > 1) {
         for (int s = KS - 1; s >= 1; --s) {
             if (ks == s) {
                 int r = 0;
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
+                for (int bt = 0; bt < NB; ++bt)
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
+                    for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-                        for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i, ++r) {
-                                float v = tot[m][rt][tt][i];
-                                if (s != KS - 1) v += buf[r * 64 + lane];
-                                buf[r * 64 + lane] = v;
-                            }
+                        for (int i = 0; i < 4; ++i, ++r) {
+                            float v = tot[bt][tt][i];
+                            if (s != KS - 1) v += buf[r * 64 + lane];
+                            buf[r * 64 + lane] = v;
+                        }
             }
             __syncthreads();
         }
     }
 
-    // hidden = SiLU(gate) * up, and its per-token maximum over this wave's rows.
-    float *mx = lds + (KS > 1 ? (size_t)RW * kTiles * 4 * 64 : 0);  // [RW][NTT][16]
+    // hidden = SiLU(gate) * up for tokens 4q + i of each token tile, rows n
+    // of each row tile; then each token's largest |hidden| over this wave's
+    // rows (a DPP row holds the 16 rows of a tile for the same 4 tokens).
+    float *mx = lds + (KS > 1 ? (size_t)RW * kTot * 64 : 0);  // [RW][NTT][16]
     float h[RT][NTT][4];
     if (ks == 0) {
         int r = 0;
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int bt = 0; bt < NB; ++bt)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-                for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i, ++r)
-                        if (KS > 1) tot[m][rt][tt][i] += buf[r * 64 + lane];
+                for (int i = 0; i < 4; ++i, ++r)
+                    if (KS > 1) tot[bt][tt][i] += buf[r * 64 + lane];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-            float m = 0.0f;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            for (int i = 0; i < 4; ++i) {
+                const int t = min(t0 + tt * 16 + 4 * q + i, T - 1);
+                const int xe = a.xe[t];
+                float m = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h[rt][tt][i] = silu(tot[0][rt][tt][i]) * tot[1][rt][tt][i];
+                for (int rt = 0; rt < RT; ++rt) {
+                    const float gv = ldexpf(tot[rt][tt][i], xe), uv = ldexpf(tot[RT + rt][tt][i], xe);
+                    h[rt][tt][i] = silu(gv) * uv;
                     m = fmaxf(m, fabsf(h[rt][tt][i]));
                 }
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            if (q == 0) mx[(rw * NTT + tt) * 16 + n] = m;
+                m = row16_max(m);
+                if (n == 0) mx[(rw * NTT + tt) * 16 + 4 * q + i] = m;
+            }
         }
     }
     __syncthreads();
     if (ks != 0) return;
 
     // Normalise per (token, H group), split into hi/lo halves, store in sigma
-    // order.  Lanes q and q^1 hold columns 0..3 and 4..7 of one 8-column block:
-    // the even lane assembles and stores the hi block, the odd lane the lo block.
-    const bool even = (q & 1) == 0;
+    // order, and store each token's factor for down.
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-        float m = 0.0f;
-        for (int w = 0; w < RW; ++w) m = fmaxf(m, mx[(w * NTT + tt) * 16 + n]);
-        const int ee = norm_exponent(m);
-        const int t = t0 + tt * 16 + n;
-        const bool valid = t < T;
-        const size_t hrow = ((size_t)e * T + (valid ? t : 0)) * d_ff;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            uint32_t hi2[2], lo2[2];
-            _Float16 hv[4], lv[4];
+        for (int i = 0; i < 4; ++i) {
+            const int tl = 4 * q + i;
+            float m = 0.0f;
+            for (int w = 0; w < RW; ++w) m = fmaxf(m, mx[(w * NTT + tt) * 16 + tl]);
+            const int ee = norm_exponent(m);
+            const int t = t0 + tt * 16 + tl;
+            if (t < T) {
+                const size_t hrow = ((size_t)e * T + t) * d_ff;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = ldexpf(h[rt][tt][i], -ee);
-                hv[i] = (_Float16)v;
-                lv[i] = (_Float16)(v - (float)hv[i]);
-            }
-            hi2[0] = __builtin_bit_cast(uint32_t, (half2v){hv[0], hv[1]});
-            hi2[1] = __builtin_bit_cast(uint32_t, (half2v){hv[2], hv[3]});
-            lo2[0] = __builtin_bit_cast(uint32_t, (half2v){lv[0], lv[1]});
-            lo2[1] = __builtin_bit_cast(uint32_t, (half2v){lv[2], lv[3]});
-            // Send what the partner assembles: the even lane sends lo, the odd lane hi.
-            const uint32_t s0 = even ? lo2[0] : hi2[0], s1 = even ? lo2[1] : hi2[1];
-            const uint32_t r0 = __shfl_xor((int)s0, 16), r1 = __shfl_xor((int)s1, 16);
-            const half2v m0 = __builtin_bit_cast(half2v, even ? hi2[0] : lo2[0]);
-            const half2v m1 = __builtin_bit_cast(half2v, even ? hi2[1] : lo2[1]);
-            const half2v p0 = __builtin_bit_cast(half2v, r0), p1 = __builtin_bit_cast(half2v, r1);
-            // Block columns (0..3 from the even lane, 4..7 from the odd lane) in
-            // sigma order: pairs (c0,c4), (c1,c5), (c2,c6), (c3,c7).
-            const half2v c03[4] = {even ? (half2v){m0[0], p0[0]} : (half2v){p0[0], m0[0]},
-                                   even ? (half2v){m0[1], p0[1]} : (half2v){p0[1], m0[1]},
-                                   even ? (half2v){m1[0], p1[0]} : (half2v){p1[0], m1[0]},
-                                   even ? (half2v){m1[1], p1[1]} : (half2v){p1[1], m1[1]}};
-            if (valid) {
-                const size_t col = (size_t)row0 + rt * 16 + 8 * (q >> 1);
-                _Float16 *dst = (even ? a.hh : a.hl) + hrow + col;
-                uint4 v;
-                v.x = __builtin_bit_cast(uint32_t, c03[0]);
-                v.y = __builtin_bit_cast(uint32_t, c03[1]);
-                v.z = __builtin_bit_cast(uint32_t, c03[2]);
-                v.w = __builtin_bit_cast(uint32_t, c03[3]);
-                *reinterpret_cast<uint4 *>(dst) = v;
+                for (int rt = 0; rt < RT; ++rt) {
+                    const float v = ldexpf(h[rt][tt][i], -ee);
+                    const _Float16 hv = (_Float16)v;
+                    const int r = row0 + rt * 16 + n;
+                    const size_t pos = hrow + (r & ~7) + sigma_pos(r & 7);
+                    a.hh[pos] = hv;
+                    a.hl[pos] = (_Float16)(v - (float)hv);
+                }
+                if (rw == 0 && n == 0) {
+                    const float rwt = a.route_w ? a.route_w[(size_t)t * E + e] : 1.0f;
+                    a.hf[((size_t)e * HG + hg) * a.t_pad + t] = ldexpf(rwt, ee);
+                }
             }
         }
-        if (valid && rw == 0 && q == 0) a.he[((size_t)e * T + t) * HG + hg] = ee;
     }
 }
 
 // -------------------------------------------------------------------------
 // Down for 16*RT*RW rows of d_model and 16*NTT tokens, summed over all
-// experts with the router weights.  Wave (rw, ks): rows rw*16*RT .. +16*RT of
-// the block, (expert, group) pairs [ks*P/KS, (ks+1)*P/KS) of P = E * d_ff/group,
-// taken in ascending order; partials over ks are added in LDS in a fixed order.
+// experts.  Wave (rw, ks): rows rw*16*RT .. +16*RT of the block, (expert,
+// group) pairs [ks*P/KS, (ks+1)*P/KS) of P = E * d_ff/group in ascending
+// order; partials over ks are added in LDS in a fixed order.
 template <int BITS, int KB, int NTT, int RT>
 __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 {
     extern __shared__ float lds[];
-    constexpr int kTiles = RT * NTT;
+    constexpr int kTot = RT * NTT * 4;
+    constexpr int DEPTH = 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KS = a.ks_dn, RW = a.rw_dn;
@@ -386,13 +405,40 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
     const int row0 = (rb * RW + rw) * 16 * RT;
     const int t0 = tb * 16 * NTT;
     const size_t rs = (size_t)d_ff * BITS / 8;
+    size_t code_off[RT], scale_off[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int row = min(row0 + rt * 16 + n, d_model - 1);
+        code_off[rt] = (size_t)row * rs + (size_t)(q * 8 * KB) * BITS / 8;
+        scale_off[rt] = (size_t)row * Gd;
+    }
+    size_t hoff[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) hoff[tt] = (size_t)min(t0 + tt * 16 + n, T - 1) * d_ff + q * 8 * KB;
 
-    int tok[NTT];
+    struct Stage {
+        TbStage<BITS, KB, NTT, RT> v;
+        f32x4 f[NTT];  // factors of tokens 4q..4q+3 of each token tile
+    };
+    auto load = [&](Stage &st, int p) {
+        const int e = p / Gd, g = p - e * Gd;
+        const QPtr D = a.down[e];
+        const size_t hb = (size_t)e * T * d_ff + (size_t)g * group;
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) tok[tt] = min(t0 + tt * 16 + n, T - 1);
-    int arow[RT];  // A-fragment row of each row tile (clamped), and output rows
+        for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) arow[rt] = min(row0 + rt * 16 + n, d_model - 1);
+            for (int j = 0; j < KB; ++j) {
+                st.v.ah[tt][j] = load_half8(a.hh + hb + hoff[tt] + 8 * j);
+                st.v.al[tt][j] = load_half8(a.hl + hb + hoff[tt] + 8 * j);
+            }
+            st.f[tt] = *reinterpret_cast<const f32x4 *>(a.hf + ((size_t)e * Gd + g) * a.t_pad + t0 + tt * 16 + 4 * q);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            load_codes<BITS, KB>(D.codes + code_off[rt] + (size_t)g * group * BITS / 8, st.v.cw[rt]);
+            st.v.s[rt] = D.scales[scale_off[rt] + g];
+        }
+    };
 
     f32x4 tot[RT][NTT];
 #pragma unroll
@@ -400,57 +446,36 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tot[rt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+    // Every wave has at least one pair (KS <= P); unconditional ring loads.
     const int P = E * Gd;
     const int pbeg = ks * P / KS, pend = (ks + 1) * P / KS;
-    for (int p = pbeg; p < pend; ++p) {
-        const int e = p / Gd, g = p - e * Gd;
-        const QPtr dm = a.down[e];
-        CodeWords<BITS, KB> cw[RT];
-        float sc[RT][4];
-        const size_t cofs = (size_t)(g * group + q * 8 * KB) * BITS / 8;
+    Stage S[DEPTH];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            load_codes(dm.codes + (size_t)arow[rt] * rs + cofs, cw[rt]);
+    for (int i = 0; i < DEPTH; ++i) load(S[i], min(pbeg + i, pend - 1));
+    for (int base = pbeg; base < pend; base += DEPTH) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = min(row0 + rt * 16 + 4 * q + i, d_model - 1);
-                sc[rt][i] = dm.scales[(size_t)r * Gd + g] * QFormat<BITS>::kInvZ;
-            }
-        }
-        half8 bh[NTT][KB], bl[NTT][KB];
-        float fac[NTT];
+        for (int i = 0; i < DEPTH; ++i) {
+            const int p = base + i;
+            if (p < pend) {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            const size_t hrow = ((size_t)e * T + tok[tt]) * d_ff + g * group + q * 8 * KB;
+                for (int rt = 0; rt < RT; ++rt) {
+                    half8 bf[KB];
 #pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                bh[tt][j] = load_half8(a.hh + hrow + 8 * j);
-                bl[tt][j] = load_half8(a.hl + hrow + 8 * j);
-            }
-            const float rwt = a.route_w ? a.route_w[(size_t)tok[tt] * E + e] : 1.0f;
-            fac[tt] = ldexpf(rwt, a.he[((size_t)e * T + tok[tt]) * Gd + g]);
-        }
+                    for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].v.cw[rt], j);
+                    const float s = S[i].v.s[rt] * QFormat<BITS>::kInvZ;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            half8 af[KB];
+                    for (int tt = 0; tt < NTT; ++tt) {
+                        const f32x4 acc = group_mfma<BITS, KB, NTT, RT>(S[i].v, bf, tt);
 #pragma unroll
-            for (int j = 0; j < KB; ++j) af[j] = code_frag<BITS, KB>(cw[rt], j);
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    acc = mfma(af[j], bh[tt][j], acc);
-                    acc = mfma(af[j], bl[tt][j], acc);
+                        for (int r = 0; r < 4; ++r) tot[rt][tt][r] = fmaf(s * S[i].f[tt][r], acc[r], tot[rt][tt][r]);
+                    }
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    tot[rt][tt][i] = fmaf(sc[rt][i] * fac[tt], acc[i], tot[rt][tt][i]);
             }
+            load(S[i], min(p + DEPTH, pend - 1));
         }
     }
 
-    float *buf = lds + (size_t)rw * kTiles * 4 * 64;
+    float *buf = lds + (size_t)rw * kTot * 64;
     if (KS > 1) {
         for (int s = KS - 1; s >= 1; --s) {
             if (ks == s) {
@@ -474,40 +499,43 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            const int t = t0 + tt * 16 + n;
+        for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i, ++r) {
                 float v = tot[rt][tt][i];
                 if (KS > 1) v += buf[r * 64 + lane];
-                const int row = row0 + rt * 16 + 4 * q + i;
+                const int t = t0 + tt * 16 + 4 * q + i;
+                const int row = row0 + rt * 16 + n;
                 if (t < T && row < d_model) a.out[(size_t)t * d_model + row] = v;
             }
-        }
 }
 
-template <int BITS, int KB, int NTT, int RT>
+template <int BITS, int KB, int NTT, int RTG, int RTD>
 hipError_t launch_tb_kernels(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    const int G = a.d_model / a.group;
-    const long pairs = (long)a.T * G;
-    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, a.x, a.T, a.d_model,
-                       a.group, a.xh, a.xl, a.xe);
+    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up<BITS, KB, NTT, RT>), dim3(pl.gu_blocks), dim3(64 * pl.gu_waves),
-                       pl.gu_lds, st, a);
+    hipLaunchKernelGGL((k_tb_gate_up<BITS, KB, NTT, RTG>), dim3(pl.gu_blocks), dim3(64 * pl.gu_waves), pl.gu_lds,
+                       st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_down<BITS, KB, NTT, RT>), dim3(pl.dn_blocks), dim3(64 * pl.dn_waves),
-                       pl.dn_lds, st, a);
+    hipLaunchKernelGGL((k_tb_down<BITS, KB, NTT, RTD>), dim3(pl.dn_blocks), dim3(64 * pl.dn_waves), pl.dn_lds, st,
+                       a);
     return hipGetLastError();
 }
 
 template <int BITS, int KB>
 hipError_t launch_tb_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    if (pl.ntt == 1) return launch_tb_kernels<BITS, KB, 1, 1>(pl, a, st);
-    return launch_tb_kernels<BITS, KB, 4, 2>(pl, a, st);
+    // gate_up row tiles: 4 for 16-token tiles and 64-column groups (one wave per
+    // group), else 2 (more would not fit the registers); down: 4 row tiles for
+    // 16-token tiles, 2 for 32.
+    if (pl.ntt == 1) {
+        if constexpr (KB == 2)
+            if (pl.rt_gu == 4) return launch_tb_kernels<BITS, KB, 1, 4, 4>(pl, a, st);
+        return launch_tb_kernels<BITS, KB, 1, 2, 4>(pl, a, st);
+    }
+    return launch_tb_kernels<BITS, KB, 2, 2, 2>(pl, a, st);
 }
 
 }  // namespace
@@ -522,34 +550,35 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     if (bits == 4 ? (kb < 1 || kb > 4) : (kb != 2 && kb != 4)) return false;
     if (d_model % group || d_ff % group) return false;
     TbPlan p{};
-    p.ntt = T <= 16 ? 1 : 4;
-    const int rt = p.ntt == 1 ? 1 : 2;
+    p.ntt = T <= 16 ? 1 : 2;
     const int ntb = (T + 16 * p.ntt - 1) / (16 * p.ntt);
     const int G = d_model / group;
     // gate_up: the block covers one quantisation group of d_ff rows.
-    p.rw_gu = group / (16 * rt);
-    if (p.rw_gu < 1 || p.rw_gu > 8 || p.rw_gu * 16 * rt != group) return false;
+    p.rt_gu = (p.ntt == 1 && kb == 2) ? 4 : 2;
+    p.rw_gu = group / (16 * p.rt_gu);
+    if (p.rw_gu < 1 || p.rw_gu > 8 || p.rw_gu * 16 * p.rt_gu != group) return false;
     const long gu_blocks = (long)n_experts * (d_ff / group) * ntb;
-    // LDS: the K-split partial sums (only when K is split) and the per-token maxima.
-    const size_t gu_buf = (size_t)p.rw_gu * (2 * rt * p.ntt) * 4 * 64 * 4;
+    const int gu_tot = 2 * p.rt_gu * p.ntt * 4;   // accumulator floats per lane
+    const size_t gu_buf = (size_t)p.rw_gu * gu_tot * 64 * 4;
     const size_t gu_max = (size_t)p.rw_gu * p.ntt * 16 * 4;
     p.ks_gu = 1;
-    while (p.ks_gu < 4 && p.rw_gu * p.ks_gu * 2 <= 8 && p.ks_gu * 2 <= G &&
-           gu_buf + gu_max <= kMaxBlockLds && gu_blocks * p.rw_gu * p.ks_gu < 2048)
+    while (p.ks_gu < 8 && p.rw_gu * p.ks_gu * 2 <= 8 && p.ks_gu * 2 <= G && gu_buf + gu_max <= kMaxBlockLds &&
+           gu_blocks * p.rw_gu * p.ks_gu < 2048)
         p.ks_gu *= 2;
     p.gu_waves = p.rw_gu * p.ks_gu;
     p.gu_blocks = gu_blocks;
     p.gu_lds = (p.ks_gu > 1 ? gu_buf : 0) + gu_max;
     // down: the block covers 16*rt*rw_dn rows of d_model; waves split the
     // (expert, group) pairs.
-    p.rw_dn = p.ntt == 1 ? 1 : 2;
+    const int rt_dn = p.ntt == 1 ? 4 : 2;
+    p.rw_dn = 1;
     const int P = n_experts * (d_ff / group);
-    p.ks_dn = 8 / p.rw_dn;
-    while (p.ks_dn > 1 && p.ks_dn > P) p.ks_dn /= 2;
-    p.dn_waves = p.rw_dn * p.ks_dn;
-    const int rows_per_block = 16 * rt * p.rw_dn;
+    const int rows_per_block = 16 * rt_dn * p.rw_dn;
     p.dn_blocks = (long)((d_model + rows_per_block - 1) / rows_per_block) * ntb;
-    p.dn_lds = p.ks_dn > 1 ? (size_t)p.rw_dn * rt * p.ntt * 4 * 64 * 4 : 0;
+    p.ks_dn = 1;
+    while (p.ks_dn < 8 && p.ks_dn * 2 <= P && p.dn_blocks * p.ks_dn < 2048) p.ks_dn *= 2;
+    p.dn_waves = p.rw_dn * p.ks_dn;
+    p.dn_lds = p.ks_dn > 1 ? (size_t)p.rw_dn * rt_dn * p.ntt * 4 * 64 * 4 : 0;
     if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
     *pl = p;
     return true;

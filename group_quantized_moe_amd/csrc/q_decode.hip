@@ -303,33 +303,30 @@ constexpr int kMaxQCols = 8192;
 template <int BITS>
 constexpr int kGroupsPerThread = (kMaxQCols / DigitLayout<BITS>::kColsPerDw + kBlockThreads - 1) / kBlockThreads;
 
-// Lanes of a whole-row wave with adjacent chunks: lpr lanes share a row and
-// lane lr owns chunks lr*NCH .. lr*NCH + NCH - 1 of it, so a lane's chunks are
-// one contiguous run of its row (and, when NCH chunks fit in one quantisation
-// group, share one scale).  Chunks past the row end are idle: their digit
+// Lanes of a whole-row wave: LPR lanes share a row and lane lr owns chunks
+// lr, lr + LPR, ..., so that each 16-byte load instruction of a wave reads one
+// contiguous run of its rows.  Chunks past the row end are idle: their digit
 // planes and epilogue constants are zero and their loads read a valid chunk.
-// Offsets are per lane and constant for the whole kernel: code bytes from the
-// start of the step's first row, scale bytes from the start of its scale row.
 template <int NCH, int LPR>
-struct AdjLanes {
+struct RowLanes {
     static constexpr int kRows = 64 / LPR;   // rows per step
     int lr, slot;
     int c[NCH];
     bool valid[NCH];
-    unsigned coff[NCH];   // slot * row_bytes + 16 * chunk
-    unsigned soff[NCH];   // 4 * (slot * gpr + group of chunk)
-    __device__ __forceinline__ AdjLanes(int cpr, int cpc, int group, size_t row_bytes, int gpr)
+    unsigned coff[NCH];   // 16 * chunk: code bytes from the start of the row
+    unsigned soff[NCH];   // 4 * group of the chunk: scale bytes from the start of the row
+    __device__ __forceinline__ RowLanes(int cpr, int cpc, int group)
     {
         const int lane = threadIdx.x & 63;
         lr = lane & (LPR - 1);
         slot = lane / LPR;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            c[k] = lr * NCH + k;
+            c[k] = lr + LPR * k;
             valid[k] = c[k] < cpr;
             const int cc = valid[k] ? c[k] : cpr - 1;
-            coff[k] = (unsigned)(slot * row_bytes + 16u * cc);
-            soff[k] = 4u * (unsigned)(slot * gpr + cc * cpc / group);
+            coff[k] = 16u * cc;
+            soff[k] = 4u * (unsigned)(cc * cpc / group);
         }
     }
     // Lane that holds the row sum after group_sum<LPR>.
@@ -368,56 +365,42 @@ __device__ __forceinline__ float silu_hw(float t)
 }
 
 // Code and scale registers of one step: NCH chunks of M matrices for the
-// lane's row.  With ONE, scale 0 stands for all of the lane's chunks.
+// lane's row.
 template <int NCH, int M>
 struct Stage {
     uint4 q[NCH][M];
     float s[NCH][M];
 };
 
-template <int NCH, int LPR, int M, bool ONE>
+// Loads of one stage: the lane's row is row0 + slot, clamped to the last row
+// (a partial last step re-reads it; its results are never stored).  A stage
+// past the end of a wave's steps is a dummy: every lane reads the first 16
+// bytes of the matrix (one cache line, nothing from HBM).  Both cases only
+// change the per-lane offsets, so every call issues the same loads and the
+// ring's waits stay exact.
+template <int NCH, int LPR, int M>
 __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *const *codes, const float *const *scales,
-                                           size_t code_row, size_t scale_row, const AdjLanes<NCH, LPR> &ln,
-                                           bool clamp, int row0, int rows, size_t row_bytes, int gpr)
+                                           const RowLanes<NCH, LPR> &ln, int row0, int rows, unsigned row_bytes,
+                                           int gpr, bool dummy)
 {
-    if (!clamp) {
+    const unsigned keep = dummy ? 0u : ~0u;
+    const unsigned r = (unsigned)min(row0 + ln.slot, rows - 1);
+    const unsigned crow = r * row_bytes, srow = r * (unsigned)gpr * 4u;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint8_t *cb = codes[m] + code_row;
-            const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]) + scale_row;
+    for (int m = 0; m < M; ++m) {
 #pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                t.q[k][m] = *reinterpret_cast<const uint4 *>(cb + ln.coff[k]);
-                if (k == 0 || !ONE) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
-            }
-        }
-    } else {
-        // Last, partial step of a matrix: rows past the end read the last row.
-        const int r = min(row0 + ln.slot, rows - 1);
-        const int dr = r - row0 - ln.slot;  // <= 0
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const uint8_t *cb = codes[m] + code_row + (ptrdiff_t)dr * (ptrdiff_t)row_bytes;
-            const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]) + scale_row + (ptrdiff_t)dr * gpr * 4;
-#pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                t.q[k][m] = *reinterpret_cast<const uint4 *>(cb + ln.coff[k]);
-                if (k == 0 || !ONE) t.s[k][m] = *reinterpret_cast<const float *>(sb + ln.soff[k]);
-            }
+        for (int k = 0; k < NCH; ++k) {
+            t.q[k][m] = *reinterpret_cast<const uint4 *>(codes[m] + ((crow + ln.coff[k]) & keep));
+            t.s[k][m] = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(scales[m]) +
+                                                         ((srow + ln.soff[k]) & keep));
         }
     }
 }
 
 // Row sums of matrix m for the lane's chunks (before the cross-lane sum).
-template <int BITS, int NCH, int M, bool ONE>
+template <int BITS, int NCH, int M>
 __device__ __forceinline__ float stage_dot(const Stage<NCH, M> &t, int m, const ChunkVec<BITS> *cv)
 {
-    if constexpr (ONE) {
-        float p = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) p += fmaf((float)chunk_idot<BITS>(t.q[k][m], cv[k]), cv[k].alpha, cv[k].beta);
-        return t.s[0][m] * p;
-    }
     float y = 0.0f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][m], t.s[k][m], cv[k]);
@@ -440,7 +423,7 @@ struct Cursor {
 // contiguous range of the E * ceil(d_ff / rs) row steps (experts in order),
 // with DEPTH steps of code and scale loads in flight ahead of the step being
 // reduced; the first DEPTH steps are issued before the planes are built.
-template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH>
 __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -450,36 +433,45 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     const int cpr = a.d_model / CPC;
     const size_t row_bytes = (size_t)a.d_model * BITS / 8;
     const int gpr = a.d_model / a.group;
-    const AdjLanes<NCH, LPR> ln(cpr, CPC, a.group, row_bytes, gpr);
+    const RowLanes<NCH, LPR> ln(cpr, CPC, a.group);
     const PlaneLds<BITS> lds(smem, a.d_model);
-    constexpr int rs = AdjLanes<NCH, LPR>::kRows;
+    constexpr int rs = RowLanes<NCH, LPR>::kRows;
     const int spe = (a.d_ff + rs - 1) / rs;
     const int nsteps = a.n_experts * spe;
     const int W = gridDim.x * nw;
     const int wg = blockIdx.x * nw + wave;
     const int sb = (int)((long)wg * nsteps / W), se = (int)((long)(wg + 1) * nsteps / W);
 
-    auto load = [&](Stage<NCH, 2> &t, const Cursor &c) {
-        const int row0 = c.s * rs;
+    auto load = [&](Stage<NCH, 2> &t, const Cursor &c, bool dummy) {
         const uint8_t *codes[2] = {a.gate[c.m].codes, a.up[c.m].codes};
         const float *scales[2] = {a.gate[c.m].scales, a.up[c.m].scales};
-        load_stage<NCH, LPR, 2, ONE>(t, codes, scales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln,
-                                     row0 + rs > a.d_ff, row0, a.d_ff, row_bytes, gpr);
+        load_stage<NCH, LPR, 2>(t, codes, scales, ln, c.s * rs, a.d_ff, (unsigned)row_bytes, gpr, dummy);
     };
 
     // The vector's loads go first, then the first steps' code loads, then the
     // digit planes (which wait only for the vector).
     VecRegs<BITS, kGroupsPerThread<BITS>> xr;
     load_vec_regs<BITS>(a.x, a.d_model, xr);
+    // The ring's loads are unconditional (past the wave's last step they are
+    // dummies), so the number of loads between a load and its use is the same
+    // on every path and the wait for a stage leaves the later stages' loads in
+    // flight.
+    const bool busy = sb < se;
     Stage<NCH, 2> S[DEPTH];
-    Cursor cl;
+    Cursor cl, first;
     cl.init(sb, spe);
+    first = cl;
+    int ls = sb;  // step that cl points at
+    auto load_next = [&](Stage<NCH, 2> &t) {
+        const bool past = ls >= se;
+        load(t, past ? first : cl, past);
+        cl.next(spe);
+        ++ls;
+    };
+    if (busy) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-        if (sb + i < se) {
-            load(S[i], cl);
-            cl.next(spe);
-        }
+        for (int i = 0; i < DEPTH; ++i) load_next(S[i]);
+    }
 
     build_planes<BITS>(xr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
@@ -493,18 +485,15 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
             if (base + i < se) {
-                float g = stage_dot<BITS, NCH, 2, ONE>(S[i], 0, cv);
-                float u = stage_dot<BITS, NCH, 2, ONE>(S[i], 1, cv);
+                float g = stage_dot<BITS, NCH, 2>(S[i], 0, cv);
+                float u = stage_dot<BITS, NCH, 2>(S[i], 1, cv);
                 g = group_sum<LPR>(g);
                 u = group_sum<LPR>(u);
                 const int r = cc.s * rs + ln.slot;
                 if (ln.writer() && r < a.d_ff) a.hidden[(size_t)cc.m * a.d_ff + r] = silu_hw(g) * u;
                 cc.next(spe);
-                if (base + i + DEPTH < se) {
-                    load(S[i], cl);
-                    cl.next(spe);
-                }
             }
+            load_next(S[i]);
         }
     }
 }
@@ -546,7 +535,7 @@ __device__ __forceinline__ float acc_value(unsigned long long sum, int n)
     return (float)((double)fixed * (1.0 / 4294967296.0));
 }
 
-template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH>
 __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -557,9 +546,9 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     const int cpr = a.d_ff / CPC;
     const size_t row_bytes = (size_t)a.d_ff * BITS / 8;
     const int gpr = a.d_ff / a.group;
-    const AdjLanes<NCH, LPR> ln(cpr, CPC, a.group, row_bytes, gpr);
+    const RowLanes<NCH, LPR> ln(cpr, CPC, a.group);
     const PlaneLds<BITS> lds(smem, a.d_ff);
-    constexpr int rs = AdjLanes<NCH, LPR>::kRows;
+    constexpr int rs = RowLanes<NCH, LPR>::kRows;
     const int e = blockIdx.x % E;
     const int bpe = gridDim.x / E;                 // blocks per expert
     const int We = bpe * nw;                       // waves per expert
@@ -573,18 +562,20 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     float *mine = reinterpret_cast<float *>(smem + ((plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15))) +
                   wave * a.dn_rows_per_wave;
     auto load = [&](Stage<NCH, 1> &t, int step) {
-        const int row0 = step * rs;
-        load_stage<NCH, LPR, 1, ONE>(t, dcodes, dscales, (size_t)row0 * row_bytes, (size_t)row0 * gpr * 4, ln,
-                                     row0 + rs > a.d_model, row0, a.d_model, row_bytes, gpr);
+        load_stage<NCH, LPR, 1>(t, dcodes, dscales, ln, step * rs, a.d_model, (unsigned)row_bytes, gpr,
+                                     step >= se);
     };
 
     if ((int)blockIdx.x >= bpe * E) return;  // whole block idle: no barrier follows for it
     VecRegs<BITS, kGroupsPerThread<BITS>> hr;
     load_vec_regs<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, hr);
+    // Unconditional ring loads, as in gate_up (past the last step they are dummies).
+    const bool busy = sb < se;
     Stage<NCH, 1> S[DEPTH];
+    if (busy) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-        if (sb + i < se) load(S[i], sb + i);
+        for (int i = 0; i < DEPTH; ++i) load(S[i], sb + i);
+    }
 
     build_planes<BITS>(hr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
@@ -597,7 +588,7 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
         for (int i = 0; i < DEPTH; ++i) {
             const int st = base + i;
             if (st < se) {
-                float y = stage_dot<BITS, NCH, 1, ONE>(S[i], 0, cv);
+                float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv);
                 y = group_sum<LPR>(y);
                 const int r = st * rs + ln.slot;
                 if (ln.writer() && r < a.d_model) {
@@ -606,8 +597,8 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
                     else
                         mine[(st - sb) * rs + ln.slot] = y * rw;
                 }
-                if (st + DEPTH < se) load(S[i], st + DEPTH);
             }
+            load(S[i], st + DEPTH);
         }
     }
 
@@ -650,25 +641,25 @@ int blocks_per_cu(const void *fn, int block, size_t lds)
     return n;
 }
 
-template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH>
 hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
     const size_t lds = plane_lds_bytes<BITS>(a.d_model);
-    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, LPR, ONE, DEPTH>);
+    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, LPR, DEPTH>);
     const long cap = (long)cus * blocks_per_cu(fn, block, lds);
     if (cap < 1) return hipErrorInvalidConfiguration;
     const long steps = (long)a.n_experts * ((a.d_ff + 64 / p.lpr_g - 1) / (64 / p.lpr_g));
     const long grid = std::max(1L, std::min(cap, (steps + p.nw - 1) / p.nw));
-    hipLaunchKernelGGL((k_gate_up<BITS, NCH, LPR, ONE, DEPTH>), dim3((unsigned)grid), dim3(block), lds, st, a);
+    hipLaunchKernelGGL((k_gate_up<BITS, NCH, LPR, DEPTH>), dim3((unsigned)grid), dim3(block), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BITS, int NCH, int LPR, bool ONE, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH>
 hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, ONE, DEPTH>);
+    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, DEPTH>);
     const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
     // Resident blocks: the occupancy query's answer, but at most two blocks of
     // this size per CU (more were measured not to be co-resident, which puts a
@@ -681,7 +672,7 @@ hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
     const long waves = per_expert * p.nw;
     a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
     const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
-    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, ONE, DEPTH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
+    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, DEPTH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
                        a);
     return hipGetLastError();
 }
@@ -748,26 +739,20 @@ bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, Decod
 }
 
 // Steps in flight per wave (the register ring of code and scale loads).
-constexpr int kGateUpDepth = 2;
-constexpr int kDownDepth = 2;
+constexpr int kGateUpDepth = 1;
+constexpr int kDownDepth = 1;
 
-// Kernels are compiled per (bits, chunks per lane, lanes per row, one scale per
-// lane): lanes per row 16, 32 or 64; chunks per lane 1..4 (4-bit) or 1..2 (2-bit).
-#define SMOE_FOR_LPR(X, B, N)                                                  \
-    X(B, N, 16, true) X(B, N, 16, false) X(B, N, 32, true) X(B, N, 32, false) \
-    X(B, N, 64, true) X(B, N, 64, false)
+// Kernels are compiled per (bits, chunks per lane, lanes per row): lanes per
+// row 16, 32 or 64; chunks per lane 1..4 (4-bit) or 1..2 (2-bit).
+#define SMOE_FOR_LPR(X, B, N) X(B, N, 16) X(B, N, 32) X(B, N, 64)
 #define SMOE_FOR_ALL(X)                                                        \
     SMOE_FOR_LPR(X, 4, 1) SMOE_FOR_LPR(X, 4, 2) SMOE_FOR_LPR(X, 4, 3) SMOE_FOR_LPR(X, 4, 4) \
     SMOE_FOR_LPR(X, 2, 1) SMOE_FOR_LPR(X, 2, 2)
 
-static bool one_scale(int bits, int nch, int group) { return group % (nch * (128 / bits)) == 0; }
-
 hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-    const bool one = one_scale(bits, p.nch_g, a.group);
-#define SMOE_RUN(B, N, L, O)                                                   \
-    if (bits == B && p.nch_g == N && p.lpr_g == L && one == O)               \
-        return run_gate_up<B, N, L, O, kGateUpDepth>(p, a, cus, st);
+#define SMOE_RUN(B, N, L)                                                      \
+    if (bits == B && p.nch_g == N && p.lpr_g == L) return run_gate_up<B, N, L, kGateUpDepth>(p, a, cus, st);
     SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
@@ -775,10 +760,8 @@ hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, in
 
 hipError_t launch_down(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-    const bool one = one_scale(bits, p.nch_d, a.group);
-#define SMOE_RUN(B, N, L, O)                                                   \
-    if (bits == B && p.nch_d == N && p.lpr_d == L && one == O)               \
-        return run_down<B, N, L, O, kDownDepth>(p, a, cus, st);
+#define SMOE_RUN(B, N, L)                                                      \
+    if (bits == B && p.nch_d == N && p.lpr_d == L) return run_down<B, N, L, kDownDepth>(p, a, cus, st);
     SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;

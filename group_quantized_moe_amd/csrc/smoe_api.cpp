@@ -106,14 +106,16 @@ DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
 }
 
 // Workspace layout of the token-batch path (T > 1), every piece 256-byte aligned:
-//   xh, xl  f16 [T][d_model]            hi/lo halves of the scaled activations
-//   xe      i32 [T][d_model/group]      their power-of-two exponents
-//   hh, hl  f16 [n_experts][T][d_ff]    hi/lo halves of the scaled hidden rows
-//   he      i32 [n_experts][T][d_ff/group]
+//   xh, xl  f16 [T][d_model]                 hi/lo halves of the scaled activations
+//   xe      i32 [T]                          their per-token exponents
+//   hh, hl  f16 [n_experts][T][d_ff]         hi/lo halves of the scaled hidden rows
+//   hf      f32 [n_experts][d_ff/group][Tp]  per (expert, group, token) factors, Tp = T rounded up to 32
 // Everything is rewritten by each call before it is read.
 struct BatchWorkspace {
-    size_t xh, xl, xe, hh, hl, he, total;
+    size_t xh, xl, xe, hh, hl, hf, total;
 };
+
+int token_pad(int T) { return (T + smoe::kTokenPad - 1) / smoe::kTokenPad * smoe::kTokenPad; }
 
 BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int group)
 {
@@ -122,10 +124,10 @@ BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int 
     w.xh = 0;
     w.xl = w.xh + align256(nx * 2);
     w.xe = w.xl + align256(nx * 2);
-    w.hh = w.xe + align256((size_t)T * (d_model / group) * 4);
+    w.hh = w.xe + align256((size_t)T * 4);
     w.hl = w.hh + align256(nh * 2);
-    w.he = w.hl + align256(nh * 2);
-    w.total = w.he + align256((size_t)n_experts * T * (d_ff / group) * 4);
+    w.hf = w.hl + align256(nh * 2);
+    w.total = w.hf + align256((size_t)n_experts * (d_ff / group) * token_pad(T) * 4);
     return w;
 }
 
@@ -287,8 +289,9 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
         a.xe = reinterpret_cast<int *>(ws + w.xe);
         a.hh = reinterpret_cast<_Float16 *>(ws + w.hh);
         a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
-        a.he = reinterpret_cast<int *>(ws + w.he);
+        a.hf = reinterpret_cast<float *>(ws + w.hf);
         a.T = T;
+        a.t_pad = token_pad(T);
         a.d_model = d_model;
         a.d_ff = d_ff;
         a.group = group;
