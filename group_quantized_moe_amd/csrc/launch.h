@@ -64,9 +64,11 @@ struct TbArgs {
     int *xe;                 // [T]
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
+    float *part;             // [ks_dn][T][d_model]: partial sums of the down splits (tiled kernels)
     int T, t_pad, d_model, d_ff, group, n_experts;
     int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
-    int ks_dn, rw_dn;        // down waves per block: rw_dn row slices x ks_dn (expert, group) slices
+    int ks_dn, rw_dn;        // down: rw_dn row slices x ks_dn (expert, group) slices, as waves of one
+                             // block, or as blocks with partial sums for the tiled kernels
 };
 
 // Tiling of the three token-batch launches: 16*ntt tokens per block, rt_gu row
@@ -83,11 +85,14 @@ struct TbPlan {
 };
 
 // Token rows of the hidden-row factors are padded to a multiple of this.
-constexpr int kTokenPad = 32;
+constexpr int kTokenPad = 64;
 
 // False if the shape is outside what the token-batch kernels cover (group
 // must be 32, 64, 96 or 128 columns at 4 bits, 64 or 128 at 2 bits).
 bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T, TbPlan *plan);
+// Upper bound of the down splits whose partial sums the token-batch path keeps
+// (1 means none are kept).
+int batch_down_splits(int d_model, int T);
 hipError_t launch_batch(int bits, const TbPlan &plan, const TbArgs &args, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
