@@ -64,17 +64,19 @@ struct TbArgs {
     int *xe;                 // [T]
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
-    float *part;             // [ks_dn][T][d_model]: partial sums of the down splits (tiled kernels)
+    float *part_gu, *part_dn; // tiled kernels: per-tile partial sums of the K splits
     int T, t_pad, d_model, d_ff, group, n_experts;
     int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
     int ks_dn, rw_dn;        // down: rw_dn row slices x ks_dn (expert, group) slices, as waves of one
-                             // block, or as blocks with partial sums for the tiled kernels
+                             // block; for the tiled kernels ks_gu / ks_dn are splits over blocks
 };
 
 // Tiling of the three token-batch launches: 16*ntt tokens per block, rt_gu row
 // tiles per gate_up wave; waves per block, block counts and dynamic LDS bytes
 // of gate_up and down.
 struct TbPlan {
+    bool tiled;              // tiled kernels (groups of 32 and 64 columns)
+    int mg;                  // tiled gate_up: quantisation groups per step
     int ntt, rt_gu;
     int rw_gu, ks_gu, gu_waves;
     long gu_blocks;
@@ -90,9 +92,16 @@ constexpr int kTokenPad = 64;
 // False if the shape is outside what the token-batch kernels cover (group
 // must be 32, 64, 96 or 128 columns at 4 bits, 64 or 128 at 2 bits).
 bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T, TbPlan *plan);
-// Upper bound of the down splits whose partial sums the token-batch path keeps
-// (1 means none are kept).
-int batch_down_splits(int d_model, int T);
+// Tiling of the tiled token-batch kernels that depends on the shape only (not
+// the group): tokens per tile / 16, tile counts, the largest K splits and the
+// partial-sum floats they need in the workspace.
+struct BatchSplits {
+    int ntt;
+    long gu_tiles, dn_tiles;
+    int ks_gu, ks_dn;
+    size_t gu_part_floats, dn_part_floats;
+};
+BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T);
 hipError_t launch_batch(int bits, const TbPlan &plan, const TbArgs &args, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

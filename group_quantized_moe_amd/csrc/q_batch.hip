@@ -148,28 +148,94 @@ __device__ __forceinline__ float row16_max(float v)
     return v;
 }
 
+// Buffer loads: a resource (base, byte extent) in scalar registers, a fixed
+// per-lane byte offset and a uniform byte offset per step, so that moving to the
+// next step writes no vector registers.  Raw buffer (stride 0) with a 32-bit
+// data format, as the memory instructions expect for untyped loads.
+using BufRes = __amdgpu_buffer_rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ BufRes buf_res(const void *base, size_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)min(bytes, (size_t)0x7fffffff),
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(BufRes r, unsigned voff, unsigned soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ unsigned buf_load4(BufRes r, unsigned voff, unsigned soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+template <int BITS, int KB>
+__device__ __forceinline__ void buf_load_codes(BufRes r, unsigned voff, unsigned soff, CodeWords<BITS, KB> &c)
+{
+    constexpr int n = CodeWords<BITS, KB>::kDwords;
+    if constexpr (n == 4) {
+        const uint4 v = buf_load16(r, voff, soff);
+        c.w[0] = v.x;
+        c.w[1] = v.y;
+        c.w[2] = v.z;
+        c.w[3] = v.w;
+    } else if constexpr (n == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+        c.w[0] = v.x;
+        c.w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < n; ++i) c.w[i] = buf_load4(r, voff + 4 * i, soff);
+    }
+}
+
 // -------------------------------------------------------------------------
-// X -> hi/lo halves in sigma order + one exponent per token.  One block per
-// token.
+// X -> hi/lo halves in sigma order + one exponent per token.  One block of
+// 256 threads per token, one pass: each thread keeps up to 4 chunks of 8
+// columns in registers (d_model <= 8192), the block finds the row's largest
+// |x|, and every chunk is written as two 16-byte stores (hi, lo).
 __global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, int cols, _Float16 *__restrict__ xh,
                                                  _Float16 *__restrict__ xl, int *__restrict__ xe)
 {
     __shared__ float s_max[4];
     const size_t base = (size_t)blockIdx.x * cols;
+    const int nch = cols / 8;
+    float v[4][8];
     float m = 0.0f;
-    for (int c = threadIdx.x; c < cols; c += blockDim.x) m = fmaxf(m, fabsf(x[base + c]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = threadIdx.x + 256 * k;
+        if (c < nch) {
+            const float4 a0 = reinterpret_cast<const float4 *>(x + base)[2 * c];
+            const float4 a1 = reinterpret_cast<const float4 *>(x + base)[2 * c + 1];
+            v[k][0] = a0.x; v[k][1] = a0.y; v[k][2] = a0.z; v[k][3] = a0.w;
+            v[k][4] = a1.x; v[k][5] = a1.y; v[k][6] = a1.z; v[k][7] = a1.w;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[k][i]));
+        }
+    }
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
     if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     const int e = norm_exponent(m);
-    for (int c = threadIdx.x; c < cols; c += blockDim.x) {
-        const float v = ldexpf(x[base + c], -e);
-        const _Float16 h = (_Float16)v;
-        const size_t pos = base + (c & ~7) + sigma_pos(c & 7);
-        xh[pos] = h;
-        xl[pos] = (_Float16)(v - (float)h);
+    constexpr int kSigma[8] = {0, 4, 1, 5, 2, 6, 3, 7};   // column at each sigma position
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = threadIdx.x + 256 * k;
+        if (c < nch) {
+            half8 hi, lo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float sv = ldexpf(v[k][kSigma[i]], -e);
+                hi[i] = (_Float16)sv;
+                lo[i] = (_Float16)(sv - (float)hi[i]);
+            }
+            reinterpret_cast<half8 *>(xh + base)[c] = hi;
+            reinterpret_cast<half8 *>(xl + base)[c] = lo;
+        }
     }
     if (threadIdx.x == 0) xe[blockIdx.x] = e;
 }
@@ -226,39 +292,41 @@ __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
     const int e = b / HG;
     const int row0 = hg * group + rw * 16 * RT;   // first d_ff row of this wave
     const int t0 = tb * 16 * NTT;
-    const size_t rs = (size_t)d_model * BITS / 8;
-    const uint8_t *code_base[NB];
-    const float *scale_base[NB];
+    // Fixed 32-bit lane offsets into buffer resources; a step moves only the
+    // uniform offsets (a matrix has at most 8192 x 8192 entries; X at most
+    // 65536 x 8192 halves).
+    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * 4;
+    const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
+    const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
+    const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
+    unsigned coff[RT], soff[RT], xoff[NTT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const QPtr M = m == 0 ? a.gate[e] : a.up[e];
-            const int row = row0 + rt * 16 + n;
-            code_base[m * RT + rt] = M.codes + (size_t)row * rs + (size_t)(q * 8 * KB) * BITS / 8;
-            scale_base[m * RT + rt] = M.scales + (size_t)row * G;
-        }
-    const _Float16 *xh_base[NTT], *xl_base[NTT];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-        const size_t off = (size_t)min(t0 + tt * 16 + n, T - 1) * d_model + q * 8 * KB;
-        xh_base[tt] = a.xh + off;
-        xl_base[tt] = a.xl + off;
+    for (int rt = 0; rt < RT; ++rt) {
+        const unsigned row = (unsigned)(row0 + rt * 16 + n);
+        coff[rt] = row * (unsigned)(d_model * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
+        soff[rt] = row * (unsigned)G * 4u;
     }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+        xoff[tt] = ((unsigned)min(t0 + tt * 16 + n, T - 1) * (unsigned)d_model + (unsigned)(q * 8 * KB)) * 2u;
     using Stage = TbStage<BITS, KB, NTT, NB>;
     auto load = [&](Stage &st, int g) {
+        const unsigned xs = (unsigned)g * (unsigned)group * 2u;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
-                st.ah[tt][j] = load_half8(xh_base[tt] + (size_t)g * group + 8 * j);
-                st.al[tt][j] = load_half8(xl_base[tt] + (size_t)g * group + 8 * j);
+                st.ah[tt][j] = __builtin_bit_cast(half8, buf_load16(xhr, xoff[tt] + 16 * j, xs));
+                st.al[tt][j] = __builtin_bit_cast(half8, buf_load16(xlr, xoff[tt] + 16 * j, xs));
             }
 #pragma unroll
-        for (int bt = 0; bt < NB; ++bt) {
-            load_codes<BITS, KB>(code_base[bt] + (size_t)g * group * BITS / 8, st.cw[bt]);
-            st.s[bt] = scale_base[bt][g];
-        }
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                buf_load_codes<BITS, KB>(cr[m], coff[rt], (unsigned)g * (unsigned)(group * BITS / 8),
+                                         st.cw[m * RT + rt]);
+                st.s[m * RT + rt] = __uint_as_float(buf_load4(sr[m], soff[rt], (unsigned)g * 4u));
+            }
     };
 
     f32x4 tot[NB][NTT];
@@ -267,33 +335,35 @@ __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tot[bt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Every wave has at least one group (KS <= G).  Ring loads are
-    // unconditional (past the last group they re-read it) so that waiting for
-    // one stage leaves the other in flight.
+    // Every wave has at least one group (KS <= G).  The loop is branch-free
+    // so that waiting for one stage leaves the others in flight: loads past
+    // the wave's last group re-read it, and those steps count with scale 0.
     const int gbeg = ks * G / KS, gend = (ks + 1) * G / KS;
     Stage S[DEPTH];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) load(S[i], min(gbeg + i, gend - 1));
+    for (int i = 0; i < DEPTH; ++i) {
+        load(S[i], min(gbeg + i, gend - 1));
+        __builtin_amdgcn_sched_barrier(0);   // keep the stages' loads in issue order
+    }
     for (int base = gbeg; base < gend; base += DEPTH) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
             const int g = base + i;
-            if (g < gend) {
 #pragma unroll
-                for (int bt = 0; bt < NB; ++bt) {
-                    half8 bf[KB];
+            for (int bt = 0; bt < NB; ++bt) {
+                half8 bf[KB];
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw[bt], j);
-                    const float s = S[i].s[bt] * QFormat<BITS>::kInvZ;
+                for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw[bt], j);
+                const float s = g < gend ? S[i].s[bt] * QFormat<BITS>::kInvZ : 0.0f;
 #pragma unroll
-                    for (int tt = 0; tt < NTT; ++tt) {
-                        const f32x4 acc = group_mfma<BITS, KB, NTT, NB>(S[i], bf, tt);
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const f32x4 acc = group_mfma<BITS, KB, NTT, NB>(S[i], bf, tt);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) tot[bt][tt][r] = fmaf(s, acc[r], tot[bt][tt][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) tot[bt][tt][r] = fmaf(s, acc[r], tot[bt][tt][r]);
                 }
             }
             load(S[i], min(g + DEPTH, gend - 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -406,17 +476,21 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
     const int tb = blockIdx.x % NTB, rb = blockIdx.x / NTB;
     const int row0 = (rb * RW + rw) * 16 * RT;
     const int t0 = tb * 16 * NTT;
-    const size_t rs = (size_t)d_ff * BITS / 8;
-    size_t code_off[RT], scale_off[RT];
+    // Fixed 32-bit lane offsets; a step moves only uniform offsets (one
+    // expert's hidden half has at most 65536 x 8192 entries).
+    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * 4;
+    const size_t hbytes = (size_t)T * d_ff * 2;
+    const BufRes fres = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
+    unsigned coff[RT], soff[RT], hoff[NTT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int row = min(row0 + rt * 16 + n, d_model - 1);
-        code_off[rt] = (size_t)row * rs + (size_t)(q * 8 * KB) * BITS / 8;
-        scale_off[rt] = (size_t)row * Gd;
+        const unsigned row = (unsigned)min(row0 + rt * 16 + n, d_model - 1);
+        coff[rt] = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
+        soff[rt] = row * (unsigned)Gd * 4u;
     }
-    size_t hoff[NTT];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) hoff[tt] = (size_t)min(t0 + tt * 16 + n, T - 1) * d_ff + q * 8 * KB;
+    for (int tt = 0; tt < NTT; ++tt)
+        hoff[tt] = ((unsigned)min(t0 + tt * 16 + n, T - 1) * (unsigned)d_ff + (unsigned)(q * 8 * KB)) * 2u;
 
     struct Stage {
         TbStage<BITS, KB, NTT, RT> v;
@@ -424,21 +498,24 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
     };
     auto load = [&](Stage &st, int p) {
         const int e = p / Gd, g = p - e * Gd;
-        const QPtr D = a.down[e];
-        const size_t hb = (size_t)e * T * d_ff + (size_t)g * group;
+        const size_t he = (size_t)e * T * d_ff;
+        const BufRes hr = buf_res(a.hh + he, hbytes), lr = buf_res(a.hl + he, hbytes);
+        const unsigned hs = (unsigned)g * (unsigned)group * 2u;
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
-                st.v.ah[tt][j] = load_half8(a.hh + hb + hoff[tt] + 8 * j);
-                st.v.al[tt][j] = load_half8(a.hl + hb + hoff[tt] + 8 * j);
+                st.v.ah[tt][j] = __builtin_bit_cast(half8, buf_load16(hr, hoff[tt] + 16 * j, hs));
+                st.v.al[tt][j] = __builtin_bit_cast(half8, buf_load16(lr, hoff[tt] + 16 * j, hs));
             }
-            st.f[tt] = *reinterpret_cast<const f32x4 *>(a.hf + ((size_t)e * Gd + g) * a.t_pad + t0 + tt * 16 + 4 * q);
+            st.f[tt] = __builtin_bit_cast(f32x4, buf_load16(fres, (unsigned)(tt * 16 + 4 * q) * 4u,
+                                                            (unsigned)(((size_t)e * Gd + g) * a.t_pad + t0) * 4u));
         }
+        const BufRes dc = buf_res(a.down[e].codes, cbytes), ds = buf_res(a.down[e].scales, sbytes);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            load_codes<BITS, KB>(D.codes + code_off[rt] + (size_t)g * group * BITS / 8, st.v.cw[rt]);
-            st.v.s[rt] = D.scales[scale_off[rt] + g];
+            buf_load_codes<BITS, KB>(dc, coff[rt], (unsigned)g * (unsigned)(group * BITS / 8), st.v.cw[rt]);
+            st.v.s[rt] = __uint_as_float(buf_load4(ds, soff[rt], (unsigned)g * 4u));
         }
     };
 
@@ -448,32 +525,35 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tot[rt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Every wave has at least one pair (KS <= P); unconditional ring loads.
+    // Every wave has at least one pair (KS <= P); branch-free ring as in
+    // gate_up (steps past the wave's last pair count with scale 0).
     const int P = E * Gd;
     const int pbeg = ks * P / KS, pend = (ks + 1) * P / KS;
     Stage S[DEPTH];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) load(S[i], min(pbeg + i, pend - 1));
+    for (int i = 0; i < DEPTH; ++i) {
+        load(S[i], min(pbeg + i, pend - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int base = pbeg; base < pend; base += DEPTH) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i) {
             const int p = base + i;
-            if (p < pend) {
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    half8 bf[KB];
+            for (int rt = 0; rt < RT; ++rt) {
+                half8 bf[KB];
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].v.cw[rt], j);
-                    const float s = S[i].v.s[rt] * QFormat<BITS>::kInvZ;
+                for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].v.cw[rt], j);
+                const float s = p < pend ? S[i].v.s[rt] * QFormat<BITS>::kInvZ : 0.0f;
 #pragma unroll
-                    for (int tt = 0; tt < NTT; ++tt) {
-                        const f32x4 acc = group_mfma<BITS, KB, NTT, RT>(S[i].v, bf, tt);
+                for (int tt = 0; tt < NTT; ++tt) {
+                    const f32x4 acc = group_mfma<BITS, KB, NTT, RT>(S[i].v, bf, tt);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) tot[rt][tt][r] = fmaf(s * S[i].f[tt][r], acc[r], tot[rt][tt][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) tot[rt][tt][r] = fmaf(s * S[i].f[tt][r], acc[r], tot[rt][tt][r]);
                 }
             }
             load(S[i], min(p + DEPTH, pend - 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -513,16 +593,19 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 }
 
 // -------------------------------------------------------------------------
-// Tiled variants for more than 16 tokens: a block of 8 waves covers 64 tokens
-// and 128 weight rows (one 16-row tile per wave).  For each quantisation group
-// (gate_up) or (expert, group) pair (down), the block loads the 64 tokens'
-// activation halves once, with coalesced 16-byte loads, into one of two LDS
-// buffers; the waves read their MFMA fragments from LDS.  One barrier per
-// step: a buffer is refilled only after every wave has passed the barrier
-// that ends the step reading it.  Codes and scales are per wave, one step
-// ahead in registers.
-constexpr int kTileTokens = 64;
+// Tiled kernels (groups of 32 and 64 columns): a block of 8 waves covers a
+// tile of TT = 16 * NTT tokens and 128 weight rows (one 16-row tile per wave).
+// For each quantisation group (gate_up) or (expert, group) pair (down) the
+// block loads the tile's activation halves once, with coalesced 16-byte loads,
+// into one of two LDS buffers, and the waves read their MFMA fragments from
+// LDS.  One barrier per step: a buffer is refilled only after every wave has
+// passed the barrier that ends the step reading it.  The K dimension (the
+// groups of d_model, or the (expert, group) pairs) is split over `ks` blocks
+// when there would otherwise be too few blocks: each writes its partial sums
+// to the workspace and a finishing kernel adds them in split order
+// (deterministic), then applies the epilogue.
 constexpr int kTileWaves = 8;
+constexpr int kTileRows = 16 * kTileWaves;
 constexpr int kTilePrefetch = 3;   // steps of loads in registers (two in flight)
 
 // The hardware hands consecutive workgroups to the 8 XCDs in turn, and each XCD
@@ -535,217 +618,131 @@ __device__ __forceinline__ int xcd_logical(int b, int n)
     return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
-// Halfs per token row of an LDS activation tile (16 bytes of padding, so that
-// the 16 token rows of a fragment read fall into different banks).
-__host__ __device__ constexpr int tile_stride(int group) { return group + 8; }
-__host__ __device__ constexpr size_t tile_bytes(int group) { return (size_t)2 * kTileTokens * tile_stride(group) * 2; }
+// LDS activation tiles pad each token row by 16 bytes, so that the 16 token
+// rows of a fragment read fall into different banks.
+// Cooperative load of one activation tile: TT token rows x MG groups of
+// 32 * KB columns of the hi and the lo halves, in pieces of 16 bytes.  A
+// thread takes pieces c = tid + 512 i (i < PP); when there are fewer than
+// 512 * PP pieces, c wraps round and a piece is loaded and stored twice (same
+// value, same place), so every thread issues the same loads.  Piece i of a
+// thread is fixed by the thread and i alone: its half (the same for the whole
+// wave: a half is a multiple of 64 pieces), its byte offset from the step's
+// first column (below 2^30 for T <= 65536 and 8192 columns) and its LDS place.
+template <int KB, int NTT, int MG = 1>
+struct TileShape {
+    static constexpr int kCols = MG * 32 * KB, kPerRow = kCols / 8, kTT = 16 * NTT;
+    static constexpr int kPerHalf = kTT * kPerRow, kPieces = 2 * kPerHalf;
+    static constexpr int kPP = (kPieces + 511) / 512;
+    static constexpr int kStride = kCols + 8;   // halfs per LDS token row
+    static constexpr size_t kBytes = (size_t)2 * kTT * kStride * 2;
+};
 
-// Buffer loads: a resource (base, byte extent) in scalar registers, a fixed
-// per-lane byte offset and a uniform byte offset per step, so that moving to the
-// next step writes no vector registers.  Raw buffer (stride 0) with a 32-bit
-// data format, as the memory instructions expect for untyped loads.
-using BufRes = __amdgpu_buffer_rsrc_t;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ BufRes buf_res(const void *base, size_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)min(bytes, (size_t)0x7fffffff),
-                                             0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(BufRes r, unsigned voff, unsigned soff)
-{
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
-}
-__device__ __forceinline__ unsigned buf_load4(BufRes r, unsigned voff, unsigned soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-}
-
-template <int BITS, int KB>
-__device__ __forceinline__ void buf_load_codes(BufRes r, unsigned voff, unsigned soff, CodeWords<BITS, KB> &c)
-{
-    constexpr int n = CodeWords<BITS, KB>::kDwords;
-    if constexpr (n == 4) {
-        const uint4 v = buf_load16(r, voff, soff);
-        c.w[0] = v.x;
-        c.w[1] = v.y;
-        c.w[2] = v.z;
-        c.w[3] = v.w;
-    } else if constexpr (n == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
-        c.w[0] = v.x;
-        c.w[1] = v.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < n; ++i) c.w[i] = buf_load4(r, voff + 4 * i, soff);
-    }
-}
-
-// Cooperative load of one activation tile: 64 token rows x group = 32 * KB
-// columns of the hi and the lo halves, KB 16-byte pieces per thread.  Piece i of
-// a thread is fixed by the thread and i alone: its half (hi or lo; the same for
-// the whole wave, since a half is 256 * KB pieces), its byte offset from the
-// step's first column (below 2^30 for T <= 65536 and 8192 columns) and its
-// place in LDS.
-template <int KB>
+template <int KB, int NTT, int MG = 1>
 struct TileRegs {
-    uint4 v[KB];
+    uint4 v[TileShape<KB, NTT, MG>::kPP];
 };
 
-template <int KB>
+template <int KB, int NTT, int MG = 1>
 struct TileMap {
-    unsigned off[KB];   // global byte offset of the piece within its half
-    unsigned lds[KB];   // LDS byte offset of the piece within a tile buffer
-    bool lo[KB];        // wave-uniform: the piece belongs to the lo half
+    static constexpr int PP = TileShape<KB, NTT, MG>::kPP;
+    unsigned off[PP];   // global byte offset of the piece within its half
+    unsigned lds[PP];   // LDS byte offset of the piece within a tile buffer
+    bool lo[PP];        // wave-uniform: the piece belongs to the lo half
 };
 
-template <int KB>
-__device__ __forceinline__ void tile_map(TileMap<KB> &m, int wave, unsigned row_stride_bytes, int t0, int T)
+template <int KB, int NTT, int MG = 1>
+__device__ __forceinline__ void tile_map(TileMap<KB, NTT, MG> &m, int wave, unsigned row_stride_bytes, int t0,
+                                         int T)
 {
-    constexpr int group = 32 * KB, per_row = group / 8, per_half = kTileTokens * per_row;
-    constexpr int st = tile_stride(group);
+    using Sh = TileShape<KB, NTT, MG>;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-        const int c = threadIdx.x + 512 * i;
-        const int hl = (wave * 64 + 512 * i) / per_half;
-        const int rem = c - hl * per_half;
-        const int tok = rem / per_row, part = rem - tok * per_row;
+    for (int i = 0; i < Sh::kPP; ++i) {
+        const int c = (threadIdx.x + 512 * i) % Sh::kPieces;
+        const int hl = ((wave * 64 + 512 * i) % Sh::kPieces) / Sh::kPerHalf;
+        const int rem = c - hl * Sh::kPerHalf;
+        const int tok = rem / Sh::kPerRow, part = rem - tok * Sh::kPerRow;
         m.lo[i] = hl != 0;
         m.off[i] = (unsigned)min(t0 + tok, T - 1) * row_stride_bytes + (unsigned)part * 16u;
-        m.lds[i] = (unsigned)((hl * kTileTokens + tok) * st + part * 8) * 2u;
+        m.lds[i] = (unsigned)((hl * Sh::kTT + tok) * Sh::kStride + part * 8) * 2u;
     }
 }
 
 // The pieces of the step whose first column is `col_bytes` into each row.
-template <int KB>
-__device__ __forceinline__ void tile_load(TileRegs<KB> &r, const TileMap<KB> &m, BufRes hi, BufRes lo,
-                                          unsigned col_bytes)
+template <int KB, int NTT, int MG = 1>
+__device__ __forceinline__ void tile_load(TileRegs<KB, NTT, MG> &r, const TileMap<KB, NTT, MG> &m, BufRes hi,
+                                          BufRes lo, unsigned col_bytes)
 {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) r.v[i] = buf_load16(m.lo[i] ? lo : hi, m.off[i], col_bytes);
+    for (int i = 0; i < TileShape<KB, NTT, MG>::kPP; ++i)
+        r.v[i] = buf_load16(m.lo[i] ? lo : hi, m.off[i], col_bytes);
 }
 
-template <int KB>
-__device__ __forceinline__ void tile_store(const TileRegs<KB> &r, const TileMap<KB> &m, _Float16 *tile)
+template <int KB, int NTT, int MG = 1>
+__device__ __forceinline__ void tile_store(const TileRegs<KB, NTT, MG> &r, const TileMap<KB, NTT, MG> &m,
+                                           uint8_t *tile)
 {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(tile) + m.lds[i]) = r.v[i];
+    for (int i = 0; i < TileShape<KB, NTT, MG>::kPP; ++i) *reinterpret_cast<uint4 *>(tile + m.lds[i]) = r.v[i];
 }
 
-// A fragments of token tile tt, K-block j, hi and lo, from an LDS tile.
-__device__ __forceinline__ void tile_frags(const _Float16 *tile, int group, int tt, int j, int KB, half8 &h, half8 &l)
+// A fragments of token tile tt, K-block j of group gi, hi and lo, from an LDS
+// tile.
+template <int KB, int NTT, int MG = 1>
+__device__ __forceinline__ void tile_frags(const uint8_t *tile, int tt, int gi, int j, half8 &h, half8 &l)
 {
-    const int st = tile_stride(group);
+    using Sh = TileShape<KB, NTT, MG>;
     const int lane = threadIdx.x & 63, q = lane >> 4, n = lane & 15;
-    const _Float16 *p = tile + (tt * 16 + n) * st + q * 8 * KB + 8 * j;
+    const _Float16 *p = reinterpret_cast<const _Float16 *>(tile) + (tt * 16 + n) * Sh::kStride + gi * 32 * KB +
+                        q * 8 * KB + 8 * j;
     h = load_half8(p);
-    l = load_half8(p + kTileTokens * st);
+    l = load_half8(p + Sh::kTT * Sh::kStride);
 }
 
-template <int BITS, int KB, int PF>
-__global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
+// Partial sums of one block of a split tile: N f32x4 per thread, lane-major
+// (consecutive threads, consecutive 16 bytes), so that storing and reloading
+// them is coalesced.
+template <int N>
+__device__ __forceinline__ void store_partial(const f32x4 (&acc)[N], float *part)
 {
-    constexpr int NTT = kTileTokens / 16;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int group = a.group, d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
-    const size_t tb_bytes = tile_bytes(group);
-    _Float16 *tiles = reinterpret_cast<_Float16 *>(smem);
-    float *mx = reinterpret_cast<float *>(smem + 2 * tb_bytes);  // [waves][NTT][16]
+#pragma unroll
+    for (int k = 0; k < N; ++k) reinterpret_cast<f32x4 *>(part)[k * 512 + threadIdx.x] = acc[k];
+}
+
+// acc = sum over the splits s = 0, 1, ... of the partial sums at part + s * stride.
+template <int N>
+__device__ __forceinline__ void sum_partials(f32x4 (&acc)[N], const float *part, size_t stride, int splits)
+{
+#pragma unroll
+    for (int k = 0; k < N; ++k) acc[k] = reinterpret_cast<const f32x4 *>(part)[k * 512 + threadIdx.x];
+    for (int s = 1; s < splits; ++s) {
+        const f32x4 *ps = reinterpret_cast<const f32x4 *>(part + (size_t)s * stride);
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const f32x4 v = ps[k * 512 + threadIdx.x];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[k][r] += v[r];
+        }
+    }
+}
+
+// gate_up epilogue of a tile: hidden = SiLU(gate) * up for the wave's 16 rows
+// and the tile's tokens (tot scaled by the tokens' 2^-xe), normalised per (token, H group) by a power of two,
+// stored as hi/lo halves in sigma order with the factor r[t][e] * 2^e for
+// down.  tot holds the gate token tiles, then the up token tiles; mx is LDS
+// for [waves][NTT][16] floats.  Contains a block barrier.
+template <int KB, int NTT>
+__device__ __forceinline__ void gu_epilogue(const TbArgs &a, const f32x4 (&tot)[2 * NTT], int e, int rb, int tb,
+                                            float *mx)
+{
+    constexpr int TT = 16 * NTT;
+    constexpr int group = 32 * KB;
+    const int d_ff = a.d_ff, T = a.T, E = a.n_experts, HG = d_ff / group;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 4, n = lane & 15;
-    const int G = d_model / group, HG = d_ff / group;
-    const int NTB = (T + kTileTokens - 1) / kTileTokens;
-    const int RB = (d_ff + 16 * kTileWaves - 1) / (16 * kTileWaves);
-    int b = xcd_logical(blockIdx.x, gridDim.x);
-    const int tb = b % NTB;
-    b /= NTB;
-    const int rb = b % RB;
-    const int e = b / RB;
-    const int t0 = tb * kTileTokens;
-    const int wrow0 = rb * 16 * kTileWaves + wave * 16;   // this wave's first d_ff row
-    // Lane offsets (32-bit: a matrix has at most 8192 x 8192 entries) and
-    // buffer resources; a step moves only the uniform offsets.
-    const unsigned row = (unsigned)min(wrow0 + n, d_ff - 1);
-    const unsigned coff = row * (unsigned)(d_model * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
-    const unsigned soff = row * (unsigned)G * 4u;
-    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * 4;
-    const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
-    const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
-    const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
-    TileMap<KB> tm;
-    tile_map<KB>(tm, wave, (unsigned)d_model * 2u, t0, T);
-
-    // Register ring of PF steps: the activation pieces this thread stores into
-    // LDS and the wave's codes and scales, PF - 1 steps ahead of the step being
-    // computed; LDS holds two steps.  The loop is branch-free so that the
-    // compiler's load waits are exact: loads past the last group repeat it,
-    // and the steps past the end (at most PF - 1) are computed with scale 0.
-    struct GuStage {
-        TileRegs<KB> tr;
-        CodeWords<BITS, KB> cw[2];
-        float sc[2];
-    };
-    GuStage S[PF];
-    auto load_step = [&](GuStage &st, int g) {
-        const unsigned gc = (unsigned)min(g, G - 1);
-        tile_load<KB>(st.tr, tm, xhr, xlr, gc * (unsigned)group * 2u);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            buf_load_codes<BITS, KB>(cr[m], coff, gc * (unsigned)(group * BITS / 8), st.cw[m]);
-            st.sc[m] = __uint_as_float(buf_load4(sr[m], soff, gc * 4u));
-        }
-    };
-
-    f32x4 tot[2][NTT];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) tot[m][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int i = 0; i < PF; ++i) load_step(S[i], i);
-    tile_store<KB>(S[0].tr, tm, tiles);
-    __syncthreads();
-    for (int base = 0; base < G; base += PF) {
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int g = base + i;
-            const _Float16 *tile = tiles + (size_t)(g & 1) * (tb_bytes / 2);
-            half8 bf[2][KB];
-            float s[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-#pragma unroll
-                for (int j = 0; j < KB; ++j) bf[m][j] = code_frag<BITS, KB>(S[i].cw[m], j);
-                s[m] = g < G ? S[i].sc[m] * QFormat<BITS>::kInvZ : 0.0f;
-            }
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) {
-                f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    half8 h, l;
-                    tile_frags(tile, group, tt, j, KB, h, l);
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        acc[m] = mfma(h, bf[m][j], acc[m]);
-                        acc[m] = mfma(l, bf[m][j], acc[m]);
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[m][tt][r] = fmaf(s[m], acc[m][r], tot[m][tt][r]);
-            }
-            tile_store<KB>(S[(i + 1) % PF].tr, tm, tiles + (size_t)((g + 1) & 1) * (tb_bytes / 2));
-            load_step(S[i], g + PF);
-            __syncthreads();
-        }
-    }
-
-    // hidden = SiLU(gate) * up; per-token maxima over this wave's 16 rows.
+    const int t0 = tb * TT;
+    const int wrow0 = rb * kTileRows + wave * 16;
+    // Per-token maxima over this wave's 16 rows.
     float h[NTT][4];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
@@ -753,23 +750,24 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
         for (int i = 0; i < 4; ++i) {
             const int t = min(t0 + tt * 16 + 4 * q + i, T - 1);
             const int xe = a.xe[t];
-            const float gv = ldexpf(tot[0][tt][i], xe), uv = ldexpf(tot[1][tt][i], xe);
+            const float gv = ldexpf(tot[tt][i], xe), uv = ldexpf(tot[NTT + tt][i], xe);
             h[tt][i] = wrow0 + n < d_ff ? silu(gv) * uv : 0.0f;
             const float m = row16_max(fabsf(h[tt][i]));
             if (n == 0) mx[(wave * NTT + tt) * 16 + 4 * q + i] = m;
         }
     __syncthreads();
     if (wrow0 >= d_ff) return;
-    const int wpg = group / 16;                       // waves per H group
+    constexpr int wpg = group / 16;                   // waves per H group
     const int w0 = wave - wave % wpg;
-    const int hg = (rb * 16 * kTileWaves + w0 * 16) / group;
+    const int hg = (rb * kTileRows + w0 * 16) / group;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tl = 4 * q + i;
             float m = 0.0f;
-            for (int w = w0; w < w0 + wpg; ++w) m = fmaxf(m, mx[(w * NTT + tt) * 16 + tl]);
+#pragma unroll
+            for (int w = 0; w < wpg; ++w) m = fmaxf(m, mx[((w0 + w) * NTT + tt) * 16 + tl]);
             const int ee = norm_exponent(m);
             const int t = t0 + tt * 16 + tl;
             if (t < T) {
@@ -787,158 +785,313 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
         }
 }
 
-// Down, tiled: block (token tile, row block, split) sums the (expert, group)
-// pairs of its split; with more than one split each writes its partial sums to
-// part[split][T][d_model] and k_tb_sum adds them in split order (deterministic).
-template <int BITS, int KB, int PF>
-__global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
+
+// gate_up, tiled: block (token tile, row block, expert, split).  A step is MG
+// quantisation groups of d_model.
+template <int BITS, int KB, int NTT, int MG, int PF>
+__global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 {
-    constexpr int NTT = kTileTokens / 16;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int group = a.group, d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
-    const size_t tb_bytes = tile_bytes(group);
-    _Float16 *tiles = reinterpret_cast<_Float16 *>(smem);
-    float *fac = reinterpret_cast<float *>(smem + 2 * tb_bytes);  // [2][64]
+    using Sh = TileShape<KB, NTT, MG>;
+    constexpr int TT = 16 * NTT;
+    constexpr int group = 32 * KB;
+    extern __shared__ __align__(16) unsigned char smem[];   // two tiles, then the epilogue's maxima
+    const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 4, n = lane & 15;
-    const int Gd = d_ff / group;
-    const int NTB = (T + kTileTokens - 1) / kTileTokens;
-    const int RB = (d_model + 16 * kTileWaves - 1) / (16 * kTileWaves);
-    int bid = xcd_logical(blockIdx.x, gridDim.x);
-    const int tb = bid % NTB;
-    bid /= NTB;
-    const int rb = bid % RB;
-    const int ks = bid / RB;
-    const int t0 = tb * kTileTokens;
-    const int wrow0 = rb * 16 * kTileWaves + wave * 16;
-    const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
-    const unsigned coff = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
-    const unsigned soff = row * (unsigned)Gd * 4u;
-    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * 4;
-    const size_t hbytes = (size_t)T * d_ff * 2;   // one expert's hidden half
-    const BufRes fr_res = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
-    TileMap<KB> tm;
-    tile_map<KB>(tm, wave, (unsigned)d_ff * 2u, t0, T);
-    const int P = E * Gd;
-    const int p0 = (int)((long)ks * P / a.ks_dn), p1 = (int)((long)(ks + 1) * P / a.ks_dn);
-    const int NP = p1 - p0;
-    float *dst = a.ks_dn > 1 ? a.part + (size_t)ks * T * d_model : a.out;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = d_model / group, NS = G / MG;
+    const int NTB = (T + TT - 1) / TT;
+    const int RB = (d_ff + kTileRows - 1) / kTileRows;
+    const int KSG = a.ks_gu;
+    // Logical block order: token tile, row block, expert, split (the blocks an
+    // XCD gets share codes across token tiles and activation tiles across row
+    // blocks and experts).
+    int b = xcd_logical(blockIdx.x, gridDim.x);
+    const int tb = b % NTB;
+    b /= NTB;
+    const int rb = b % RB;
+    b /= RB;
+    const int e = b % E;
+    const int ks = b / E;
+    const int t0 = tb * TT;
+    const int wrow0 = rb * kTileRows + wave * 16;   // this wave's first d_ff row
+    const int s0 = (int)((long)ks * NS / KSG), NSS = (int)((long)(ks + 1) * NS / KSG) - s0;
 
-    f32x4 tot[NTT];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) tot[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // Lane offsets (32-bit: a matrix has at most 8192 x 8192 entries) and
+    // buffer resources; a step moves only the uniform offsets.
+    const unsigned row = (unsigned)min(wrow0 + n, d_ff - 1);
+    const unsigned coff = row * (unsigned)(d_model * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
+    const unsigned soff = row * (unsigned)G * 4u;
+    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * 4;
+    const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
+    const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
+    const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
+    TileMap<KB, NTT, MG> tm;
+    tile_map<KB, NTT, MG>(tm, wave, (unsigned)d_model * 2u, t0, T);
 
-    if (NP > 0) {
-        // Register ring of PF steps (hidden tile pieces, the 64 tokens' factors,
-        // the wave's codes and scale), branch-free as in gate_up: loads past
-        // the split's end repeat its last pair, and those steps count with
-        // scale 0.
-        struct DnStage {
-            TileRegs<KB> tr;
-            CodeWords<BITS, KB> cw;
-            float fr, sc;
-        };
-        DnStage S[PF];
-        auto load_step = [&](DnStage &st, int i) {
-            const int p = p0 + min(i, NP - 1);
-            const int e = p / Gd, g = p - e * Gd;
-            const size_t ho = (size_t)e * T * d_ff;
-            tile_load<KB>(st.tr, tm, buf_res(a.hh + ho, hbytes), buf_res(a.hl + ho, hbytes),
-                          (unsigned)g * (unsigned)group * 2u);
-            st.fr = __uint_as_float(buf_load4(fr_res, (unsigned)lane * 4u,
-                                              (unsigned)(((size_t)e * Gd + g) * a.t_pad + t0) * 4u));
-            buf_load_codes<BITS, KB>(buf_res(a.down[e].codes, cbytes), coff, (unsigned)g * (unsigned)(group * BITS / 8),
-                                     st.cw);
-            st.sc = __uint_as_float(buf_load4(buf_res(a.down[e].scales, sbytes), soff, (unsigned)g * 4u));
-        };
-        auto store_step = [&](const DnStage &st, int buf) {
-            tile_store<KB>(st.tr, tm, tiles + (size_t)buf * (tb_bytes / 2));
-            fac[buf * 64 + lane] = st.fr;
-        };
+    // Register ring of PF steps: the activation pieces this thread stores into
+    // LDS and the wave's codes and scales, PF - 1 steps ahead of the step being
+    // computed; LDS holds two steps.  The loop is branch-free so that the
+    // compiler's load waits are exact: loads past the split's last step
+    // repeat it, and the steps past the end (at most PF - 1) count with scale 0.
+    struct GuStage {
+        TileRegs<KB, NTT, MG> tr;
+        CodeWords<BITS, KB> cw[2][MG];
+        float sc[2][MG];
+    };
+    GuStage S[PF];
+    auto load_step = [&](GuStage &st, int i) {
+        const unsigned g = (unsigned)((s0 + min(i, NSS - 1)) * MG);
+        tile_load<KB, NTT, MG>(st.tr, tm, xhr, xlr, g * (unsigned)group * 2u);
 #pragma unroll
-        for (int i = 0; i < PF; ++i) load_step(S[i], i);
-        store_step(S[0], 0);
-        __syncthreads();
-        for (int base = 0; base < NP; base += PF) {
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                const int st = base + i;
-                const int buf = st & 1;
-                const _Float16 *tile = tiles + (size_t)buf * (tb_bytes / 2);
-                half8 bf[KB];
+            for (int gi = 0; gi < MG; ++gi) {
+                buf_load_codes<BITS, KB>(cr[m], coff, (g + gi) * (unsigned)(group * BITS / 8), st.cw[m][gi]);
+                st.sc[m][gi] = __uint_as_float(buf_load4(sr[m], soff, (g + gi) * 4u));
+            }
+    };
+
+    f32x4 tot[2 * NTT];   // gate token tiles, then up token tiles
 #pragma unroll
-                for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw, j);
-                const float s = st < NP ? S[i].sc * QFormat<BITS>::kInvZ : 0.0f;
+    for (int k = 0; k < 2 * NTT; ++k) tot[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        load_step(S[i], i);
+        __builtin_amdgcn_sched_barrier(0);   // keep the stages' loads in issue order
+    }
+    tile_store<KB, NTT, MG>(S[0].tr, tm, smem);
+    __syncthreads();
+    for (int base = 0; base < NSS; base += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int st = base + i;
+            const uint8_t *tile = smem + (size_t)(st & 1) * Sh::kBytes;
+#pragma unroll
+            for (int gi = 0; gi < MG; ++gi) {
+                half8 bf[2][KB];
+                float s[2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                    for (int j = 0; j < KB; ++j) bf[m][j] = code_frag<BITS, KB>(S[i].cw[m][gi], j);
+                    s[m] = st < NSS ? S[i].sc[m][gi] * QFormat<BITS>::kInvZ : 0.0f;
+                }
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                     for (int j = 0; j < KB; ++j) {
                         half8 h, l;
-                        tile_frags(tile, group, tt, j, KB, h, l);
-                        acc = mfma(h, bf[j], acc);
-                        acc = mfma(l, bf[j], acc);
-                    }
-                    const f32x4 f = *reinterpret_cast<const f32x4 *>(fac + buf * 64 + tt * 16 + 4 * q);
+                        tile_frags<KB, NTT, MG>(tile, tt, gi, j, h, l);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[tt][r] = fmaf(s * f[r], acc[r], tot[tt][r]);
+                        for (int m = 0; m < 2; ++m) {
+                            acc[m] = mfma(h, bf[m][j], acc[m]);
+                            acc[m] = mfma(l, bf[m][j], acc[m]);
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            tot[m * NTT + tt][r] = fmaf(s[m], acc[m][r], tot[m * NTT + tt][r]);
                 }
-                store_step(S[(i + 1) % PF], buf ^ 1);
-                load_step(S[i], st + PF);
-                __syncthreads();
             }
+            tile_store<KB, NTT, MG>(S[(i + 1) % PF].tr, tm, smem + (size_t)((st + 1) & 1) * Sh::kBytes);
+            load_step(S[i], st + PF);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
         }
     }
+
+    if (KSG > 1) {
+        const int tile_id = (e * RB + rb) * NTB + tb;
+        store_partial<2 * NTT>(tot, a.part_gu + ((size_t)tile_id * KSG + ks) * (2 * NTT * 4 * 512));
+        return;
+    }
+    gu_epilogue<KB, NTT>(a, tot, e, rb, tb, reinterpret_cast<float *>(smem + 2 * Sh::kBytes));
+}
+
+// gate_up finish for split tiles: one block per (expert, row block, token
+// tile) adds the splits' partial sums in split order, then the epilogue.
+template <int KB, int NTT>
+__global__ __launch_bounds__(512) void k_tb_gu_finish(TbArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int TT = 16 * NTT;
+    const int NTB = (a.T + TT - 1) / TT;
+    const int RB = (a.d_ff + kTileRows - 1) / kTileRows;
+    const int tile_id = blockIdx.x;
+    const int tb = tile_id % NTB, rb = (tile_id / NTB) % RB, e = tile_id / NTB / RB;
+    constexpr size_t stride = (size_t)2 * NTT * 4 * 512;
+    f32x4 tot[2 * NTT];
+    sum_partials<2 * NTT>(tot, a.part_gu + (size_t)tile_id * a.ks_gu * stride, stride, a.ks_gu);
+    gu_epilogue<KB, NTT>(a, tot, e, rb, tb, reinterpret_cast<float *>(smem));
+}
+
+// out rows of the wave's 16 d_model rows for the tile's tokens.
+template <int NTT>
+__device__ __forceinline__ void dn_store(const TbArgs &a, const f32x4 (&tot)[NTT], int rb, int tb)
+{
+    const int lane = threadIdx.x & 63, q = lane >> 4, n = lane & 15;
+    const int wrow0 = rb * kTileRows + (threadIdx.x >> 6) * 16;
+    const int t0 = tb * 16 * NTT;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + tt * 16 + 4 * q + i;
             const int r = wrow0 + n;
-            if (t < T && r < d_model) dst[(size_t)t * d_model + r] = tot[tt][i];
+            if (t < a.T && r < a.d_model) a.out[(size_t)t * a.d_model + r] = tot[tt][i];
         }
 }
 
-// out = sum over the down splits of their partial sums, in split order.  The
-// partial slabs are 16-byte aligned (T * d_model is a multiple of 32); out is
-// only 4-byte aligned, so it is written one float at a time.
-__global__ __launch_bounds__(256) void k_tb_sum(const float *__restrict__ part, int splits, size_t count,
-                                                float *__restrict__ out)
+// down, tiled: block (token tile, row block, split) sums the (expert, group)
+// pairs of its split, all experts together (the router weights are in the
+// hidden factors).
+template <int BITS, int KB, int NTT, int PF>
+__global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
 {
-    const size_t n4 = count / 4;
-    for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        float4 acc = reinterpret_cast<const float4 *>(part)[i];
-        for (int s = 1; s < splits; ++s) {
-            const float4 v = reinterpret_cast<const float4 *>(part + (size_t)s * count)[i];
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
-        }
-        out[4 * i] = acc.x;
-        out[4 * i + 1] = acc.y;
-        out[4 * i + 2] = acc.z;
-        out[4 * i + 3] = acc.w;
+    constexpr int TT = 16 * NTT;
+    constexpr int group = 32 * KB;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
+    constexpr size_t tb_bytes = TileShape<KB, NTT>::kBytes;
+    float *fac = reinterpret_cast<float *>(smem + 2 * tb_bytes);  // [2][TT]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = lane >> 4, n = lane & 15;
+    const int Gd = d_ff / group;
+    const int NTB = (T + TT - 1) / TT;
+    const int KSD = a.ks_dn;
+    // Logical block order: token tile, row block, split (the blocks an XCD
+    // gets share codes across token tiles and hidden tiles across row blocks).
+    const int RB = (d_model + kTileRows - 1) / kTileRows;
+    int bid = xcd_logical(blockIdx.x, gridDim.x);
+    const int tb = bid % NTB;
+    bid /= NTB;
+    const int rb = bid % RB;
+    const int ks = bid / RB;
+    const int t0 = tb * TT;
+    const int wrow0 = rb * kTileRows + wave * 16;
+    const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
+    const unsigned coff = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
+    const unsigned soff = row * (unsigned)Gd * 4u;
+    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * 4;
+    const size_t hbytes = (size_t)T * d_ff * 2;   // one expert's hidden half
+    const BufRes fr_res = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
+    TileMap<KB, NTT> tm;
+    tile_map<KB, NTT>(tm, wave, (unsigned)d_ff * 2u, t0, T);
+    const int P = E * Gd;
+    const int p0 = (int)((long)ks * P / KSD), NP = (int)((long)(ks + 1) * P / KSD) - p0;
+    const unsigned flane = (unsigned)(lane & (TT - 1));   // a token of the tile (repeats for TT < 64)
+
+    f32x4 tot[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) tot[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // Register ring of PF steps (hidden tile pieces, the tile's factors, the
+    // wave's codes and scale), branch-free as in gate_up.
+    struct DnStage {
+        TileRegs<KB, NTT> tr;
+        CodeWords<BITS, KB> cw;
+        float fr, sc;
+    };
+    DnStage S[PF];
+    auto load_step = [&](DnStage &st, int i) {
+        const int p = p0 + min(i, NP - 1);
+        const int e = p / Gd, g = p - e * Gd;
+        const size_t ho = (size_t)e * T * d_ff;
+        tile_load<KB, NTT>(st.tr, tm, buf_res(a.hh + ho, hbytes), buf_res(a.hl + ho, hbytes),
+                           (unsigned)g * (unsigned)group * 2u);
+        st.fr = __uint_as_float(buf_load4(fr_res, flane * 4u, (unsigned)(((size_t)e * Gd + g) * a.t_pad + t0) * 4u));
+        buf_load_codes<BITS, KB>(buf_res(a.down[e].codes, cbytes), coff, (unsigned)g * (unsigned)(group * BITS / 8),
+                                 st.cw);
+        st.sc = __uint_as_float(buf_load4(buf_res(a.down[e].scales, sbytes), soff, (unsigned)g * 4u));
+    };
+    auto store_step = [&](const DnStage &st, int buf) {
+        tile_store<KB, NTT>(st.tr, tm, smem + (size_t)buf * tb_bytes);
+        fac[buf * TT + flane] = st.fr;
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        load_step(S[i], i);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    store_step(S[0], 0);
+    __syncthreads();
+    for (int base = 0; base < NP; base += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int st = base + i;
+            const int buf = st & 1;
+            const uint8_t *tile = smem + (size_t)buf * tb_bytes;
+            half8 bf[KB];
+#pragma unroll
+            for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw, j);
+            const float s = st < NP ? S[i].sc * QFormat<BITS>::kInvZ : 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < KB; ++j) {
+                    half8 h, l;
+                    tile_frags<KB, NTT>(tile, tt, 0, j, h, l);
+                    acc = mfma(h, bf[j], acc);
+                    acc = mfma(l, bf[j], acc);
+                }
+                const f32x4 f = *reinterpret_cast<const f32x4 *>(fac + buf * TT + tt * 16 + 4 * q);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tot[tt][r] = fmaf(s * f[r], acc[r], tot[tt][r]);
+            }
+            store_step(S[(i + 1) % PF], buf ^ 1);
+            load_step(S[i], st + PF);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        }
+    }
+
+    if (KSD > 1) {
+        store_partial<NTT>(tot, a.part_dn + ((size_t)(rb * NTB + tb) * KSD + ks) * (NTT * 4 * 512));
+        return;
+    }
+    dn_store<NTT>(a, tot, rb, tb);
 }
 
-template <int BITS, int KB>
+// down finish for split tiles: one block per (row block, token tile) adds
+// the splits' partial sums in split order and writes out.
+template <int NTT>
+__global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
+{
+    constexpr int TT = 16 * NTT;
+    const int NTB = (a.T + TT - 1) / TT;
+    const int tile_id = blockIdx.x;
+    constexpr size_t stride = (size_t)NTT * 4 * 512;
+    f32x4 tot[NTT];
+    sum_partials<NTT>(tot, a.part_dn + (size_t)tile_id * a.ks_dn * stride, stride, a.ks_dn);
+    dn_store<NTT>(a, tot, tile_id / NTB, tile_id % NTB);
+}
+
+template <int BITS, int KB, int NTT, int MG>
 hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
     hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, kTilePrefetch>), dim3(pl.gu_blocks), dim3(64 * kTileWaves),
-                       pl.gu_lds, st, a);
+    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, kTilePrefetch>), dim3(pl.gu_blocks),
+                       dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, kTilePrefetch>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
+    if (a.ks_gu > 1) {
+        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu), dim3(64 * kTileWaves),
+                           (size_t)kTileWaves * NTT * 16 * 4, st, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, kTilePrefetch>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
                        pl.dn_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_dn > 1) {
-        const size_t count = (size_t)a.T * a.d_model;
-        const unsigned blocks = (unsigned)std::min<size_t>((count / 4 + 255) / 256 + 1, 2048);
-        hipLaunchKernelGGL(k_tb_sum, dim3(blocks), dim3(256), 0, st, a.part, a.ks_dn, count, a.out);
+        hipLaunchKernelGGL(k_tb_dn_finish<NTT>, dim3(pl.dn_blocks / a.ks_dn), dim3(64 * kTileWaves), 0, st, a);
         err = hipGetLastError();
     }
     return err;
@@ -961,16 +1114,20 @@ hipError_t launch_tb_kernels(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 template <int BITS, int KB>
 hipError_t launch_tb_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    // gate_up row tiles: 4 for 16-token tiles and 64-column groups (one wave per
-    // group), else 2 (more would not fit the registers); down: 4 row tiles for
-    // 16-token tiles, 2 for 32.
-    if (pl.ntt == 1) {
-        if constexpr (KB == 2)
-            if (pl.rt_gu == 4) return launch_tb_kernels<BITS, KB, 1, 4, 4>(pl, a, st);
-        return launch_tb_kernels<BITS, KB, 1, 2, 4>(pl, a, st);
+    if constexpr (KB <= 2) {
+        if (pl.tiled) {
+            if (pl.ntt == 1) {
+                if (pl.mg == 2) return launch_tb_tiled<BITS, KB, 1, 2>(pl, a, st);
+                return launch_tb_tiled<BITS, KB, 1, 1>(pl, a, st);
+            }
+            if (pl.ntt == 2) return launch_tb_tiled<BITS, KB, 2, 1>(pl, a, st);
+            return launch_tb_tiled<BITS, KB, 4, 1>(pl, a, st);
+        }
     }
-    if constexpr (KB <= 2)
-        if (pl.ntt == kTileTokens / 16) return launch_tb_tiled<BITS, KB>(pl, a, st);
+    // Direct kernels (groups of 96 and 128 columns).  gate_up row tiles: 2
+    // (more would not fit the registers); down: 4 row tiles for 16-token
+    // tiles, 2 for 32.
+    if (pl.ntt == 1) return launch_tb_kernels<BITS, KB, 1, 2, 4>(pl, a, st);
     return launch_tb_kernels<BITS, KB, 2, 2, 2>(pl, a, st);
 }
 
@@ -979,16 +1136,30 @@ hipError_t launch_tb_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 // Dynamic LDS per block is kept within 64 KB.
 constexpr size_t kMaxBlockLds = 64 * 1024;
 
-// Splits of the tiled down kernel's (expert, group) pairs over blocks: enough
-// to give about two 8-wave blocks per compute unit, at most 8.
-int batch_down_splits(int d_model, int T)
+// Tokens per tile of the tiled kernels: 16, 32 or 64.
+int tile_ntt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
+
+// Splits of K over blocks: the smallest power of two (at most 16) that gives
+// `tiles` x splits >= 256 blocks of 8 waves, one per compute unit.
+int splits_for(long tiles)
 {
-    if (T <= 16) return 1;
-    const long blocks = (long)((d_model + 16 * kTileWaves - 1) / (16 * kTileWaves)) *
-                        ((T + kTileTokens - 1) / kTileTokens);
     int s = 1;
-    while (s < 8 && blocks * s < 512) s *= 2;
+    while (s < 16 && tiles * s < 256) s *= 2;
     return s;
+}
+
+BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T)
+{
+    BatchSplits b{};
+    b.ntt = tile_ntt(T);
+    const long ntb = (T + 16 * b.ntt - 1) / (16 * b.ntt);
+    b.gu_tiles = (long)n_experts * ((d_ff + kTileRows - 1) / kTileRows) * ntb;
+    b.dn_tiles = (long)((d_model + kTileRows - 1) / kTileRows) * ntb;
+    b.ks_gu = splits_for(b.gu_tiles);
+    b.ks_dn = splits_for(b.dn_tiles);
+    b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
+    b.dn_part_floats = b.ks_dn > 1 ? (size_t)b.dn_tiles * b.ks_dn * b.ntt * 4 * 512 : 0;
+    return b;
 }
 
 bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T, TbPlan *pl)
@@ -998,17 +1169,26 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     if (bits == 4 ? (kb < 1 || kb > 4) : (kb != 2 && kb != 4)) return false;
     if (d_model % group || d_ff % group) return false;
     TbPlan p{};
-    if (T > 16 && (group == 32 || group == 64)) {
-        // Tiled kernels: 64 tokens x 128 rows per 8-wave block.
-        p.ntt = kTileTokens / 16;
-        const long ntb = (T + kTileTokens - 1) / kTileTokens;
-        const int rows = 16 * kTileWaves;
+    if (group == 32 || group == 64) {
+        // Tiled kernels: 16 * ntt tokens x 128 rows per 8-wave block, K split
+        // over blocks as the workspace allows (at most one split per group).
+        const BatchSplits bs = batch_splits(n_experts, d_model, d_ff, T);
+        p.tiled = true;
+        p.ntt = bs.ntt;
         p.gu_waves = p.dn_waves = kTileWaves;
-        p.gu_blocks = (long)n_experts * ((d_ff + rows - 1) / rows) * ntb;
-        p.ks_dn = std::min(batch_down_splits(d_model, T), n_experts * (d_ff / group));
-        p.dn_blocks = (long)((d_model + rows - 1) / rows) * ntb * p.ks_dn;
-        p.gu_lds = 2 * tile_bytes(group) + (size_t)kTileWaves * (kTileTokens / 16) * 16 * 4;
-        p.dn_lds = 2 * tile_bytes(group) + 2 * 64 * 4;
+        // gate_up steps of mg groups: 2 for 16-token tiles, else 1 (1 if 2 does
+        // not divide the groups of d_model).
+        const int G = d_model / group;
+        p.mg = p.ntt == 1 ? 2 : 1;
+        while (G % p.mg) p.mg /= 2;
+        p.ks_gu = std::min(bs.ks_gu, G / p.mg);
+        p.ks_dn = std::min(bs.ks_dn, n_experts * (d_ff / group));
+        p.gu_blocks = bs.gu_tiles * p.ks_gu;
+        p.dn_blocks = bs.dn_tiles * p.ks_dn;
+        const int tt = 16 * p.ntt;
+        const size_t gtile = (size_t)2 * tt * (p.mg * group + 8) * 2;
+        p.gu_lds = 2 * gtile + (size_t)kTileWaves * p.ntt * 16 * 4;
+        p.dn_lds = 2 * ((size_t)2 * tt * (group + 8) * 2) + 2 * tt * 4;
         if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
         *pl = p;
         return true;
@@ -1017,7 +1197,7 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     const int ntb = (T + 16 * p.ntt - 1) / (16 * p.ntt);
     const int G = d_model / group;
     // gate_up: the block covers one quantisation group of d_ff rows.
-    p.rt_gu = (p.ntt == 1 && kb == 2) ? 4 : 2;
+    p.rt_gu = 2;
     p.rw_gu = group / (16 * p.rt_gu);
     if (p.rw_gu < 1 || p.rw_gu > 8 || p.rw_gu * 16 * p.rt_gu != group) return false;
     const long gu_blocks = (long)n_experts * (d_ff / group) * ntb;

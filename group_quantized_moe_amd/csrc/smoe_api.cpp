@@ -110,10 +110,10 @@ DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
 //   xe      i32 [T]                          their per-token exponents
 //   hh, hl  f16 [n_experts][T][d_ff]         hi/lo halves of the scaled hidden rows
 //   hf      f32 [n_experts][d_ff/group][Tp]  per (expert, group, token) factors, Tp = T rounded up to 64
-//   part    f32 [S][T][d_model]              partial sums of the S down splits (S = 1: none)
+//   pg, pd  f32                              partial sums of the gate_up / down K splits, per tile
 // Everything is rewritten by each call before it is read.
 struct BatchWorkspace {
-    size_t xh, xl, xe, hh, hl, hf, part, total;
+    size_t xh, xl, xe, hh, hl, hf, pg, pd, total;
 };
 
 int token_pad(int T) { return (T + smoe::kTokenPad - 1) / smoe::kTokenPad * smoe::kTokenPad; }
@@ -122,15 +122,16 @@ BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int 
 {
     BatchWorkspace w;
     const size_t nx = (size_t)T * d_model, nh = (size_t)n_experts * T * d_ff;
+    const smoe::BatchSplits bs = smoe::batch_splits(n_experts, d_model, d_ff, T);
     w.xh = 0;
     w.xl = w.xh + align256(nx * 2);
     w.xe = w.xl + align256(nx * 2);
     w.hh = w.xe + align256((size_t)T * 4);
     w.hl = w.hh + align256(nh * 2);
     w.hf = w.hl + align256(nh * 2);
-    w.part = w.hf + align256((size_t)n_experts * (d_ff / group) * token_pad(T) * 4);
-    const int splits = smoe::batch_down_splits(d_model, T);
-    w.total = w.part + (splits > 1 ? align256((size_t)splits * nx * 4) : 0);
+    w.pg = w.hf + align256((size_t)n_experts * (d_ff / group) * token_pad(T) * 4);
+    w.pd = w.pg + align256(bs.gu_part_floats * 4);
+    w.total = w.pd + align256(bs.dn_part_floats * 4);
     return w;
 }
 
@@ -293,7 +294,8 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
         a.hh = reinterpret_cast<_Float16 *>(ws + w.hh);
         a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
         a.hf = reinterpret_cast<float *>(ws + w.hf);
-        a.part = reinterpret_cast<float *>(ws + w.part);
+        a.part_gu = reinterpret_cast<float *>(ws + w.pg);
+        a.part_dn = reinterpret_cast<float *>(ws + w.pd);
         a.T = T;
         a.t_pad = token_pad(T);
         a.d_model = d_model;

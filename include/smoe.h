@@ -129,7 +129,8 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  * 2 <= T <= SMOE_MAX_TOKENS runs the token-batch kernels on the matrix cores,
  * in which every expert processes every token: an activation pass, a gate_up
  * pass and a down pass that sums the experts in a fixed order (deterministic,
- * no atomics).  They need group = 32, 64, 96 or 128 at 4 bits and 64 or 128 at
+ * no atomics).  With few tokens the K dimension of either pass is split over
+ * blocks whose partial sums a finishing pass adds in a fixed order.  They need group = 32, 64, 96 or 128 at 4 bits and 64 or 128 at
  * 2 bits, else SMOE_ERR_GROUP.  Activations are carried to the matrix cores
  * as two f16 halves scaled by a power of two per group, about 22 significant
  * bits; non-finite inputs give non-finite outputs.
