@@ -12,6 +12,9 @@ Other rows of the path, one JSON line each with --workload:
                       experts on the matrix cores (bound by HBM at T = 16, by
                       the f16 MFMA rate above)
   bf16                --shape q_proj|o_proj|kv_proj|lm_head dense matvec
+  bf16_batch          q, k and v projections (8192x4096, 2 x 512x4096) over
+                      one x as one batched launch, with the three separate
+                      launches timed beside it
 
 Inputs are seeded synthetic weights with the shapes and distributions of the
 Metal Compute Kernels page (S-MoE docs) workloads; they stand in for trained
@@ -324,6 +327,76 @@ def bf16_bench(args):
     }
 
 
+def bf16_batch_bench(args):
+    """The batched bf16 matvec: a token's q, k and v projections over one x in
+    one launch, against the same three matvecs launched one by one."""
+    import torch
+    import workloads
+    import group_quantized_moe_amd as gq
+    L = gq.lib()
+    jobs = workloads.BF16_BATCH
+    Ws, x = workloads.make_bf16_batch(jobs)
+    cols = jobs[0][1]
+    wbytes = sum(r * c * 2 for r, c, _, _ in jobs)
+    nbytes = wbytes + cols * 4 + sum(r * 4 for r, _, _, _ in jobs)
+    replicas = replica_count(wbytes)
+    dWs = [to_dev(W) for W in Ws]
+    reps = [dWs] + [[w.clone() for w in dWs] for _ in range(replicas - 1)]
+    xd = to_dev(x)
+    ys = [torch.empty(r, dtype=torch.float32, device="cuda") for r, _, _, _ in jobs]
+    arrays = [gq.bf16_job_array([(w, xd, y) for w, y in zip(rep, ys)]) for rep in reps]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        rc = L.matvec_bf16_batch(arrays[i % replicas], len(jobs), sp)
+        if rc != 0:
+            raise gq.SmoeError("matvec_bf16_batch", rc)
+
+    def step_separate(i):
+        for w, y, (r, c, _, _) in zip(reps[i % replicas], ys, jobs):
+            rc = L.matvec_bf16(w.data_ptr(), r, c, xd.data_ptr(), y.data_ptr(), None, 0, sp)
+            if rc != 0:
+                raise gq.SmoeError("matvec_bf16", rc)
+
+    us_step, per_call, wall_us = time_steps(step, args.steps, args.warmup, stream)
+    us_sep, per_sep, _ = time_steps(step_separate, args.steps, args.warmup, stream)
+    gbs = nbytes / (us_step * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        n, dt, cores = cpu_oracle(lambda: [oracle.matvec_bf16(W, x) for W in Ws], args.cpu_budget, 1)
+        cpu = {"value": round(n * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"{n} whole q/k/v batches (f64 oracle, {dt:.1f} s)"}
+    shapes = "+".join(f"{r}x{c}" for r, c, _, _ in jobs)
+    return {
+        "metric": f"effective HBM GB/s of one batched bf16 matvec launch ({shapes}, shared x)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(us_step / 1e3, 6),
+        "us_per_call": round(us_step, 3),
+        "us_per_call_separate_launches": round(us_sep, 3),
+        "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "wall_us_per_step": round(wall_us, 3),
+        "dtype": "bf16 x f32 -> f32",
+        "config": {"workload": f"bf16_batch_qkv_{shapes}", "jobs": [list(j[:3]) for j in jobs],
+                   "algorithmic_bytes_per_step": nbytes, "replicas_rotated": replicas,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_matvec_bf16_batch (one launch per call)",
+            "achieved": round(nbytes / (per_call * 1e-6) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (per_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic("bf16_batch_qkv", "bf16"),
+            "per_call_us_events": round(per_call, 3),
+            "per_call_us_events_separate_launches": round(per_sep, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+
+
 def copy_calibration(args):
     """A plain device-to-device copy of 256 MiB (torch's copy kernel): the
     counter runs divide FETCH_SIZE / WRITE_SIZE of a kernel by what the same
@@ -345,7 +418,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "prefill", "bf16", "copy"])
+    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "prefill", "bf16", "bf16_batch", "copy"])
     ap.add_argument("--tokens", type=int, default=16, help="prefill: tokens per call")
     ap.add_argument("--shape", default="q_proj", help="bf16: q_proj, o_proj, kv_proj or lm_head")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -369,6 +442,8 @@ def main():
         line = prefill_bench(args)
     elif args.workload == "copy":
         line = copy_calibration(args)
+    elif args.workload == "bf16_batch":
+        line = bf16_batch_bench(args)
     else:
         line = bf16_bench(args)
     head = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,

@@ -19,7 +19,8 @@ SMOE_OK = 0
 SMOE_MAX_EXPERTS = 16
 
 EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
-           "matvec_bf16_workspace", "matvec_bf16", "smoe_status_str")
+           "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_status_str")
+SMOE_MAX_BF16_JOBS = 16
 
 
 class SmoeError(RuntimeError):
@@ -34,6 +35,11 @@ class QMat(ctypes.Structure):
 
 class Expert(ctypes.Structure):
     _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class Bf16Job(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("rows", ctypes.c_int), ("cols", ctypes.c_int)]
 
 
 _lib = None
@@ -56,6 +62,7 @@ def lib():
         L.matvec_bf16_workspace.argtypes = [i, i]
         L.matvec_bf16_workspace.restype = sz
         L.matvec_bf16.argtypes = [vp, i, i, vp, vp, vp, sz, vp]
+        L.matvec_bf16_batch.argtypes = [vp, i, vp]
         L.smoe_status_str.argtypes = [i]
         L.smoe_status_str.restype = ctypes.c_char_p
         for name in ("smoe_gate_up", "smoe_down", "smoe_expert_ffn", "matvec_bf16"):
@@ -179,3 +186,23 @@ def matvec_bf16(W, x, y, workspace=None, stream=None):
     _check("matvec_bf16", lib().matvec_bf16(
         W.data_ptr(), rows, cols, _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"),
         pw, nw, _stream(stream)))
+
+
+def bf16_job_array(jobs):
+    """ctypes array of smoe_bf16_job from (W, x, y) torch tensors (W bf16 or
+    int16 bit patterns [rows, cols], x f32 [cols], y f32 [rows])."""
+    import torch
+    arr = (Bf16Job * len(jobs))()
+    for j, (W, x, y) in enumerate(jobs):
+        if W.dtype not in (torch.bfloat16, torch.int16):
+            raise TypeError("W must be torch.bfloat16 (or int16 bit patterns)")
+        rows, cols = W.shape
+        arr[j] = Bf16Job(_dev(W, W.dtype, "W"), _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"),
+                         rows, cols)
+    return arr
+
+
+def matvec_bf16_batch(jobs, stream=None):
+    """y_j = W_j x_j for a list of (W, x, y) tensor triples, in one launch."""
+    arr = bf16_job_array(jobs)
+    _check("matvec_bf16_batch", lib().matvec_bf16_batch(arr, len(jobs), _stream(stream)))

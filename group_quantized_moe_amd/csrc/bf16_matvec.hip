@@ -7,6 +7,11 @@
 // contiguous slices, LPR lanes share a row inside a wave, every lane keeps its
 // x slice in registers and streams ITER row steps of 16-byte loads issued up
 // front; DPP reduction inside the wave, LDS across waves.
+//
+// The batched form ("Batched Scout Matvec": several independent matvecs of
+// one layer in one submission) runs N such matvecs in one launch: the blocks
+// are dealt to the jobs in order, each job getting ceil(rows / rows per block)
+// of them, all with the lane map of the widest job.
 #include "launch.h"
 
 namespace smoe {
@@ -25,8 +30,9 @@ __device__ __forceinline__ float bf16_chunk_dot(const uint4 q, const float *xv, 
     return a0 + a1;
 }
 
+// Rows row0 .. row0 + RS*ITER - 1 of y = W x (one block's share).
 template <int LPR, int NCH, int ITER>
-__global__ __launch_bounds__(512) void k_matvec_bf16(const Bf16Args a)
+__device__ __forceinline__ void matvec_rows(const Bf16Args &a, int row0)
 {
     constexpr int RS = 64 / LPR;
     constexpr int RB = RS * ITER;
@@ -36,7 +42,6 @@ __global__ __launch_bounds__(512) void k_matvec_bf16(const Bf16Args a)
     const int lr = lane % LPR, slot = lane / LPR;
     const int cpr = a.cols / 8;
     const int sl = (cpr + nw - 1) / nw;
-    const int row0 = blockIdx.x * RB;
     const uint8_t *W = reinterpret_cast<const uint8_t *>(a.W);
     const size_t row_bytes = (size_t)a.cols * 2;
 
@@ -96,11 +101,40 @@ __global__ __launch_bounds__(512) void k_matvec_bf16(const Bf16Args a)
 }
 
 template <int LPR, int NCH, int ITER>
+__global__ __launch_bounds__(512) void k_matvec_bf16(const Bf16Args a)
+{
+    matvec_rows<LPR, NCH, ITER>(a, blockIdx.x * (64 / LPR) * ITER);
+}
+
+// Block b serves the job j with blk_start[j] <= b < blk_start[j + 1].
+template <int LPR, int NCH, int ITER>
+__global__ __launch_bounds__(512) void k_matvec_bf16_batch(const Bf16BatchArgs a)
+{
+    const int b = blockIdx.x;
+    int j = 0;
+    while (j + 1 < a.n && b >= a.blk_start[j + 1]) ++j;
+    const Bf16Job &jb = a.job[j];
+    const Bf16Args one{jb.W, jb.x, jb.y, jb.rows, jb.cols};
+    matvec_rows<LPR, NCH, ITER>(one, (b - a.blk_start[j]) * (64 / LPR) * ITER);
+}
+
+template <int LPR, int NCH, int ITER>
 hipError_t run_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream_t st)
 {
     constexpr int RB = (64 / LPR) * ITER;
     const dim3 grid((a.rows + RB - 1) / RB), block(64 * cfg.nw);
     hipLaunchKernelGGL((k_matvec_bf16<LPR, NCH, ITER>), grid, block, sizeof(float) * RB * cfg.nw, st, a);
+    return hipGetLastError();
+}
+
+template <int LPR, int NCH, int ITER>
+hipError_t run_bf16_batch(const MapConfig &cfg, Bf16BatchArgs a, hipStream_t st)
+{
+    constexpr int RB = (64 / LPR) * ITER;
+    a.blk_start[0] = 0;
+    for (int j = 0; j < a.n; ++j) a.blk_start[j + 1] = a.blk_start[j] + (a.job[j].rows + RB - 1) / RB;
+    const dim3 grid((unsigned)a.blk_start[a.n]), block(64 * cfg.nw);
+    hipLaunchKernelGGL((k_matvec_bf16_batch<LPR, NCH, ITER>), grid, block, sizeof(float) * RB * cfg.nw, st, a);
     return hipGetLastError();
 }
 
@@ -147,6 +181,15 @@ hipError_t launch_matvec_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream
 {
 #define SMOE_RUN(L, N, I) \
     if (cfg.lpr == L && cfg.nch == N && cfg.iter == I) return run_bf16<L, N, I>(cfg, a, st);
+    SMOE_BMAP_ALL(SMOE_RUN)
+#undef SMOE_RUN
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_matvec_bf16_batch(const MapConfig &cfg, const Bf16BatchArgs &a, hipStream_t st)
+{
+#define SMOE_RUN(L, N, I) \
+    if (cfg.lpr == L && cfg.nch == N && cfg.iter == I) return run_bf16_batch<L, N, I>(cfg, a, st);
     SMOE_BMAP_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;

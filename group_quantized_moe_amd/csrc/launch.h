@@ -126,4 +126,20 @@ struct Bf16Args {
 bool choose_bf16map(int chunks, int rows, MapConfig *cfg);
 hipError_t launch_matvec_bf16(const MapConfig &cfg, const Bf16Args &a, hipStream_t stream);
 
+// Batched bf16 matvec: up to kMaxBf16Jobs independent jobs in one launch;
+// blk_start (filled by the launcher) is the first block of each job.
+constexpr int kMaxBf16Jobs = 16;
+struct Bf16Job {
+    const uint16_t *W;
+    const float *x;
+    float *y;
+    int rows, cols;
+};
+struct Bf16BatchArgs {
+    Bf16Job job[kMaxBf16Jobs];
+    int blk_start[kMaxBf16Jobs + 1];
+    int n;
+};
+hipError_t launch_matvec_bf16_batch(const MapConfig &cfg, const Bf16BatchArgs &a, hipStream_t stream);
+
 }  // namespace smoe

@@ -3,12 +3,16 @@
 // argument returns an error with nothing enqueued (and needs no GPU).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
 
 #include "../../include/smoe.h"
 #include "launch.h"
+
+static_assert(SMOE_MAX_BF16_JOBS == smoe::kMaxBf16Jobs, "job limit of the header and the kernels");
 
 using smoe::DecodePlan;
 using smoe::MapConfig;
@@ -355,6 +359,41 @@ int matvec_bf16(const uint16_t *W, int rows, int cols, const float *x, float *y,
     if (rc) return rc;
     smoe::Bf16Args a{W, x, y, rows, cols};
     return launch_status(smoe::launch_matvec_bf16(cfg, a, (hipStream_t)stream));
+}
+
+int matvec_bf16_batch(const smoe_bf16_job *jobs, int n_jobs, void *stream)
+{
+    if (!jobs) return SMOE_ERR_NULL;
+    if (n_jobs < 1 || n_jobs > SMOE_MAX_BF16_JOBS) return SMOE_ERR_SHAPE;
+    int max_cols = 0;
+    long total_rows = 0;
+    for (int j = 0; j < n_jobs; ++j) {
+        const smoe_bf16_job &b = jobs[j];
+        if (!b.W || !b.x || !b.y) return SMOE_ERR_NULL;
+        if (b.rows <= 0 || b.cols <= 0 || b.cols % 8 || b.cols > SMOE_MAX_BF16_COLS) return SMOE_ERR_SHAPE;
+        if (!aligned(b.W, 16) || !aligned(b.x, 16) || !aligned(b.y, 4)) return SMOE_ERR_ALIGN;
+        max_cols = std::max(max_cols, b.cols);
+        total_rows += b.rows;
+    }
+    for (int j = 0; j < n_jobs; ++j) {
+        const size_t ny = (size_t)jobs[j].rows * 4;
+        for (int k = 0; k < n_jobs; ++k) {
+            const smoe_bf16_job &o = jobs[k];
+            if (overlap(jobs[j].y, ny, o.W, (size_t)o.rows * o.cols * 2) ||
+                overlap(jobs[j].y, ny, o.x, (size_t)o.cols * 4) ||
+                (k != j && overlap(jobs[j].y, ny, o.y, (size_t)o.rows * 4)))
+                return SMOE_ERR_ALIAS;
+        }
+    }
+    MapConfig cfg;
+    if (total_rows > INT_MAX || !smoe::choose_bf16map(max_cols / 8, (int)total_rows, &cfg)) return SMOE_ERR_SHAPE;
+    int rc = check_device(nullptr);
+    if (rc) return rc;
+    smoe::Bf16BatchArgs a{};
+    for (int j = 0; j < n_jobs; ++j)
+        a.job[j] = smoe::Bf16Job{jobs[j].W, jobs[j].x, jobs[j].y, jobs[j].rows, jobs[j].cols};
+    a.n = n_jobs;
+    return launch_status(smoe::launch_matvec_bf16_batch(cfg, a, (hipStream_t)stream));
 }
 
 }  // extern "C"

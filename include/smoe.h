@@ -15,6 +15,8 @@
  *                   one submission as in "Grouped Expert Dispatch").
  *  - matvec_bf16    y = W x with bf16 W and f32 x ("Coalesced Dense Matvec --
  *                   the Same Contract for bf16").
+ *  - matvec_bf16_batch  several independent bf16 matvecs in one launch
+ *                   ("Batched Scout Matvec").
  *
  * Weight format (the "Layout assumptions the kernels rely on" contract):
  *   A quantised matrix of rows x cols is a smoe_qmat:
@@ -75,6 +77,8 @@ enum {
 #define SMOE_MAX_QCOLS 8192
 /* Largest cols of a bf16 matrix. */
 #define SMOE_MAX_BF16_COLS 16384
+/* Jobs per matvec_bf16_batch call. */
+#define SMOE_MAX_BF16_JOBS 16
 /* Largest token count T of smoe_expert_ffn. */
 #define SMOE_MAX_TOKENS 65536
 
@@ -153,6 +157,28 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
 size_t matvec_bf16_workspace(int rows, int cols);
 int matvec_bf16(const uint16_t *W, int rows, int cols, const float *x, float *y,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Several independent bf16 matvecs in one launch ("Batched Scout Matvec":
+ * the matvecs of one layer, such as a projection pair, go out as one
+ * submission instead of one each):
+ *   y_j = W_j x_j   for j = 0 .. n_jobs-1
+ *   jobs   : host array of n_jobs descriptors (1..SMOE_MAX_BF16_JOBS), read
+ *            during the call; each job has the contract of matvec_bf16
+ *            (W_j bf16 [rows_j x cols_j], 16-byte aligned, cols_j % 8 == 0,
+ *            cols_j <= SMOE_MAX_BF16_COLS; x_j f32 [cols_j], 16-byte aligned;
+ *            y_j f32 [rows_j], 4-byte aligned).  Jobs may share W or x.
+ *   y_j must not overlap any job's W, x or (another job's) y.
+ * No workspace.  Each y_j is computed as matvec_bf16 would (within the same
+ * tolerance; the summation order may differ).
+ */
+typedef struct {
+    const uint16_t *W;
+    const float *x;
+    float *y;
+    int rows, cols;
+} smoe_bf16_job;
+int matvec_bf16_batch(const smoe_bf16_job *jobs, int n_jobs, void *stream);
 
 /* Message for a status code (static string). */
 const char *smoe_status_str(int status);

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
         "smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
-        "matvec_bf16_workspace", "matvec_bf16", "smoe_status_str"}
+        "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_status_str"}
 
 
 def test_library_exports_every_declared_symbol(gq):
@@ -86,6 +86,35 @@ def test_down_and_bf16_refusals(gq):
     assert L.matvec_bf16(A, 16, 16, A + 0x8000000, A + 16, None, 0, None) == -7
     assert L.matvec_bf16(A, 16, 16, A + 0x8000000, A + 0x9000000, None, 0, None) == -8
     assert L.matvec_bf16_workspace(512, 4096) == 0
+
+
+def test_bf16_batch_refusals(gq):
+    """Every out-of-contract batch is refused before the device is touched;
+    a valid one reaches the device check (-8 without a GPU)."""
+    L = gq.lib()
+    J = gq.Bf16Job
+
+    def call(*jobs, n=None):
+        arr = (J * max(1, len(jobs)))(*jobs)
+        return L.matvec_bf16_batch(arr, len(jobs) if n is None else n, None)
+
+    W0, W1 = A, A + 0x1000000
+    x0, y0, y1 = A + 0x8000000, A + 0x9000000, A + 0xA000000
+    ok0, ok1 = J(W0, x0, y0, 512, 4096), J(W1, x0, y1, 64, 4096)
+    assert L.matvec_bf16_batch(None, 1, None) == -1
+    assert call(ok0, n=0) == -4
+    assert call(*([ok0] * 17)) == -4                      # above SMOE_MAX_BF16_JOBS
+    assert call(ok0, J(W1, None, y1, 64, 4096)) == -1
+    assert call(ok0, J(W1, x0, y1, 64, 4092)) == -4        # cols % 8
+    assert call(ok0, J(W1, x0, y1, 0, 4096)) == -4
+    assert call(ok0, J(W1, x0, y1, 64, 16392)) == -4       # above SMOE_MAX_BF16_COLS
+    assert call(ok0, J(W1 + 8, x0, y1, 64, 4096)) == -5
+    assert call(ok0, J(W1, x0 + 4, y1, 64, 4096)) == -5
+    assert call(ok0, J(W1, x0, y0 + 64, 64, 4096)) == -7   # y overlaps another job's y
+    assert call(ok0, J(W1, x0, W0 + 4096, 64, 4096)) == -7  # y overlaps another job's W
+    assert call(ok0, J(W1, x0, x0 + 256, 64, 4096)) == -7   # y overlaps a shared x
+    assert call(ok0, ok1) == -8                           # valid (shared x): reaches the device check
+    assert call(*([J(W0, x0, A + 0xB000000 + 0x10000 * k, 512, 4096) for k in range(16)])) == -8
 
 
 def test_expert_ffn_refusals(gq):

@@ -186,6 +186,13 @@ BF16_SHAPES = [  # (rows, cols, role, seed)
     (151936, 4096, "lm_head", 33),
 ]
 BATCH_TOKENS = {16: 40, 64: 41, 256: 42}   # T -> seed of X; weights are Q4_GROUP8's
+# One launch of several bf16 matvecs: a token's attention input projections
+# (q, k, v) over one shared x.  (rows, cols, role, seed of W); x uses the first seed.
+BF16_BATCH = [
+    (8192, 4096, "q_proj", 34),
+    (512, 4096, "k_proj", 35),
+    (512, 4096, "v_proj", 36),
+]
 
 
 def make_group(spec: dict) -> ExpertGroup:
@@ -205,6 +212,15 @@ def make_bf16(rows: int, cols: int, seed: int, sigma: float = 0.02):
     W = bf16_normal(seed, (_TAG_BF16_W,), rows, cols, sigma)
     x = normal_f32(seed, (_TAG_BF16_X,), cols)
     return W, x
+
+
+def make_bf16_batch(jobs=BF16_BATCH):
+    """([W bf16 bits uint16 [rows, cols] per job], x f32 [cols]) with one x
+    shared by all jobs (all jobs must have the same cols)."""
+    cols = jobs[0][1]
+    assert all(j[1] == cols for j in jobs)
+    Ws = [bf16_normal(seed, (_TAG_BF16_W,), rows, cols, 0.02) for rows, _, _, seed in jobs]
+    return Ws, normal_f32(jobs[0][3], (_TAG_BF16_X,), cols)
 
 
 def make_batch_inputs(T: int, seed: int | None = None, d_model: int = 4096):
