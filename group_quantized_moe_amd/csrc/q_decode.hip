@@ -26,18 +26,21 @@
 //    contribution is s * (float(I) * 2^-k / Z + beta), where beta restores the
 //    code offset from the exact digit sum of the chunk.
 //
-//  * Whole rows per wave.  lpr lanes (8..64, chosen per shape) share a row
-//    and lane lr owns chunks lr, lr + lpr, ... of it, so a wave covers 64/lpr
-//    rows per step; the row sum is a DPP / lane-shuffle reduction.  A lane
+//  * Whole rows per wave.  LPR lanes (16, 32 or 64, a template parameter)
+//    share a row and lane lr owns chunks lr, lr + LPR, ... of it, so a wave
+//    covers 64/LPR rows per step and the row sum is a DPP reduction.  A lane
 //    always reads the same column chunks, so it copies those chunks' digit
 //    planes from LDS into registers once and the row loop touches no LDS and
 //    has no barrier.
 //
-//  * Persistent, pipelined waves.  Each block first builds the digit planes of
-//    the vector in LDS (one barrier); its waves then walk their row steps in a
-//    grid stride, two steps of 16-byte code loads and scale loads always in
-//    flight ahead of the step being reduced.  Loads are issued from clamped,
-//    always valid addresses so that no lane's load is conditional.
+//  * Persistent waves, one step of loads in flight each.  Each block first
+//    builds the digit planes of the vector in LDS (one barrier); each wave then
+//    walks a contiguous range of row steps with the next step's 16-byte code
+//    loads and scale loads in flight while it reduces the current one (more
+//    steps in flight per wave measured slower: the waves of a CU already keep
+//    the memory system busy).  Loads come from a uniform base plus a 32-bit lane
+//    offset and are issued on every path (past the wave's last step the offsets
+//    are masked to zero), so that the compiler's load waits are exact.
 //
 //  * Deterministic expert combine.  down blocks are bound to one expert each.
 //    A wave keeps its router-weighted rows in LDS and, at its end, adds each
