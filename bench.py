@@ -8,6 +8,8 @@ bytes / time), microseconds per group and fraction of the 8 TB/s HBM peak.
 
 Other rows of the path, one JSON line each with --workload:
   decode_q2           the same group with 2-bit codes
+  decode_q4_s16, decode_q2_s16
+                      the groups with 2-byte (binary16) scales
   prefill             --tokens T (16, 64 or 256): every token through all 8
                       experts on the matrix cores (bound by HBM at T = 16, by
                       the f16 MFMA rate above)
@@ -168,8 +170,10 @@ def decode_bench(args, spec, profile):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
 
+    fmt = g.bits | (gq.SMOE_SCALE_F16 if g.scale_f16 else 0)
+
     def step(i):
-        rc = L.smoe_expert_ffn(arrays[i % replicas], E, rd.data_ptr(), g.bits, g.group, g.d_model, g.d_ff, 1,
+        rc = L.smoe_expert_ffn(arrays[i % replicas], E, rd.data_ptr(), fmt, g.group, g.d_model, g.d_ff, 1,
                                xd.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), sp)
         if rc != 0:
             raise gq.SmoeError("smoe_expert_ffn", rc)
@@ -185,7 +189,8 @@ def decode_bench(args, spec, profile):
                "sample": f"{n} whole {E}-expert Q{g.bits} groups (f64 oracle, {dt:.1f} s)",
                "us_per_group": round(dt / n * 1e6, 1)}
     return {
-        "metric": f"effective HBM GB/s per Q{g.bits} {E}-expert FFN group (decode, T=1)",
+        "metric": f"effective HBM GB/s per Q{g.bits} {E}-expert FFN group (decode, T=1"
+                  + (", f16 scales)" if g.scale_f16 else ")"),
         "value": round(gbs, 1),
         "unit": "GB/s",
         "ms_per_step": round(us_step / 1e3, 6),
@@ -194,7 +199,7 @@ def decode_bench(args, spec, profile):
         "wall_us_per_step": round(wall_us, 3),
         "dtype": f"u{g.bits} codes x i4 digit planes -> i32, f32 epilogue",
         "config": {"workload": spec["name"], "d_model": g.d_model, "d_ff": g.d_ff, "n_experts": E,
-                   "bits": g.bits, "group": g.group, "scales": "f32", "tokens": 1,
+                   "bits": g.bits, "group": g.group, "scales": "f16" if g.scale_f16 else "f32", "tokens": 1,
                    "algorithmic_bytes_per_step": nbytes, "replicas_rotated": replicas,
                    "parallelism": "single GPU"},
         "roofline": {
@@ -425,7 +430,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "prefill", "bf16", "bf16_batch", "copy"])
+    ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "decode_q4_s16", "decode_q2_s16", "prefill", "bf16",
+                             "bf16_batch", "copy"])
     ap.add_argument("--tokens", type=int, default=16, help="prefill: tokens per call")
     ap.add_argument("--shape", default="q_proj", help="bf16: q_proj, o_proj, kv_proj or lm_head")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -445,6 +451,10 @@ def main():
         line = decode_bench(args, workloads.Q4_GROUP8, "decode_q4")
     elif args.workload == "decode_q2":
         line = decode_bench(args, workloads.Q2_GROUP8, "decode_q2")
+    elif args.workload == "decode_q4_s16":
+        line = decode_bench(args, workloads.Q4_GROUP8_S16, "decode_q4_s16")
+    elif args.workload == "decode_q2_s16":
+        line = decode_bench(args, workloads.Q2_GROUP8_S16, "decode_q2_s16")
     elif args.workload == "prefill":
         line = prefill_bench(args)
     elif args.workload == "copy":

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 
 SMOE_OK = 0
 SMOE_MAX_EXPERTS = 16
+SMOE_SCALE_F16 = 0x100   # ORed into `bits`: 2-byte IEEE binary16 scales instead of f32
 
 EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
            "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_status_str")
@@ -98,21 +99,23 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _qmat(codes, scales, name):
+def _qmat(codes, scales, name, bits):
+    """Scales must be float16 when `bits` carries SMOE_SCALE_F16, else float32."""
     import torch
-    return QMat(_dev(codes, torch.uint8, name + ".codes"), _dev(scales, torch.float32, name + ".scales"))
+    sdt = torch.float16 if bits & SMOE_SCALE_F16 else torch.float32
+    return QMat(_dev(codes, torch.uint8, name + ".codes"), _dev(scales, sdt, name + ".scales"))
 
 
 def _dims(codes, bits):
     """(rows, cols) of a packed matrix [rows, cols*bits/8]."""
-    return codes.shape[0], codes.shape[1] * 8 // bits
+    return codes.shape[0], codes.shape[1] * 8 // (bits & ~SMOE_SCALE_F16)
 
 
 def smoe_gate_up(gate_codes, gate_scales, up_codes, up_scales, bits, group, x, hidden, stream=None):
     """hidden[d_ff] = SiLU(G x) * (U x); G, U packed [d_ff, d_model*bits/8]."""
     import torch
     d_ff, d_model = _dims(gate_codes, bits)
-    G, U = _qmat(gate_codes, gate_scales, "gate"), _qmat(up_codes, up_scales, "up")
+    G, U = _qmat(gate_codes, gate_scales, "gate", bits), _qmat(up_codes, up_scales, "up", bits)
     _check("smoe_gate_up", lib().smoe_gate_up(
         ctypes.byref(G), ctypes.byref(U), bits, group, d_ff, d_model,
         _dev(x, torch.float32, "x"), _dev(hidden, torch.float32, "hidden"), _stream(stream)))
@@ -122,7 +125,7 @@ def smoe_down(down_codes, down_scales, bits, group, hidden, out, stream=None):
     """out[d_model] = D hidden; D packed [d_model, d_ff*bits/8]."""
     import torch
     d_model, d_ff = _dims(down_codes, bits)
-    D = _qmat(down_codes, down_scales, "down")
+    D = _qmat(down_codes, down_scales, "down", bits)
     _check("smoe_down", lib().smoe_down(
         ctypes.byref(D), bits, group, d_model, d_ff, _dev(hidden, torch.float32, "hidden"),
         _dev(out, torch.float32, "out"), _stream(stream)))
@@ -132,9 +135,10 @@ def smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T=1) -> int:
     return int(lib().smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T))
 
 
-def _expert_array(experts):
+def _expert_array(experts, bits=4):
     """experts: sequence of objects with .gate/.up/.down, each with .codes/.scales
-    (torch GPU tensors), or 6-tuples (gc, gs, uc, us, dc, ds)."""
+    (torch GPU tensors), or 6-tuples (gc, gs, uc, us, dc, ds); scales float16
+    when `bits` carries SMOE_SCALE_F16, else float32."""
     arr = (Expert * len(experts))()
     for k, e in enumerate(experts):
         if isinstance(e, (tuple, list)):
@@ -142,8 +146,8 @@ def _expert_array(experts):
         else:
             gc, gs, uc, us, dc, ds = (e.gate.codes, e.gate.scales, e.up.codes, e.up.scales,
                                       e.down.codes, e.down.scales)
-        arr[k] = Expert(_qmat(gc, gs, f"experts[{k}].gate"), _qmat(uc, us, f"experts[{k}].up"),
-                        _qmat(dc, ds, f"experts[{k}].down"))
+        arr[k] = Expert(_qmat(gc, gs, f"experts[{k}].gate", bits), _qmat(uc, us, f"experts[{k}].up", bits),
+                        _qmat(dc, ds, f"experts[{k}].down", bits))
     return arr
 
 
@@ -160,7 +164,7 @@ def smoe_expert_ffn(experts, bits, group, x, out, route_w=None, workspace=None, 
     import torch
     d_ff, d_model = _dims(_first_gate_codes(experts), bits)
     T = x.numel() // d_model
-    arr = _expert_array(experts)
+    arr = _expert_array(experts, bits)
     pr = None if route_w is None else _dev(route_w, torch.float32, "route_w")
     if workspace is None:
         raise ValueError("smoe_expert_ffn needs a caller-owned workspace tensor")

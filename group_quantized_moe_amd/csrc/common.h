@@ -10,7 +10,7 @@ constexpr int kMaxExperts = 16;
 
 struct QPtr {
     const uint8_t *codes;
-    const float *scales;
+    const void *scales;   // f32, or f16 when the launch says scale_bytes == 2
 };
 
 // Zero point of a b-bit affine code: 7.5 at 4 bits, 1.5 at 2 bits (Metal Compute

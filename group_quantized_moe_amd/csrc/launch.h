@@ -36,6 +36,7 @@ struct DecodeArgs {
     float *out;              // [d_model]
     unsigned long long *row_acc;  // [d_model] exact expert sums, zero on entry and exit (n_experts > 1)
     int d_model, d_ff, group, n_experts;
+    int scale_bytes;         // 4: f32 scales, 2: IEEE binary16 scales
     int dn_rows_per_wave;    // set by the down launcher
 };
 
@@ -66,6 +67,7 @@ struct TbArgs {
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
     float *part_gu, *part_dn; // tiled kernels: per-tile partial sums of the K splits
     int T, t_pad, d_model, d_ff, group, n_experts;
+    int scale_bytes;         // 4: f32 scales, 2: IEEE binary16 scales
     int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
     int ks_dn, rw_dn;        // down: rw_dn row slices x ks_dn (expert, group) slices, as waves of one
                              // block; for the tiled kernels ks_gu / ks_dn are splits over blocks

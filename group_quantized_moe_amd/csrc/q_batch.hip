@@ -170,6 +170,20 @@ __device__ __forceinline__ unsigned buf_load4(BufRes r, unsigned voff, unsigned 
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
+// Scale g of a row whose f32 scales would start `row_off4` bytes into the
+// buffer: f32 (SB = 4), or IEEE binary16 widened exactly to f32 (SB = 2, at half
+// the offsets).
+template <int SB>
+__device__ __forceinline__ float buf_load_scale(BufRes r, unsigned row_off4, unsigned g)
+{
+    if constexpr (SB == 4) {
+        return __uint_as_float(buf_load4(r, row_off4, g * 4u));
+    } else {
+        const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(row_off4 >> 1), (int)(g * 2u), 0);
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+}
+
 template <int BITS, int KB>
 __device__ __forceinline__ void buf_load_codes(BufRes r, unsigned voff, unsigned soff, CodeWords<BITS, KB> &c)
 {
@@ -270,7 +284,7 @@ __device__ __forceinline__ f32x4 group_mfma(const TbStage<BITS, KB, NTT, NB> &st
 // [ks*G/KS, (ks+1)*G/KS) of d_model; partial sums over ks are added in LDS in
 // a fixed order.  The hidden rows are normalised per (token, H group), split
 // into hi/lo halves and stored with the factor r[t][e] * 2^e for down.
-template <int BITS, int KB, int NTT, int RT>
+template <int BITS, int KB, int NTT, int RT, int SB>
 __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
 {
     extern __shared__ float lds[];
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
     // Fixed 32-bit lane offsets into buffer resources; a step moves only the
     // uniform offsets (a matrix has at most 8192 x 8192 entries; X at most
     // 65536 x 8192 halves).
-    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * 4;
+    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * SB;
     const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
     const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
     const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
@@ -325,7 +339,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
             for (int rt = 0; rt < RT; ++rt) {
                 buf_load_codes<BITS, KB>(cr[m], coff[rt], (unsigned)g * (unsigned)(group * BITS / 8),
                                          st.cw[m * RT + rt]);
-                st.s[m * RT + rt] = __uint_as_float(buf_load4(sr[m], soff[rt], (unsigned)g * 4u));
+                st.s[m * RT + rt] = buf_load_scale<SB>(sr[m], soff[rt], (unsigned)g);
             }
     };
 
@@ -459,7 +473,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
 // experts.  Wave (rw, ks): rows rw*16*RT .. +16*RT of the block, (expert,
 // group) pairs [ks*P/KS, (ks+1)*P/KS) of P = E * d_ff/group in ascending
 // order; partials over ks are added in LDS in a fixed order.
-template <int BITS, int KB, int NTT, int RT>
+template <int BITS, int KB, int NTT, int RT, int SB>
 __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 {
     extern __shared__ float lds[];
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
     const int t0 = tb * 16 * NTT;
     // Fixed 32-bit lane offsets; a step moves only uniform offsets (one
     // expert's hidden half has at most 65536 x 8192 entries).
-    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * 4;
+    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * SB;
     const size_t hbytes = (size_t)T * d_ff * 2;
     const BufRes fres = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
     unsigned coff[RT], soff[RT], hoff[NTT];
@@ -515,7 +529,7 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             buf_load_codes<BITS, KB>(dc, coff[rt], (unsigned)g * (unsigned)(group * BITS / 8), st.v.cw[rt]);
-            st.v.s[rt] = __uint_as_float(buf_load4(ds, soff[rt], (unsigned)g * 4u));
+            st.v.s[rt] = buf_load_scale<SB>(ds, soff[rt], (unsigned)g);
         }
     };
 
@@ -788,7 +802,7 @@ __device__ __forceinline__ void gu_epilogue(const TbArgs &a, const f32x4 (&tot)[
 
 // gate_up, tiled: block (token tile, row block, expert, split).  A step is MG
 // quantisation groups of d_model.
-template <int BITS, int KB, int NTT, int MG, int PF>
+template <int BITS, int KB, int NTT, int MG, int PF, int SB>
 __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 {
     using Sh = TileShape<KB, NTT, MG>;
@@ -822,7 +836,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     const unsigned row = (unsigned)min(wrow0 + n, d_ff - 1);
     const unsigned coff = row * (unsigned)(d_model * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
     const unsigned soff = row * (unsigned)G * 4u;
-    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * 4;
+    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * SB;
     const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
     const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
     const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
@@ -848,7 +862,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 #pragma unroll
             for (int gi = 0; gi < MG; ++gi) {
                 buf_load_codes<BITS, KB>(cr[m], coff, (g + gi) * (unsigned)(group * BITS / 8), st.cw[m][gi]);
-                st.sc[m][gi] = __uint_as_float(buf_load4(sr[m], soff, (g + gi) * 4u));
+                st.sc[m][gi] = buf_load_scale<SB>(sr[m], soff, g + gi);
             }
     };
 
@@ -950,7 +964,7 @@ __device__ __forceinline__ void dn_store(const TbArgs &a, const f32x4 (&tot)[NTT
 // down, tiled: block (token tile, row block, split) sums the (expert, group)
 // pairs of its split, all experts together (the router weights are in the
 // hidden factors).
-template <int BITS, int KB, int NTT, int PF>
+template <int BITS, int KB, int NTT, int PF, int SB>
 __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
 {
     constexpr int TT = 16 * NTT;
@@ -978,7 +992,7 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
     const unsigned coff = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
     const unsigned soff = row * (unsigned)Gd * 4u;
-    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * 4;
+    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * SB;
     const size_t hbytes = (size_t)T * d_ff * 2;   // one expert's hidden half
     const BufRes fr_res = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
     TileMap<KB, NTT> tm;
@@ -1008,7 +1022,7 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
         st.fr = __uint_as_float(buf_load4(fr_res, flane * 4u, (unsigned)(((size_t)e * Gd + g) * a.t_pad + t0) * 4u));
         buf_load_codes<BITS, KB>(buf_res(a.down[e].codes, cbytes), coff, (unsigned)g * (unsigned)(group * BITS / 8),
                                  st.cw);
-        st.sc = __uint_as_float(buf_load4(buf_res(a.down[e].scales, sbytes), soff, (unsigned)g * 4u));
+        st.sc = buf_load_scale<SB>(buf_res(a.down[e].scales, sbytes), soff, (unsigned)g);
     };
     auto store_step = [&](const DnStage &st, int buf) {
         tile_store<KB, NTT>(st.tr, tm, smem + (size_t)buf * tb_bytes);
@@ -1073,13 +1087,13 @@ __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
     dn_store<NTT>(a, tot, tile_id / NTB, tile_id % NTB);
 }
 
-template <int BITS, int KB, int NTT, int MG>
+template <int BITS, int KB, int NTT, int MG, int SB>
 hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
     hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, kTilePrefetch>), dim3(pl.gu_blocks),
+    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, kTilePrefetch, SB>), dim3(pl.gu_blocks),
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_gu > 1) {
@@ -1087,7 +1101,7 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
                            (size_t)kTileWaves * NTT * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, kTilePrefetch>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
+    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, kTilePrefetch, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
                        pl.dn_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_dn > 1) {
@@ -1097,38 +1111,58 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
     return err;
 }
 
-template <int BITS, int KB, int NTT, int RTG, int RTD>
+template <int BITS, int KB, int NTT, int RTG, int RTD, int SB>
 hipError_t launch_tb_kernels(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
     hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up<BITS, KB, NTT, RTG>), dim3(pl.gu_blocks), dim3(64 * pl.gu_waves), pl.gu_lds,
+    hipLaunchKernelGGL((k_tb_gate_up<BITS, KB, NTT, RTG, SB>), dim3(pl.gu_blocks), dim3(64 * pl.gu_waves), pl.gu_lds,
                        st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_down<BITS, KB, NTT, RTD>), dim3(pl.dn_blocks), dim3(64 * pl.dn_waves), pl.dn_lds, st,
+    hipLaunchKernelGGL((k_tb_down<BITS, KB, NTT, RTD, SB>), dim3(pl.dn_blocks), dim3(64 * pl.dn_waves), pl.dn_lds, st,
                        a);
     return hipGetLastError();
 }
 
-template <int BITS, int KB>
+template <int BITS, int KB, int SB>
 hipError_t launch_tb_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
     if constexpr (KB <= 2) {
         if (pl.tiled) {
             if (pl.ntt == 1) {
-                if (pl.mg == 2) return launch_tb_tiled<BITS, KB, 1, 2>(pl, a, st);
-                return launch_tb_tiled<BITS, KB, 1, 1>(pl, a, st);
+                if (pl.mg == 2) return launch_tb_tiled<BITS, KB, 1, 2, SB>(pl, a, st);
+                return launch_tb_tiled<BITS, KB, 1, 1, SB>(pl, a, st);
             }
-            if (pl.ntt == 2) return launch_tb_tiled<BITS, KB, 2, 1>(pl, a, st);
-            return launch_tb_tiled<BITS, KB, 4, 1>(pl, a, st);
+            if (pl.ntt == 2) return launch_tb_tiled<BITS, KB, 2, 1, SB>(pl, a, st);
+            return launch_tb_tiled<BITS, KB, 4, 1, SB>(pl, a, st);
         }
     }
     // Direct kernels (groups of 96 and 128 columns).  gate_up row tiles: 2
     // (more would not fit the registers); down: 4 row tiles for 16-token
     // tiles, 2 for 32.
-    if (pl.ntt == 1) return launch_tb_kernels<BITS, KB, 1, 2, 4>(pl, a, st);
-    return launch_tb_kernels<BITS, KB, 2, 2, 2>(pl, a, st);
+    if (pl.ntt == 1) return launch_tb_kernels<BITS, KB, 1, 2, 4, SB>(pl, a, st);
+    return launch_tb_kernels<BITS, KB, 2, 2, 2, SB>(pl, a, st);
+}
+
+template <int SB>
+hipError_t launch_tb_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    const int kb = a.group / 32;
+    if (bits == 4) {
+        switch (kb) {
+        case 1: return launch_tb_kb<4, 1, SB>(pl, a, st);
+        case 2: return launch_tb_kb<4, 2, SB>(pl, a, st);
+        case 3: return launch_tb_kb<4, 3, SB>(pl, a, st);
+        case 4: return launch_tb_kb<4, 4, SB>(pl, a, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (kb) {
+    case 2: return launch_tb_kb<2, 2, SB>(pl, a, st);
+    case 4: return launch_tb_kb<2, 4, SB>(pl, a, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -1229,21 +1263,7 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
 
 hipError_t launch_batch(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    const int kb = a.group / 32;
-    if (bits == 4) {
-        switch (kb) {
-        case 1: return launch_tb_kb<4, 1>(pl, a, st);
-        case 2: return launch_tb_kb<4, 2>(pl, a, st);
-        case 3: return launch_tb_kb<4, 3>(pl, a, st);
-        case 4: return launch_tb_kb<4, 4>(pl, a, st);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    switch (kb) {
-    case 2: return launch_tb_kb<2, 2>(pl, a, st);
-    case 4: return launch_tb_kb<2, 4>(pl, a, st);
-    default: return hipErrorInvalidValue;
-    }
+    return a.scale_bytes == 2 ? launch_tb_fmt<2>(bits, pl, a, st) : launch_tb_fmt<4>(bits, pl, a, st);
 }
 
 }  // namespace smoe

@@ -381,8 +381,10 @@ struct Stage {
 // bytes of the matrix (one cache line, nothing from HBM).  Both cases only
 // change the per-lane offsets, so every call issues the same loads and the
 // ring's waits stay exact.
-template <int NCH, int LPR, int M>
-__device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *const *codes, const float *const *scales,
+// Scales are f32 (SB = 4) or IEEE binary16 (SB = 2, widened exactly to f32;
+// byte offsets are half the f32 ones).
+template <int NCH, int LPR, int M, int SB>
+__device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *const *codes, const void *const *scales,
                                            const RowLanes<NCH, LPR> &ln, int row0, int rows, unsigned row_bytes,
                                            int gpr, bool dummy)
 {
@@ -394,8 +396,11 @@ __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *cons
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             t.q[k][m] = *reinterpret_cast<const uint4 *>(codes[m] + ((crow + ln.coff[k]) & keep));
-            t.s[k][m] = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(scales[m]) +
-                                                         ((srow + ln.soff[k]) & keep));
+            const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]);
+            if constexpr (SB == 4)
+                t.s[k][m] = *reinterpret_cast<const float *>(sb + ((srow + ln.soff[k]) & keep));
+            else
+                t.s[k][m] = (float)*reinterpret_cast<const _Float16 *>(sb + (((srow + ln.soff[k]) >> 1) & keep));
         }
     }
 }
@@ -426,7 +431,7 @@ struct Cursor {
 // contiguous range of the E * ceil(d_ff / rs) row steps (experts in order),
 // with DEPTH steps of code and scale loads in flight ahead of the step being
 // reduced; the first DEPTH steps are issued before the planes are built.
-template <int BITS, int NCH, int LPR, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH, int SB>
 __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -447,8 +452,8 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
 
     auto load = [&](Stage<NCH, 2> &t, const Cursor &c, bool dummy) {
         const uint8_t *codes[2] = {a.gate[c.m].codes, a.up[c.m].codes};
-        const float *scales[2] = {a.gate[c.m].scales, a.up[c.m].scales};
-        load_stage<NCH, LPR, 2>(t, codes, scales, ln, c.s * rs, a.d_ff, (unsigned)row_bytes, gpr, dummy);
+        const void *scales[2] = {a.gate[c.m].scales, a.up[c.m].scales};
+        load_stage<NCH, LPR, 2, SB>(t, codes, scales, ln, c.s * rs, a.d_ff, (unsigned)row_bytes, gpr, dummy);
     };
 
     // The vector's loads go first, then the first steps' code loads, then the
@@ -538,7 +543,7 @@ __device__ __forceinline__ float acc_value(unsigned long long sum, int n)
     return (float)((double)fixed * (1.0 / 4294967296.0));
 }
 
-template <int BITS, int NCH, int LPR, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH, int SB>
 __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -559,13 +564,13 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     const int iw = (blockIdx.x / E) * nw + wave;   // this wave among its expert's waves
     const int sb = (int)((long)iw * nsteps / We), se = (int)((long)(iw + 1) * nsteps / We);
     const uint8_t *dcodes[1] = {a.down[e].codes};
-    const float *dscales[1] = {a.down[e].scales};
+    const void *dscales[1] = {a.down[e].scales};
     const float rw = a.route_w ? a.route_w[e] : 1.0f;
     // This wave's router-weighted rows, kept until the deferred combine.
     float *mine = reinterpret_cast<float *>(smem + ((plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15))) +
                   wave * a.dn_rows_per_wave;
     auto load = [&](Stage<NCH, 1> &t, int step) {
-        load_stage<NCH, LPR, 1>(t, dcodes, dscales, ln, step * rs, a.d_model, (unsigned)row_bytes, gpr,
+        load_stage<NCH, LPR, 1, SB>(t, dcodes, dscales, ln, step * rs, a.d_model, (unsigned)row_bytes, gpr,
                                      step >= se);
     };
 
@@ -644,25 +649,25 @@ int blocks_per_cu(const void *fn, int block, size_t lds)
     return n;
 }
 
-template <int BITS, int NCH, int LPR, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH, int SB>
 hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
     const size_t lds = plane_lds_bytes<BITS>(a.d_model);
-    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, LPR, DEPTH>);
+    const void *fn = reinterpret_cast<const void *>(&k_gate_up<BITS, NCH, LPR, DEPTH, SB>);
     const long cap = (long)cus * blocks_per_cu(fn, block, lds);
     if (cap < 1) return hipErrorInvalidConfiguration;
     const long steps = (long)a.n_experts * ((a.d_ff + 64 / p.lpr_g - 1) / (64 / p.lpr_g));
     const long grid = std::max(1L, std::min(cap, (steps + p.nw - 1) / p.nw));
-    hipLaunchKernelGGL((k_gate_up<BITS, NCH, LPR, DEPTH>), dim3((unsigned)grid), dim3(block), lds, st, a);
+    hipLaunchKernelGGL((k_gate_up<BITS, NCH, LPR, DEPTH, SB>), dim3((unsigned)grid), dim3(block), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BITS, int NCH, int LPR, int DEPTH>
+template <int BITS, int NCH, int LPR, int DEPTH, int SB>
 hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, DEPTH>);
+    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, DEPTH, SB>);
     const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
     // Resident blocks: the occupancy query's answer, but at most two blocks of
     // this size per CU (more were measured not to be co-resident, which puts a
@@ -675,7 +680,7 @@ hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
     const long waves = per_expert * p.nw;
     a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
     const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
-    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, DEPTH>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
+    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, DEPTH, SB>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
                        a);
     return hipGetLastError();
 }
@@ -754,8 +759,10 @@ constexpr int kDownDepth = 1;
 
 hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, N, L)                                                      \
-    if (bits == B && p.nch_g == N && p.lpr_g == L) return run_gate_up<B, N, L, kGateUpDepth>(p, a, cus, st);
+#define SMOE_RUN(B, N, L)                                                                  \
+    if (bits == B && p.nch_g == N && p.lpr_g == L)                                         \
+        return a.scale_bytes == 2 ? run_gate_up<B, N, L, kGateUpDepth, 2>(p, a, cus, st)   \
+                                  : run_gate_up<B, N, L, kGateUpDepth, 4>(p, a, cus, st);
     SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
@@ -763,8 +770,10 @@ hipError_t launch_gate_up(int bits, const DecodePlan &p, const DecodeArgs &a, in
 
 hipError_t launch_down(int bits, const DecodePlan &p, const DecodeArgs &a, int cus, hipStream_t st)
 {
-#define SMOE_RUN(B, N, L)                                                      \
-    if (bits == B && p.nch_d == N && p.lpr_d == L) return run_down<B, N, L, kDownDepth>(p, a, cus, st);
+#define SMOE_RUN(B, N, L)                                                                  \
+    if (bits == B && p.nch_d == N && p.lpr_d == L)                                         \
+        return a.scale_bytes == 2 ? run_down<B, N, L, kDownDepth, 2>(p, a, cus, st)        \
+                                  : run_down<B, N, L, kDownDepth, 4>(p, a, cus, st);
     SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;

@@ -61,33 +61,42 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb)
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-int check_format(int bits, int group)
+// Weight format: the code width and the scale size, from the `bits` argument
+// (2 or 4, optionally with SMOE_SCALE_F16 set).
+struct Fmt {
+    int bits;   // 2 or 4
+    int sb;     // bytes per scale: 4 (f32) or 2 (f16)
+};
+
+int check_format(int fmt, int group, Fmt *f)
 {
-    if (bits != 4 && bits != 2) return SMOE_ERR_BITS;
-    const int unit = 128 / bits;  // codes in a 16-byte chunk
+    f->bits = fmt & ~SMOE_SCALE_F16;
+    f->sb = (fmt & SMOE_SCALE_F16) ? 2 : 4;
+    if (f->bits != 4 && f->bits != 2) return SMOE_ERR_BITS;
+    const int unit = 128 / f->bits;  // codes in a 16-byte chunk
     if (group <= 0 || group % unit) return SMOE_ERR_GROUP;
     return SMOE_OK;
 }
 
 // rows x cols quantised matrix: sizes, group divisibility, pointers, alignment.
-int check_qmat(const smoe_qmat *m, int bits, int group, long rows, long cols)
+int check_qmat(const smoe_qmat *m, const Fmt &f, int group, long rows, long cols)
 {
     if (!m || !m->codes || !m->scales) return SMOE_ERR_NULL;
-    if (rows <= 0 || cols <= 0 || cols % (128 / bits) || cols > SMOE_MAX_QCOLS) return SMOE_ERR_SHAPE;
+    if (rows <= 0 || cols <= 0 || cols % (128 / f.bits) || cols > SMOE_MAX_QCOLS) return SMOE_ERR_SHAPE;
     if (cols % group) return SMOE_ERR_GROUP;
-    if (!aligned(m->codes, 16) || !aligned(m->scales, 4)) return SMOE_ERR_ALIGN;
+    if (!aligned(m->codes, 16) || !aligned(m->scales, (uintptr_t)f.sb)) return SMOE_ERR_ALIGN;
     return SMOE_OK;
 }
 
 size_t qmat_code_bytes(int bits, long rows, long cols) { return (size_t)rows * cols * bits / 8; }
-size_t qmat_scale_bytes(int group, long rows, long cols) { return (size_t)rows * (cols / group) * 4; }
+size_t qmat_scale_bytes(int sb, int group, long rows, long cols) { return (size_t)rows * (cols / group) * sb; }
 
 // out overlaps either array of a quantised matrix.
-bool overlaps_qmat(const void *out, size_t nout, const smoe_qmat *m, int bits, int group, long rows,
+bool overlaps_qmat(const void *out, size_t nout, const smoe_qmat *m, const Fmt &f, int group, long rows,
                    long cols)
 {
-    return overlap(out, nout, m->codes, qmat_code_bytes(bits, rows, cols)) ||
-           overlap(out, nout, m->scales, qmat_scale_bytes(group, rows, cols));
+    return overlap(out, nout, m->codes, qmat_code_bytes(f.bits, rows, cols)) ||
+           overlap(out, nout, m->scales, qmat_scale_bytes(f.sb, group, rows, cols));
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SMOE_OK : SMOE_ERR_LAUNCH; }
@@ -163,7 +172,7 @@ const char *smoe_status_str(int status)
     switch (status) {
     case SMOE_OK: return "ok";
     case SMOE_ERR_NULL: return "a required pointer is NULL";
-    case SMOE_ERR_BITS: return "bits must be 2 or 4";
+    case SMOE_ERR_BITS: return "bits must be 2 or 4 (optionally with SMOE_SCALE_F16)";
     case SMOE_ERR_GROUP: return "group must be a multiple of 32 (4-bit) or 64 (2-bit) and divide cols";
     case SMOE_ERR_SHAPE: return "a size is out of range or not a multiple of the 16-byte chunk width";
     case SMOE_ERR_ALIGN: return "codes/W must be 16-byte aligned and f32 arrays 4-byte aligned";
@@ -175,22 +184,23 @@ const char *smoe_status_str(int status)
     }
 }
 
-int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group, int d_ff,
+int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int fmt, int group, int d_ff,
                  int d_model, const float *x, float *hidden, void *stream)
 {
-    int rc = check_format(bits, group);
+    Fmt f;
+    int rc = check_format(fmt, group, &f);
     if (rc) return rc;
     if (!x || !hidden) return SMOE_ERR_NULL;
-    if ((rc = check_qmat(gate, bits, group, d_ff, d_model))) return rc;
-    if ((rc = check_qmat(up, bits, group, d_ff, d_model))) return rc;
+    if ((rc = check_qmat(gate, f, group, d_ff, d_model))) return rc;
+    if ((rc = check_qmat(up, f, group, d_ff, d_model))) return rc;
     if (!aligned(x, 16) || !aligned(hidden, 4)) return SMOE_ERR_ALIGN;
     const size_t nh = (size_t)d_ff * 4;
     if (overlap(hidden, nh, x, (size_t)d_model * 4) ||
-        overlaps_qmat(hidden, nh, gate, bits, group, d_ff, d_model) ||
-        overlaps_qmat(hidden, nh, up, bits, group, d_ff, d_model))
+        overlaps_qmat(hidden, nh, gate, f, group, d_ff, d_model) ||
+        overlaps_qmat(hidden, nh, up, f, group, d_ff, d_model))
         return SMOE_ERR_ALIAS;
     DecodePlan plan;
-    if (!smoe::plan_decode(smoe::kGateUpOnly, bits, d_model, d_ff, 1, &plan)) return SMOE_ERR_SHAPE;
+    if (!smoe::plan_decode(smoe::kGateUpOnly, f.bits, d_model, d_ff, 1, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
@@ -202,24 +212,26 @@ int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;
+    a.scale_bytes = f.sb;
     a.n_experts = 1;
-    return launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, (hipStream_t)stream));
+    return launch_status(smoe::launch_gate_up(f.bits, plan, a, dev.cus, (hipStream_t)stream));
 }
 
-int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff, const float *hidden,
+int smoe_down(const smoe_qmat *down, int fmt, int group, int d_model, int d_ff, const float *hidden,
               float *out, void *stream)
 {
-    int rc = check_format(bits, group);
+    Fmt f;
+    int rc = check_format(fmt, group, &f);
     if (rc) return rc;
     if (!hidden || !out) return SMOE_ERR_NULL;
-    if ((rc = check_qmat(down, bits, group, d_model, d_ff))) return rc;
+    if ((rc = check_qmat(down, f, group, d_model, d_ff))) return rc;
     if (!aligned(hidden, 16) || !aligned(out, 4)) return SMOE_ERR_ALIGN;
     const size_t no = (size_t)d_model * 4;
     if (overlap(out, no, hidden, (size_t)d_ff * 4) ||
-        overlaps_qmat(out, no, down, bits, group, d_model, d_ff))
+        overlaps_qmat(out, no, down, f, group, d_model, d_ff))
         return SMOE_ERR_ALIAS;
     DecodePlan plan;
-    if (!smoe::plan_decode(smoe::kDownOnly, bits, d_model, d_ff, 1, &plan)) return SMOE_ERR_SHAPE;
+    if (!smoe::plan_decode(smoe::kDownOnly, f.bits, d_model, d_ff, 1, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
@@ -230,8 +242,9 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;
+    a.scale_bytes = f.sb;
     a.n_experts = 1;
-    return launch_status(smoe::launch_down(bits, plan, a, dev.cus, (hipStream_t)stream));
+    return launch_status(smoe::launch_down(f.bits, plan, a, dev.cus, (hipStream_t)stream));
 }
 
 size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
@@ -242,24 +255,25 @@ size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
     return batch_workspace(n_experts, d_model, d_ff, T, kMinBatchGroup).total;
 }
 
-int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int bits,
+int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int fmt,
                     int group, int d_model, int d_ff, int T, const float *x, float *out,
                     void *workspace, size_t workspace_bytes, void *stream)
 {
-    int rc = check_format(bits, group);
+    Fmt f;
+    int rc = check_format(fmt, group, &f);
     if (rc) return rc;
     if (!experts || !x || !out) return SMOE_ERR_NULL;
     if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS || T < 1 || T > SMOE_MAX_TOKENS)
         return SMOE_ERR_SHAPE;
     for (int e = 0; e < n_experts; ++e) {
-        if ((rc = check_qmat(&experts[e].gate, bits, group, d_ff, d_model))) return rc;
-        if ((rc = check_qmat(&experts[e].up, bits, group, d_ff, d_model))) return rc;
-        if ((rc = check_qmat(&experts[e].down, bits, group, d_model, d_ff))) return rc;
+        if ((rc = check_qmat(&experts[e].gate, f, group, d_ff, d_model))) return rc;
+        if ((rc = check_qmat(&experts[e].up, f, group, d_ff, d_model))) return rc;
+        if ((rc = check_qmat(&experts[e].down, f, group, d_model, d_ff))) return rc;
     }
     if (!aligned(x, 16) || !aligned(out, 4) || (route_w && !aligned(route_w, 4)))
         return SMOE_ERR_ALIGN;
     smoe::TbPlan tplan{};
-    if (T > 1 && !smoe::plan_batch(bits, group, d_model, d_ff, n_experts, T, &tplan))
+    if (T > 1 && !smoe::plan_batch(f.bits, group, d_model, d_ff, n_experts, T, &tplan))
         return SMOE_ERR_GROUP;
 
     const size_t need = smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T);
@@ -273,12 +287,12 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
         return SMOE_ERR_ALIAS;
     for (int e = 0; e < n_experts; ++e) {
         const smoe_expert &ex = experts[e];
-        if (overlaps_qmat(out, no, &ex.gate, bits, group, d_ff, d_model) ||
-            overlaps_qmat(out, no, &ex.up, bits, group, d_ff, d_model) ||
-            overlaps_qmat(out, no, &ex.down, bits, group, d_model, d_ff) ||
-            overlaps_qmat(workspace, need, &ex.gate, bits, group, d_ff, d_model) ||
-            overlaps_qmat(workspace, need, &ex.up, bits, group, d_ff, d_model) ||
-            overlaps_qmat(workspace, need, &ex.down, bits, group, d_model, d_ff))
+        if (overlaps_qmat(out, no, &ex.gate, f, group, d_ff, d_model) ||
+            overlaps_qmat(out, no, &ex.up, f, group, d_ff, d_model) ||
+            overlaps_qmat(out, no, &ex.down, f, group, d_model, d_ff) ||
+            overlaps_qmat(workspace, need, &ex.gate, f, group, d_ff, d_model) ||
+            overlaps_qmat(workspace, need, &ex.up, f, group, d_ff, d_model) ||
+            overlaps_qmat(workspace, need, &ex.down, f, group, d_model, d_ff))
             return SMOE_ERR_ALIAS;
     }
     hipStream_t st = (hipStream_t)stream;
@@ -305,16 +319,17 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
         a.d_model = d_model;
         a.d_ff = d_ff;
         a.group = group;
+        a.scale_bytes = f.sb;
         a.n_experts = n_experts;
         a.ks_gu = tplan.ks_gu;
         a.rw_gu = tplan.rw_gu;
         a.ks_dn = tplan.ks_dn;
         a.rw_dn = tplan.rw_dn;
-        return launch_status(smoe::launch_batch(bits, tplan, a, st));
+        return launch_status(smoe::launch_batch(f.bits, tplan, a, st));
     }
 
     DecodePlan plan;
-    if (!smoe::plan_decode(smoe::kBoth, bits, d_model, d_ff, n_experts, &plan)) return SMOE_ERR_SHAPE;
+    if (!smoe::plan_decode(smoe::kBoth, f.bits, d_model, d_ff, n_experts, &plan)) return SMOE_ERR_SHAPE;
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
@@ -330,9 +345,10 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;
+    a.scale_bytes = f.sb;
     a.n_experts = n_experts;
-    if ((rc = launch_status(smoe::launch_gate_up(bits, plan, a, dev.cus, st)))) return rc;
-    return launch_status(smoe::launch_down(bits, plan, a, dev.cus, st));
+    if ((rc = launch_status(smoe::launch_gate_up(f.bits, plan, a, dev.cus, st)))) return rc;
+    return launch_status(smoe::launch_down(f.bits, plan, a, dev.cus, st));
 }
 
 size_t matvec_bf16_workspace(int rows, int cols)

@@ -60,7 +60,8 @@ def lib():
         L.oracle_down.argtypes = [vp, i, i, l, l, vp, vp]
         L.oracle_expert_ffn.argtypes = [vp, i, vp, i, i, l, l, l, vp, vp]
         L.oracle_matvec_bf16.argtypes = [vp, l, l, vp, vp]
-        for name in ("oracle_unpack", "oracle_dequant", "oracle_qmatvec", "oracle_gate_up",
+        L.oracle_f16_widen.argtypes = [vp, l, vp]
+        for name in ("oracle_f16_widen", "oracle_unpack", "oracle_dequant", "oracle_qmatvec", "oracle_gate_up",
                      "oracle_down", "oracle_expert_ffn", "oracle_matvec_bf16"):
             getattr(L, name).restype = i
         _lib = L
@@ -90,7 +91,7 @@ def unpack(codes, bits, rows, cols):
 
 def dequant(codes, scales, bits, group, rows, cols):
     codes, pc = _c(codes, np.uint8)
-    scales, ps = _c(scales, np.float32)
+    scales, ps = _c(_scales_f32(scales), np.float32)
     w = np.empty((rows, cols), dtype=np.float64)
     _ok(lib().oracle_dequant(pc, ps, bits, group, rows, cols,
                              w.ctypes.data_as(ctypes.c_void_p)), "dequant")
@@ -99,7 +100,7 @@ def dequant(codes, scales, bits, group, rows, cols):
 
 def qmatvec(codes, scales, bits, group, rows, cols, x):
     codes, pc = _c(codes, np.uint8)
-    scales, ps = _c(scales, np.float32)
+    scales, ps = _c(_scales_f32(scales), np.float32)
     x, px = _c(x, np.float64)
     y = np.empty(rows, dtype=np.float64)
     _ok(lib().oracle_qmatvec(pc, ps, bits, group, rows, cols, px,
@@ -111,9 +112,25 @@ def silu(t: float) -> float:
     return lib().oracle_silu(float(t))
 
 
+def f16_widen(h):
+    """f32 values of IEEE binary16 patterns (uint16 or float16 array), by the
+    oracle's own decoder."""
+    h = np.ascontiguousarray(h)
+    bits = h.view(np.uint16) if h.dtype == np.float16 else h.astype(np.uint16)
+    out = np.empty(bits.shape, dtype=np.float32)
+    _ok(lib().oracle_f16_widen(bits.ctypes.data_as(ctypes.c_void_p), bits.size,
+                               out.ctypes.data_as(ctypes.c_void_p)), "f16_widen")
+    return out
+
+
+def _scales_f32(scales):
+    """A matrix's scales as f32: 2-byte (float16) scales are widened exactly."""
+    return f16_widen(scales) if np.asarray(scales).dtype == np.float16 else scales
+
+
 def _qmat_struct(m, keep):
     c, pc = _c(m.codes, np.uint8)
-    s, ps = _c(m.scales, np.float32)
+    s, ps = _c(_scales_f32(m.scales), np.float32)
     keep += [c, s]
     return _QMat(pc, ps)
 

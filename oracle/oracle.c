@@ -163,6 +163,32 @@ out:
     return rc;
 }
 
+/* IEEE 754 binary16 to double, from the format's definition: sign bit 15,
+ * exponent bits 10..14 with bias 15, fraction bits 0..9.  An exponent field of
+ * 0 is a subnormal, fraction * 2^-24; 31 is an infinity (fraction 0) or a NaN;
+ * otherwise the value is (1024 + fraction) * 2^(exponent - 25).  Every
+ * binary16 value is exactly a binary32 value.  Used for the 2-byte scale
+ * layout, which the kernels' callers may pass instead of f32 scales. */
+static double f16_value(uint16_t h)
+{
+    const int sign = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+int oracle_f16_widen(const uint16_t *h, long n, float *out)
+{
+    if (!h || !out || n < 0) return -1;
+    for (long i = 0; i < n; ++i) out[i] = (float)f16_value(h[i]);
+    return 0;
+}
+
 /* bf16 bits to f32: the bf16 pattern is the upper half of the f32 pattern, so
  * widening is exact ("Coalesced Dense Matvec -- the Same Contract for bf16"). */
 static double bf16_value(uint16_t b)

@@ -47,6 +47,11 @@ typedef struct {
     oracle_qmat down;       /* [d_model][d_ff] */
 } oracle_expert;
 
+/* 2-byte scales: out[i] = the IEEE 754 binary16 value of h[i], widened to f32
+ * (exact).  A matrix with 2-byte scales is the matrix whose f32 scales are
+ * these values. */
+int oracle_f16_widen(const uint16_t *h, long n, float *out);
+
 /* Number of OpenMP threads the oracle's row loops use (1 without OpenMP). */
 int oracle_threads(void);
 

@@ -61,7 +61,7 @@ def dev_experts(group):
 def run_ffn(gq, dexp, bits, group_size, x, route=None, T=None):
     """smoe_expert_ffn through the C ABI; returns the f32 output as numpy."""
     import torch
-    d_model = dexp[0].gate.codes.shape[1] * 8 // bits
+    d_model = dexp[0].gate.codes.shape[1] * 8 // (bits & 0xFF)
     d_ff = dexp[0].gate.codes.shape[0]
     xd = x if isinstance(x, torch.Tensor) else dev(np.asarray(x, np.float32))
     T = xd.numel() // d_model

@@ -36,6 +36,7 @@ def bind(L):
     L.oracle_down.argtypes = [vp, ci, ci, cl, cl, vp, vp]
     L.oracle_expert_ffn.argtypes = [vp, ci, vp, ci, ci, cl, cl, cl, vp, vp]
     L.oracle_matvec_bf16.argtypes = [vp, cl, cl, vp, vp]
+    L.oracle_f16_widen.argtypes = [vp, cl, vp]
     return L
 
 
@@ -225,6 +226,33 @@ def pin_bf16(L):
     return fails
 
 
+def load_f16_patterns():
+    with open(os.path.join(GOLDEN, "f16_patterns.json")) as f:
+        return json.load(f)["patterns"]
+
+
+def pin_f16(L):
+    """2-byte scales: IEEE binary16 patterns worked by hand widen to their
+    values, and all 65536 patterns agree with numpy's binary16 (NaN for NaN)."""
+    fails = []
+    pats = load_f16_patterns()
+    h = np.array([int(p["bits"], 16) for p in pats], np.uint16)
+    out = np.empty(len(pats), np.float32)
+    assert L.oracle_f16_widen(_p(h), len(pats), _p(out)) == 0
+    for p, v in zip(pats, out):
+        want = float(p["value"])
+        if not (v == want and np.signbit(v) == np.signbit(want)):
+            fails.append(f"f16 {p['bits']}: {v!r} != {p['value']}")
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = np.empty(allh.size, np.float32)
+    assert L.oracle_f16_widen(_p(allh), allh.size, _p(got)) == 0
+    ref = allh.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    if not (np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))):
+        fails.append("f16 widening differs from numpy's binary16 on some pattern")
+    return fails
+
+
 def make_expert(rng, d_model, d_ff, bits, group):
     def m(rows, cols):
         codes = rng.integers(0, 1 << bits, size=(rows, cols), dtype=np.uint8)
@@ -301,7 +329,7 @@ def pin_ffn_composition(L, seed=11):
 
 
 CORE_PINS = [pin_worked_examples, pin_unpack_exhaustive, pin_affine_identity, pin_silu,
-             pin_bf16, pin_ffn_composition]
+             pin_bf16, pin_f16, pin_ffn_composition]
 
 
 def run_core_pins(L):

@@ -88,6 +88,29 @@ def test_down_and_bf16_refusals(gq):
     assert L.matvec_bf16_workspace(512, 4096) == 0
 
 
+def test_scale_format_flag(gq):
+    """Unknown format bits are refused; f16 scales need 2-byte alignment only."""
+    L = gq.lib()
+    F16 = gq.SMOE_SCALE_F16
+    G = gq.QMat(A, A + 0x1000000)
+    U = gq.QMat(A + 0x2000000, A + 0x3000000)
+    x, h = A + 0x8000000, A + 0x9000000
+    args = lambda bits: (ctypes.byref(G), ctypes.byref(U), bits, 64, 512, 256, x, h, None)
+    assert L.smoe_gate_up(*args(4 | 0x200)) == -2
+    assert L.smoe_gate_up(*args(8 | F16)) == -2
+    assert L.smoe_gate_up(*args(4 | F16)) == -8           # valid: reaches the device check
+    U2 = gq.QMat(A + 0x2000000, A + 0x3000002)             # scales 2-byte aligned
+    a2 = (ctypes.byref(G), ctypes.byref(U2), 4 | F16, 64, 512, 256, x, h, None)
+    assert L.smoe_gate_up(*a2) == -8
+    a2f = (ctypes.byref(G), ctypes.byref(U2), 4, 64, 512, 256, x, h, None)
+    assert L.smoe_gate_up(*a2f) == -5                      # f32 scales need 4-byte alignment
+    U1 = gq.QMat(A + 0x2000000, A + 0x3000001)
+    assert L.smoe_gate_up(ctypes.byref(G), ctypes.byref(U1), 4 | F16, 64, 512, 256, x, h, None) == -5
+    # hidden inside the gate scales: 512 rows x 4 groups x 2 bytes = 4096 bytes of f16 scales
+    assert L.smoe_gate_up(ctypes.byref(G), ctypes.byref(U), 4 | F16, 64, 512, 256, x, A + 0x1000000 + 4092, None) == -7
+    assert L.smoe_gate_up(ctypes.byref(G), ctypes.byref(U), 4 | F16, 64, 512, 256, x, A + 0x1000000 + 4096, None) == -8
+
+
 def test_bf16_batch_refusals(gq):
     """Every out-of-contract batch is refused before the device is touched;
     a valid one reaches the device check (-8 without a GPU)."""

@@ -22,6 +22,8 @@ MUTANTS = {
     "row_stride": ("codes + r * (cols * bits / 8)", "codes + r * (cols / 2)"),
     "silu_sign": ("t / (1.0 + exp(-t))", "t / (1.0 + exp(t))"),
     "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "f16_bias": ("(double)(1024 + m), e - 25)", "(double)(1024 + m), e - 24)"),
+    "f16_subnormal": ("ldexp((double)m, -24)", "ldexp((double)(1024 + m), -25)"),
     "combine_overwrite": ("o[j] += r * y[j]", "o[j] = r * y[j]"),
     "hidden_product": ("hidden[i] = oracle_silu(g[i]) * u[i]", "hidden[i] = oracle_silu(u[i]) * g[i]"),
 }

@@ -113,7 +113,8 @@ def softmax_f32(logits: np.ndarray) -> np.ndarray:
 
 @dataclass
 class QMat:
-    """One packed matrix: ``codes`` uint8 [rows, cols*bits/8], ``scales`` f32 [rows, cols/group]."""
+    """One packed matrix: ``codes`` uint8 [rows, cols*bits/8], ``scales`` [rows, cols/group],
+    f32, or float16 for the 2-byte scale layout."""
     codes: np.ndarray
     scales: np.ndarray
 
@@ -132,6 +133,7 @@ class ExpertGroup:
     d_model: int
     d_ff: int
     experts: list = field(default_factory=list)
+    scale_f16: bool = False
 
     def byte_count(self) -> int:
         return sum(m.codes.nbytes + m.scales.nbytes
@@ -139,24 +141,36 @@ class ExpertGroup:
 
 
 def qmat(seed: int, expert: int, name: str, rows: int, cols: int, bits: int, group: int,
-         scale_lo: float = 0.01, scale_hi: float = 0.05) -> QMat:
+         scale_lo: float = 0.01, scale_hi: float = 0.05, scale_f16: bool = False) -> QMat:
+    """Codes uniform; scales U[scale_lo, scale_hi) as f32, or those f32 values
+    rounded to the nearest binary16 (ties to even) for the 2-byte layout."""
     if (cols * bits) % 8 or cols % group:
         raise ValueError("cols must fill whole bytes and whole groups")
     m = _MAT[name]
     codes = random_bytes(seed, (expert, m, _KIND_CODES), rows * cols * bits // 8)
     scales = uniform_f32(seed, (expert, m, _KIND_SCALES), rows * (cols // group), scale_lo, scale_hi)
+    if scale_f16:
+        scales = scales.astype(np.float16)
     return QMat(codes.reshape(rows, cols * bits // 8), scales.reshape(rows, cols // group))
 
 
 def expert_group(seed: int, n_experts: int, d_model: int, d_ff: int, bits: int,
-                 group: int = 64) -> ExpertGroup:
-    g = ExpertGroup(bits=bits, group=group, d_model=d_model, d_ff=d_ff)
+                 group: int = 64, scale_f16: bool = False) -> ExpertGroup:
+    g = ExpertGroup(bits=bits, group=group, d_model=d_model, d_ff=d_ff, scale_f16=scale_f16)
     for e in range(n_experts):
         g.experts.append(Expert(
-            gate=qmat(seed, e, "gate", d_ff, d_model, bits, group),
-            up=qmat(seed, e, "up", d_ff, d_model, bits, group),
-            down=qmat(seed, e, "down", d_model, d_ff, bits, group)))
+            gate=qmat(seed, e, "gate", d_ff, d_model, bits, group, scale_f16=scale_f16),
+            up=qmat(seed, e, "up", d_ff, d_model, bits, group, scale_f16=scale_f16),
+            down=qmat(seed, e, "down", d_model, d_ff, bits, group, scale_f16=scale_f16)))
     return g
+
+
+def widened_scales(g: ExpertGroup) -> ExpertGroup:
+    """The same group with every 2-byte scale stored as the f32 of equal value."""
+    w = ExpertGroup(bits=g.bits, group=g.group, d_model=g.d_model, d_ff=g.d_ff, scale_f16=False)
+    for e in g.experts:
+        w.experts.append(Expert(*[QMat(m.codes, m.scales.astype(np.float32)) for m in (e.gate, e.up, e.down)]))
+    return w
 
 
 def activation(seed: int, d_model: int) -> np.ndarray:
@@ -179,6 +193,9 @@ def router_weights(seed: int, n_experts: int, T: int = 1) -> np.ndarray:
 TINY = dict(name="q4_tiny_1expert_256x512", seed=0, n_experts=1, d_model=256, d_ff=512, bits=4)
 Q4_GROUP8 = dict(name="q4_8expert_4096x1536", seed=1, n_experts=8, d_model=4096, d_ff=1536, bits=4)
 Q2_GROUP8 = dict(name="q2_8expert_4096x1536", seed=2, n_experts=8, d_model=4096, d_ff=1536, bits=2)
+# The same groups with 2-byte (binary16) scales: same codes, scales rounded to f16.
+Q4_GROUP8_S16 = dict(Q4_GROUP8, name="q4_8expert_4096x1536_f16scales", scale_f16=True)
+Q2_GROUP8_S16 = dict(Q2_GROUP8, name="q2_8expert_4096x1536_f16scales", scale_f16=True)
 BF16_SHAPES = [  # (rows, cols, role, seed)
     (8192, 4096, "q_proj", 30),
     (4096, 8192, "o_proj", 31),
@@ -196,7 +213,8 @@ BF16_BATCH = [
 
 
 def make_group(spec: dict) -> ExpertGroup:
-    return expert_group(spec["seed"], spec["n_experts"], spec["d_model"], spec["d_ff"], spec["bits"])
+    return expert_group(spec["seed"], spec["n_experts"], spec["d_model"], spec["d_ff"], spec["bits"],
+                        scale_f16=spec.get("scale_f16", False))
 
 
 def make_decode_inputs(spec: dict):
