@@ -14,6 +14,8 @@ Other rows of the path, one JSON line each with --workload:
                       experts on the matrix cores (bound by HBM at T = 16, by
                       the f16 MFMA rate above)
   bf16                --shape q_proj|o_proj|kv_proj|lm_head dense matvec
+  routed              --tokens T --topk K: routed prefill, each token through its
+                      top-K of the 8 experts (top-K of N(0,1) logits)
   bf16_batch          q, k and v projections (8192x4096, 2 x 512x4096) over
                       one x as one batched launch, with the three separate
                       launches timed beside it
@@ -283,6 +285,75 @@ def prefill_bench(args):
     }
 
 
+def routed_bench(args):
+    """Routed prefill: T tokens, each through its top_k of the 8 Q4 experts."""
+    import torch
+    import workloads
+    import group_quantized_moe_amd as gq
+    L = gq.lib()
+    T, k = args.tokens, args.topk
+    spec = workloads.Q4_GROUP8
+    g = workloads.make_group(spec)
+    X, ids, w = workloads.make_routed_inputs(T, k, workloads.ROUTED["seed"])
+    E = spec["n_experts"]
+    used = sorted(set(int(e) for e in ids.ravel()))
+    flops = 2 * T * k * 3 * g.d_model * g.d_ff
+    per_expert = g.byte_count() // E
+    nbytes = per_expert * len(used) + T * g.d_model * 4 * 2 + T * k * 8
+    replicas = replica_count(g.byte_count())
+    arrays, _keep = expert_arrays(gq, g, E, replicas)
+    xd, idd, wd = to_dev(X), to_dev(ids), to_dev(w)
+    out = torch.empty(T * g.d_model, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(gq.smoe_routed_ffn_workspace(E, g.d_model, g.d_ff, T, k), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        rc = L.smoe_routed_ffn(arrays[i % replicas], E, 4, 64, g.d_model, g.d_ff, T, k, idd.data_ptr(),
+                               wd.data_ptr(), xd.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        if rc != 0:
+            raise gq.SmoeError("smoe_routed_ffn", rc)
+
+    us_step, per_call, wall_us = time_steps(step, args.steps, args.warmup, stream)
+    tflops = flops / (per_call * 1e-6) / 1e12
+    gbs = nbytes / (per_call * 1e-6) / 1e9
+    hbm_bound = T * k <= 16 * E
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        ns = 4
+        n, dt, cores = cpu_oracle(lambda: oracle.routed_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X[:ns], ids[:ns],
+                                                            w[:ns]), args.cpu_budget, ns)
+        cpu = {"value": round(n * ns * 2 * k * 3 * g.d_model * g.d_ff / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": cores, "kind": "oracle",
+               "sample": f"{n} calls of {ns} tokens x top-{k} (f64 oracle, {dt:.1f} s)"}
+    return {
+        "metric": f"routed prefill tokens/s, {T} tokens x top-{k} of 8 Q4 experts",
+        "value": round(T / (us_step * 1e-6), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(us_step / 1e3, 6),
+        "us_per_call": round(us_step, 3),
+        "tflops": round(flops / (us_step * 1e-6) / 1e12, 2),
+        "hbm_gbs": round(nbytes / (us_step * 1e-6) / 1e9, 1),
+        "wall_us_per_step": round(wall_us, 3),
+        "dtype": "f16 exact codes x f16 hi/lo activations -> f32",
+        "config": {"workload": f"routed_prefill_q4_8expert_4096x1536_T{T}_top{k}", "tokens": T, "top_k": k,
+                   "experts_used": len(used), "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                   "replicas_rotated": replicas, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm" if hbm_bound else "mfma",
+            "kernel": "one smoe_routed_ffn call (bucket, prep, gate_up [+ finish], down, combine)",
+            "achieved": round(gbs if hbm_bound else tflops, 2),
+            "peak": PEAK_HBM_GBS if hbm_bound else PEAK_F16_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round((gbs / PEAK_HBM_GBS) if hbm_bound else (tflops / PEAK_F16_TFLOPS), 4),
+            "traffic": load_traffic(f"routed_t{T}_k{k}", "prefill"),
+            "per_call_us_events": round(per_call, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+
+
 def bf16_bench(args):
     import torch
     import workloads
@@ -431,8 +502,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "decode_q4_s16", "decode_q2_s16", "prefill", "bf16",
-                             "bf16_batch", "copy"])
-    ap.add_argument("--tokens", type=int, default=16, help="prefill: tokens per call")
+                             "bf16_batch", "routed", "copy"])
+    ap.add_argument("--tokens", type=int, default=16, help="prefill / routed: tokens per call")
+    ap.add_argument("--topk", type=int, default=2, help="routed: experts per token")
     ap.add_argument("--shape", default="q_proj", help="bf16: q_proj, o_proj, kv_proj or lm_head")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
@@ -459,6 +531,8 @@ def main():
         line = prefill_bench(args)
     elif args.workload == "copy":
         line = copy_calibration(args)
+    elif args.workload == "routed":
+        line = routed_bench(args)
     elif args.workload == "bf16_batch":
         line = bf16_batch_bench(args)
     else:

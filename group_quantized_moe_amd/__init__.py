@@ -20,7 +20,8 @@ SMOE_MAX_EXPERTS = 16
 SMOE_SCALE_F16 = 0x100   # ORed into `bits`: 2-byte IEEE binary16 scales instead of f32
 
 EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
-           "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_status_str")
+           "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_routed_ffn_workspace",
+           "smoe_routed_ffn", "smoe_status_str")
 SMOE_MAX_BF16_JOBS = 16
 
 
@@ -64,6 +65,9 @@ def lib():
         L.matvec_bf16_workspace.restype = sz
         L.matvec_bf16.argtypes = [vp, i, i, vp, vp, vp, sz, vp]
         L.matvec_bf16_batch.argtypes = [vp, i, vp]
+        L.smoe_routed_ffn_workspace.argtypes = [i, i, i, i, i]
+        L.smoe_routed_ffn_workspace.restype = sz
+        L.smoe_routed_ffn.argtypes = [vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.smoe_status_str.argtypes = [i]
         L.smoe_status_str.restype = ctypes.c_char_p
         for name in ("smoe_gate_up", "smoe_down", "smoe_expert_ffn", "matvec_bf16"):
@@ -210,3 +214,22 @@ def matvec_bf16_batch(jobs, stream=None):
     """y_j = W_j x_j for a list of (W, x, y) tensor triples, in one launch."""
     arr = bf16_job_array(jobs)
     _check("matvec_bf16_batch", lib().matvec_bf16_batch(arr, len(jobs), _stream(stream)))
+
+
+def smoe_routed_ffn_workspace(n_experts, d_model, d_ff, T, top_k) -> int:
+    return int(lib().smoe_routed_ffn_workspace(n_experts, d_model, d_ff, T, top_k))
+
+
+def smoe_routed_ffn(experts, bits, group, x, expert_ids, expert_w, out, workspace, stream=None):
+    """out[T, d_model] = per token, sum over its top_k slots of w * FFN_id(x[t]).
+
+    expert_ids: int32 [T, top_k] GPU tensor; expert_w: f32 [T, top_k]; x, out: f32 [T, d_model];
+    workspace: uint8 GPU tensor of at least smoe_routed_ffn_workspace(...) bytes."""
+    import torch
+    d_ff, d_model = _dims(_first_gate_codes(experts), bits)
+    T, top_k = expert_ids.shape
+    arr = _expert_array(experts, bits)
+    _check("smoe_routed_ffn", lib().smoe_routed_ffn(
+        arr, len(experts), bits, group, d_model, d_ff, T, top_k, _dev(expert_ids, torch.int32, "expert_ids"),
+        _dev(expert_w, torch.float32, "expert_w"), _dev(x, torch.float32, "x"), _dev(out, torch.float32, "out"),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))

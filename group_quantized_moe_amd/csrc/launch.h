@@ -66,6 +66,17 @@ struct TbArgs {
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
     float *part_gu, *part_dn; // tiled kernels: per-tile partial sums of the K splits
+    // Routed mode (top_k > 0; tiled kernels only): slot s = t*top_k + j of token
+    // t goes to expert ids[s] with weight slot_w[s].  list[e*T + p], p <
+    // cnt[e], are expert e's slots in ascending order; the hidden rows,
+    // factors and partial sums of expert e are indexed by p instead of the
+    // token.  down writes each slot's weighted output row to ys [T*top_k]
+    // [d_model] and slot_ok[s] says whether slot s was processed.
+    const int *ids;
+    const float *slot_w;
+    int top_k;
+    int *list, *cnt, *slot_ok;
+    float *ys;
     int T, t_pad, d_model, d_ff, group, n_experts;
     int scale_bytes;         // 4: f32 scales, 2: IEEE binary16 scales
     int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
@@ -104,6 +115,10 @@ struct BatchSplits {
     size_t gu_part_floats, dn_part_floats;
 };
 BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T);
+// Routed mode: tiling from the average slots per expert, T * top_k / n_experts.
+bool plan_routed(int bits, int group, int d_model, int d_ff, int n_experts, int T, int top_k, TbPlan *plan);
+BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k);
+hipError_t launch_routed(int bits, const TbPlan &plan, const TbArgs &args, hipStream_t stream);
 hipError_t launch_batch(int bits, const TbPlan &plan, const TbArgs &args, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

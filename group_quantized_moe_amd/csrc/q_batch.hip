@@ -664,9 +664,11 @@ struct TileMap {
     bool lo[PP];        // wave-uniform: the piece belongs to the lo half
 };
 
+// Tile rows t0 .. t0+TT-1 of a table of `rows` rows (clamped to the last);
+// with a row list (routed mode) tile row p reads table row list[p] / top_k.
 template <int KB, int NTT, int MG = 1>
 __device__ __forceinline__ void tile_map(TileMap<KB, NTT, MG> &m, int wave, unsigned row_stride_bytes, int t0,
-                                         int T)
+                                         int rows, const int *list = nullptr, int top_k = 1)
 {
     using Sh = TileShape<KB, NTT, MG>;
 #pragma unroll
@@ -675,8 +677,10 @@ __device__ __forceinline__ void tile_map(TileMap<KB, NTT, MG> &m, int wave, unsi
         const int hl = ((wave * 64 + 512 * i) % Sh::kPieces) / Sh::kPerHalf;
         const int rem = c - hl * Sh::kPerHalf;
         const int tok = rem / Sh::kPerRow, part = rem - tok * Sh::kPerRow;
+        const int p = min(t0 + tok, rows - 1);
+        const int row = list ? list[p] / top_k : p;
         m.lo[i] = hl != 0;
-        m.off[i] = (unsigned)min(t0 + tok, T - 1) * row_stride_bytes + (unsigned)part * 16u;
+        m.off[i] = (unsigned)row * row_stride_bytes + (unsigned)part * 16u;
         m.lds[i] = (unsigned)((hl * Sh::kTT + tok) * Sh::kStride + part * 8) * 2u;
     }
 }
@@ -756,13 +760,17 @@ __device__ __forceinline__ void gu_epilogue(const TbArgs &a, const f32x4 (&tot)[
     const int q = lane >> 4, n = lane & 15;
     const int t0 = tb * TT;
     const int wrow0 = rb * kTileRows + wave * 16;
+    // Rows of the tile: tokens (dense mode) or positions in expert e's slot list.
+    const int *list = a.top_k ? a.list + (size_t)e * T : nullptr;
+    const int rows = a.top_k ? a.cnt[e] : T;
     // Per-token maxima over this wave's 16 rows.
     float h[NTT][4];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = min(t0 + tt * 16 + 4 * q + i, T - 1);
+            const int pc = min(t0 + tt * 16 + 4 * q + i, rows - 1);
+            const int t = list ? list[pc] / a.top_k : pc;
             const int xe = a.xe[t];
             const float gv = ldexpf(tot[tt][i], xe), uv = ldexpf(tot[NTT + tt][i], xe);
             h[tt][i] = wrow0 + n < d_ff ? silu(gv) * uv : 0.0f;
@@ -783,22 +791,21 @@ __device__ __forceinline__ void gu_epilogue(const TbArgs &a, const f32x4 (&tot)[
 #pragma unroll
             for (int w = 0; w < wpg; ++w) m = fmaxf(m, mx[((w0 + w) * NTT + tt) * 16 + tl]);
             const int ee = norm_exponent(m);
-            const int t = t0 + tt * 16 + tl;
-            if (t < T) {
+            const int p = t0 + tt * 16 + tl;
+            if (p < rows) {
                 const float v = ldexpf(h[tt][i], -ee);
                 const _Float16 hv = (_Float16)v;
                 const int r = wrow0 + n;
-                const size_t pos = ((size_t)e * T + t) * d_ff + (r & ~7) + sigma_pos(r & 7);
+                const size_t pos = ((size_t)e * T + p) * d_ff + (r & ~7) + sigma_pos(r & 7);
                 a.hh[pos] = hv;
                 a.hl[pos] = (_Float16)(v - (float)hv);
                 if (wave == w0 && n == 0) {
-                    const float rwt = a.route_w ? a.route_w[(size_t)t * E + e] : 1.0f;
-                    a.hf[((size_t)e * HG + hg) * a.t_pad + t] = ldexpf(rwt, ee);
+                    const float rwt = list ? a.slot_w[list[p]] : a.route_w ? a.route_w[(size_t)p * E + e] : 1.0f;
+                    a.hf[((size_t)e * HG + hg) * a.t_pad + p] = ldexpf(rwt, ee);
                 }
             }
         }
 }
-
 
 // gate_up, tiled: block (token tile, row block, expert, split).  A step is MG
 // quantisation groups of d_model.
@@ -828,6 +835,9 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     const int e = b % E;
     const int ks = b / E;
     const int t0 = tb * TT;
+    // Routed mode: the tile's rows are expert e's slots; tiles past its count are empty.
+    const int rows = a.top_k ? a.cnt[e] : T;
+    if (t0 >= rows) return;   // whole block, before any barrier
     const int wrow0 = rb * kTileRows + wave * 16;   // this wave's first d_ff row
     const int s0 = (int)((long)ks * NS / KSG), NSS = (int)((long)(ks + 1) * NS / KSG) - s0;
 
@@ -841,7 +851,8 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
     const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
     TileMap<KB, NTT, MG> tm;
-    tile_map<KB, NTT, MG>(tm, wave, (unsigned)d_model * 2u, t0, T);
+    tile_map<KB, NTT, MG>(tm, wave, (unsigned)d_model * 2u, t0, rows, a.top_k ? a.list + (size_t)e * T : nullptr,
+                          a.top_k);
 
     // Register ring of PF steps: the activation pieces this thread stores into
     // LDS and the wave's codes and scales, PF - 1 steps ahead of the step being
@@ -938,6 +949,7 @@ __global__ __launch_bounds__(512) void k_tb_gu_finish(TbArgs a)
     const int RB = (a.d_ff + kTileRows - 1) / kTileRows;
     const int tile_id = blockIdx.x;
     const int tb = tile_id % NTB, rb = (tile_id / NTB) % RB, e = tile_id / NTB / RB;
+    if (a.top_k && tb * TT >= a.cnt[e]) return;   // routed mode: an empty tile
     constexpr size_t stride = (size_t)2 * NTT * 4 * 512;
     f32x4 tot[2 * NTT];
     sum_partials<2 * NTT>(tot, a.part_gu + (size_t)tile_id * a.ks_gu * stride, stride, a.ks_gu);
@@ -986,8 +998,10 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     const int tb = bid % NTB;
     bid /= NTB;
     const int rb = bid % RB;
-    const int ks = bid / RB;
+    const int ks = bid / RB;   // routed mode (one split): the block's expert
     const int t0 = tb * TT;
+    const int rows = a.top_k ? a.cnt[ks] : T;   // routed mode: expert ks's slots
+    if (t0 >= rows) return;                      // whole block, before any barrier
     const int wrow0 = rb * kTileRows + wave * 16;
     const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
     const unsigned coff = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
@@ -996,9 +1010,12 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     const size_t hbytes = (size_t)T * d_ff * 2;   // one expert's hidden half
     const BufRes fr_res = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
     TileMap<KB, NTT> tm;
-    tile_map<KB, NTT>(tm, wave, (unsigned)d_ff * 2u, t0, T);
+    tile_map<KB, NTT>(tm, wave, (unsigned)d_ff * 2u, t0, rows);
+    // The (expert, group) pairs of this block: its split of all of them, or in
+    // routed mode the groups of its expert.
     const int P = E * Gd;
-    const int p0 = (int)((long)ks * P / KSD), NP = (int)((long)(ks + 1) * P / KSD) - p0;
+    const int p0 = a.top_k ? ks * Gd : (int)((long)ks * P / KSD);
+    const int NP = a.top_k ? Gd : (int)((long)(ks + 1) * P / KSD) - p0;
     const unsigned flane = (unsigned)(lane & (TT - 1));   // a token of the tile (repeats for TT < 64)
 
     f32x4 tot[NTT];
@@ -1066,6 +1083,18 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
         }
     }
 
+    if (a.top_k) {
+        // Routed mode: the weighted output row of each of the tile's slots.
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = t0 + tt * 16 + 4 * q + i;
+                const int r = wrow0 + n;
+                if (p < rows && r < d_model) a.ys[(size_t)a.list[(size_t)ks * T + p] * d_model + r] = tot[tt][i];
+            }
+        return;
+    }
     if (KSD > 1) {
         store_partial<NTT>(tot, a.part_dn + ((size_t)(rb * NTB + tb) * KSD + ks) * (NTT * 4 * 512));
         return;
@@ -1109,6 +1138,120 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
         err = hipGetLastError();
     }
     return err;
+}
+
+// -------------------------------------------------------------------------
+// Routed mode ("Token-Batch Fused FFN": per expert, the tokens that chose it
+// run through it together).  Slot s = t*top_k + j of token t goes to expert
+// ids[s].  One block per expert lists that expert's slots in ascending order
+// (a ballot prefix count per 256 slots), so the lists and hence every sum
+// downstream are deterministic.  An expert keeps at most T slots (a token's
+// ids are distinct, so no slot is lost); slot_ok[s] marks the kept slots of
+// ids in [0, n_experts).
+__global__ __launch_bounds__(256) void k_route_bucket(const int *__restrict__ ids, int T, int top_k, int *list,
+                                                      int *cnt, int *slot_ok)
+{
+    __shared__ int s_wave[4];
+    const int e = blockIdx.x, n = T * top_k;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int base = 0;
+    for (int c0 = 0; c0 < n; c0 += 256) {
+        const int s = c0 + threadIdx.x;
+        const bool mine = s < n && ids[s] == e;
+        const unsigned long long mask = __ballot(mine);
+        const int below = __popcll(mask & ((1ull << lane) - 1ull));
+        if (lane == 0) s_wave[wave] = __popcll(mask);
+        __syncthreads();
+        int before = base;
+        for (int w = 0; w < wave; ++w) before += s_wave[w];
+        const int total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+        if (mine) {
+            const int pos = before + below;
+            if (pos < T) list[(size_t)e * T + pos] = s;
+            slot_ok[s] = pos < T;
+        }
+        base += total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) cnt[e] = min(base, T);
+}
+
+// out[t][:] = sum over the token's slots j (ascending) that were processed of
+// ys[t*top_k + j][:] (each already weighted by its router weight).  Block
+// (t, c) covers columns 1024 c .. 1024 c + 1023 of token t, four per thread
+// (d_model is a multiple of 32, and 16-byte aligned rows of ys).
+__global__ __launch_bounds__(256) void k_route_combine(const int *__restrict__ ids, const int *__restrict__ slot_ok,
+                                                       const float *__restrict__ ys, int top_k, int n_experts,
+                                                       int d_model, float *__restrict__ out)
+{
+    const int t = blockIdx.x;
+    const int r = blockIdx.y * 1024 + threadIdx.x * 4;
+    if (r >= d_model) return;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < top_k; ++j) {
+        const int s = t * top_k + j, e = ids[s];
+        if (e >= 0 && e < n_experts && slot_ok[s]) {
+            const float4 v = *reinterpret_cast<const float4 *>(ys + (size_t)s * d_model + r);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+    }
+    float *o = out + (size_t)t * d_model + r;   // out is only 4-byte aligned
+    o[0] = acc.x;
+    o[1] = acc.y;
+    o[2] = acc.z;
+    o[3] = acc.w;
+}
+
+template <int BITS, int KB, int NTT, int MG, int SB>
+hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_route_bucket, dim3((unsigned)a.n_experts), dim3(256), 0, st, a.ids, a.T, a.top_k, a.list,
+                       a.cnt, a.slot_ok);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, kTilePrefetch, SB>), dim3(pl.gu_blocks),
+                       dim3(64 * kTileWaves), pl.gu_lds, st, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.ks_gu > 1) {
+        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu), dim3(64 * kTileWaves),
+                           (size_t)kTileWaves * NTT * 16 * 4, st, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, kTilePrefetch, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
+                       pl.dn_lds, st, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_route_combine, dim3((unsigned)a.T, (unsigned)((a.d_model + 1023) / 1024)), dim3(256), 0, st,
+                       a.ids, a.slot_ok, a.ys, a.top_k, a.n_experts, a.d_model, a.out);
+    return hipGetLastError();
+}
+
+template <int BITS, int KB, int SB>
+hipError_t launch_routed_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    if (pl.ntt == 1) {
+        if (pl.mg == 2) return launch_routed_tiled<BITS, KB, 1, 2, SB>(pl, a, st);
+        return launch_routed_tiled<BITS, KB, 1, 1, SB>(pl, a, st);
+    }
+    if (pl.ntt == 2) return launch_routed_tiled<BITS, KB, 2, 1, SB>(pl, a, st);
+    return launch_routed_tiled<BITS, KB, 4, 1, SB>(pl, a, st);
+}
+
+template <int SB>
+hipError_t launch_routed_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    const int kb = a.group / 32;
+    if (bits == 4) {
+        if (kb == 1) return launch_routed_kb<4, 1, SB>(pl, a, st);
+        if (kb == 2) return launch_routed_kb<4, 2, SB>(pl, a, st);
+        return hipErrorInvalidValue;
+    }
+    if (kb == 2) return launch_routed_kb<2, 2, SB>(pl, a, st);
+    return hipErrorInvalidValue;
 }
 
 template <int BITS, int KB, int NTT, int RTG, int RTD, int SB>
@@ -1259,6 +1402,57 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
     *pl = p;
     return true;
+}
+
+// Routed mode: tiles sized for the average slots per expert (T * top_k /
+// n_experts), grids for the largest possible count (T per expert; tiles past
+// an expert's count exit at once), K split chosen from the expected active
+// tiles.
+BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k)
+{
+    BatchSplits b{};
+    const long avg = ((long)T * top_k + n_experts - 1) / n_experts;
+    b.ntt = tile_ntt((int)std::max(1L, std::min<long>(avg, T)));
+    const int tt = 16 * b.ntt;
+    const long ntb = (T + tt - 1) / tt, ntb_avg = (std::min<long>(avg, T) + tt - 1) / tt;
+    const long rbg = (d_ff + kTileRows - 1) / kTileRows;
+    b.gu_tiles = (long)n_experts * rbg * ntb;
+    b.dn_tiles = (long)n_experts * ((d_model + kTileRows - 1) / kTileRows) * ntb;
+    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg);
+    b.ks_dn = 1;
+    b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
+    b.dn_part_floats = 0;
+    return b;
+}
+
+bool plan_routed(int bits, int group, int d_model, int d_ff, int n_experts, int T, int top_k, TbPlan *pl)
+{
+    if (T < 1 || n_experts < 1 || top_k < 1) return false;
+    if (!(group == 32 && bits == 4) && group != 64) return false;
+    if (d_model % group || d_ff % group) return false;
+    const BatchSplits bs = routed_splits(n_experts, d_model, d_ff, T, top_k);
+    TbPlan p{};
+    p.tiled = true;
+    p.ntt = bs.ntt;
+    p.gu_waves = p.dn_waves = kTileWaves;
+    const int G = d_model / group;
+    p.mg = p.ntt == 1 ? 2 : 1;
+    while (G % p.mg) p.mg /= 2;
+    p.ks_gu = std::min(bs.ks_gu, G / p.mg);
+    p.ks_dn = 1;
+    p.gu_blocks = bs.gu_tiles * p.ks_gu;
+    p.dn_blocks = bs.dn_tiles;
+    const int tt = 16 * p.ntt;
+    p.gu_lds = 2 * ((size_t)2 * tt * (p.mg * group + 8) * 2) + (size_t)kTileWaves * p.ntt * 16 * 4;
+    p.dn_lds = 2 * ((size_t)2 * tt * (group + 8) * 2) + 2 * tt * 4;
+    if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
+    *pl = p;
+    return true;
+}
+
+hipError_t launch_routed(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    return a.scale_bytes == 2 ? launch_routed_fmt<2>(bits, pl, a, st) : launch_routed_fmt<4>(bits, pl, a, st);
 }
 
 hipError_t launch_batch(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)

@@ -148,6 +148,39 @@ BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int 
     return w;
 }
 
+// Workspace layout of the routed path, every piece 256-byte aligned:
+//   xh, xl, xe                     as the token batch, [T] tokens
+//   hh, hl  f16 [n_experts][T][d_ff] hidden rows by position in the expert's slot list
+//   hf      f32 [n_experts][d_ff/32][Tp] their factors (slot weight * 2^e)
+//   pg      f32                      partial sums of the gate_up K splits
+//   list    i32 [n_experts][T]       each expert's slots, ascending; cnt i32 [n_experts]
+//   ok      i32 [T*top_k]            slot processed
+//   ys      f32 [T*top_k][d_model]   weighted output row of each slot
+// Everything is rewritten by each call before it is read.
+struct RoutedWorkspace {
+    size_t xh, xl, xe, hh, hl, hf, pg, list, cnt, ok, ys, total;
+};
+
+RoutedWorkspace routed_workspace(int n_experts, int d_model, int d_ff, int T, int top_k)
+{
+    RoutedWorkspace w;
+    const size_t nx = (size_t)T * d_model, nh = (size_t)n_experts * T * d_ff, ns = (size_t)T * top_k;
+    const smoe::BatchSplits bs = smoe::routed_splits(n_experts, d_model, d_ff, T, top_k);
+    w.xh = 0;
+    w.xl = w.xh + align256(nx * 2);
+    w.xe = w.xl + align256(nx * 2);
+    w.hh = w.xe + align256((size_t)T * 4);
+    w.hl = w.hh + align256(nh * 2);
+    w.hf = w.hl + align256(nh * 2);
+    w.pg = w.hf + align256((size_t)n_experts * (d_ff / 32) * token_pad(T) * 4);
+    w.list = w.pg + align256(bs.gu_part_floats * 4);
+    w.cnt = w.list + align256((size_t)n_experts * T * 4);
+    w.ok = w.cnt + align256((size_t)n_experts * 4);
+    w.ys = w.ok + align256(ns * 4);
+    w.total = w.ys + align256(ns * d_model * 4);
+    return w;
+}
+
 // The smallest group the token-batch layout can need (32 columns) gives the
 // largest exponent arrays; the workspace size does not depend on the group.
 constexpr int kMinBatchGroup = 32;
@@ -349,6 +382,84 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     a.n_experts = n_experts;
     if ((rc = launch_status(smoe::launch_gate_up(f.bits, plan, a, dev.cus, st)))) return rc;
     return launch_status(smoe::launch_down(f.bits, plan, a, dev.cus, st));
+}
+
+size_t smoe_routed_ffn_workspace(int n_experts, int d_model, int d_ff, int T, int top_k)
+{
+    if (n_experts <= 0 || d_model <= 0 || d_ff <= 0 || T <= 0 || T > SMOE_MAX_TOKENS || top_k <= 0) return 0;
+    return routed_workspace(n_experts, d_model, d_ff, T, top_k).total;
+}
+
+int smoe_routed_ffn(const smoe_expert *experts, int n_experts, int fmt, int group, int d_model, int d_ff,
+                    int T, int top_k, const int *expert_ids, const float *expert_w, const float *x, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    Fmt f;
+    int rc = check_format(fmt, group, &f);
+    if (rc) return rc;
+    if (!experts || !expert_ids || !expert_w || !x || !out) return SMOE_ERR_NULL;
+    if (n_experts < 1 || n_experts > SMOE_MAX_EXPERTS || T < 1 || T > SMOE_MAX_TOKENS || top_k < 1 ||
+        top_k > SMOE_MAX_EXPERTS)
+        return SMOE_ERR_SHAPE;
+    for (int e = 0; e < n_experts; ++e) {
+        if ((rc = check_qmat(&experts[e].gate, f, group, d_ff, d_model))) return rc;
+        if ((rc = check_qmat(&experts[e].up, f, group, d_ff, d_model))) return rc;
+        if ((rc = check_qmat(&experts[e].down, f, group, d_model, d_ff))) return rc;
+    }
+    if (!aligned(x, 16) || !aligned(out, 4) || !aligned(expert_ids, 4) || !aligned(expert_w, 4))
+        return SMOE_ERR_ALIGN;
+    smoe::TbPlan plan{};
+    if (!smoe::plan_routed(f.bits, group, d_model, d_ff, n_experts, T, top_k, &plan)) return SMOE_ERR_GROUP;
+    const size_t need = smoe_routed_ffn_workspace(n_experts, d_model, d_ff, T, top_k);
+    if (!workspace || workspace_bytes < need) return SMOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SMOE_ERR_ALIGN;
+    const size_t no = (size_t)T * d_model * 4, nx = no, ns = (size_t)T * top_k * 4;
+    if (overlap(out, no, x, nx) || overlap(out, no, workspace, need) || overlap(out, no, expert_ids, ns) ||
+        overlap(out, no, expert_w, ns) || overlap(workspace, need, x, nx) ||
+        overlap(workspace, need, expert_ids, ns) || overlap(workspace, need, expert_w, ns))
+        return SMOE_ERR_ALIAS;
+    for (int e = 0; e < n_experts; ++e) {
+        const smoe_expert &ex = experts[e];
+        if (overlaps_qmat(out, no, &ex.gate, f, group, d_ff, d_model) ||
+            overlaps_qmat(out, no, &ex.up, f, group, d_ff, d_model) ||
+            overlaps_qmat(out, no, &ex.down, f, group, d_model, d_ff) ||
+            overlaps_qmat(workspace, need, &ex.gate, f, group, d_ff, d_model) ||
+            overlaps_qmat(workspace, need, &ex.up, f, group, d_ff, d_model) ||
+            overlaps_qmat(workspace, need, &ex.down, f, group, d_model, d_ff))
+            return SMOE_ERR_ALIAS;
+    }
+    DeviceInfo dev;
+    if ((rc = check_device(&dev))) return rc;
+    const RoutedWorkspace w = routed_workspace(n_experts, d_model, d_ff, T, top_k);
+    char *ws = static_cast<char *>(workspace);
+    smoe::TbArgs a{};
+    fill_experts(a, experts, n_experts);
+    a.x = x;
+    a.out = out;
+    a.xh = reinterpret_cast<_Float16 *>(ws + w.xh);
+    a.xl = reinterpret_cast<_Float16 *>(ws + w.xl);
+    a.xe = reinterpret_cast<int *>(ws + w.xe);
+    a.hh = reinterpret_cast<_Float16 *>(ws + w.hh);
+    a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
+    a.hf = reinterpret_cast<float *>(ws + w.hf);
+    a.part_gu = reinterpret_cast<float *>(ws + w.pg);
+    a.list = reinterpret_cast<int *>(ws + w.list);
+    a.cnt = reinterpret_cast<int *>(ws + w.cnt);
+    a.slot_ok = reinterpret_cast<int *>(ws + w.ok);
+    a.ys = reinterpret_cast<float *>(ws + w.ys);
+    a.ids = expert_ids;
+    a.slot_w = expert_w;
+    a.top_k = top_k;
+    a.T = T;
+    a.t_pad = token_pad(T);
+    a.d_model = d_model;
+    a.d_ff = d_ff;
+    a.group = group;
+    a.scale_bytes = f.sb;
+    a.n_experts = n_experts;
+    a.ks_gu = plan.ks_gu;
+    a.ks_dn = 1;
+    return launch_status(smoe::launch_routed(f.bits, plan, a, (hipStream_t)stream));
 }
 
 size_t matvec_bf16_workspace(int rows, int cols)

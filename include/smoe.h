@@ -15,6 +15,8 @@
  *                   one submission as in "Grouped Expert Dispatch").
  *  - matvec_bf16    y = W x with bf16 W and f32 x ("Coalesced Dense Matvec --
  *                   the Same Contract for bf16").
+ *  - smoe_routed_ffn  the routed (top-k) token batch: each token through
+ *                   its own experts only ("Token-Batch Fused FFN").
  *  - matvec_bf16_batch  several independent bf16 matvecs in one launch
  *                   ("Batched Scout Matvec").
  *
@@ -167,6 +169,34 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
 size_t matvec_bf16_workspace(int rows, int cols);
 int matvec_bf16(const uint16_t *W, int rows, int cols, const float *x, float *y,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Routed experts over T tokens ("Token-Batch Fused FFN": per expert, the
+ * tokens that chose it run through it together; the experts' outputs of a
+ * token are combined with its router weights):
+ *   out[t][:] = sum over slots j < top_k, ascending, of
+ *               expert_w[t][j] * down_e( SiLU(gate_e x[t]) * (up_e x[t]) ),
+ *               e = expert_ids[t][j]
+ *   expert_ids : i32 [T][top_k] device array; the ids of one token must be
+ *                distinct (as a top-k selection gives: an expert then takes at
+ *                most T slots); a slot whose id is outside [0, n_experts) adds
+ *                nothing
+ *   expert_w   : f32 [T][top_k] device array
+ *   x, out     : f32 [T][d_model]; out must not overlap any input or the workspace
+ *   workspace  : smoe_routed_ffn_workspace(...) bytes, 256-byte aligned; every
+ *                call rewrites it, nothing in it needs to be zero
+ * 1 <= T <= SMOE_MAX_TOKENS, 1 <= top_k <= SMOE_MAX_EXPERTS.  Only each slot's
+ * expert processes the token: a device pass lists every expert's slots in
+ * ascending order, the gate_up and down passes run per expert over those
+ * lists on the matrix cores, and a last pass adds each token's slots in slot
+ * order (deterministic, no atomics).  Needs group 32 (4-bit) or 64, else
+ * SMOE_ERR_GROUP.  `bits` may carry SMOE_SCALE_F16.
+ */
+size_t smoe_routed_ffn_workspace(int n_experts, int d_model, int d_ff, int T, int top_k);
+int smoe_routed_ffn(const smoe_expert *experts, int n_experts, int bits, int group,
+                    int d_model, int d_ff, int T, int top_k, const int *expert_ids,
+                    const float *expert_w, const float *x, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Several independent bf16 matvecs in one launch ("Batched Scout Matvec":

@@ -61,7 +61,8 @@ def lib():
         L.oracle_expert_ffn.argtypes = [vp, i, vp, i, i, l, l, l, vp, vp]
         L.oracle_matvec_bf16.argtypes = [vp, l, l, vp, vp]
         L.oracle_f16_widen.argtypes = [vp, l, vp]
-        for name in ("oracle_f16_widen", "oracle_unpack", "oracle_dequant", "oracle_qmatvec", "oracle_gate_up",
+        L.oracle_routed_ffn.argtypes = [vp, i, i, i, l, l, l, i, vp, vp, vp, vp]
+        for name in ("oracle_routed_ffn", "oracle_f16_widen", "oracle_unpack", "oracle_dequant", "oracle_qmatvec", "oracle_gate_up",
                      "oracle_down", "oracle_expert_ffn", "oracle_matvec_bf16"):
             getattr(L, name).restype = i
         _lib = L
@@ -176,6 +177,25 @@ def expert_ffn(experts, bits, group, d_model, d_ff, x, route_w=None):
     _ok(lib().oracle_expert_ffn(arr, len(experts), pr, bits, group, d_model, d_ff, T, px,
                                 out.ctypes.data_as(ctypes.c_void_p)), "expert_ffn")
     return out[0] if single else out
+
+
+def routed_ffn(experts, bits, group, d_model, d_ff, x, ids, w):
+    """x f32 [T, d_model]; ids int32 [T, top_k] (expert of each slot); w f32 [T, top_k].
+    Returns f64 [T, d_model]: per token, the router-weighted sum of its slots'
+    expert FFNs (slots with an id outside [0, n_experts) add nothing)."""
+    keep = []
+    arr = (_Expert * len(experts))()
+    for k, e in enumerate(experts):
+        arr[k] = _Expert(_qmat_struct(e.gate, keep), _qmat_struct(e.up, keep),
+                         _qmat_struct(e.down, keep))
+    X, px = _c(np.asarray(x, dtype=np.float32).reshape(-1, d_model), np.float32)
+    T = X.shape[0]
+    I, pi = _c(np.asarray(ids).reshape(T, -1), np.int32)
+    W, pw = _c(np.asarray(w).reshape(T, -1), np.float32)
+    out = np.empty((T, d_model), dtype=np.float64)
+    _ok(lib().oracle_routed_ffn(arr, len(experts), bits, group, d_model, d_ff, T, I.shape[1], pi, pw, px,
+                                out.ctypes.data_as(ctypes.c_void_p)), "routed_ffn")
+    return out
 
 
 def matvec_bf16(W, x):

@@ -163,6 +163,42 @@ out:
     return rc;
 }
 
+/* Routed experts: token t goes through the top_k experts listed for it, each
+ * listed slot being one expert application ("Token-Batch Fused FFN": the
+ * tokens that chose an expert are run through it together; per token, its
+ * experts' outputs are combined with the router weights).
+ *   out[t][:] = sum over slots j < top_k, ascending, of w[t][j] * FFN_{ids[t][j]}(x[t]);
+ * a slot whose id is outside [0, n_experts) adds nothing. */
+int oracle_routed_ffn(const oracle_expert *experts, int n_experts, int bits, int group, long d_model,
+                      long d_ff, long T, int top_k, const int *ids, const float *w, const float *x,
+                      double *out)
+{
+    if (!experts || !ids || !w || !x || !out || n_experts <= 0 || T <= 0 || top_k <= 0) return -1;
+    if (check(bits, group, d_ff, d_model) || check(bits, group, d_model, d_ff)) return -1;
+    double *h = malloc(sizeof(double) * d_ff);
+    double *y = malloc(sizeof(double) * d_model);
+    int rc = -1;
+    if (!h || !y) goto out;
+    for (long t = 0; t < T; ++t) {
+        double *o = out + t * d_model;
+        for (long j = 0; j < d_model; ++j) o[j] = 0.0;
+        for (int s = 0; s < top_k; ++s) {
+            const int e = ids[t * top_k + s];
+            if (e < 0 || e >= n_experts) continue;
+            const oracle_expert *ex = &experts[e];
+            if (oracle_gate_up(&ex->gate, &ex->up, bits, group, d_ff, d_model,
+                               x + t * d_model, h)) goto out;
+            if (oracle_down(&ex->down, bits, group, d_model, d_ff, h, y)) goto out;
+            const double r = (double)w[t * top_k + s];
+            for (long j = 0; j < d_model; ++j) o[j] += r * y[j];
+        }
+    }
+    rc = 0;
+out:
+    free(h); free(y);
+    return rc;
+}
+
 /* IEEE 754 binary16 to double, from the format's definition: sign bit 15,
  * exponent bits 10..14 with bias 15, fraction bits 0..9.  An exponent field of
  * 0 is a subnormal, fraction * 2^-24; 31 is an infinity (fraction 0) or a NaN;

@@ -47,6 +47,13 @@ typedef struct {
     oracle_qmat down;       /* [d_model][d_ff] */
 } oracle_expert;
 
+/* Routed experts, token t, for t in [0, T):
+ *   out[t][:] = sum over slots s < top_k (ascending) of w[t][s] * FFN_{ids[t][s]}(x[t]),
+ * ids and w [T][top_k]; a slot whose id is outside [0, n_experts) adds nothing. */
+int oracle_routed_ffn(const oracle_expert *experts, int n_experts, int bits, int group, long d_model,
+                      long d_ff, long T, int top_k, const int *ids, const float *w, const float *x,
+                      double *out);
+
 /* 2-byte scales: out[i] = the IEEE 754 binary16 value of h[i], widened to f32
  * (exact).  A matrix with 2-byte scales is the matrix whose f32 scales are
  * these values. */

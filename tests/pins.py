@@ -37,6 +37,7 @@ def bind(L):
     L.oracle_expert_ffn.argtypes = [vp, ci, vp, ci, ci, cl, cl, cl, vp, vp]
     L.oracle_matvec_bf16.argtypes = [vp, cl, cl, vp, vp]
     L.oracle_f16_widen.argtypes = [vp, cl, vp]
+    L.oracle_routed_ffn.argtypes = [vp, ci, ci, ci, cl, cl, cl, ci, vp, vp, vp, vp]
     return L
 
 
@@ -328,8 +329,53 @@ def pin_ffn_composition(L, seed=11):
     return fails
 
 
+def routed(L, experts, bits, group, d_model, d_ff, X, ids, w):
+    X = np.ascontiguousarray(X, np.float32).reshape(-1, d_model)
+    T = X.shape[0]
+    ids = np.ascontiguousarray(ids, np.int32).reshape(T, -1)
+    w = np.ascontiguousarray(w, np.float32).reshape(T, -1)
+    out = np.empty((T, d_model), np.float64)
+    arr = expert_struct(experts)
+    assert L.oracle_routed_ffn(arr, len(experts), bits, group, d_model, d_ff, T, ids.shape[1], _p(ids), _p(w),
+                               _p(X), _p(out)) == 0
+    return out
+
+
+def pin_routed(L, seed=13):
+    """Routed experts (each token through its own slots) against the BLAS
+    route, and its special cases: routing every token to every expert in
+    ascending order with weights r is the dense router-weighted FFN (same
+    sums, same order: bitwise); slots with an id outside [0, n) add nothing;
+    a single slot of weight 1 is that expert alone."""
+    fails = []
+    rng = np.random.default_rng(seed)
+    for bits in (4, 2):
+        d_model, d_ff, group, n, T = 128, 192, 64, 4, 3
+        exps = [make_expert(rng, d_model, d_ff, bits, group) for _ in range(n)]
+        X = rng.standard_normal((T, d_model)).astype(np.float32)
+        ids = np.array([[2, 0], [1, 3], [3, 2]], np.int32)
+        w = rng.uniform(0.1, 1.0, size=(T, 2)).astype(np.float32)
+        out = routed(L, exps, bits, group, d_model, d_ff, X, ids, w)
+        for t in range(T):
+            want = sum(float(w[t, s]) * numpy_ffn_one(exps[ids[t, s]], bits, group, X[t]) for s in range(2))
+            err = np.max(np.abs(out[t] - want)) / max(1.0, np.max(np.abs(want)))
+            if err > 1e-12:
+                fails.append(f"Q{bits} token {t}: routed vs BLAS route rel err {err:.3g}")
+        R = rng.uniform(0.1, 1.0, size=(T, n)).astype(np.float32)
+        full = routed(L, exps, bits, group, d_model, d_ff, X, np.tile(np.arange(n, dtype=np.int32), (T, 1)), R)
+        if not np.array_equal(full, ffn(L, exps, bits, group, d_model, d_ff, X, R)):
+            fails.append(f"Q{bits}: full ascending routing differs from the dense FFN")
+        skip = routed(L, exps, bits, group, d_model, d_ff, X, np.c_[ids[:, :1], [[-1], [n], [7]]], np.c_[w[:, :1], w[:, 1:]])
+        if not np.array_equal(skip, routed(L, exps, bits, group, d_model, d_ff, X, ids[:, :1], w[:, :1])):
+            fails.append(f"Q{bits}: out-of-range slots changed the result")
+        one = routed(L, exps, bits, group, d_model, d_ff, X[:1], np.array([[3]], np.int32), np.ones((1, 1), np.float32))
+        if not np.array_equal(one, ffn(L, exps[3:4], bits, group, d_model, d_ff, X[:1], None)):
+            fails.append(f"Q{bits}: a single weight-1 slot is not that expert alone")
+    return fails
+
+
 CORE_PINS = [pin_worked_examples, pin_unpack_exhaustive, pin_affine_identity, pin_silu,
-             pin_bf16, pin_f16, pin_ffn_composition]
+             pin_bf16, pin_f16, pin_ffn_composition, pin_routed]
 
 
 def run_core_pins(L):

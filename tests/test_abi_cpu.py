@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
         "smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
-        "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_status_str"}
+        "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_routed_ffn_workspace",
+        "smoe_routed_ffn", "smoe_status_str"}
 
 
 def test_library_exports_every_declared_symbol(gq):
@@ -109,6 +110,32 @@ def test_scale_format_flag(gq):
     # hidden inside the gate scales: 512 rows x 4 groups x 2 bytes = 4096 bytes of f16 scales
     assert L.smoe_gate_up(ctypes.byref(G), ctypes.byref(U), 4 | F16, 64, 512, 256, x, A + 0x1000000 + 4092, None) == -7
     assert L.smoe_gate_up(ctypes.byref(G), ctypes.byref(U), 4 | F16, 64, 512, 256, x, A + 0x1000000 + 4096, None) == -8
+
+
+def test_routed_ffn_refusals(gq):
+    """smoe_routed_ffn checks its arguments before touching the device."""
+    L = gq.lib()
+    n, T, k, dm, dff = 2, 8, 2, 256, 512
+    arr = (gq.Expert * n)()
+    for e in range(n):
+        b = A + 0x1000000 * (1 + 6 * e)
+        arr[e] = gq.Expert(gq.QMat(b, b + 0x1000000), gq.QMat(b + 0x2000000, b + 0x3000000),
+                           gq.QMat(b + 0x4000000, b + 0x5000000))
+    ids, w, x, out = A + 0x70000000, A + 0x71000000, A + 0x72000000, A + 0x73000000
+    need = L.smoe_routed_ffn_workspace(n, dm, dff, T, k)
+    assert need > 0 and L.smoe_routed_ffn_workspace(n, dm, dff, T, 0) == 0
+    ws = A + 0x40000000
+    call = lambda **o: L.smoe_routed_ffn(arr, o.get("n", n), o.get("bits", 4), o.get("group", 64), dm, dff,
+                                         o.get("T", T), o.get("k", k), o.get("ids", ids), o.get("w", w), x,
+                                         o.get("out", out), ws, o.get("need", need), None)
+    assert call() == -8                       # valid: reaches the device check
+    assert call(ids=None) == -1
+    assert call(k=0) == -4 and call(k=17) == -4 and call(T=0) == -4 and call(n=17) == -4
+    assert call(group=96) == -3               # the routed path tiles groups of 32 and 64 only
+    assert call(w=w + 2) == -5
+    assert call(need=need - 1) == -6
+    assert call(out=ids) == -7                # out overlaps the slot ids
+    assert call(bits=3) == -2
 
 
 def test_bf16_batch_refusals(gq):

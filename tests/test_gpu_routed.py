@@ -1,0 +1,105 @@
+"""GPU parity of the routed (top-k) token batch against the f64 oracle,
+through the C ABI: each token runs only through its slots' experts, and its
+output is the router-weighted sum of those experts' FFNs."""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import assert_parity, dev, dev_experts
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import torch
+    import group_quantized_moe_amd as gq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gq.lib()
+    return gq
+
+
+@pytest.fixture(scope="module")
+def q4_group8():
+    g = workloads.make_group(workloads.Q4_GROUP8)
+    return g, dev_experts(g)
+
+
+def run_routed(gq, de, bits, group, X, ids, w):
+    import torch
+    X = np.asarray(X, np.float32)
+    T, d_model = X.shape
+    d_ff = de[0].gate.codes.shape[0]
+    out = torch.empty(T * d_model, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gq.smoe_routed_ffn_workspace(len(de), d_model, d_ff, T, ids.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    ws.fill_(0xA5)   # nothing in the workspace needs to be zero: fill it with garbage
+    gq.smoe_routed_ffn(de, bits, group, dev(X), dev(np.asarray(ids, np.int32)), dev(np.asarray(w, np.float32)),
+                       out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(T, d_model)
+
+
+def test_routed_prefill_workload(gq, oracle_lib, q4_group8):
+    """256 tokens, top-2 of 8 Q4 experts: sampled tokens against the oracle,
+    and a second call bit for bit equal (deterministic)."""
+    g, de = q4_group8
+    cfg = workloads.ROUTED
+    X, ids, w = workloads.make_routed_inputs(cfg["T"], cfg["top_k"], cfg["seed"])
+    got = run_routed(gq, de, 4, 64, X, ids, w)
+    rows = [0, 1, 63, 64, 127, 200, 255]
+    want = oracle_lib.routed_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X[rows], ids[rows], w[rows])
+    assert_parity(got[rows], want, "routed T=256 top-2")
+    assert np.array_equal(got, run_routed(gq, de, 4, 64, X, ids, w))
+
+
+def test_routed_full_routing_equals_dense(gq, q4_group8):
+    """Every token to every expert with the dense router's weights is the
+    dense token batch (different kernels and order: within the bar)."""
+    g, de = q4_group8
+    X, R = workloads.make_batch_inputs(16)
+    ids = np.tile(np.arange(8, dtype=np.int32), (16, 1))
+    got = run_routed(gq, de, 4, 64, X, ids, R)
+    import torch
+    from gpu_helpers import run_ffn
+    assert_parity(got, run_ffn(gq, de, 4, 64, X, route=R).reshape(16, -1), "routed full vs dense")
+
+
+ROUTED_EDGE = [  # bits, group, d_model, d_ff, n_experts, T, top_k, routing
+    (4, 64, 256, 512, 4, 1, 2, "topk"),
+    (4, 64, 256, 512, 4, 5, 1, "topk"),
+    (4, 32, 96, 160, 3, 33, 2, "topk"),
+    (2, 64, 256, 384, 4, 70, 3, "topk"),
+    (4, 64, 256, 512, 6, 40, 2, "skewed"),      # every token's first slot on expert 0
+    (4, 64, 256, 512, 4, 20, 3, "holes"),       # some slots out of range
+    (4, 64, 8192, 128, 2, 9, 1, "topk"),
+]
+
+
+@pytest.mark.parametrize("bits,group,d_model,d_ff,n,T,k,routing", ROUTED_EDGE, ids=lambda v: str(v))
+def test_routed_edge_shapes(gq, oracle_lib, bits, group, d_model, d_ff, n, T, k, routing):
+    g = workloads.expert_group(700 + d_model + T, n, d_model, d_ff, bits, group)
+    X = workloads.activation_batch(701 + T, T, d_model)
+    ids, w = workloads.top_k_routing(702 + T, T, n, k)
+    if routing == "skewed":
+        ids[:, 0] = 0
+        ids[:, 1] = np.where(ids[:, 1] == 0, 1, ids[:, 1])
+    if routing == "holes":
+        ids[::3, 1] = -1
+        ids[1::4, 2] = n
+    got = run_routed(gq, dev_experts(g), bits, group, X, ids, w)
+    want = oracle_lib.routed_ffn(g.experts, bits, group, d_model, d_ff, X, ids, w)
+    assert_parity(got, want, f"routed Q{bits} g{group} {d_model}x{d_ff} E={n} T={T} k={k} {routing}")
+
+
+def test_routed_f16_scales_and_duplicate_tokens(gq, oracle_lib):
+    """f16 scales on the routed path; equal tokens with equal routing give
+    equal rows."""
+    g = workloads.expert_group(710, 4, 256, 512, 4, 64, scale_f16=True)
+    X = workloads.activation_batch(711, 12, 256)
+    X[7] = X[2]
+    ids, w = workloads.top_k_routing(712, 12, 4, 2)
+    ids[7], w[7] = ids[2], w[2]
+    got = run_routed(gq, dev_experts(g), 4 | gq.SMOE_SCALE_F16, 64, X, ids, w)
+    assert_parity(got, oracle_lib.routed_ffn(g.experts, 4, 64, 256, 512, X, ids, w), "routed f16 scales")
+    assert np.array_equal(got[7], got[2])

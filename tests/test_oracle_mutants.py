@@ -26,6 +26,8 @@ MUTANTS = {
     "f16_subnormal": ("ldexp((double)m, -24)", "ldexp((double)(1024 + m), -25)"),
     "combine_overwrite": ("o[j] += r * y[j]", "o[j] = r * y[j]"),
     "hidden_product": ("hidden[i] = oracle_silu(g[i]) * u[i]", "hidden[i] = oracle_silu(u[i]) * g[i]"),
+    "routed_slot_weight": ("(double)w[t * top_k + s]", "(double)w[t * top_k]"),
+    "routed_slot_index": ("ids[t * top_k + s]", "ids[s * T + t]"),
 }
 
 

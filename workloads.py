@@ -241,6 +241,24 @@ def make_bf16_batch(jobs=BF16_BATCH):
     return Ws, normal_f32(jobs[0][3], (_TAG_BF16_X,), cols)
 
 
+ROUTED = dict(T=256, top_k=2, seed=43)   # routed prefill over Q4_GROUP8's 8 experts
+
+
+def top_k_routing(seed: int, T: int, n_experts: int, top_k: int):
+    """Synthetic top-k routing: per token, N(0,1) f32 logits over the experts;
+    ids = the top_k largest (ties to the lower id), weights = softmax of those
+    logits.  Returns (ids int32 [T, top_k], w f32 [T, top_k])."""
+    logits = normal_f32(seed, (_TAG_ROUTER, 1), T * n_experts).reshape(T, n_experts)
+    ids = np.argsort(-logits, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    return ids, softmax_f32(np.take_along_axis(logits, ids, axis=1))
+
+
+def make_routed_inputs(T: int, top_k: int, seed: int = 43, n_experts: int = 8, d_model: int = 4096):
+    """(X f32 [T, d_model], ids int32 [T, top_k], w f32 [T, top_k])."""
+    ids, w = top_k_routing(seed, T, n_experts, top_k)
+    return activation_batch(seed, T, d_model), ids, w
+
+
 def make_batch_inputs(T: int, seed: int | None = None, d_model: int = 4096):
     """(X f32 [T, d_model], router f32 [T, 8]) for the token-batch workload."""
     seed = BATCH_TOKENS[T] if seed is None else seed
