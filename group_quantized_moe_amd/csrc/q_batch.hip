@@ -204,6 +204,71 @@ __device__ __forceinline__ void buf_load_codes(BufRes r, unsigned voff, unsigned
     }
 }
 
+// Raw bits of scale element idx (f32, or binary16 in the low half), and its
+// value: the widening is kept apart from the load so that a load issued ahead
+// is not waited for where it is issued.
+template <int SB>
+__device__ __forceinline__ unsigned buf_load_scale_bits(BufRes r, unsigned idx)
+{
+    if constexpr (SB == 4)
+        return buf_load4(r, idx * 4u, 0u);
+    else
+        return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2u), 0, 0);
+}
+template <int SB>
+__device__ __forceinline__ float scale_value(unsigned bits)
+{
+    if constexpr (SB == 4)
+        return __uint_as_float(bits);
+    else
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
+}
+
+// Code unit: the 16 bytes of a row that one lane loads at once, spanning
+// kGroups consecutive quantisation groups (two groups of 32 bytes for 4-bit
+// codes in 64-column groups; four groups of 16 bytes otherwise).  A
+// per-group load would read only 16 or 32 bytes of each 128-byte line per
+// instruction, and the cost of these loads goes with the lines an instruction
+// touches.  Lane row q (lanes 16q .. 16q+15) loads bytes 16q .. 16q+15 of the
+// unit; unit_split then exchanges words between lane rows so that each lane
+// holds its column block of every group of the unit.  The column block of
+// lane row q is CodeUnit::cb(q): the identity for four groups, rows 1 and 2
+// swapped for two.
+template <int BITS, int KB>
+struct CodeUnit {
+    static constexpr int kDw = CodeWords<BITS, KB>::kDwords;   // dwords per lane per group
+    static_assert(kDw == 1 || kDw == 2, "code units take 16 or 32 bytes per row and group");
+    static constexpr int kGroups = 4 / kDw;
+    static __device__ __forceinline__ int cb(int q) { return kDw == 2 ? ((q & 1) << 1) | (q >> 1) : q; }
+};
+
+// v_permlane32_swap(x, y) exchanges lanes 32..63 of x with lanes 0..31 of y;
+// v_permlane16_swap(x, y) exchanges the odd 16-lane rows of x with the even
+// rows of y.  Two groups (lane rows 0, 1 hold group 0, rows 2, 3 group 1, in
+// 16-byte halves): swapping dwords 0, 1 of rows 2, 3 with dwords 2, 3 of rows
+// 0, 1 leaves every row with 8 bytes of each group, at byte 8 cb(q) of it.
+// Four groups (row q holds group q): the 32-lane swap and then the 16-lane
+// swap transpose the 4 x 4 dwords, so row q holds dword q of each group.
+template <int BITS, int KB>
+__device__ __forceinline__ void unit_split(uint4 raw, CodeWords<BITS, KB> (&cw)[CodeUnit<BITS, KB>::kGroups])
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(raw.x, raw.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(raw.y, raw.w, false, false);
+    if constexpr (CodeUnit<BITS, KB>::kDw == 2) {
+        cw[0].w[0] = a[0];
+        cw[0].w[1] = b[0];
+        cw[1].w[0] = a[1];
+        cw[1].w[1] = b[1];
+    } else {
+        const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+        const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+        cw[0].w[0] = c[0];
+        cw[1].w[0] = c[1];
+        cw[2].w[0] = d[0];
+        cw[3].w[0] = d[1];
+    }
+}
+
 // -------------------------------------------------------------------------
 // X -> hi/lo halves in sigma order + one exponent per token.  One block of
 // 256 threads per token, one pass: each thread keeps up to 4 chunks of 8
@@ -704,14 +769,14 @@ __device__ __forceinline__ void tile_store(const TileRegs<KB, NTT, MG> &r, const
 }
 
 // A fragments of token tile tt, K-block j of group gi, hi and lo, from an LDS
-// tile.
+// tile, for a lane that owns column block cb of the group.
 template <int KB, int NTT, int MG = 1>
-__device__ __forceinline__ void tile_frags(const uint8_t *tile, int tt, int gi, int j, half8 &h, half8 &l)
+__device__ __forceinline__ void tile_frags(const uint8_t *tile, int tt, int gi, int j, int cb, half8 &h, half8 &l)
 {
     using Sh = TileShape<KB, NTT, MG>;
-    const int lane = threadIdx.x & 63, q = lane >> 4, n = lane & 15;
+    const int n = threadIdx.x & 15;
     const _Float16 *p = reinterpret_cast<const _Float16 *>(tile) + (tt * 16 + n) * Sh::kStride + gi * 32 * KB +
-                        q * 8 * KB + 8 * j;
+                        cb * 8 * KB + 8 * j;
     h = load_half8(p);
     l = load_half8(p + Sh::kTT * Sh::kStride);
 }
@@ -808,11 +873,16 @@ __device__ __forceinline__ void gu_epilogue(const TbArgs &a, const f32x4 (&tot)[
 }
 
 // gate_up, tiled: block (token tile, row block, expert, split).  A step is MG
-// quantisation groups of d_model.
-template <int BITS, int KB, int NTT, int MG, int PF, int SB>
+// quantisation groups of d_model; one loop iteration is 4 / MG steps (four
+// groups), so that the code units and scale quads start at fixed steps of it.
+template <int BITS, int KB, int NTT, int MG, int SB>
 __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 {
     using Sh = TileShape<KB, NTT, MG>;
+    using CU = CodeUnit<BITS, KB>;
+    static_assert(MG == 1 || MG == 2, "a step is one or two groups");
+    constexpr int kG = CU::kGroups;
+    constexpr int U = 4 / MG;   // steps per iteration
     constexpr int TT = 16 * NTT;
     constexpr int group = 32 * KB;
     extern __shared__ __align__(16) unsigned char smem[];   // two tiles, then the epilogue's maxima
@@ -839,13 +909,20 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     const int rows = a.top_k ? a.cnt[e] : T;
     if (t0 >= rows) return;   // whole block, before any barrier
     const int wrow0 = rb * kTileRows + wave * 16;   // this wave's first d_ff row
-    const int s0 = (int)((long)ks * NS / KSG), NSS = (int)((long)(ks + 1) * NS / KSG) - s0;
+    // The split's steps: whole iterations (only the last split may end inside
+    // one); the plan keeps every split non-empty.
+    const int NI = (NS + U - 1) / U;
+    const int s0 = U * (int)((long)ks * NI / KSG);
+    const int NSS = min(U * (int)((long)(ks + 1) * NI / KSG), NS) - s0;
+    const int g0 = s0 * MG;   // the split's first group
 
     // Lane offsets (32-bit: a matrix has at most 8192 x 8192 entries) and
-    // buffer resources; a step moves only the uniform offsets.
+    // buffer resources.
     const unsigned row = (unsigned)min(wrow0 + n, d_ff - 1);
-    const unsigned coff = row * (unsigned)(d_model * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
-    const unsigned soff = row * (unsigned)G * 4u;
+    const unsigned crow = row * (unsigned)(d_model * BITS / 8) + 16u * (unsigned)(q % CU::kDw);
+    const int cq = q / CU::kDw;   // the lane's group within a code unit
+    const unsigned srow = row * (unsigned)G;
+    const int cb = CU::cb(q);
     const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * SB;
     const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
     const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
@@ -854,54 +931,77 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     tile_map<KB, NTT, MG>(tm, wave, (unsigned)d_model * 2u, t0, rows, a.top_k ? a.list + (size_t)e * T : nullptr,
                           a.top_k);
 
-    // Register ring of PF steps: the activation pieces this thread stores into
-    // LDS and the wave's codes and scales, PF - 1 steps ahead of the step being
-    // computed; LDS holds two steps.  The loop is branch-free so that the
-    // compiler's load waits are exact: loads past the split's last step
-    // repeat it, and the steps past the end (at most PF - 1) count with scale 0.
-    struct GuStage {
-        TileRegs<KB, NTT, MG> tr;
-        CodeWords<BITS, KB> cw[2][MG];
-        float sc[2][MG];
+    // Loads, all issued at the start of a step and never waited for there:
+    //  * activation pieces of step s into ring slot s & 1 at the start of step
+    //    s - 2; stored into LDS (buffer s & 1) at the end of step s - 1;
+    //  * the raw code unit and scale quad after the current ones, as soon as
+    //    those have been unpacked at the start of their first step.
+    // The loop is branch-free so that the compiler's load waits are exact:
+    // loads past the split's last step repeat it or clamp to the last group,
+    // and the steps past the end (at most U - 1) count with scale 0.
+    TileRegs<KB, NTT, MG> tr[2];
+    uint4 craw[2];                     // next code unit, gate and up
+    unsigned sraw[2];                  // next scale quad, gate and up
+    CodeWords<BITS, KB> cw[2][kG];     // current code unit
+    float sc[2][4];                    // current scale quad, divided by Z
+    auto load_tile = [&](TileRegs<KB, NTT, MG> &t, int s) {
+        const unsigned g = (unsigned)((s0 + min(s, NSS - 1)) * MG);
+        tile_load<KB, NTT, MG>(t, tm, xhr, xlr, g * (unsigned)group * 2u);
     };
-    GuStage S[PF];
-    auto load_step = [&](GuStage &st, int i) {
-        const unsigned g = (unsigned)((s0 + min(i, NSS - 1)) * MG);
-        tile_load<KB, NTT, MG>(st.tr, tm, xhr, xlr, g * (unsigned)group * 2u);
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int gi = 0; gi < MG; ++gi) {
-                buf_load_codes<BITS, KB>(cr[m], coff, (g + gi) * (unsigned)(group * BITS / 8), st.cw[m][gi]);
-                st.sc[m][gi] = buf_load_scale<SB>(sr[m], soff, g + gi);
-            }
+    auto load_unit = [&](int u) {   // groups g0 + kG u .. of the wave's rows
+        const unsigned off = crow + (unsigned)min(g0 + kG * u + cq, G - 1) * (unsigned)(16 * CU::kDw);
+        craw[0] = buf_load16(cr[0], off, 0u);
+        craw[1] = buf_load16(cr[1], off, 0u);
+    };
+    auto load_quad = [&](int k) {   // lane row q: group g0 + 4 k + q of its row
+        const unsigned idx = srow + (unsigned)min(g0 + 4 * k + q, G - 1);
+        sraw[0] = buf_load_scale_bits<SB>(sr[0], idx);
+        sraw[1] = buf_load_scale_bits<SB>(sr[1], idx);
     };
 
     f32x4 tot[2 * NTT];   // gate token tiles, then up token tiles
 #pragma unroll
     for (int k = 0; k < 2 * NTT; ++k) tot[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-        load_step(S[i], i);
-        __builtin_amdgcn_sched_barrier(0);   // keep the stages' loads in issue order
-    }
-    tile_store<KB, NTT, MG>(S[0].tr, tm, smem);
+    load_unit(0);
+    load_quad(0);
+    load_tile(tr[0], 0);
+    load_tile(tr[1], 1);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads in issue order
+    tile_store<KB, NTT, MG>(tr[0], tm, smem);
     __syncthreads();
-    for (int base = 0; base < NSS; base += PF) {
+    for (int base = 0; base < NSS; base += U) {
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
+        for (int i = 0; i < U; ++i) {
             const int st = base + i;
-            const uint8_t *tile = smem + (size_t)(st & 1) * Sh::kBytes;
+            if ((i * MG) % kG == 0) {   // a code unit starts (fixed per i)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) unit_split<BITS, KB>(craw[m], cw[m]);
+                load_unit((st * MG) / kG + 1);
+            }
+            if (i == 0) {   // a scale quad starts: group j of it from lane row j
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        sc[m][j] = scale_value<SB>((unsigned)__builtin_amdgcn_ds_bpermute(
+                                       (n + 16 * j) * 4, (int)sraw[m])) *
+                                   QFormat<BITS>::kInvZ;
+                load_quad(base * MG / 4 + 1);
+            }
+            load_tile(tr[i & 1], st + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const uint8_t *tile = smem + (size_t)(i & 1) * Sh::kBytes;   // base is even
 #pragma unroll
             for (int gi = 0; gi < MG; ++gi) {
+                const int ug = (i * MG + gi) % kG;   // group within the unit
                 half8 bf[2][KB];
                 float s[2];
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) bf[m][j] = code_frag<BITS, KB>(S[i].cw[m][gi], j);
-                    s[m] = st < NSS ? S[i].sc[m][gi] * QFormat<BITS>::kInvZ : 0.0f;
+                    for (int j = 0; j < KB; ++j) bf[m][j] = code_frag<BITS, KB>(cw[m][ug], j);
+                    s[m] = st < NSS ? sc[m][i * MG + gi] : 0.0f;
                 }
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt) {
@@ -909,7 +1009,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 #pragma unroll
                     for (int j = 0; j < KB; ++j) {
                         half8 h, l;
-                        tile_frags<KB, NTT, MG>(tile, tt, gi, j, h, l);
+                        tile_frags<KB, NTT, MG>(tile, tt, gi, j, cb, h, l);
 #pragma unroll
                         for (int m = 0; m < 2; ++m) {
                             acc[m] = mfma(h, bf[m][j], acc[m]);
@@ -923,8 +1023,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
                             tot[m * NTT + tt][r] = fmaf(s[m], acc[m][r], tot[m * NTT + tt][r]);
                 }
             }
-            tile_store<KB, NTT, MG>(S[(i + 1) % PF].tr, tm, smem + (size_t)((st + 1) & 1) * Sh::kBytes);
-            load_step(S[i], st + PF);
+            tile_store<KB, NTT, MG>(tr[(i + 1) & 1], tm, smem + (size_t)((i + 1) & 1) * Sh::kBytes);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
         }
@@ -1068,7 +1167,7 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
 #pragma unroll
                 for (int j = 0; j < KB; ++j) {
                     half8 h, l;
-                    tile_frags<KB, NTT>(tile, tt, 0, j, h, l);
+                    tile_frags<KB, NTT>(tile, tt, 0, j, q, h, l);
                     acc = mfma(h, bf[j], acc);
                     acc = mfma(l, bf[j], acc);
                 }
@@ -1122,7 +1221,7 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
     hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, kTilePrefetch, SB>), dim3(pl.gu_blocks),
+    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, SB>), dim3(pl.gu_blocks),
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_gu > 1) {
@@ -1214,7 +1313,7 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, kTilePrefetch, SB>), dim3(pl.gu_blocks),
+    hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, SB>), dim3(pl.gu_blocks),
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_gu > 1) {
@@ -1348,7 +1447,8 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     TbPlan p{};
     if (group == 32 || group == 64) {
         // Tiled kernels: 16 * ntt tokens x 128 rows per 8-wave block, K split
-        // over blocks as the workspace allows (at most one split per group).
+        // over blocks as the workspace allows (gate_up: at most one split per
+        // 4-group iteration; down: one per group).
         const BatchSplits bs = batch_splits(n_experts, d_model, d_ff, T);
         p.tiled = true;
         p.ntt = bs.ntt;
@@ -1358,7 +1458,7 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
         const int G = d_model / group;
         p.mg = p.ntt == 1 ? 2 : 1;
         while (G % p.mg) p.mg /= 2;
-        p.ks_gu = std::min(bs.ks_gu, G / p.mg);
+        p.ks_gu = std::min(bs.ks_gu, (G + 3) / 4);   // splits of whole 4-group iterations
         p.ks_dn = std::min(bs.ks_dn, n_experts * (d_ff / group));
         p.gu_blocks = bs.gu_tiles * p.ks_gu;
         p.dn_blocks = bs.dn_tiles * p.ks_dn;
@@ -1438,7 +1538,7 @@ bool plan_routed(int bits, int group, int d_model, int d_ff, int n_experts, int 
     const int G = d_model / group;
     p.mg = p.ntt == 1 ? 2 : 1;
     while (G % p.mg) p.mg /= 2;
-    p.ks_gu = std::min(bs.ks_gu, G / p.mg);
+    p.ks_gu = std::min(bs.ks_gu, (G + 3) / 4);   // splits of whole 4-group iterations
     p.ks_dn = 1;
     p.gu_blocks = bs.gu_tiles * p.ks_gu;
     p.dn_blocks = bs.dn_tiles;
