@@ -685,7 +685,6 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 // (deterministic), then applies the epilogue.
 constexpr int kTileWaves = 8;
 constexpr int kTileRows = 16 * kTileWaves;
-constexpr int kTilePrefetch = 3;   // steps of loads in registers (two in flight)
 
 // The hardware hands consecutive workgroups to the 8 XCDs in turn, and each XCD
 // has its own L2.  This maps the launch index to a logical one so that the
@@ -1075,9 +1074,11 @@ __device__ __forceinline__ void dn_store(const TbArgs &a, const f32x4 (&tot)[NTT
 // down, tiled: block (token tile, row block, split) sums the (expert, group)
 // pairs of its split, all experts together (the router weights are in the
 // hidden factors).
-template <int BITS, int KB, int NTT, int PF, int SB>
+template <int BITS, int KB, int NTT, int SB>
 __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
 {
+    using CU = CodeUnit<BITS, KB>;
+    constexpr int kG = CU::kGroups;
     constexpr int TT = 16 * NTT;
     constexpr int group = 32 * KB;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1103,80 +1104,121 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     if (t0 >= rows) return;                      // whole block, before any barrier
     const int wrow0 = rb * kTileRows + wave * 16;
     const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
-    const unsigned coff = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
-    const unsigned soff = row * (unsigned)Gd * 4u;
+    const unsigned crow = row * (unsigned)(d_ff * BITS / 8) + 16u * (unsigned)(q % CU::kDw);
+    const int cq = q / CU::kDw;
+    const unsigned srow = row * (unsigned)Gd;
+    const int cb = CU::cb(q);
     const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * SB;
     const size_t hbytes = (size_t)T * d_ff * 2;   // one expert's hidden half
     const BufRes fr_res = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
     TileMap<KB, NTT> tm;
     tile_map<KB, NTT>(tm, wave, (unsigned)d_ff * 2u, t0, rows);
-    // The (expert, group) pairs of this block: its split of all of them, or in
-    // routed mode the groups of its expert.
-    const int P = E * Gd;
-    const int p0 = a.top_k ? ks * Gd : (int)((long)ks * P / KSD);
-    const int NP = a.top_k ? Gd : (int)((long)(ks + 1) * P / KSD) - p0;
+    // The block's K range, in iterations of 4 groups of one expert (IPE per
+    // expert; a group index past Gd is a dead step): its split of all the
+    // experts' iterations, or in routed mode those of its expert.  Step s of
+    // the block is group 4 (it % IPE) + s % 4 of expert it / IPE, it = it0 + s / 4.
+    const int IPE = (Gd + 3) / 4;
+    const int it0 = a.top_k ? ks * IPE : (int)((long)ks * (E * IPE) / KSD);
+    const int NSS = 4 * ((a.top_k ? it0 + IPE : (int)((long)(ks + 1) * (E * IPE) / KSD)) - it0);
     const unsigned flane = (unsigned)(lane & (TT - 1));   // a token of the tile (repeats for TT < 64)
+    struct Pos {
+        int e, g;   // expert, first group of an iteration
+    };
+    auto iter_pos = [&](int it) -> Pos {   // iteration it of the block (clamped to its last)
+        const int ia = it0 + min(it, NSS / 4 - 1);
+        const int e = ia / IPE;
+        return {e, 4 * (ia - e * IPE)};
+    };
 
     f32x4 tot[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) tot[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Register ring of PF steps (hidden tile pieces, the tile's factors, the
-    // wave's codes and scale), branch-free as in gate_up.
-    struct DnStage {
-        TileRegs<KB, NTT> tr;
-        CodeWords<BITS, KB> cw;
-        float fr, sc;
-    };
-    DnStage S[PF];
-    auto load_step = [&](DnStage &st, int i) {
-        const int p = p0 + min(i, NP - 1);
-        const int e = p / Gd, g = p - e * Gd;
-        const size_t ho = (size_t)e * T * d_ff;
-        tile_load<KB, NTT>(st.tr, tm, buf_res(a.hh + ho, hbytes), buf_res(a.hl + ho, hbytes),
+    // Loads and rings as in gate_up: hidden pieces and the tile's factors of
+    // step s in slot s & 1 (issued at the start of step s - 2, stored to LDS at
+    // the end of step s - 1); the next code unit and scale quad once the
+    // current ones are unpacked.  Loads past the range repeat its last
+    // iteration; dead steps clamp to the expert's last group; both count with
+    // scale 0.
+    TileRegs<KB, NTT> tr[2];
+    float frr[2];
+    uint4 craw;
+    unsigned sraw;
+    CodeWords<BITS, KB> cw[kG];
+    float sc[4];
+    auto load_tile = [&](int slot, Pos ps, int r) {   // group ps.g + r of expert ps.e
+        const int g = min(ps.g + r, Gd - 1);
+        const size_t ho = (size_t)ps.e * T * d_ff;
+        tile_load<KB, NTT>(tr[slot], tm, buf_res(a.hh + ho, hbytes), buf_res(a.hl + ho, hbytes),
                            (unsigned)g * (unsigned)group * 2u);
-        st.fr = __uint_as_float(buf_load4(fr_res, flane * 4u, (unsigned)(((size_t)e * Gd + g) * a.t_pad + t0) * 4u));
-        buf_load_codes<BITS, KB>(buf_res(a.down[e].codes, cbytes), coff, (unsigned)g * (unsigned)(group * BITS / 8),
-                                 st.cw);
-        st.sc = buf_load_scale<SB>(buf_res(a.down[e].scales, sbytes), soff, (unsigned)g);
+        frr[slot] = __uint_as_float(
+            buf_load4(fr_res, flane * 4u, (unsigned)(((size_t)ps.e * Gd + g) * a.t_pad + t0) * 4u));
     };
-    auto store_step = [&](const DnStage &st, int buf) {
-        tile_store<KB, NTT>(st.tr, tm, smem + (size_t)buf * tb_bytes);
-        fac[buf * TT + flane] = st.fr;
+    auto load_unit = [&](Pos ps, int r) {   // the unit whose first group is ps.g + r
+        const unsigned off = crow + (unsigned)min(ps.g + r + cq, Gd - 1) * (unsigned)(16 * CU::kDw);
+        craw = buf_load16(buf_res(a.down[ps.e].codes, cbytes), off, 0u);
     };
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-        load_step(S[i], i);
-        __builtin_amdgcn_sched_barrier(0);
+    auto load_quad = [&](Pos ps) {
+        sraw = buf_load_scale_bits<SB>(buf_res(a.down[ps.e].scales, sbytes), srow + (unsigned)min(ps.g + q, Gd - 1));
+    };
+    auto store_tile = [&](int slot) {
+        tile_store<KB, NTT>(tr[slot], tm, smem + (size_t)slot * tb_bytes);
+        fac[slot * TT + flane] = frr[slot];
+    };
+
+    {
+        const Pos p0 = iter_pos(0);
+        load_unit(p0, 0);
+        load_quad(p0);
+        load_tile(0, p0, 0);
+        load_tile(1, p0, 1);
     }
-    store_step(S[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile(0);
     __syncthreads();
-    for (int base = 0; base < NP; base += PF) {
+    for (int base = 0; base < NSS; base += 4) {
+        const Pos cur = iter_pos(base / 4), nxt = iter_pos(base / 4 + 1);
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int st = base + i;
-            const int buf = st & 1;
-            const uint8_t *tile = smem + (size_t)buf * tb_bytes;
+        for (int i = 0; i < 4; ++i) {
+            if (i % kG == 0) {   // a code unit starts; load the next one
+                unit_split<BITS, KB>(craw, cw);
+                if (i + kG < 4)
+                    load_unit(cur, i + kG);
+                else
+                    load_unit(nxt, 0);
+            }
+            if (i == 0) {   // a scale quad starts: group j of it from lane row j
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sc[j] = scale_value<SB>((unsigned)__builtin_amdgcn_ds_bpermute((n + 16 * j) * 4, (int)sraw)) *
+                            QFormat<BITS>::kInvZ;
+                load_quad(nxt);
+            }
+            if (i + 2 < 4)
+                load_tile(i & 1, cur, i + 2);
+            else
+                load_tile(i & 1, nxt, i - 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const uint8_t *tile = smem + (size_t)(i & 1) * tb_bytes;
             half8 bf[KB];
 #pragma unroll
-            for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw, j);
-            const float s = st < NP ? S[i].sc * QFormat<BITS>::kInvZ : 0.0f;
+            for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(cw[i % kG], j);
+            const float s = cur.g + i < Gd ? sc[i] : 0.0f;
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < KB; ++j) {
                     half8 h, l;
-                    tile_frags<KB, NTT>(tile, tt, 0, j, q, h, l);
+                    tile_frags<KB, NTT>(tile, tt, 0, j, cb, h, l);
                     acc = mfma(h, bf[j], acc);
                     acc = mfma(l, bf[j], acc);
                 }
-                const f32x4 f = *reinterpret_cast<const f32x4 *>(fac + buf * TT + tt * 16 + 4 * q);
+                const f32x4 f = *reinterpret_cast<const f32x4 *>(fac + (i & 1) * TT + tt * 16 + 4 * q);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) tot[tt][r] = fmaf(s * f[r], acc[r], tot[tt][r]);
             }
-            store_step(S[(i + 1) % PF], buf ^ 1);
-            load_step(S[i], st + PF);
+            store_tile((i + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
         }
@@ -1229,7 +1271,7 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
                            (size_t)kTileWaves * NTT * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, kTilePrefetch, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
+    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
                        pl.dn_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_dn > 1) {
@@ -1321,7 +1363,7 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
                            (size_t)kTileWaves * NTT * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, kTilePrefetch, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
+    hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
                        pl.dn_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_route_combine, dim3((unsigned)a.T, (unsigned)((a.d_model + 1023) / 1024)), dim3(256), 0, st,
@@ -1447,8 +1489,8 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     TbPlan p{};
     if (group == 32 || group == 64) {
         // Tiled kernels: 16 * ntt tokens x 128 rows per 8-wave block, K split
-        // over blocks as the workspace allows (gate_up: at most one split per
-        // 4-group iteration; down: one per group).
+        // over blocks as the workspace allows (at most one split per 4-group
+        // iteration).
         const BatchSplits bs = batch_splits(n_experts, d_model, d_ff, T);
         p.tiled = true;
         p.ntt = bs.ntt;
@@ -1459,7 +1501,7 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
         p.mg = p.ntt == 1 ? 2 : 1;
         while (G % p.mg) p.mg /= 2;
         p.ks_gu = std::min(bs.ks_gu, (G + 3) / 4);   // splits of whole 4-group iterations
-        p.ks_dn = std::min(bs.ks_dn, n_experts * (d_ff / group));
+        p.ks_dn = std::min(bs.ks_dn, n_experts * ((d_ff / group + 3) / 4));
         p.gu_blocks = bs.gu_tiles * p.ks_gu;
         p.dn_blocks = bs.dn_tiles * p.ks_dn;
         const int tt = 16 * p.ntt;
