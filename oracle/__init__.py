@@ -62,8 +62,14 @@ def lib():
         L.oracle_matvec_bf16.argtypes = [vp, l, l, vp, vp]
         L.oracle_f16_widen.argtypes = [vp, l, vp]
         L.oracle_routed_ffn.argtypes = [vp, i, i, i, l, l, l, i, vp, vp, vp, vp]
+        d = ctypes.c_double
+        L.oracle_head_rmsnorm.argtypes = [vp, l, l, vp, d, vp]
+        L.oracle_rope.argtypes = [vp, l, l, l, d]
+        L.oracle_gqa_attend.argtypes = [vp, l, l, l, vp, vp, l, l, vp]
+        L.oracle_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, l, l, l, l, vp, l, d, vp, vp, l, vp, vp, vp]
         for name in ("oracle_routed_ffn", "oracle_f16_widen", "oracle_unpack", "oracle_dequant", "oracle_qmatvec", "oracle_gate_up",
-                     "oracle_down", "oracle_expert_ffn", "oracle_matvec_bf16"):
+                     "oracle_down", "oracle_expert_ffn", "oracle_matvec_bf16", "oracle_head_rmsnorm", "oracle_rope",
+                     "oracle_gqa_attend", "oracle_attn_decode"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -206,3 +212,72 @@ def matvec_bf16(W, x):
     _ok(lib().oracle_matvec_bf16(pw, rows, cols, px, y.ctypes.data_as(ctypes.c_void_p)),
         "matvec_bf16")
     return y
+
+
+# ---------------------------------------------------------------------------
+# Decode attention block (Metal Compute Kernels page of the S-MoE docs,
+# section "GPU-Resident Decode Attention").
+
+def head_rmsnorm(x, w, eps=1e-6):
+    """x: [n_heads, hd]; w: f32 [hd].  y[h] = x[h] / sqrt(mean(x[h]^2) + eps) * w."""
+    X, px = _c(np.asarray(x, dtype=np.float64), np.float64)
+    n_heads, hd = X.shape
+    W, pw = _c(w, np.float32)
+    y = np.empty_like(X)
+    _ok(lib().oracle_head_rmsnorm(px, n_heads, hd, pw, eps, y.ctypes.data_as(ctypes.c_void_p)), "head_rmsnorm")
+    return y
+
+
+def rope(x, pos, base):
+    """x: [n_heads, hd]; returns a rotated copy (pair (i, i + hd/2), angle pos * base^(-2i/hd))."""
+    X = np.array(x, dtype=np.float64, order="C", copy=True)
+    n_heads, hd = X.shape
+    _ok(lib().oracle_rope(X.ctypes.data_as(ctypes.c_void_p), n_heads, hd, pos, base), "rope")
+    return X
+
+
+def gqa_attend(q, K, V, n_ctx):
+    """q: [n_head, hd]; K, V: f32 [n_kv, ctx_stride, hd].  Returns att f64 [n_head, hd]."""
+    Q, pq = _c(np.asarray(q, dtype=np.float64), np.float64)
+    n_head, hd = Q.shape
+    Kc, pk = _c(K, np.float32)
+    Vc, pv = _c(V, np.float32)
+    n_kv, stride, _ = Kc.shape
+    att = np.empty((n_head, hd), dtype=np.float64)
+    _ok(lib().oracle_gqa_attend(pq, n_head, n_kv, hd, pk, pv, stride, n_ctx, att.ctypes.data_as(ctypes.c_void_p)),
+        "gqa_attend")
+    return att
+
+
+def attn_decode(w, x, pos, rope_base, k_cache, v_cache):
+    """One token of the decode attention block.
+
+    w: object with wq, wk, wv, wo (uint16 bf16 patterns) and q_norm, k_norm (f32);
+    x f32 [d_model]; k_cache, v_cache f32 [n_kv, ctx_stride, hd] (not modified:
+    the oracle works on copies).  Returns (out f64 [d_model], q_rot f64
+    [n_head, hd], att f64 [n_head, hd], k_cache', v_cache') where the primed
+    caches are copies with row pos written."""
+    keep = []
+    def arr(a, dt):
+        A, p = _c(a, dt)
+        keep.append(A)
+        return A, p
+    Kc = np.array(k_cache, dtype=np.float32, order="C", copy=True)
+    Vc = np.array(v_cache, dtype=np.float32, order="C", copy=True)
+    n_kv, stride, hd = Kc.shape
+    Wq, pq = arr(w.wq, np.uint16)
+    _, pk = arr(w.wk, np.uint16)
+    _, pv = arr(w.wv, np.uint16)
+    Wo, po = arr(w.wo, np.uint16)
+    _, pqn = arr(w.q_norm, np.float32)
+    _, pkn = arr(w.k_norm, np.float32)
+    X, px = arr(x, np.float32)
+    d_model = X.shape[0]
+    n_head = Wq.shape[0] // hd
+    out = np.empty(d_model, dtype=np.float64)
+    q_rot = np.empty((n_head, hd), dtype=np.float64)
+    att = np.empty((n_head, hd), dtype=np.float64)
+    vpp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _ok(lib().oracle_attn_decode(pq, pk, pv, po, pqn, pkn, d_model, n_head, n_kv, hd, px, pos, float(rope_base),
+                                 vpp(Kc), vpp(Vc), stride, vpp(out), vpp(q_rot), vpp(att)), "attn_decode")
+    return out, q_rot, att, Kc, Vc

@@ -247,3 +247,149 @@ int oracle_matvec_bf16(const uint16_t *W, long rows, long cols, const float *x, 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Decode attention block (S-MoE docs, Metal Compute Kernels page, section
+ * "GPU-Resident Decode Attention": the Q/K/V projections, a per-head QK RMS
+ * norm with 1e-6 added to the mean of squares, RoPE, K/V appended to the KV
+ * cache, causal GQA attention for the new token, and the output projection).
+ * ------------------------------------------------------------------------ */
+
+/* y[h][d] = x[h][d] / sqrt(mean over d of x[h][d]^2 + eps) * w[d], each of
+ * n_heads rows of hd values on its own.  The gain w (one per dimension,
+ * shared by the heads) is the usual learned gain of an RMS norm; the page
+ * names the norm and its 1e-6 only. */
+int oracle_head_rmsnorm(const double *x, long n_heads, long hd, const float *w, double eps, double *y)
+{
+    if (!x || !w || !y || n_heads <= 0 || hd <= 0) return -1;
+    for (long h = 0; h < n_heads; ++h) {
+        const double *xh = x + h * hd;
+        double ss = 0.0;
+        for (long d = 0; d < hd; ++d) ss += xh[d] * xh[d];
+        const double inv = 1.0 / sqrt(ss / (double)hd + eps);
+        for (long d = 0; d < hd; ++d) y[h * hd + d] = xh[d] * inv * (double)w[d];
+    }
+    return 0;
+}
+
+/* Rotary position embedding at position pos, in place, each head on its
+ * own: for i < hd/2 the pair (a, b) = (x[i], x[i + hd/2]) turns by the angle
+ * pos * base^(-2i/hd), giving (a cos - b sin, a sin + b cos).  The page names
+ * RoPE only; the half-split pairing and these frequencies are the rotary
+ * embedding of the model family the page runs, taken as the reading. */
+int oracle_rope(double *x, long n_heads, long hd, long pos, double base)
+{
+    if (!x || n_heads <= 0 || hd <= 0 || hd % 2 || pos < 0 || !(base > 0.0)) return -1;
+    const long half = hd / 2;
+    for (long h = 0; h < n_heads; ++h) {
+        double *xh = x + h * hd;
+        for (long i = 0; i < half; ++i) {
+            const double ang = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
+            const double cs = cos(ang), sn = sin(ang);
+            const double a = xh[i], b = xh[i + half];
+            xh[i] = a * cs - b * sn;
+            xh[i + half] = a * sn + b * cs;
+        }
+    }
+    return 0;
+}
+
+/* Attention of one query per head over cached positions 0 .. n_ctx-1 (the
+ * causal window of the newest token), grouped-query: head h reads KV head
+ * h / (n_head / n_kv).
+ *   s_j = (q_h . K[g][j]) / sqrt(hd),  p = softmax(s),  att[h] = sum_j p_j V[g][j].
+ * The softmax is evaluated as exp(s_j - max s) / sum_k exp(s_k - max s).
+ * K, V: f32 [n_kv][ctx_stride][hd]. */
+int oracle_gqa_attend(const double *q, long n_head, long n_kv, long hd, const float *K, const float *V,
+                      long ctx_stride, long n_ctx, double *att)
+{
+    if (!q || !K || !V || !att || n_head <= 0 || n_kv <= 0 || n_head % n_kv || hd <= 0 || n_ctx <= 0 ||
+        n_ctx > ctx_stride)
+        return -1;
+    double *s = malloc(sizeof(double) * (size_t)n_ctx);
+    if (!s) return -1;
+    for (long h = 0; h < n_head; ++h) {
+        const long g = h / (n_head / n_kv);
+        const float *Kg = K + g * ctx_stride * hd, *Vg = V + g * ctx_stride * hd;
+        double mx = -INFINITY;
+        for (long j = 0; j < n_ctx; ++j) {
+            double dot = 0.0;
+            for (long d = 0; d < hd; ++d) dot += q[h * hd + d] * (double)Kg[j * hd + d];
+            s[j] = dot / sqrt((double)hd);
+            if (s[j] > mx) mx = s[j];
+        }
+        double den = 0.0;
+        for (long j = 0; j < n_ctx; ++j) {
+            s[j] = exp(s[j] - mx);
+            den += s[j];
+        }
+        for (long d = 0; d < hd; ++d) {
+            double acc = 0.0;
+            for (long j = 0; j < n_ctx; ++j) acc += s[j] * (double)Vg[j * hd + d];
+            att[h * hd + d] = acc / den;
+        }
+    }
+    free(s);
+    return 0;
+}
+
+/* y = W x for bf16 W and an f64 x. */
+static void matvec_bf16_f64(const uint16_t *W, long rows, long cols, const double *x, double *y)
+{
+    for (long r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (long j = 0; j < cols; ++j) acc += bf16_value(W[r * cols + j]) * x[j];
+        y[r] = acc;
+    }
+}
+
+/* The block for one token at position pos:
+ *   q = Wq x, k = Wk x, v = Wv x                   (bf16 weights, f32 x)
+ *   q, k: per-head RMS norm (eps 1e-6; gains q_norm, k_norm), then RoPE at pos
+ *   K[g][pos] = f32(k_g), V[g][pos] = f32(v_g)      (the cache holds f32)
+ *   att = GQA attention over positions 0 .. pos
+ *   out = Wo att
+ * Wq [n_head*hd][d_model], Wk and Wv [n_kv*hd][d_model], Wo [d_model][n_head*hd].
+ * The caches are read at positions < pos and written at pos; nothing else in
+ * them changes.  q_rot and att_out (may be NULL) receive the rotated queries
+ * and the attention output, [n_head*hd] each. */
+int oracle_attn_decode(const uint16_t *wq, const uint16_t *wk, const uint16_t *wv, const uint16_t *wo,
+                       const float *q_norm, const float *k_norm, long d_model, long n_head, long n_kv,
+                       long hd, const float *x, long pos, double rope_base, float *k_cache, float *v_cache,
+                       long ctx_stride, double *out, double *q_rot, double *att_out)
+{
+    if (!wq || !wk || !wv || !wo || !q_norm || !k_norm || !x || !k_cache || !v_cache || !out ||
+        d_model <= 0 || n_head <= 0 || n_kv <= 0 || n_head % n_kv || hd <= 0 || hd % 2 || pos < 0 ||
+        pos >= ctx_stride)
+        return -1;
+    const long nq = n_head * hd, nk = n_kv * hd;
+    double *q = malloc(sizeof(double) * (size_t)nq), *k = malloc(sizeof(double) * (size_t)nk);
+    double *v = malloc(sizeof(double) * (size_t)nk), *qn = malloc(sizeof(double) * (size_t)nq);
+    double *kn = malloc(sizeof(double) * (size_t)nk), *att = malloc(sizeof(double) * (size_t)nq);
+    int rc = -1;
+    if (!q || !k || !v || !qn || !kn || !att) goto done;
+    if (oracle_matvec_bf16(wq, nq, d_model, x, q) || oracle_matvec_bf16(wk, nk, d_model, x, k) ||
+        oracle_matvec_bf16(wv, nk, d_model, x, v))
+        goto done;
+    if (oracle_head_rmsnorm(q, n_head, hd, q_norm, 1e-6, qn) || oracle_head_rmsnorm(k, n_kv, hd, k_norm, 1e-6, kn))
+        goto done;
+    if (oracle_rope(qn, n_head, hd, pos, rope_base) || oracle_rope(kn, n_kv, hd, pos, rope_base)) goto done;
+    for (long g = 0; g < n_kv; ++g)
+        for (long d = 0; d < hd; ++d) {
+            k_cache[(g * ctx_stride + pos) * hd + d] = (float)kn[g * hd + d];
+            v_cache[(g * ctx_stride + pos) * hd + d] = (float)v[g * hd + d];
+        }
+    if (oracle_gqa_attend(qn, n_head, n_kv, hd, k_cache, v_cache, ctx_stride, pos + 1, att)) goto done;
+    matvec_bf16_f64(wo, d_model, nq, att, out);
+    if (q_rot) memcpy(q_rot, qn, sizeof(double) * (size_t)nq);
+    if (att_out) memcpy(att_out, att, sizeof(double) * (size_t)nq);
+    rc = 0;
+done:
+    free(q);
+    free(k);
+    free(v);
+    free(qn);
+    free(kn);
+    free(att);
+    return rc;
+}

@@ -1,6 +1,6 @@
 /*
- * oracle.h -- plain f64 CPU oracle for the group-quantised expert FFN and the
- * bf16 dense matvec.
+ * oracle.h -- plain f64 CPU oracle for the group-quantised expert FFN, the
+ * bf16 dense matvec and the decode attention block.
  *
  * TEST INFRASTRUCTURE ONLY.  This library exists to check the GPU library
  * against.  Only the test suite, the smoke check and the benchmark's CPU
@@ -93,6 +93,28 @@ int oracle_expert_ffn(const oracle_expert *experts, int n_experts, const float *
 /* y[r] = sum_j bf16_to_f32(W[r][j]) * x[j], j ascending, f64 accumulator.
  * W holds raw bf16 bit patterns. */
 int oracle_matvec_bf16(const uint16_t *W, long rows, long cols, const float *x, double *y);
+
+/* Decode attention (section "GPU-Resident Decode Attention").
+ * Per-head RMS norm: y[h][d] = x[h][d] / sqrt(mean_d x[h][d]^2 + eps) * w[d]. */
+int oracle_head_rmsnorm(const double *x, long n_heads, long hd, const float *w, double eps, double *y);
+
+/* RoPE at position pos, in place: pair (x[i], x[i + hd/2]), i < hd/2, turns by
+ * pos * base^(-2i/hd):  (a, b) -> (a cos - b sin, a sin + b cos). */
+int oracle_rope(double *x, long n_heads, long hd, long pos, double base);
+
+/* att[h] = sum_j softmax_j((q_h . K[g][j]) / sqrt(hd)) V[g][j] over j < n_ctx,
+ * g = h / (n_head / n_kv); K, V f32 [n_kv][ctx_stride][hd]. */
+int oracle_gqa_attend(const double *q, long n_head, long n_kv, long hd, const float *K, const float *V,
+                      long ctx_stride, long n_ctx, double *att);
+
+/* The decode attention block of one token at position pos: q/k/v projections
+ * (bf16), per-head RMS norm (eps 1e-6, gains q_norm and k_norm) and RoPE of q
+ * and k, K/V rows appended to the f32 caches at pos, GQA attention over
+ * positions 0..pos, out = Wo att.  q_rot and att_out may be NULL. */
+int oracle_attn_decode(const uint16_t *wq, const uint16_t *wk, const uint16_t *wv, const uint16_t *wo,
+                       const float *q_norm, const float *k_norm, long d_model, long n_head, long n_kv,
+                       long hd, const float *x, long pos, double rope_base, float *k_cache, float *v_cache,
+                       long ctx_stride, double *out, double *q_rot, double *att_out);
 
 #ifdef __cplusplus
 }

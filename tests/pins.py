@@ -10,7 +10,8 @@ deliberately broken copies of the oracle (see ``test_oracle_mutants.py``).
 Sources: Metal Compute Kernels (S-MoE docs), sections "Fused FFN Kernels --
 One Simdgroup Per Output Row" (affine codes, Z, group scales, SiLU(gate)*up,
 down projection), "Layout assumptions the kernels rely on" (group and chunk
-contract) and "Coalesced Dense Matvec -- the Same Contract for bf16".
+contract), "Coalesced Dense Matvec -- the Same Contract for bf16" and
+"GPU-Resident Decode Attention" (QK RMS norm, RoPE, KV append, GQA attention).
 """
 from __future__ import annotations
 
@@ -38,6 +39,11 @@ def bind(L):
     L.oracle_matvec_bf16.argtypes = [vp, cl, cl, vp, vp]
     L.oracle_f16_widen.argtypes = [vp, cl, vp]
     L.oracle_routed_ffn.argtypes = [vp, ci, ci, ci, cl, cl, cl, ci, vp, vp, vp, vp]
+    cd = ctypes.c_double
+    L.oracle_head_rmsnorm.argtypes = [vp, cl, cl, vp, cd, vp]
+    L.oracle_rope.argtypes = [vp, cl, cl, cl, cd]
+    L.oracle_gqa_attend.argtypes = [vp, cl, cl, cl, vp, vp, cl, cl, vp]
+    L.oracle_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, cl, cl, cl, cl, vp, cl, cd, vp, vp, cl, vp, vp, vp]
     return L
 
 
@@ -374,12 +380,220 @@ def pin_routed(L, seed=13):
     return fails
 
 
+# ---------------------------------------------------------------------------
+# Decode attention block (section "GPU-Resident Decode Attention": per-head
+# QK RMS norm with 1e-6 under the root, RoPE, K/V appended to the cache,
+# causal GQA attention, output projection).
+
+def _rmsnorm(L, x, w, eps=1e-6):
+    x = np.ascontiguousarray(x, np.float64)
+    w = np.ascontiguousarray(w, np.float32)
+    y = np.empty_like(x)
+    assert L.oracle_head_rmsnorm(_p(x), x.shape[0], x.shape[1], _p(w), eps, _p(y)) == 0
+    return y
+
+
+def _rope(L, x, pos, base):
+    x = np.array(x, np.float64, order="C", copy=True)
+    assert L.oracle_rope(_p(x), x.shape[0], x.shape[1], pos, base) == 0
+    return x
+
+
+def _attend(L, q, K, V, n_ctx):
+    q = np.ascontiguousarray(q, np.float64)
+    K = np.ascontiguousarray(K, np.float32)
+    V = np.ascontiguousarray(V, np.float32)
+    att = np.empty_like(q)
+    assert L.oracle_gqa_attend(_p(q), q.shape[0], K.shape[0], q.shape[1], _p(K), _p(V), K.shape[1], n_ctx,
+                               _p(att)) == 0
+    return att
+
+
+def pin_head_rmsnorm(L):
+    """Closed forms of x / sqrt(mean x^2 + eps) * w."""
+    fails = []
+    hd, eps = 8, 1e-6
+    w = np.array([1.0, 2.0, 0.5, -1.0, 3.0, 1.0, 0.25, 4.0], np.float32)
+    # a constant row c: every entry is c / sqrt(c^2 + eps) * w[d]
+    c = 0.75
+    y = _rmsnorm(L, np.full((1, hd), c), w)
+    want = c / math.sqrt(c * c + eps) * w.astype(np.float64)
+    if not np.allclose(y[0], want, rtol=1e-14, atol=0):
+        fails.append("constant row")
+    # a spike a e_k: entry k is a / sqrt(a^2 / hd + eps) * w[k], the rest 0; a
+    # small a makes eps matter (a^2 / hd = 1.25e-7)
+    for a, k in ((1e-3, 3), (-5.0, 6), (2.0, 0)):
+        x = np.zeros((1, hd))
+        x[0, k] = a
+        y = _rmsnorm(L, x, w)
+        want = np.zeros(hd)
+        want[k] = a / math.sqrt(a * a / hd + eps) * float(w[k])
+        if not np.allclose(y[0], want, rtol=1e-13, atol=0):
+            fails.append(f"spike a={a} at {k}")
+    # heads are normalised on their own: scaling one head leaves the others
+    x = np.arange(1.0, 17.0).reshape(2, hd)
+    y1 = _rmsnorm(L, x, w)
+    x2 = x.copy()
+    x2[1] *= 1000.0
+    y2 = _rmsnorm(L, x2, w)
+    if not np.array_equal(y1[0], y2[0]):
+        fails.append("a head's norm depends on another head")
+    # a zero row stays zero
+    if np.any(_rmsnorm(L, np.zeros((1, hd)), w)):
+        fails.append("zero row")
+    return fails
+
+
+def pin_rope(L):
+    """Rotations of basis vectors by the defined angles, and invariants."""
+    fails = []
+    # hd = 4, base 1e4: pair (x0, x2) turns by pos * 1, pair (x1, x3) by pos * 1e4^(-1/2) = pos / 100
+    for pos in (1, 3):
+        t0, t1 = float(pos), pos / 100.0
+        y = _rope(L, np.eye(4), pos, 1e4)
+        want = np.array([[math.cos(t0), 0, math.sin(t0), 0],
+                         [0, math.cos(t1), 0, math.sin(t1)],
+                         [-math.sin(t0), 0, math.cos(t0), 0],
+                         [0, -math.sin(t1), 0, math.cos(t1)]])
+        if not np.allclose(y, want, rtol=0, atol=1e-15):
+            fails.append(f"basis rotation at pos {pos}")
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((3, 16))
+    if not np.array_equal(_rope(L, x, 0, 1e6), x):
+        fails.append("position 0 is not the identity")
+    y = _rope(L, x, 77, 1e6)
+    # each pair keeps its length
+    if not np.allclose(x[:, :8] ** 2 + x[:, 8:] ** 2, y[:, :8] ** 2 + y[:, 8:] ** 2, rtol=1e-13):
+        fails.append("pair lengths change")
+    # the dot product of two rotated vectors depends on the position difference only
+    a, b = x[0:1], x[1:2]
+    d1 = float(_rope(L, a, 40, 1e6)[0] @ _rope(L, b, 25, 1e6)[0])
+    d2 = float(_rope(L, a, 115, 1e6)[0] @ _rope(L, b, 100, 1e6)[0])
+    if abs(d1 - d2) > 1e-12 * max(1.0, abs(d1)):
+        fails.append("rotated dot products depend on the absolute position")
+    return fails
+
+
+def pin_gqa_attend(L):
+    """One position, per-group constant values, a two-key closed form, the causal bound."""
+    fails = []
+    rng = np.random.default_rng(29)
+    n_head, n_kv, hd, stride = 8, 2, 4, 5
+    q = rng.standard_normal((n_head, hd))
+    K = rng.standard_normal((n_kv, stride, hd)).astype(np.float32)
+    V = rng.standard_normal((n_kv, stride, hd)).astype(np.float32)
+    # one position: every head returns its group's value row
+    att = _attend(L, q, K, V, 1)
+    for h in range(n_head):
+        if not np.array_equal(att[h], V[h // (n_head // n_kv), 0].astype(np.float64)):
+            fails.append(f"single position, head {h}")
+            break
+    # values constant over positions (g + 1 in group g): the weights do not matter
+    Vc = np.empty_like(V)
+    for g in range(n_kv):
+        Vc[g] = g + 1.0
+    att = _attend(L, q, K, Vc, 4)
+    want = np.array([[h // (n_head // n_kv) + 1.0] * hd for h in range(n_head)])
+    if not np.allclose(att, want, rtol=1e-15, atol=0):
+        fails.append("query heads read the wrong KV head")
+    # two keys: scores s/sqrt(hd) and 0, values e0 and e1 -> (p, 1 - p, 0, 0), p = 1/(1 + e^(-s/2))
+    s = 1.7
+    q2 = np.zeros((n_head, hd))
+    q2[:, 0] = s
+    K2 = np.zeros((n_kv, stride, hd), np.float32)
+    K2[:, 0, 0] = 1.0
+    V2 = np.zeros((n_kv, stride, hd), np.float32)
+    V2[:, 0, 0] = 1.0
+    V2[:, 1, 1] = 1.0
+    att = _attend(L, q2, K2, V2, 2)
+    p = 1.0 / (1.0 + math.exp(-s / 2.0))
+    if not np.allclose(att, np.tile([p, 1.0 - p, 0.0, 0.0], (n_head, 1)), rtol=1e-14, atol=1e-16):
+        fails.append("two-key softmax closed form")
+    # positions at and past n_ctx are never read
+    K3, V3 = K.copy(), V.copy()
+    K3[:, 3:] = 1e4
+    V3[:, 3:] = -7.0
+    if not np.array_equal(_attend(L, q, K3, V3, 3), _attend(L, q, K, V, 3)):
+        fails.append("positions past the window are read")
+    # ... and the last position of the window is
+    V4 = V.copy()
+    V4[:, 2] += 1.0
+    if np.array_equal(_attend(L, q, K, V4, 3), _attend(L, q, K, V, 3)):
+        fails.append("the window's last position is not read")
+    return fails
+
+
+def _bf16_bits(a):
+    return (np.ascontiguousarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_attn_block(L):
+    """Compositions with selection weights: at position 0 the output is the
+    value row, gathered per group; with zero keys the window averages."""
+    fails = []
+    rng = np.random.default_rng(31)
+    n_head, n_kv, hd, stride = 4, 2, 8, 6
+    d_model = n_head * hd
+    wq = _bf16_bits(rng.standard_normal((n_head * hd, d_model)).astype(np.float32) * 0.1)
+    wk = _bf16_bits(rng.standard_normal((n_kv * hd, d_model)).astype(np.float32) * 0.1)
+    sel = np.zeros((n_kv * hd, d_model), np.float32)
+    sel[np.arange(n_kv * hd), np.arange(n_kv * hd)] = 1.0   # v = x[: n_kv * hd]
+    wv = _bf16_bits(sel)
+    wo = _bf16_bits(np.eye(d_model, dtype=np.float32))      # out = att
+    qn = (1.0 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    kn = (1.0 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    x = rng.standard_normal(d_model).astype(np.float32)
+
+    def block(wk_, pos, K, V):
+        K = np.array(K, np.float32, order="C", copy=True)
+        V = np.array(V, np.float32, order="C", copy=True)
+        out = np.empty(d_model)
+        rc = L.oracle_attn_decode(_p(wq), _p(wk_), _p(wv), _p(wo), _p(qn), _p(kn), d_model, n_head, n_kv, hd,
+                                  _p(x), pos, 1e6, _p(K), _p(V), stride, _p(out), None, None)
+        assert rc == 0
+        return out, K, V
+
+    K0 = rng.standard_normal((n_kv, stride, hd)).astype(np.float32)
+    V0 = rng.standard_normal((n_kv, stride, hd)).astype(np.float32)
+    out, K, V = block(wk, 0, K0, V0)
+    want = np.concatenate([x[(h // (n_head // n_kv)) * hd:(h // (n_head // n_kv) + 1) * hd] for h in range(n_head)])
+    if not np.array_equal(out, want.astype(np.float64)):
+        fails.append("position 0: out is not the gathered value rows")
+    if not np.array_equal(V[:, 0], x[: n_kv * hd].reshape(n_kv, hd)):
+        fails.append("position 0: the value row appended is not v")
+    if not (np.array_equal(K[:, 1:], K0[:, 1:]) and np.array_equal(V[:, 1:], V0[:, 1:])):
+        fails.append("rows other than pos changed")
+    # zero key weights: k = 0 after norm and rotation, every score is q . 0 = 0,
+    # so the window 0..pos averages its values (the new one is v)
+    pos = 3
+    zk = np.zeros_like(wk)
+    Kz = np.zeros((n_kv, stride, hd), np.float32)
+    Vz = np.zeros((n_kv, stride, hd), np.float32)
+    for g in range(n_kv):
+        for j in range(pos):
+            Vz[g, j] = 10.0 * g + j + 1.0
+    out, K, V = block(zk, pos, Kz, Vz)
+    want = []
+    for h in range(n_head):
+        g = h // (n_head // n_kv)
+        want.append((Vz[g, :pos].astype(np.float64).sum(axis=0) + x[g * hd:(g + 1) * hd]) / (pos + 1))
+    if not np.allclose(out, np.concatenate(want), rtol=1e-14, atol=1e-15):
+        fails.append("zero keys: the window 0..pos is not averaged")
+    if np.any(K[:, pos]):
+        fails.append("zero keys: the appended key is not 0")
+    return fails
+
+
 CORE_PINS = [pin_worked_examples, pin_unpack_exhaustive, pin_affine_identity, pin_silu,
-             pin_bf16, pin_f16, pin_ffn_composition, pin_routed]
+             pin_bf16, pin_f16, pin_ffn_composition, pin_routed, pin_head_rmsnorm, pin_rope,
+             pin_gqa_attend, pin_attn_block]
 
 
 def run_core_pins(L):
     fails = []
     for pin in CORE_PINS:
-        fails += [f"{pin.__name__}: {m}" for m in pin(L)]
+        try:
+            fails += [f"{pin.__name__}: {m}" for m in pin(L)]
+        except Exception as exc:   # a broken oracle may refuse its arguments
+            fails.append(f"{pin.__name__}: raised {type(exc).__name__}: {exc}")
     return fails

@@ -28,6 +28,17 @@ MUTANTS = {
     "hidden_product": ("hidden[i] = oracle_silu(g[i]) * u[i]", "hidden[i] = oracle_silu(u[i]) * g[i]"),
     "routed_slot_weight": ("(double)w[t * top_k + s]", "(double)w[t * top_k]"),
     "routed_slot_index": ("ids[t * top_k + s]", "ids[s * T + t]"),
+    "norm_eps_outside": ("1.0 / sqrt(ss / (double)hd + eps)", "1.0 / (sqrt(ss / (double)hd) + eps)"),
+    "norm_gain_index": ("xh[d] * inv * (double)w[d]", "xh[d] * inv * (double)w[0]"),
+    "rope_pairing": ("i + half]", "i ^ 1]"),
+    "rope_sign": ("xh[i] = a * cs - b * sn", "xh[i] = a * cs + b * sn"),
+    "rope_frequency": ("-2.0 * (double)i / (double)hd", "-1.0 * (double)i / (double)hd"),
+    "gqa_index": ("const long g = h / (n_head / n_kv);", "const long g = h % n_kv;"),
+    "attn_scale": ("s[j] = dot / sqrt((double)hd);", "s[j] = dot;"),
+    "softmax_denominator": ("att[h * hd + d] = acc / den;", "att[h * hd + d] = acc;"),
+    "attn_window": ("ctx_stride, pos + 1, att)", "ctx_stride, pos > 0 ? pos : 1, att)"),
+    "append_row": ("v_cache[(g * ctx_stride + pos) * hd + d]", "v_cache[(g * ctx_stride + (pos > 0 ? pos - 1 : 0)) * hd + d]"),
+    "append_swap": ("= (float)kn[g * hd + d];", "= (float)v[g * hd + d];"),
 }
 
 

@@ -32,3 +32,17 @@ def test_bf16_rounding_ties_to_even():
     f = np.array([1.0, 1.00390625, 1.01171875, -2.5], np.float32)  # 1+2^-8 is a tie
     bits = workloads.f32_to_bf16_bits(f)
     assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0xC020]
+
+
+def test_attn_inputs_shapes_and_determinism():
+    spec = workloads.ATTN_SMALL
+    w, x, K, V = workloads.make_attn_inputs(spec)
+    nq, nk, hd = spec["n_head"] * spec["head_dim"], spec["n_kv"] * spec["head_dim"], spec["head_dim"]
+    assert w.wq.shape == (nq, spec["d_model"]) and w.wq.dtype == np.uint16
+    assert w.wk.shape == w.wv.shape == (nk, spec["d_model"])
+    assert w.wo.shape == (spec["d_model"], nq)
+    assert w.q_norm.shape == w.k_norm.shape == (hd,) and w.q_norm.dtype == np.float32
+    assert K.shape == V.shape == (spec["n_kv"], spec["max_ctx"], hd) and K.dtype == np.float32
+    w2, x2, K2, _ = workloads.make_attn_inputs(spec)
+    assert np.array_equal(w.wo, w2.wo) and np.array_equal(x, x2) and np.array_equal(K, K2)
+    assert not np.array_equal(K, V)

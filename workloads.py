@@ -263,3 +263,56 @@ def make_batch_inputs(T: int, seed: int | None = None, d_model: int = 4096):
     """(X f32 [T, d_model], router f32 [T, 8]) for the token-batch workload."""
     seed = BATCH_TOKENS[T] if seed is None else seed
     return activation_batch(seed, T, d_model), router_weights(seed, 8, T)
+
+
+# ----------------------------------------------------------------------------
+# Decode attention block (section "GPU-Resident Decode Attention"): the bf16
+# projection table's shapes (q 8192 x 4096, k/v 512 x 4096, o 4096 x 8192),
+# i.e. 64 query heads and 4 KV heads of 128 dimensions, a 4096-position f32
+# KV cache, and the newest token at the cache's last position.
+_TAG_ATTN = 300
+ATTN = dict(name="attn_decode_4096_h64_kv4_d128", seed=50, d_model=4096, n_head=64, n_kv=4, head_dim=128,
+            max_ctx=4096, pos=4095, rope_base=1e6)
+# A small block for parity at every position of a short cache.
+ATTN_SMALL = dict(name="attn_decode_256_h8_kv2_d64", seed=51, d_model=256, n_head=8, n_kv=2, head_dim=64,
+                  max_ctx=100, pos=37, rope_base=1e4)
+
+
+@dataclass
+class AttnWeights:
+    wq: np.ndarray       # bf16 bits [n_head*hd, d_model]
+    wk: np.ndarray       # bf16 bits [n_kv*hd, d_model]
+    wv: np.ndarray       # bf16 bits [n_kv*hd, d_model]
+    wo: np.ndarray       # bf16 bits [d_model, n_head*hd]
+    q_norm: np.ndarray   # f32 [hd]
+    k_norm: np.ndarray   # f32 [hd]
+
+
+def attn_weights(seed: int, d_model: int, n_head: int, n_kv: int, head_dim: int) -> AttnWeights:
+    """Projections bf16 ~ N(0, 0.02^2); norm gains f32 1 + N(0, 0.1^2)."""
+    nq, nk = n_head * head_dim, n_kv * head_dim
+    return AttnWeights(
+        wq=bf16_normal(seed, (_TAG_ATTN, 0), nq, d_model, 0.02),
+        wk=bf16_normal(seed, (_TAG_ATTN, 1), nk, d_model, 0.02),
+        wv=bf16_normal(seed, (_TAG_ATTN, 2), nk, d_model, 0.02),
+        wo=bf16_normal(seed, (_TAG_ATTN, 3), d_model, nq, 0.02),
+        q_norm=(1.0 + normal_f32(seed, (_TAG_ATTN, 4), head_dim, 0.1)).astype(np.float32),
+        k_norm=(1.0 + normal_f32(seed, (_TAG_ATTN, 5), head_dim, 0.1)).astype(np.float32))
+
+
+def kv_cache(seed: int, n_kv: int, max_ctx: int, head_dim: int):
+    """(K, V) f32 [n_kv, max_ctx, head_dim], N(0, 1) entries: cached keys are
+    RMS-normed rows (unit RMS before the gain) and values are projections of
+    unit-variance inputs by N(0, 0.02^2) weights over 4096 columns (RMS about 1.3),
+    so unit-variance draws stand in for both."""
+    K = normal_f32(seed, (_TAG_ATTN, 6), n_kv * max_ctx * head_dim).reshape(n_kv, max_ctx, head_dim)
+    V = normal_f32(seed, (_TAG_ATTN, 7), n_kv * max_ctx * head_dim).reshape(n_kv, max_ctx, head_dim)
+    return K, V
+
+
+def make_attn_inputs(spec: dict):
+    """(AttnWeights, x f32 [d_model], K, V) for an attention workload."""
+    w = attn_weights(spec["seed"], spec["d_model"], spec["n_head"], spec["n_kv"], spec["head_dim"])
+    x = normal_f32(spec["seed"], (_TAG_ATTN, 8), spec["d_model"])
+    K, V = kv_cache(spec["seed"], spec["n_kv"], spec["max_ctx"], spec["head_dim"])
+    return w, x, K, V
