@@ -21,8 +21,9 @@ SMOE_SCALE_F16 = 0x100   # ORed into `bits`: 2-byte IEEE binary16 scales instead
 
 EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
            "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_routed_ffn_workspace",
-           "smoe_routed_ffn", "smoe_status_str")
+           "smoe_routed_ffn", "smoe_attn_decode_workspace", "smoe_attn_decode", "smoe_status_str")
 SMOE_MAX_BF16_JOBS = 16
+SMOE_MAX_ATTN_GROUP = 16
 
 
 class SmoeError(RuntimeError):
@@ -37,6 +38,11 @@ class QMat(ctypes.Structure):
 
 class Expert(ctypes.Structure):
     _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class AttnWeights(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("wv", ctypes.c_void_p),
+                ("wo", ctypes.c_void_p), ("q_norm", ctypes.c_void_p), ("k_norm", ctypes.c_void_p)]
 
 
 class Bf16Job(ctypes.Structure):
@@ -68,6 +74,10 @@ def lib():
         L.smoe_routed_ffn_workspace.argtypes = [i, i, i, i, i]
         L.smoe_routed_ffn_workspace.restype = sz
         L.smoe_routed_ffn.argtypes = [vp, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.smoe_attn_decode_workspace.argtypes = [i, i, i, i, i]
+        L.smoe_attn_decode_workspace.restype = sz
+        L.smoe_attn_decode.argtypes = [vp, i, i, i, i, vp, i, ctypes.c_double, vp, vp, i, vp, vp, sz, vp]
+        L.smoe_attn_decode.restype = i
         L.smoe_status_str.argtypes = [i]
         L.smoe_status_str.restype = ctypes.c_char_p
         for name in ("smoe_gate_up", "smoe_down", "smoe_expert_ffn", "matvec_bf16"):
@@ -233,3 +243,34 @@ def smoe_routed_ffn(experts, bits, group, x, expert_ids, expert_w, out, workspac
         arr, len(experts), bits, group, d_model, d_ff, T, top_k, _dev(expert_ids, torch.int32, "expert_ids"),
         _dev(expert_w, torch.float32, "expert_w"), _dev(x, torch.float32, "x"), _dev(out, torch.float32, "out"),
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def smoe_attn_decode_workspace(d_model, n_head, n_kv, head_dim, max_ctx) -> int:
+    return int(lib().smoe_attn_decode_workspace(d_model, n_head, n_kv, head_dim, max_ctx))
+
+
+def _bf16(t, name):
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError(f"{name} must be torch.bfloat16 (or int16 bit patterns)")
+    return _dev(t, t.dtype, name)
+
+
+def smoe_attn_decode(wq, wk, wv, wo, q_norm, k_norm, x, pos, rope_base, k_cache, v_cache, out, workspace,
+                     stream=None):
+    """One token's decode attention block; appends k, v at `pos` in the caches.
+
+    wq [n_head*hd, d_model], wk/wv [n_kv*hd, d_model], wo [d_model, n_head*hd]: bf16;
+    q_norm, k_norm f32 [hd]; x, out f32 [d_model]; k_cache, v_cache f32
+    [n_kv, max_ctx, hd]; workspace uint8 of smoe_attn_decode_workspace(...) bytes."""
+    import torch
+    n_kv, max_ctx, hd = k_cache.shape
+    d_model = x.numel()
+    n_head = wq.shape[0] // hd
+    w = AttnWeights(_bf16(wq, "wq"), _bf16(wk, "wk"), _bf16(wv, "wv"), _bf16(wo, "wo"),
+                    _dev(q_norm, torch.float32, "q_norm"), _dev(k_norm, torch.float32, "k_norm"))
+    _check("smoe_attn_decode", lib().smoe_attn_decode(
+        ctypes.byref(w), d_model, n_head, n_kv, hd, _dev(x, torch.float32, "x"), int(pos), float(rope_base),
+        _dev(k_cache, torch.float32, "k_cache"), _dev(v_cache, torch.float32, "v_cache"), max_ctx,
+        _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))

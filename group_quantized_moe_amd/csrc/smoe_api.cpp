@@ -196,6 +196,39 @@ void fill_experts(Args &a, const smoe_expert *experts, int n)
 }
 
 
+// Workspace layout of the attention block, every piece 256-byte aligned (f32):
+//   q [n_head*hd], k [n_kv*hd], v [n_kv*hd], qr [n_head*hd], att [n_head*hd],
+//   part_o [n_kv][n_chunks][G][hd], part_ml [n_kv][n_chunks][G][2],
+//   n_chunks = max_ctx / 32 rounded up.  Everything is rewritten before it is read.
+struct AttnWorkspace {
+    size_t q, k, v, qr, att, part_o, part_ml, total;
+};
+
+AttnWorkspace attn_workspace(int n_head, int n_kv, int head_dim, int max_ctx)
+{
+    AttnWorkspace w;
+    const size_t nq = (size_t)n_head * head_dim, nk = (size_t)n_kv * head_dim;
+    const size_t nc = (size_t)smoe::attn_chunks(max_ctx);
+    w.q = 0;
+    w.k = w.q + align256(nq * 4);
+    w.v = w.k + align256(nk * 4);
+    w.qr = w.v + align256(nk * 4);
+    w.att = w.qr + align256(nq * 4);
+    w.part_o = w.att + align256(nq * 4);
+    w.part_ml = w.part_o + align256(nc * nq * 4);
+    w.total = w.part_ml + align256(nc * (size_t)n_head * 2 * 4);
+    return w;
+}
+
+bool attn_shape_ok(int d_model, int n_head, int n_kv, int head_dim, int max_ctx)
+{
+    if (d_model <= 0 || d_model % 8 || d_model > SMOE_MAX_BF16_COLS) return false;
+    if (n_head <= 0 || n_kv <= 0 || n_head % n_kv || n_head / n_kv > SMOE_MAX_ATTN_GROUP) return false;
+    if (head_dim != 64 && head_dim != 128) return false;
+    if ((long)n_head * head_dim > SMOE_MAX_BF16_COLS || max_ctx <= 0) return false;
+    return (long)n_kv * max_ctx * head_dim <= INT_MAX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -521,6 +554,85 @@ int matvec_bf16_batch(const smoe_bf16_job *jobs, int n_jobs, void *stream)
         a.job[j] = smoe::Bf16Job{jobs[j].W, jobs[j].x, jobs[j].y, jobs[j].rows, jobs[j].cols};
     a.n = n_jobs;
     return launch_status(smoe::launch_matvec_bf16_batch(cfg, a, (hipStream_t)stream));
+}
+
+size_t smoe_attn_decode_workspace(int d_model, int n_head, int n_kv, int head_dim, int max_ctx)
+{
+    if (!attn_shape_ok(d_model, n_head, n_kv, head_dim, max_ctx)) return 0;
+    return attn_workspace(n_head, n_kv, head_dim, max_ctx).total;
+}
+
+int smoe_attn_decode(const smoe_attn_weights *w, int d_model, int n_head, int n_kv, int head_dim, const float *x,
+                     int pos, double rope_base, float *k_cache, float *v_cache, int max_ctx, float *out,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!w || !w->wq || !w->wk || !w->wv || !w->wo || !w->q_norm || !w->k_norm || !x || !k_cache || !v_cache ||
+        !out)
+        return SMOE_ERR_NULL;
+    if (!attn_shape_ok(d_model, n_head, n_kv, head_dim, max_ctx)) return SMOE_ERR_SHAPE;
+    if (pos < 0 || pos >= max_ctx || !(rope_base > 0.0) || rope_base > 1e300) return SMOE_ERR_SHAPE;
+    if (!aligned(w->wq, 16) || !aligned(w->wk, 16) || !aligned(w->wv, 16) || !aligned(w->wo, 16) ||
+        !aligned(w->q_norm, 4) || !aligned(w->k_norm, 4) || !aligned(x, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16) || !aligned(out, 4))
+        return SMOE_ERR_ALIGN;
+    const AttnWorkspace ws = attn_workspace(n_head, n_kv, head_dim, max_ctx);
+    if (!workspace || workspace_bytes < ws.total) return SMOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SMOE_ERR_ALIGN;
+    const size_t nq = (size_t)n_head * head_dim, nk = (size_t)n_kv * head_dim;
+    const size_t cache = nk * (size_t)max_ctx * 4;
+    // Written ranges (out, the caches, the workspace) against everything else.
+    struct Range {
+        const void *p;
+        size_t n;
+    };
+    const Range in[] = {{w->wq, nq * d_model * 2}, {w->wk, nk * d_model * 2}, {w->wv, nk * d_model * 2},
+                        {w->wo, (size_t)d_model * nq * 2}, {w->q_norm, (size_t)head_dim * 4},
+                        {w->k_norm, (size_t)head_dim * 4}, {x, (size_t)d_model * 4}};
+    const Range wr[] = {{out, (size_t)d_model * 4}, {k_cache, cache}, {v_cache, cache}, {workspace, ws.total}};
+    for (const Range &a : wr) {
+        for (const Range &b : in)
+            if (overlap(a.p, a.n, b.p, b.n)) return SMOE_ERR_ALIAS;
+        for (const Range &b : wr)
+            if (&a != &b && overlap(a.p, a.n, b.p, b.n)) return SMOE_ERR_ALIAS;
+    }
+    MapConfig cfg_qkv, cfg_o;
+    if (!smoe::choose_bf16map(d_model / 8, (int)(nq + 2 * nk), &cfg_qkv) ||
+        !smoe::choose_bf16map((int)(nq / 8), d_model, &cfg_o))
+        return SMOE_ERR_SHAPE;
+    int rc = check_device(nullptr);
+    if (rc) return rc;
+    char *wsb = static_cast<char *>(workspace);
+    float *q = reinterpret_cast<float *>(wsb + ws.q), *k = reinterpret_cast<float *>(wsb + ws.k);
+    float *v = reinterpret_cast<float *>(wsb + ws.v), *att = reinterpret_cast<float *>(wsb + ws.att);
+    const hipStream_t st = (hipStream_t)stream;
+    smoe::Bf16BatchArgs b{};
+    b.job[0] = smoe::Bf16Job{w->wq, x, q, (int)nq, d_model};
+    b.job[1] = smoe::Bf16Job{w->wk, x, k, (int)nk, d_model};
+    b.job[2] = smoe::Bf16Job{w->wv, x, v, (int)nk, d_model};
+    b.n = 3;
+    if ((rc = launch_status(smoe::launch_matvec_bf16_batch(cfg_qkv, b, st)))) return rc;
+    smoe::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_norm = w->q_norm;
+    a.k_norm = w->k_norm;
+    a.qr = reinterpret_cast<float *>(wsb + ws.qr);
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.part_o = reinterpret_cast<float *>(wsb + ws.part_o);
+    a.part_ml = reinterpret_cast<float *>(wsb + ws.part_ml);
+    a.att = att;
+    a.rope_base = rope_base;
+    a.n_head = n_head;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.max_ctx = max_ctx;
+    a.pos = pos;
+    a.n_chunks = smoe::attn_chunks(max_ctx);
+    if ((rc = launch_status(smoe::launch_attn_core(a, st)))) return rc;
+    smoe::Bf16Args o{w->wo, att, out, d_model, (int)nq};
+    return launch_status(smoe::launch_matvec_bf16(cfg_o, o, st));
 }
 
 }  // extern "C"

@@ -19,6 +19,9 @@
  *                   its own experts only ("Token-Batch Fused FFN").
  *  - matvec_bf16_batch  several independent bf16 matvecs in one launch
  *                   ("Batched Scout Matvec").
+ *  - smoe_attn_decode  one token's attention block: q/k/v projections, QK
+ *                   RMS norm, RoPE, KV append, GQA attention, o_proj
+ *                   ("GPU-Resident Decode Attention").
  *
  * Weight format (the "Layout assumptions the kernels rely on" contract):
  *   A quantised matrix of rows x cols is a smoe_qmat:
@@ -219,6 +222,49 @@ typedef struct {
     int rows, cols;
 } smoe_bf16_job;
 int matvec_bf16_batch(const smoe_bf16_job *jobs, int n_jobs, void *stream);
+
+/* Query heads per KV head in smoe_attn_decode. */
+#define SMOE_MAX_ATTN_GROUP 16
+
+/*
+ * The decode attention block of one token ("GPU-Resident Decode Attention":
+ * the layer's attention as one submission with no host round trip):
+ *   q = Wq x, k = Wk x, v = Wv x                  (bf16 weights, f32 x)
+ *   q and k, per head: RMS norm  y = x / sqrt(mean(x^2) + 1e-6) * gain,
+ *     then RoPE at position pos: for i < head_dim/2 the pair
+ *     (y[i], y[i + head_dim/2]) turns by pos * rope_base^(-2i/head_dim)
+ *   k_cache[g][pos][:] = k_g,  v_cache[g][pos][:] = v_g   (f32)
+ *   att[h] = sum_{j <= pos} softmax_j(q_h . K[g][j] / sqrt(head_dim)) V[g][j],
+ *     g = h / (n_head / n_kv)
+ *   out = Wo att
+ * Arguments:
+ *   w        : host struct of device pointers: wq bf16 [n_head*head_dim][d_model],
+ *              wk and wv bf16 [n_kv*head_dim][d_model], wo bf16
+ *              [d_model][n_head*head_dim] (16-byte aligned), q_norm and k_norm
+ *              f32 [head_dim]
+ *   x        : f32 [d_model], 16-byte aligned
+ *   k_cache, v_cache : f32 [n_kv][max_ctx][head_dim], 16-byte aligned, caller
+ *              owned; rows 0..pos-1 are read, row pos is written, nothing else
+ *              changes
+ *   out      : f32 [d_model]; must not overlap any other argument
+ *   workspace: smoe_attn_decode_workspace(...) bytes, 256-byte aligned, device
+ *              memory the call may overwrite (nothing in it needs to be zero)
+ * Limits: d_model % 8 == 0, d_model and n_head*head_dim <= SMOE_MAX_BF16_COLS,
+ * n_head % n_kv == 0 with n_head / n_kv <= SMOE_MAX_ATTN_GROUP, head_dim 64 or
+ * 128, 0 <= pos < max_ctx, rope_base > 0; else SMOE_ERR_SHAPE.  Five launches
+ * on `stream`: the three projections in one, the norm / rotation / append,
+ * the attention over 32-position chunks (one block serves a KV head's query
+ * heads), the chunk merge in chunk order (deterministic), and o_proj.
+ * Rotation angles are formed in f64; everything else is f32.
+ */
+typedef struct {
+    const uint16_t *wq, *wk, *wv, *wo;
+    const float *q_norm, *k_norm;
+} smoe_attn_weights;
+size_t smoe_attn_decode_workspace(int d_model, int n_head, int n_kv, int head_dim, int max_ctx);
+int smoe_attn_decode(const smoe_attn_weights *w, int d_model, int n_head, int n_kv, int head_dim,
+                     const float *x, int pos, double rope_base, float *k_cache, float *v_cache, int max_ctx,
+                     float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Message for a status code (static string). */
 const char *smoe_status_str(int status);

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
         "smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
         "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_routed_ffn_workspace",
-        "smoe_routed_ffn", "smoe_status_str"}
+        "smoe_routed_ffn", "smoe_attn_decode_workspace", "smoe_attn_decode", "smoe_status_str"}
 
 
 def test_library_exports_every_declared_symbol(gq):
@@ -217,3 +217,38 @@ def test_expert_ffn_batch_refusals(gq):
     assert call() == -8
     assert call(group=32) == -8
     assert call(bits=2, group=64) == -8
+
+
+def test_attn_decode_refusals(gq):
+    """smoe_attn_decode checks shapes, pointers, alignment, workspace and
+    aliasing before touching the device; a valid call reaches the device check."""
+    L = gq.lib()
+    dm, H, KV, hd, ctx = 4096, 64, 4, 128, 4096
+    need = L.smoe_attn_decode_workspace(dm, H, KV, hd, ctx)
+    assert need > 0
+    assert L.smoe_attn_decode_workspace(dm, H, KV, 96, ctx) == 0          # head_dim 64 or 128
+    assert L.smoe_attn_decode_workspace(dm, H, 3, hd, ctx) == 0           # n_head % n_kv
+    assert L.smoe_attn_decode_workspace(dm, 64, 2, hd, ctx) == 0          # 32 query heads per KV head
+    assert L.smoe_attn_decode_workspace(dm + 4, H, KV, hd, ctx) == 0      # d_model % 8
+    G = 1 << 28
+    wq, wk, wv, wo = A, A + G, A + 2 * G, A + 3 * G
+    qn, kn, x, out = A + 4 * G, A + 4 * G + 0x10000, A + 4 * G + 0x20000, A + 4 * G + 0x30000
+    kc, vc, ws = A + 5 * G, A + 6 * G, A + 7 * G
+
+    def call(**o):
+        w = gq.AttnWeights(o.get("wq", wq), wk, wv, o.get("wo", wo), qn, kn)
+        return L.smoe_attn_decode(ctypes.byref(w), o.get("dm", dm), H, KV, o.get("hd", hd), o.get("x", x),
+                                  o.get("pos", ctx - 1), o.get("base", 1e6), o.get("kc", kc), vc, ctx,
+                                  o.get("out", out), o.get("ws", ws), o.get("need", need), None)
+    assert call() == -8                        # valid: reaches the device check
+    assert call(pos=0) == -8
+    assert call(wq=None) == -1 and call(x=None) == -1 and call(kc=None) == -1
+    assert call(pos=ctx) == -4 and call(pos=-1) == -4 and call(base=0.0) == -4 and call(base=-1.0) == -4
+    assert call(hd=96) == -4 and call(dm=4100) == -4
+    assert call(wo=wo + 2) == -5 and call(x=x + 4) == -5 and call(kc=kc + 4) == -5
+    assert call(need=need - 1) == -6 and call(ws=None) == -6
+    assert call(ws=ws + 64) == -5
+    assert call(out=x) == -7                   # out overlaps x
+    assert call(out=kc + 64) == -7             # out overlaps the K cache
+    assert call(kc=vc) == -7                   # the caches overlap
+    assert call(ws=wq) == -7                   # the workspace overlaps Wq
