@@ -19,6 +19,10 @@ Other rows of the path, one JSON line each with --workload:
   bf16_batch          q, k and v projections (8192x4096, 2 x 512x4096) over
                       one x as one batched launch, with the three separate
                       launches timed beside it
+  attn                one token's decode attention block (64 query and 4 KV
+                      heads of 128, d_model 4096, f32 KV cache of 4096
+                      positions, the token at the last one): projections,
+                      QK norm, RoPE, KV append, GQA attention, o_proj
 
 Inputs are seeded synthetic weights with the shapes and distributions of the
 Metal Compute Kernels page (S-MoE docs) workloads; they stand in for trained
@@ -53,6 +57,7 @@ KERNEL_SOURCES = {
     "decode": [CSRC + "q_decode.hip", CSRC + "common.h"],
     "prefill": [CSRC + "q_batch.hip", CSRC + "common.h"],
     "bf16": [CSRC + "bf16_matvec.hip", CSRC + "common.h"],
+    "attn": [CSRC + "attn.hip", CSRC + "bf16_matvec.hip", CSRC + "common.h"],
 }
 
 
@@ -480,6 +485,76 @@ def bf16_batch_bench(args):
     }
 
 
+def attn_bench(args):
+    """One token's decode attention block (smoe_attn_decode) over a full
+    4096-position cache, with every weight and cache replica rotated."""
+    import torch
+    import workloads
+    import group_quantized_moe_amd as gq
+    L = gq.lib()
+    spec = workloads.ATTN
+    w, x, K, V = workloads.make_attn_inputs(spec)
+    dm, H, KV, hd, ctx, pos = (spec[k] for k in ("d_model", "n_head", "n_kv", "head_dim", "max_ctx", "pos"))
+    nq, nk = H * hd, KV * hd
+    wbytes = 2 * (nq * dm + 2 * nk * dm + dm * nq) + 4 * 2 * hd
+    kv_read = 2 * KV * pos * hd * 4            # cached rows 0..pos-1 of K and V
+    # Algorithmic bytes: every weight once, the cached rows once, x and out, the appended rows.
+    nbytes = wbytes + kv_read + 4 * dm * 2 + 2 * nk * 4
+    replicas = replica_count(wbytes + 2 * KV * ctx * hd * 4)
+    base = [to_dev(a) for a in (w.wq, w.wk, w.wv, w.wo, w.q_norm, w.k_norm, K, V)]
+    reps = [base] + [[t.clone() for t in base] for _ in range(replicas - 1)]
+    structs = [gq.AttnWeights(*(t.data_ptr() for t in rep[:6])) for rep in reps]
+    xd = to_dev(x)
+    out = torch.empty(dm, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gq.smoe_attn_decode_workspace(dm, H, KV, hd, ctx), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        r = i % replicas
+        rc = L.smoe_attn_decode(ctypes.byref(structs[r]), dm, H, KV, hd, xd.data_ptr(), pos, spec["rope_base"],
+                                reps[r][6].data_ptr(), reps[r][7].data_ptr(), ctx, out.data_ptr(), ws.data_ptr(),
+                                ws.numel(), sp)
+        if rc != 0:
+            raise gq.SmoeError("smoe_attn_decode", rc)
+
+    us_step, per_call, wall_us = time_steps(step, args.steps, args.warmup, stream)
+    gbs = nbytes / (us_step * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        n, dt, cores = cpu_oracle(lambda: oracle.attn_decode(w, x, pos, spec["rope_base"], K, V),
+                                  args.cpu_budget, 1)
+        cpu = {"value": round(n * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"{n} whole attention blocks at position {pos} (f64 oracle, {dt:.1f} s)",
+               "us_per_block": round(dt / n * 1e6, 1)}
+    return {
+        "metric": "effective HBM GB/s per decode attention block (64/4 heads x 128, 4096-position f32 KV cache)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(us_step / 1e3, 6),
+        "us_per_block": round(us_step, 3),
+        "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "wall_us_per_step": round(wall_us, 3),
+        "dtype": "bf16 x f32 -> f32 projections, f32 attention",
+        "config": {"workload": spec["name"], "d_model": dm, "n_head": H, "n_kv": KV, "head_dim": hd,
+                   "max_ctx": ctx, "pos": pos, "rope_base": spec["rope_base"],
+                   "algorithmic_bytes_per_step": nbytes, "replicas_rotated": replicas,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "one smoe_attn_decode call = qkv batch + prep + partial + combine + o_proj on one stream",
+            "achieved": round(nbytes / (per_call * 1e-6) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (per_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic("attn_decode", "attn"),
+            "per_call_us_events": round(per_call, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+
+
 def copy_calibration(args):
     """A plain device-to-device copy of 256 MiB (torch's copy kernel): the
     counter runs divide FETCH_SIZE / WRITE_SIZE of a kernel by what the same
@@ -502,7 +577,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_q4", choices=["decode_q4", "decode_q2", "decode_q4_s16", "decode_q2_s16", "prefill", "bf16",
-                             "bf16_batch", "routed", "copy"])
+                             "bf16_batch", "routed", "attn", "copy"])
     ap.add_argument("--tokens", type=int, default=16, help="prefill / routed: tokens per call")
     ap.add_argument("--topk", type=int, default=2, help="routed: experts per token")
     ap.add_argument("--shape", default="q_proj", help="bf16: q_proj, o_proj, kv_proj or lm_head")
@@ -535,6 +610,8 @@ def main():
         line = routed_bench(args)
     elif args.workload == "bf16_batch":
         line = bf16_batch_bench(args)
+    elif args.workload == "attn":
+        line = attn_bench(args)
     else:
         line = bf16_bench(args)
     head = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,

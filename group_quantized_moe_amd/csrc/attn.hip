@@ -12,8 +12,8 @@
 //      the query heads of that KV head (the group shares every K and V row it
 //      stages in LDS): scores, the chunk's max and exp-sum per head, and the
 //      chunk's unnormalised output rows;
-//   4. k_attn_combine: one block per query head merges the chunks in chunk
-//      order (deterministic) into the attention output;
+//   4. k_attn_combine: one block per query head merges the chunks into the
+//      attention output, summing in a fixed order (deterministic);
 //   5. the output projection as a bf16 matvec.
 // Everything is f32 but the rotation angles, which are formed and reduced in
 // f64: pos * base^(-2i/hd) reaches thousands of radians, where an f32 angle
@@ -164,26 +164,54 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
     }
 }
 
-// Query head h: merge the chunks in order.  att[h][d] = sum_c e^(m_c - M) o_c[d]
-// / sum_c e^(m_c - M) l_c.
+// Query head h: merge the chunks.  att[h][d] = sum_c e^(m_c - M) o_c[d] /
+// sum_c e^(m_c - M) l_c, M = max_c m_c.  The 512 threads take column d and one
+// of P = 512 / HD contiguous chunk ranges each (independent loads, several in
+// flight), and the P range sums are added in range order: deterministic.
+constexpr int kCombineThreads = 512;
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a)
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
 {
-    const int h = blockIdx.x, d = threadIdx.x;
+    constexpr int P = kCombineThreads / HD;
+    __shared__ float red[kCombineThreads / 64];
+    __shared__ float part_o[P][HD];
+    __shared__ float part_l[P];
+    const int h = blockIdx.x, t = threadIdx.x;
     const int G = a.n_head / a.n_kv, g = h / G, hq = h - g * G;
     const int nc = (a.pos + 1 + kAttnChunk - 1) / kAttnChunk;
     const float *ml = a.part_ml + ((size_t)g * a.n_chunks * G + hq) * 2;
     const size_t cstride = (size_t)G * 2;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[c * cstride]);
-    float L = 0.0f, o = 0.0f;
+    float m = -INFINITY;
+    for (int c = t; c < nc; c += kCombineThreads) m = fmaxf(m, ml[c * cstride]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
+    const int d = t % HD, pr = t / HD;
+    const int c0 = (int)((long)pr * nc / P), c1 = (int)((long)(pr + 1) * nc / P);
     const float *po = a.part_o + ((size_t)g * a.n_chunks * G + hq) * HD + d;
-    for (int c = 0; c < nc; ++c) {
+    float L = 0.0f, o = 0.0f;
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
         const float w = expf(ml[c * cstride] - M);
         L += w * ml[c * cstride + 1];
         o += w * po[(size_t)c * G * HD];
     }
-    a.att[(size_t)h * HD + d] = o / L;
+    part_o[pr][d] = o;
+    if (d == 0) part_l[pr] = L;
+    __syncthreads();
+    if (pr == 0) {
+        float os = part_o[0][d], ls = part_l[0];
+#pragma unroll
+        for (int q = 1; q < P; ++q) {
+            os += part_o[q][d];
+            ls += part_l[q];
+        }
+        a.att[(size_t)h * HD + d] = os / ls;
+    }
 }
 
 template <int HD>
@@ -196,7 +224,7 @@ hipError_t launch_attn_hd(const AttnArgs &a, hipStream_t st)
     const int nc = (a.pos + 1 + kAttnChunk - 1) / kAttnChunk;
     hipLaunchKernelGGL(k_attn_partial<HD>, dim3(nc, a.n_kv), dim3(kAttnThreads), 0, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_attn_combine<HD>, dim3(a.n_head), dim3(HD), 0, st, a);
+    hipLaunchKernelGGL(k_attn_combine<HD>, dim3(a.n_head), dim3(kCombineThreads), 0, st, a);
     return hipGetLastError();
 }
 
