@@ -543,7 +543,7 @@ def attn_bench(args):
                    "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "one smoe_attn_decode call = qkv batch + prep + partial + combine + o_proj on one stream",
+            "kernel": "one smoe_attn_decode call = qkv batch + partial (norm, rotation, append, chunk attention) + combine + o_proj on one stream",
             "achieved": round(nbytes / (per_call * 1e-6) / 1e9, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -6,18 +6,19 @@
 //
 // Launch sequence (one stream, no host synchronisation):
 //   1. the three projections as one batched bf16 matvec launch;
-//   2. k_attn_prep: one wave per head (query heads, then KV heads): RMS norm,
-//      rotation, and for KV heads the cache append of k and v;
-//   3. k_attn_partial: one block per (32-position chunk, KV head) serves all
+//   2. k_attn_partial: one block per (32-position chunk, KV head) serves all
 //      the query heads of that KV head (the group shares every K and V row it
-//      stages in LDS): scores, the chunk's max and exp-sum per head, and the
-//      chunk's unnormalised output rows;
-//   4. k_attn_combine: one block per query head merges the chunks into the
+//      stages in LDS).  It normalises and rotates those queries itself (a few
+//      thousand flops per block, cheaper than a launch), and the block whose
+//      chunk holds the new token also normalises and rotates k and appends k
+//      and v to the caches.  Then the scores, the chunk's max and exp-sum per
+//      head, and the chunk's unnormalised output rows;
+//   3. k_attn_combine: one block per query head merges the chunks into the
 //      attention output, summing in a fixed order (deterministic);
-//   5. the output projection as a bf16 matvec.
-// Everything is f32 but the rotation angles, which are formed and reduced in
-// f64: pos * base^(-2i/hd) reaches thousands of radians, where an f32 angle
-// would be off by about 1e-4.
+//   4. the output projection as a bf16 matvec.
+// Everything is f32 but the rotation angles, which are formed and reduced to
+// [-pi, pi] in f64: pos * base^(-2i/hd) reaches thousands of radians, where an
+// f32 angle would be off by about 1e-4.
 #include "common.h"
 #include "launch.h"
 
@@ -48,119 +49,192 @@ __device__ __forceinline__ float half_sum(float v)
     return v;
 }
 
-// One wave per head.  Lane l owns the rotation pairs i = l + 64 p (i < HD/2),
-// each pair (i, i + HD/2) as the rotation takes it.
-template <int HD>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_prep(AttnArgs a)
+// RMS norm and rotation of one head's hd values held as pairs (i, i + HD/2)
+// by the lanes of a wave (lane l: pairs i = l + 64 p); cs / sn are the pair
+// angles' cosine and sine; lanes past the last pair hold zeros.
+template <int NP>
+__device__ __forceinline__ void norm_rotate(const float (&x0)[NP], const float (&x1)[NP], const float (&g0)[NP],
+                                            const float (&g1)[NP], const float (&cs)[NP], const float (&sn)[NP],
+                                            int hd, float (&y0)[NP], float (&y1)[NP])
 {
-    constexpr int HALF = HD / 2;
-    constexpr int NP = (HALF + 63) / 64;
-    const int lane = threadIdx.x & 63;
-    const int head = blockIdx.x * (kAttnThreads / 64) + (threadIdx.x >> 6);
-    const int H = a.n_head, KV = a.n_kv;
-    if (head >= H + KV) return;   // whole wave; no barrier in this kernel
-    const bool is_q = head < H;
-    const int g = head - H;
-    const float *src = is_q ? a.q + (size_t)head * HD : a.k + (size_t)g * HD;
-    const float *gain = is_q ? a.q_norm : a.k_norm;
-    float va[NP], vb[NP];
     float ss = 0.0f;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int i = lane + 64 * p;
-        va[p] = i < HALF ? src[i] : 0.0f;
-        vb[p] = i < HALF ? src[i + HALF] : 0.0f;
-        ss += va[p] * va[p] + vb[p] * vb[p];
-    }
+    for (int p = 0; p < NP; ++p) ss += x0[p] * x0[p] + x1[p] * x1[p];
     ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)HD + 1e-6f);
-    float *dst = is_q ? a.qr + (size_t)head * HD : a.k_cache + ((size_t)g * a.max_ctx + a.pos) * HD;
-    const double l2b = log2(a.rope_base);
+    const float inv = 1.0f / sqrtf(ss / (float)hd + 1e-6f);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const int i = lane + 64 * p;
-        if (i >= HALF) continue;
-        const float x0 = va[p] * inv * gain[i], x1 = vb[p] * inv * gain[i + HALF];
-        const double ang = (double)a.pos * exp2(-(2.0 * i / HD) * l2b);
-        double sd, cd;
-        sincos(ang, &sd, &cd);
-        const float s = (float)sd, c = (float)cd;
-        dst[i] = x0 * c - x1 * s;
-        dst[i + HALF] = x0 * s + x1 * c;
-    }
-    if (!is_q) {
-        const float *vs = a.v + (size_t)g * HD;
-        float *vd = a.v_cache + ((size_t)g * a.max_ctx + a.pos) * HD;
-        for (int d = lane; d < HD; d += 64) vd[d] = vs[d];
+        const float a0 = x0[p] * inv * g0[p], a1 = x1[p] * inv * g1[p];
+        y0[p] = a0 * cs[p] - a1 * sn[p];
+        y1[p] = a0 * sn[p] + a1 * cs[p];
     }
 }
 
-// Chunk c of the window 0..pos for KV head g and its G query heads.  LDS rows
-// are padded by 4 floats so that the 32 rows a half wave reads at one column
-// fall in different banks.
+// Chunk c of the window 0..pos for KV head g and its G query heads, with the
+// norm and rotation of those queries done in the block (each wave takes
+// heads w, w + 4, ...), and, in the block whose chunk holds pos, the norm,
+// rotation and cache append of the new k and v.  LDS rows of K and V are
+// padded by 4 floats so that the rows a half wave reads at one column fall in
+// different banks.  Heads past G are zero rows.
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
 {
     constexpr int RS = HD + 4;
+    constexpr int HALF = HD / 2;
+    constexpr int NP = (HALF + 63) / 64;
+    constexpr int GP = kMaxAttnGroup;
     __shared__ __align__(16) float Ks[kAttnChunk * RS];
     __shared__ __align__(16) float Vs[kAttnChunk * RS];
-    __shared__ __align__(16) float Qs[kMaxAttnGroup * HD];
-    __shared__ float P[kMaxAttnGroup * kAttnChunk];
+    __shared__ __align__(16) float Qs[GP * HD];
+    __shared__ __align__(16) float Pt[kAttnChunk * GP];   // [j][head]
     const int c = blockIdx.x, g = blockIdx.y;
     const int G = a.n_head / a.n_kv;
     const int n_ctx = a.pos + 1;
     const int j0 = c * kAttnChunk;
     const int nj = min(kAttnChunk, n_ctx - j0);
-    const int tid = threadIdx.x;
-    // Stage the chunk's K and V rows (rows past the window are zero) and the group's queries.
+    const int jnew = a.pos - j0;   // row of the new token in this chunk (in range only in the last chunk)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Every global load first, so that one round trip covers them: the chunk's
+    // cached K and V rows (rows past the window are zero; the new token's row
+    // is computed below), and the raw queries of this wave's heads.
+    constexpr int NKV = kAttnChunk * HD / 4 / kAttnThreads;   // float4 of K (and of V) per thread
+    constexpr int HPW = GP / (kAttnThreads / 64);              // query heads per wave
     const float *Kg = a.k_cache + ((size_t)g * a.max_ctx + j0) * HD;
     const float *Vg = a.v_cache + ((size_t)g * a.max_ctx + j0) * HD;
-    for (int e = tid; e < kAttnChunk * HD / 4; e += kAttnThreads) {
-        const int j = e / (HD / 4), d4 = e - j * (HD / 4);
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-        if (j < nj) {
-            kv = reinterpret_cast<const float4 *>(Kg + (size_t)j * HD)[d4];
-            vv = reinterpret_cast<const float4 *>(Vg + (size_t)j * HD)[d4];
+    float4 kr[NKV], vr[NKV];
+#pragma unroll
+    for (int r = 0; r < NKV; ++r) {
+        const int e = tid + r * kAttnThreads, j = e / (HD / 4), d4 = e - j * (HD / 4);
+        kr[r] = vr[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < nj && j != jnew) {
+            kr[r] = reinterpret_cast<const float4 *>(Kg + (size_t)j * HD)[d4];
+            vr[r] = reinterpret_cast<const float4 *>(Vg + (size_t)j * HD)[d4];
         }
-        *reinterpret_cast<float4 *>(Ks + j * RS + 4 * d4) = kv;
-        *reinterpret_cast<float4 *>(Vs + j * RS + 4 * d4) = vv;
     }
-    const float *Qg = a.qr + (size_t)g * G * HD;
-    for (int e = tid; e < G * HD / 4; e += kAttnThreads)
-        reinterpret_cast<float4 *>(Qs)[e] = reinterpret_cast<const float4 *>(Qg)[e];
+    float qx0[HPW][NP], qx1[HPW][NP];
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+        const float *src = a.q + ((size_t)g * G + min(wave + 4 * k, G - 1)) * HD;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {   // lanes past the last pair hold zeros (they add nothing to the norm)
+            const int i = min(lane + 64 * p, HALF - 1);
+            qx0[k][p] = lane + 64 * p < HALF ? src[i] : 0.0f;
+            qx1[k][p] = lane + 64 * p < HALF ? src[i + HALF] : 0.0f;
+        }
+    }
+    // Pair angles: pos * base^(-2i/hd) formed in f64 and reduced to [-pi, pi]
+    // there, so that the f32 sine and cosine see a small argument.
+    float cs[NP], sn[NP], qg0[NP], qg1[NP];
+    const double l2b = log2(a.rope_base);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int i = min(lane + 64 * p, HALF - 1);
+        const double ang = (double)a.pos * exp2(-(2.0 * i / HD) * l2b);
+        const double twopi = 6.283185307179586476925286766559;
+        const float r = (float)(ang - twopi * rint(ang / twopi));
+        sincosf(r, &sn[p], &cs[p]);
+        qg0[p] = a.q_norm[i];
+        qg1[p] = a.q_norm[i + HALF];
+    }
+#pragma unroll
+    for (int r = 0; r < NKV; ++r) {
+        const int e = tid + r * kAttnThreads, j = e / (HD / 4), d4 = e - j * (HD / 4);
+        *reinterpret_cast<float4 *>(Ks + j * RS + 4 * d4) = kr[r];
+        *reinterpret_cast<float4 *>(Vs + j * RS + 4 * d4) = vr[r];
+    }
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+        const int hq = wave + 4 * k;
+        float y0[NP], y1[NP];
+        norm_rotate<NP>(qx0[k], qx1[k], qg0, qg1, cs, sn, HD, y0, y1);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int i = lane + 64 * p;
+            if (i < HALF) {
+                Qs[hq * HD + i] = hq < G ? y0[p] : 0.0f;
+                Qs[hq * HD + i + HALF] = hq < G ? y1[p] : 0.0f;
+            }
+        }
+    }
+    if (jnew >= 0 && jnew < kAttnChunk && wave == 0) {   // the chunk holding the new token
+        float x0[NP], x1[NP], g0[NP], g1[NP], y0[NP], y1[NP];
+        const float *src = a.k + (size_t)g * HD;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int i = min(lane + 64 * p, HALF - 1);
+            x0[p] = lane + 64 * p < HALF ? src[i] : 0.0f;
+            x1[p] = lane + 64 * p < HALF ? src[i + HALF] : 0.0f;
+            g0[p] = a.k_norm[i];
+            g1[p] = a.k_norm[i + HALF];
+        }
+        norm_rotate<NP>(x0, x1, g0, g1, cs, sn, HD, y0, y1);
+        float *kd = a.k_cache + ((size_t)g * a.max_ctx + a.pos) * HD;
+        float *vd = a.v_cache + ((size_t)g * a.max_ctx + a.pos) * HD;
+        const float *vs = a.v + (size_t)g * HD;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int i = lane + 64 * p;
+            if (i < HALF) {
+                Ks[jnew * RS + i] = kd[i] = y0[p];
+                Ks[jnew * RS + i + HALF] = kd[i + HALF] = y1[p];
+            }
+        }
+        for (int d = lane; d < HD; d += 64) Vs[jnew * RS + d] = vd[d] = vs[d];
+    }
     __syncthreads();
-    // Scores and the per-head softmax pieces: thread (hq, j), j = lane % 32.
-    const int j = tid & (kAttnChunk - 1);
-    const float scale = 1.0f / sqrtf((float)HD);
-    for (int hq = tid / kAttnChunk; hq < kMaxAttnGroup; hq += kAttnThreads / kAttnChunk) {
-        // hq is uniform over the half wave, so the exits below keep half waves whole.
-        if (hq >= G) break;
-        float dot = 0.0f;
+    // Scores of heads hg and hg + 8 against row j (one K read serves both),
+    // then each head's max and exp-sum over the chunk's rows.
+    {
+        const int j = tid & (kAttnChunk - 1), hg = tid / kAttnChunk;   // hg: uniform over the half wave
+        const float scale = 1.0f / sqrtf((float)HD);
+        float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll 8
         for (int d4 = 0; d4 < HD / 4; ++d4) {
             const float4 k4 = *reinterpret_cast<const float4 *>(Ks + j * RS + 4 * d4);
-            const float4 q4 = *reinterpret_cast<const float4 *>(Qs + hq * HD + 4 * d4);
-            dot += k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w;
+            const float4 q0 = *reinterpret_cast<const float4 *>(Qs + hg * HD + 4 * d4);
+            const float4 q1 = *reinterpret_cast<const float4 *>(Qs + (hg + 8) * HD + 4 * d4);
+            d0 += k4.x * q0.x + k4.y * q0.y + k4.z * q0.z + k4.w * q0.w;
+            d1 += k4.x * q1.x + k4.y * q1.y + k4.z * q1.z + k4.w * q1.w;
         }
-        const float s = j < nj ? dot * scale : -INFINITY;
-        const float m = half_max(s);
-        const float p = j < nj ? expf(s - m) : 0.0f;
-        const float l = half_sum(p);
-        P[hq * kAttnChunk + j] = p;
-        if (j == 0) {
-            float *ml = a.part_ml + (((size_t)g * a.n_chunks + c) * G + hq) * 2;
-            ml[0] = m;
-            ml[1] = l;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int hq = hg + 8 * k;
+            const float s = j < nj ? (k ? d1 : d0) * scale : -INFINITY;
+            const float m = half_max(s);
+            const float p = j < nj ? expf(s - m) : 0.0f;
+            const float l = half_sum(p);
+            Pt[j * GP + hq] = hq < G ? p : 0.0f;
+            if (j == 0 && hq < G) {
+                float *ml = a.part_ml + (((size_t)g * a.n_chunks + c) * G + hq) * 2;
+                ml[0] = m;
+                ml[1] = l;
+            }
         }
     }
     __syncthreads();
-    // Unnormalised output rows: o[hq][d] = sum_j P[hq][j] V[j][d].
-    for (int e = tid; e < G * HD; e += kAttnThreads) {
-        const int hq = e / HD, d = e - hq * HD;
-        float o = 0.0f;
-#pragma unroll 8
-        for (int jj = 0; jj < kAttnChunk; ++jj) o += P[hq * kAttnChunk + jj] * Vs[jj * RS + d];
-        a.part_o[(((size_t)g * a.n_chunks + c) * G + hq) * HD + d] = o;
+    // Unnormalised output rows o[hq][d] = sum_j P[hq][j] V[j][d]: thread
+    // (column d, head group) reads each V value once for HPT heads.
+    {
+        constexpr int HPT = GP * HD / kAttnThreads;   // heads per thread: 8 (HD 128) or 4 (HD 64)
+        const int d = tid % HD, h0 = (tid / HD) * HPT;
+        float o[HPT];
+#pragma unroll
+        for (int k = 0; k < HPT; ++k) o[k] = 0.0f;
+#pragma unroll 4
+        for (int j = 0; j < kAttnChunk; ++j) {
+            const float v = Vs[j * RS + d];
+#pragma unroll
+            for (int k4 = 0; k4 < HPT / 4; ++k4) {
+                const float4 p4 = *reinterpret_cast<const float4 *>(Pt + j * GP + h0 + 4 * k4);
+                o[4 * k4] += p4.x * v;
+                o[4 * k4 + 1] += p4.y * v;
+                o[4 * k4 + 2] += p4.z * v;
+                o[4 * k4 + 3] += p4.w * v;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < HPT; ++k)
+            if (h0 + k < G) a.part_o[(((size_t)g * a.n_chunks + c) * G + h0 + k) * HD + d] = o[k];
     }
 }
 
@@ -217,13 +291,10 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
 template <int HD>
 hipError_t launch_attn_hd(const AttnArgs &a, hipStream_t st)
 {
-    const int heads = a.n_head + a.n_kv;
-    hipLaunchKernelGGL(k_attn_prep<HD>, dim3((heads + 3) / 4), dim3(kAttnThreads), 0, st, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const int nc = (a.pos + 1 + kAttnChunk - 1) / kAttnChunk;
     hipLaunchKernelGGL(k_attn_partial<HD>, dim3(nc, a.n_kv), dim3(kAttnThreads), 0, st, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_attn_combine<HD>, dim3(a.n_head), dim3(kCombineThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -160,13 +160,12 @@ struct Bf16BatchArgs {
 hipError_t launch_matvec_bf16_batch(const MapConfig &cfg, const Bf16BatchArgs &a, hipStream_t stream);
 
 // Decode attention core (the part between the projections): per-head norm
-// and rotation of q and k with the cache append, chunked GQA attention and
+// and rotation of q and k with the cache append, chunked GQA attention, and
 // the chunk merge.  The projections use the bf16 matvec launches.
 constexpr int kMaxAttnGroup = 16;   // query heads per KV head
 struct AttnArgs {
     const float *q, *k, *v;         // projections: [n_head*hd], [n_kv*hd], [n_kv*hd]
     const float *q_norm, *k_norm;   // RMS norm gains [hd]
-    float *qr;                      // rotated queries [n_head*hd]
     float *k_cache, *v_cache;       // [n_kv][max_ctx][hd]
     float *part_o, *part_ml;        // [n_kv][n_chunks][G][hd], [n_kv][n_chunks][G][2]
     float *att;                     // attention output [n_head*hd]

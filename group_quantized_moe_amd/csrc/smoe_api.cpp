@@ -197,11 +197,11 @@ void fill_experts(Args &a, const smoe_expert *experts, int n)
 
 
 // Workspace layout of the attention block, every piece 256-byte aligned (f32):
-//   q [n_head*hd], k [n_kv*hd], v [n_kv*hd], qr [n_head*hd], att [n_head*hd],
+//   q [n_head*hd], k [n_kv*hd], v [n_kv*hd], att [n_head*hd],
 //   part_o [n_kv][n_chunks][G][hd], part_ml [n_kv][n_chunks][G][2],
 //   n_chunks = max_ctx / 32 rounded up.  Everything is rewritten before it is read.
 struct AttnWorkspace {
-    size_t q, k, v, qr, att, part_o, part_ml, total;
+    size_t q, k, v, att, part_o, part_ml, total;
 };
 
 AttnWorkspace attn_workspace(int n_head, int n_kv, int head_dim, int max_ctx)
@@ -212,8 +212,7 @@ AttnWorkspace attn_workspace(int n_head, int n_kv, int head_dim, int max_ctx)
     w.q = 0;
     w.k = w.q + align256(nq * 4);
     w.v = w.k + align256(nk * 4);
-    w.qr = w.v + align256(nk * 4);
-    w.att = w.qr + align256(nq * 4);
+    w.att = w.v + align256(nk * 4);
     w.part_o = w.att + align256(nq * 4);
     w.part_ml = w.part_o + align256(nc * nq * 4);
     w.total = w.part_ml + align256(nc * (size_t)n_head * 2 * 4);
@@ -617,7 +616,6 @@ int smoe_attn_decode(const smoe_attn_weights *w, int d_model, int n_head, int n_
     a.v = v;
     a.q_norm = w->q_norm;
     a.k_norm = w->k_norm;
-    a.qr = reinterpret_cast<float *>(wsb + ws.qr);
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.part_o = reinterpret_cast<float *>(wsb + ws.part_o);

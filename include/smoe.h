@@ -251,10 +251,10 @@ int matvec_bf16_batch(const smoe_bf16_job *jobs, int n_jobs, void *stream);
  *              memory the call may overwrite (nothing in it needs to be zero)
  * Limits: d_model % 8 == 0, d_model and n_head*head_dim <= SMOE_MAX_BF16_COLS,
  * n_head % n_kv == 0 with n_head / n_kv <= SMOE_MAX_ATTN_GROUP, head_dim 64 or
- * 128, 0 <= pos < max_ctx, rope_base > 0; else SMOE_ERR_SHAPE.  Five launches
- * on `stream`: the three projections in one, the norm / rotation / append,
- * the attention over 32-position chunks (one block serves a KV head's query
- * heads), the chunk merge in chunk order (deterministic), and o_proj.
+ * 128, 0 <= pos < max_ctx, rope_base > 0; else SMOE_ERR_SHAPE.  Four launches
+ * on `stream`: the three projections in one; the norm, rotation and append
+ * with the attention over 32-position chunks (one block serves a KV head's
+ * query heads); the chunk merge in a fixed order (deterministic); o_proj.
  * Rotation angles are formed in f64; everything else is f32.
  */
 typedef struct {
