@@ -25,28 +25,21 @@
 namespace smoe {
 namespace {
 
-constexpr int kAttnChunk = 32;    // cache positions per partial block
-constexpr int kAttnThreads = 256;
+constexpr int kAttnChunk = 32;     // cache positions per partial block
+constexpr int kAttnThreads = 512;  // 8 waves: two query heads per wave, one (head, row) score per thread
 
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-// Max / sum over the 32 lanes of a half wave.
+// Sums and maxima over aligned groups of W lanes (W = 32 or 64), every lane
+// of a group receiving the result: DPP within 16-lane rows, then one or two
+// cross-row shuffles.
+__device__ __forceinline__ float wave_sum(float v) { return lane_group_sum<64>(v); }
+__device__ __forceinline__ float half_sum(float v) { return lane_group_sum<32>(v); }
 __device__ __forceinline__ float half_max(float v)
 {
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
-    return v;
-}
-__device__ __forceinline__ float half_sum(float v)
-{
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 32);
-    return v;
+    v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+    return fmaxf(v, __shfl_xor(v, 16));
 }
 
 // RMS norm and rotation of one head's hd values held as pairs (i, i + HD/2)
@@ -71,8 +64,8 @@ __device__ __forceinline__ void norm_rotate(const float (&x0)[NP], const float (
 }
 
 // Chunk c of the window 0..pos for KV head g and its G query heads, with the
-// norm and rotation of those queries done in the block (each wave takes
-// heads w, w + 4, ...), and, in the block whose chunk holds pos, the norm,
+// norm and rotation of those queries done in the block (each of the 8 waves
+// takes heads w and w + 8), and, in the block whose chunk holds pos, the norm,
 // rotation and cache append of the new k and v.  LDS rows of K and V are
 // padded by 4 floats so that the rows a half wave reads at one column fall in
 // different banks.  Heads past G are zero rows.
@@ -114,7 +107,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
     float qx0[HPW][NP], qx1[HPW][NP];
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
-        const float *src = a.q + ((size_t)g * G + min(wave + 4 * k, G - 1)) * HD;
+        const float *src = a.q + ((size_t)g * G + min(wave + (kAttnThreads / 64) * k, G - 1)) * HD;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {   // lanes past the last pair hold zeros (they add nothing to the norm)
             const int i = min(lane + 64 * p, HALF - 1);
@@ -137,14 +130,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
         qg1[p] = a.q_norm[i + HALF];
     }
 #pragma unroll
-    for (int r = 0; r < NKV; ++r) {
+    for (int r = 0; r < NKV; ++r) {   // row jnew is written by wave 0 below, and only there
         const int e = tid + r * kAttnThreads, j = e / (HD / 4), d4 = e - j * (HD / 4);
-        *reinterpret_cast<float4 *>(Ks + j * RS + 4 * d4) = kr[r];
-        *reinterpret_cast<float4 *>(Vs + j * RS + 4 * d4) = vr[r];
+        if (j != jnew) {
+            *reinterpret_cast<float4 *>(Ks + j * RS + 4 * d4) = kr[r];
+            *reinterpret_cast<float4 *>(Vs + j * RS + 4 * d4) = vr[r];
+        }
     }
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
-        const int hq = wave + 4 * k;
+        const int hq = wave + (kAttnThreads / 64) * k;
         float y0[NP], y1[NP];
         norm_rotate<NP>(qx0[k], qx1[k], qg0, qg1, cs, sn, HD, y0, y1);
 #pragma unroll
@@ -182,55 +177,44 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
         for (int d = lane; d < HD; d += 64) Vs[jnew * RS + d] = vd[d] = vs[d];
     }
     __syncthreads();
-    // Scores of heads hg and hg + 8 against row j (one K read serves both),
-    // then each head's max and exp-sum over the chunk's rows.
+    // Score of head hq against row j (thread (hq, j); hq uniform over the half
+    // wave), then each head's max and exp-sum over the chunk's rows.
     {
-        const int j = tid & (kAttnChunk - 1), hg = tid / kAttnChunk;   // hg: uniform over the half wave
+        static_assert(kAttnThreads == GP * kAttnChunk, "one (head, row) score per thread");
+        const int j = tid & (kAttnChunk - 1), hq = tid / kAttnChunk;
         const float scale = 1.0f / sqrtf((float)HD);
-        float d0 = 0.0f, d1 = 0.0f;
+        float dot = 0.0f;
 #pragma unroll 8
         for (int d4 = 0; d4 < HD / 4; ++d4) {
             const float4 k4 = *reinterpret_cast<const float4 *>(Ks + j * RS + 4 * d4);
-            const float4 q0 = *reinterpret_cast<const float4 *>(Qs + hg * HD + 4 * d4);
-            const float4 q1 = *reinterpret_cast<const float4 *>(Qs + (hg + 8) * HD + 4 * d4);
-            d0 += k4.x * q0.x + k4.y * q0.y + k4.z * q0.z + k4.w * q0.w;
-            d1 += k4.x * q1.x + k4.y * q1.y + k4.z * q1.z + k4.w * q1.w;
+            const float4 q4 = *reinterpret_cast<const float4 *>(Qs + hq * HD + 4 * d4);
+            dot += k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w;
         }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int hq = hg + 8 * k;
-            const float s = j < nj ? (k ? d1 : d0) * scale : -INFINITY;
-            const float m = half_max(s);
-            const float p = j < nj ? expf(s - m) : 0.0f;
-            const float l = half_sum(p);
-            Pt[j * GP + hq] = hq < G ? p : 0.0f;
-            if (j == 0 && hq < G) {
-                float *ml = a.part_ml + (((size_t)g * a.n_chunks + c) * G + hq) * 2;
-                ml[0] = m;
-                ml[1] = l;
-            }
+        const float s = j < nj ? dot * scale : -INFINITY;
+        const float m = half_max(s);
+        const float p = j < nj ? expf(s - m) : 0.0f;
+        const float l = half_sum(p);
+        Pt[j * GP + hq] = hq < G ? p : 0.0f;
+        if (j == 0 && hq < G) {
+            float *ml = a.part_ml + (((size_t)g * a.n_chunks + c) * G + hq) * 2;
+            ml[0] = m;
+            ml[1] = l;
         }
     }
     __syncthreads();
     // Unnormalised output rows o[hq][d] = sum_j P[hq][j] V[j][d]: thread
     // (column d, head group) reads each V value once for HPT heads.
     {
-        constexpr int HPT = GP * HD / kAttnThreads;   // heads per thread: 8 (HD 128) or 4 (HD 64)
+        constexpr int HPT = GP * HD / kAttnThreads;   // heads per thread: 4 (HD 128) or 2 (HD 64)
         const int d = tid % HD, h0 = (tid / HD) * HPT;
         float o[HPT];
 #pragma unroll
         for (int k = 0; k < HPT; ++k) o[k] = 0.0f;
-#pragma unroll 4
+#pragma unroll 8
         for (int j = 0; j < kAttnChunk; ++j) {
             const float v = Vs[j * RS + d];
 #pragma unroll
-            for (int k4 = 0; k4 < HPT / 4; ++k4) {
-                const float4 p4 = *reinterpret_cast<const float4 *>(Pt + j * GP + h0 + 4 * k4);
-                o[4 * k4] += p4.x * v;
-                o[4 * k4 + 1] += p4.y * v;
-                o[4 * k4 + 2] += p4.z * v;
-                o[4 * k4 + 3] += p4.w * v;
-            }
+            for (int k = 0; k < HPT; ++k) o[k] += Pt[j * GP + h0 + k] * v;
         }
 #pragma unroll
         for (int k = 0; k < HPT; ++k)
@@ -239,10 +223,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
 }
 
 // Query head h: merge the chunks.  att[h][d] = sum_c e^(m_c - M) o_c[d] /
-// sum_c e^(m_c - M) l_c, M = max_c m_c.  The 512 threads take column d and one
-// of P = 512 / HD contiguous chunk ranges each (independent loads, several in
+// sum_c e^(m_c - M) l_c, M = max_c m_c.  The 1024 threads take column d and
+// one of P = 1024 / HD contiguous chunk ranges each (independent loads, all in
 // flight), and the P range sums are added in range order: deterministic.
-constexpr int kCombineThreads = 512;
+constexpr int kCombineThreads = 1024;
 template <int HD>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
 {
@@ -257,8 +241,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
     const size_t cstride = (size_t)G * 2;
     float m = -INFINITY;
     for (int c = t; c < nc; c += kCombineThreads) m = fmaxf(m, ml[c * cstride]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = half_max(m);
+    m = fmaxf(m, __shfl_xor(m, 32));
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
     float M = red[0];
@@ -268,7 +252,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
     const int c0 = (int)((long)pr * nc / P), c1 = (int)((long)(pr + 1) * nc / P);
     const float *po = a.part_o + ((size_t)g * a.n_chunks * G + hq) * HD + d;
     float L = 0.0f, o = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
     for (int c = c0; c < c1; ++c) {
         const float w = expf(ml[c * cstride] - M);
         L += w * ml[c * cstride + 1];
