@@ -165,10 +165,16 @@ bool choose_bf16map(int chunks, int rows, MapConfig *cfg)
                 }
             }
     if (!pick.nw) return false;
+    // Row steps whose loads a lane issues up front: the most that still gives
+    // 4096 waves, as long as the loads (4 ITER NCH registers) and the x slice
+    // (8 NCH) stay within 96 registers, so that two 8-wave blocks fit on a
+    // compute unit and one block's reduction overlaps the other's loads
+    // (measured: the 151936 x 4096 LM head 244 -> 187 us, 4096 x 8192 15.7 ->
+    // 14.5 us).
     const int rs = 64 / pick.lpr;
     for (int iter : {8, 4, 2, 1}) {
         const long blocks = (rows + rs * iter - 1) / (rs * iter);
-        if (iter == 1 || blocks * pick.nw >= 4096) {
+        if (iter == 1 || (blocks * pick.nw >= 4096 && 4 * iter * pick.nch + 8 * pick.nch <= 96)) {
             pick.iter = iter;
             break;
         }
