@@ -95,6 +95,8 @@ BATCH_EDGE = [  # bits, group, d_model, d_ff, n_experts, T
     (2, 64, 256, 384, 3, 20),
     (2, 128, 512, 256, 2, 9),
     (2, 64, 192, 128, 1, 65),
+    (4, 64, 384, 320, 2, 9),     # 6 gate_up groups in 2 K splits (the second ends in a dead step), 5 down groups
+    (2, 64, 320, 448, 3, 40),    # 5 and 7 groups: partial 4-group code units and scale quads on both passes
 ]
 
 

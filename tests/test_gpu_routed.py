@@ -73,6 +73,7 @@ ROUTED_EDGE = [  # bits, group, d_model, d_ff, n_experts, T, top_k, routing
     (4, 64, 256, 512, 6, 40, 2, "skewed"),      # every token's first slot on expert 0
     (4, 64, 256, 512, 4, 20, 3, "holes"),       # some slots out of range
     (4, 64, 8192, 128, 2, 9, 1, "topk"),
+    (4, 64, 384, 320, 3, 50, 2, "topk"),       # 6 and 5 groups: partial iterations in routed mode
 ]
 
 
