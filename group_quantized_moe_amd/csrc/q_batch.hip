@@ -1135,13 +1135,17 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     for (int tt = 0; tt < NTT; ++tt) tot[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // Loads and rings as in gate_up: hidden pieces and the tile's factors of
-    // step s in slot s & 1 (issued at the start of step s - 2, stored to LDS at
+    // step s in slot s % R (issued at the start of step s - R, stored to LDS at
     // the end of step s - 1); the next code unit and scale quad once the
-    // current ones are unpacked.  Loads past the range repeat its last
-    // iteration; dead steps clamp to the expert's last group; both count with
-    // scale 0.
-    TileRegs<KB, NTT> tr[2];
-    float frr[2];
+    // current ones are unpacked.  Loads complete in issue order, so the ring's
+    // depth bounds how far ahead the tile loads run; 16-token tiles, with
+    // little work a step and a few registers a slot, gain from four (about a
+    // tenth of the kernel's time), larger tiles and deeper code-unit rings
+    // measured no gain.  Loads past the range repeat its last iteration; dead
+    // steps clamp to the expert's last group; both count with scale 0.
+    constexpr int R = NTT == 1 ? 4 : 2;
+    TileRegs<KB, NTT> tr[R];
+    float frr[R];
     uint4 craw;
     unsigned sraw;
     CodeWords<BITS, KB> cw[kG];
@@ -1161,20 +1165,20 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     auto load_quad = [&](Pos ps) {
         sraw = buf_load_scale_bits<SB>(buf_res(a.down[ps.e].scales, sbytes), srow + (unsigned)min(ps.g + q, Gd - 1));
     };
-    auto store_tile = [&](int slot) {
-        tile_store<KB, NTT>(tr[slot], tm, smem + (size_t)slot * tb_bytes);
-        fac[slot * TT + flane] = frr[slot];
+    auto store_tile = [&](int slot, int buf) {
+        tile_store<KB, NTT>(tr[slot], tm, smem + (size_t)buf * tb_bytes);
+        fac[buf * TT + flane] = frr[slot];
     };
 
     {
         const Pos p0 = iter_pos(0);
         load_unit(p0, 0);
         load_quad(p0);
-        load_tile(0, p0, 0);
-        load_tile(1, p0, 1);
+#pragma unroll
+        for (int j = 0; j < R; ++j) load_tile(j, p0, j);
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_tile(0);
+    store_tile(0, 0);
     __syncthreads();
     for (int base = 0; base < NSS; base += 4) {
         const Pos cur = iter_pos(base / 4), nxt = iter_pos(base / 4 + 1);
@@ -1194,10 +1198,10 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
                             QFormat<BITS>::kInvZ;
                 load_quad(nxt);
             }
-            if (i + 2 < 4)
-                load_tile(i & 1, cur, i + 2);
+            if (i + R < 4)
+                load_tile(i % R, cur, i + R);
             else
-                load_tile(i & 1, nxt, i - 2);
+                load_tile(i % R, nxt, i + R - 4);
             __builtin_amdgcn_sched_barrier(0);
             const uint8_t *tile = smem + (size_t)(i & 1) * tb_bytes;
             half8 bf[KB];
@@ -1218,7 +1222,7 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) tot[tt][r] = fmaf(s * f[r], acc[r], tot[tt][r]);
             }
-            store_tile((i + 1) & 1);
+            store_tile((i + 1) % R, (i + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
         }

@@ -34,13 +34,13 @@
 //    has no barrier.
 //
 //  * Persistent waves, one step of loads in flight each.  Each block first
+//    loads the vector and waits for it, then issues its waves' first steps and
 //    builds the digit planes of the vector in LDS (one barrier); each wave then
 //    walks a contiguous range of row steps with the next step's 16-byte code
 //    loads and scale loads in flight while it reduces the current one (more
 //    steps in flight per wave measured slower: the waves of a CU already keep
 //    the memory system busy).  Loads come from a uniform base plus a 32-bit lane
-//    offset and are issued on every path (past the wave's last step the offsets
-//    are masked to zero), so that the compiler's load waits are exact.
+//    offset; nothing is loaded past a wave's last step.
 //
 //  * Deterministic expert combine.  down blocks are bound to one expert each.
 //    A wave keeps its router-weighted rows in LDS and, at its end, adds each
@@ -376,31 +376,26 @@ struct Stage {
 };
 
 // Loads of one stage: the lane's row is row0 + slot, clamped to the last row
-// (a partial last step re-reads it; its results are never stored).  A stage
-// past the end of a wave's steps is a dummy: every lane reads the first 16
-// bytes of the matrix (one cache line, nothing from HBM).  Both cases only
-// change the per-lane offsets, so every call issues the same loads and the
-// ring's waits stay exact.
+// (a partial last step re-reads it; its results are never stored).
 // Scales are f32 (SB = 4) or IEEE binary16 (SB = 2, widened exactly to f32;
 // byte offsets are half the f32 ones).
 template <int NCH, int LPR, int M, int SB>
 __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *const *codes, const void *const *scales,
                                            const RowLanes<NCH, LPR> &ln, int row0, int rows, unsigned row_bytes,
-                                           int gpr, bool dummy)
+                                           int gpr)
 {
-    const unsigned keep = dummy ? 0u : ~0u;
     const unsigned r = (unsigned)min(row0 + ln.slot, rows - 1);
     const unsigned crow = r * row_bytes, srow = r * (unsigned)gpr * 4u;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            t.q[k][m] = *reinterpret_cast<const uint4 *>(codes[m] + ((crow + ln.coff[k]) & keep));
+            t.q[k][m] = *reinterpret_cast<const uint4 *>(codes[m] + (crow + ln.coff[k]));
             const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]);
             if constexpr (SB == 4)
-                t.s[k][m] = *reinterpret_cast<const float *>(sb + ((srow + ln.soff[k]) & keep));
+                t.s[k][m] = *reinterpret_cast<const float *>(sb + (srow + ln.soff[k]));
             else
-                t.s[k][m] = (float)*reinterpret_cast<const _Float16 *>(sb + (((srow + ln.soff[k]) >> 1) & keep));
+                t.s[k][m] = (float)*reinterpret_cast<const _Float16 *>(sb + ((srow + ln.soff[k]) >> 1));
         }
     }
 }
@@ -414,6 +409,10 @@ __device__ __forceinline__ float stage_dot(const Stage<NCH, M> &t, int m, const 
     for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][m], t.s[k][m], cv[k]);
     return y;
 }
+
+// s_waitcnt vmcnt(0), expcnt and lgkmcnt left alone: every vector memory load
+// this wave has issued is in.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Step cursor over the steps of consecutive matrices: `spm` steps of `rs`
 // rows per matrix; tracks the matrix index and first row without division.
@@ -450,29 +449,28 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     const int wg = blockIdx.x * nw + wave;
     const int sb = (int)((long)wg * nsteps / W), se = (int)((long)(wg + 1) * nsteps / W);
 
-    auto load = [&](Stage<NCH, 2> &t, const Cursor &c, bool dummy) {
+    auto load = [&](Stage<NCH, 2> &t, const Cursor &c) {
         const uint8_t *codes[2] = {a.gate[c.m].codes, a.up[c.m].codes};
         const void *scales[2] = {a.gate[c.m].scales, a.up[c.m].scales};
-        load_stage<NCH, LPR, 2, SB>(t, codes, scales, ln, c.s * rs, a.d_ff, (unsigned)row_bytes, gpr, dummy);
+        load_stage<NCH, LPR, 2, SB>(t, codes, scales, ln, c.s * rs, a.d_ff, (unsigned)row_bytes, gpr);
     };
 
-    // The vector's loads go first, then the first steps' code loads, then the
-    // digit planes (which wait only for the vector).
+    // The vector's loads go first and are waited for before the first steps'
+    // code loads go out (behind those, the vector's loads took a few
+    // microseconds to come back, and the first steps waited for the planes);
+    // then the digit planes are built while the code loads are in flight.
     VecRegs<BITS, kGroupsPerThread<BITS>> xr;
     load_vec_regs<BITS>(a.x, a.d_model, xr);
-    // The ring's loads are unconditional (past the wave's last step they are
-    // dummies), so the number of loads between a load and its use is the same
-    // on every path and the wait for a stage leaves the later stages' loads in
-    // flight.
+    wait_vm_all();
+    // Nothing is loaded past the wave's last step: such loads all went to one
+    // address and queued there at the end of every wave.
     const bool busy = sb < se;
     Stage<NCH, 2> S[DEPTH];
-    Cursor cl, first;
+    Cursor cl;
     cl.init(sb, spe);
-    first = cl;
     int ls = sb;  // step that cl points at
     auto load_next = [&](Stage<NCH, 2> &t) {
-        const bool past = ls >= se;
-        load(t, past ? first : cl, past);
+        if (ls < se) load(t, cl);
         cl.next(spe);
         ++ls;
     };
@@ -570,19 +568,19 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     float *mine = reinterpret_cast<float *>(smem + ((plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15))) +
                   wave * a.dn_rows_per_wave;
     auto load = [&](Stage<NCH, 1> &t, int step) {
-        load_stage<NCH, LPR, 1, SB>(t, dcodes, dscales, ln, step * rs, a.d_model, (unsigned)row_bytes, gpr,
-                                     step >= se);
+        load_stage<NCH, LPR, 1, SB>(t, dcodes, dscales, ln, step * rs, a.d_model, (unsigned)row_bytes, gpr);
     };
 
     if ((int)blockIdx.x >= bpe * E) return;  // whole block idle: no barrier follows for it
     VecRegs<BITS, kGroupsPerThread<BITS>> hr;
     load_vec_regs<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, hr);
-    // Unconditional ring loads, as in gate_up (past the last step they are dummies).
+    wait_vm_all();   // the hidden vector before the code loads, as in gate_up
     const bool busy = sb < se;
     Stage<NCH, 1> S[DEPTH];
     if (busy) {
 #pragma unroll
-        for (int i = 0; i < DEPTH; ++i) load(S[i], sb + i);
+        for (int i = 0; i < DEPTH; ++i)
+            if (sb + i < se) load(S[i], sb + i);
     }
 
     build_planes<BITS>(hr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
@@ -606,7 +604,7 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
                         mine[(st - sb) * rs + ln.slot] = y * rw;
                 }
             }
-            load(S[i], st + DEPTH);
+            if (st + DEPTH < se) load(S[i], st + DEPTH);
         }
     }
 
