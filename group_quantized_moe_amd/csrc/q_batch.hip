@@ -790,17 +790,19 @@ __device__ __forceinline__ void store_partial(const f32x4 (&acc)[N], float *part
     for (int k = 0; k < N; ++k) reinterpret_cast<f32x4 *>(part)[k * 512 + threadIdx.x] = acc[k];
 }
 
-// acc = sum over the splits s = 0, 1, ... of the partial sums at part + s * stride.
+// acc[k] = sum over the splits s = 0, 1, ... of the partial sums at
+// part + s * stride, accumulator slot at[k] of them.
 template <int N>
-__device__ __forceinline__ void sum_partials(f32x4 (&acc)[N], const float *part, size_t stride, int splits)
+__device__ __forceinline__ void sum_partials(f32x4 (&acc)[N], const float *part, size_t stride, int splits,
+                                             const int (&at)[N])
 {
 #pragma unroll
-    for (int k = 0; k < N; ++k) acc[k] = reinterpret_cast<const f32x4 *>(part)[k * 512 + threadIdx.x];
+    for (int k = 0; k < N; ++k) acc[k] = reinterpret_cast<const f32x4 *>(part)[at[k] * 512 + threadIdx.x];
     for (int s = 1; s < splits; ++s) {
         const f32x4 *ps = reinterpret_cast<const f32x4 *>(part + (size_t)s * stride);
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const f32x4 v = ps[k * 512 + threadIdx.x];
+            const f32x4 v = ps[at[k] * 512 + threadIdx.x];
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[k][r] += v[r];
         }
@@ -1037,7 +1039,9 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 }
 
 // gate_up finish for split tiles: one block per (expert, row block, token
-// tile) adds the splits' partial sums in split order, then the epilogue.
+// tile, 16 tokens of it) adds the splits' partial sums in split order, then
+// the epilogue for those 16 tokens (the NTT blocks of a tile share nothing:
+// NTT times the blocks, each a fraction of the work).
 template <int KB, int NTT>
 __global__ __launch_bounds__(512) void k_tb_gu_finish(TbArgs a)
 {
@@ -1045,13 +1049,14 @@ __global__ __launch_bounds__(512) void k_tb_gu_finish(TbArgs a)
     constexpr int TT = 16 * NTT;
     const int NTB = (a.T + TT - 1) / TT;
     const int RB = (a.d_ff + kTileRows - 1) / kTileRows;
-    const int tile_id = blockIdx.x;
+    const int tile_id = blockIdx.x / NTT, tt = blockIdx.x % NTT;
     const int tb = tile_id % NTB, rb = (tile_id / NTB) % RB, e = tile_id / NTB / RB;
-    if (a.top_k && tb * TT >= a.cnt[e]) return;   // routed mode: an empty tile
+    const int tb16 = tb * NTT + tt;   // the block's 16 tokens, as a 16-token tile
+    if (a.top_k && tb16 * 16 >= a.cnt[e]) return;   // routed mode: no slots there
     constexpr size_t stride = (size_t)2 * NTT * 4 * 512;
-    f32x4 tot[2 * NTT];
-    sum_partials<2 * NTT>(tot, a.part_gu + (size_t)tile_id * a.ks_gu * stride, stride, a.ks_gu);
-    gu_epilogue<KB, NTT>(a, tot, e, rb, tb, reinterpret_cast<float *>(smem));
+    f32x4 tot[2];
+    sum_partials<2>(tot, a.part_gu + (size_t)tile_id * a.ks_gu * stride, stride, a.ks_gu, {tt, NTT + tt});
+    gu_epilogue<KB, 1>(a, tot, e, rb, tb16, reinterpret_cast<float *>(smem));
 }
 
 // out rows of the wave's 16 d_model rows for the tile's tokens.
@@ -1247,18 +1252,18 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     dn_store<NTT>(a, tot, rb, tb);
 }
 
-// down finish for split tiles: one block per (row block, token tile) adds
-// the splits' partial sums in split order and writes out.
+// down finish for split tiles: one block per (row block, token tile, 16
+// tokens of it) adds the splits' partial sums in split order and writes out.
 template <int NTT>
 __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
 {
     constexpr int TT = 16 * NTT;
     const int NTB = (a.T + TT - 1) / TT;
-    const int tile_id = blockIdx.x;
+    const int tile_id = blockIdx.x / NTT, tt = blockIdx.x % NTT;
     constexpr size_t stride = (size_t)NTT * 4 * 512;
-    f32x4 tot[NTT];
-    sum_partials<NTT>(tot, a.part_dn + (size_t)tile_id * a.ks_dn * stride, stride, a.ks_dn);
-    dn_store<NTT>(a, tot, tile_id / NTB, tile_id % NTB);
+    f32x4 tot[1];
+    sum_partials<1>(tot, a.part_dn + (size_t)tile_id * a.ks_dn * stride, stride, a.ks_dn, {tt});
+    dn_store<1>(a, tot, tile_id / NTB, (tile_id % NTB) * NTT + tt);
 }
 
 template <int BITS, int KB, int NTT, int MG, int SB>
@@ -1271,15 +1276,16 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_gu > 1) {
-        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu), dim3(64 * kTileWaves),
-                           (size_t)kTileWaves * NTT * 16 * 4, st, a);
+        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu * NTT), dim3(64 * kTileWaves),
+                           (size_t)kTileWaves * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
                        pl.dn_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_dn > 1) {
-        hipLaunchKernelGGL(k_tb_dn_finish<NTT>, dim3(pl.dn_blocks / a.ks_dn), dim3(64 * kTileWaves), 0, st, a);
+        hipLaunchKernelGGL(k_tb_dn_finish<NTT>, dim3(pl.dn_blocks / a.ks_dn * NTT), dim3(64 * kTileWaves), 0, st,
+                           a);
         err = hipGetLastError();
     }
     return err;
@@ -1363,8 +1369,8 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_gu > 1) {
-        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu), dim3(64 * kTileWaves),
-                           (size_t)kTileWaves * NTT * 16 * 4, st, a);
+        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu * NTT), dim3(64 * kTileWaves),
+                           (size_t)kTileWaves * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
