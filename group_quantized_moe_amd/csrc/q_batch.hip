@@ -1468,17 +1468,23 @@ constexpr size_t kMaxBlockLds = 64 * 1024;
 int tile_ntt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 
 // Splits of K over blocks: the smallest power of two (at most 16) that gives
-// `tiles` x splits >= 192 blocks of 8 waves: three quarters of the compute
-// units.  Every split adds f32 partial sums written here and read by a
-// finishing pass (64 KB per split of a 64-token tile), so the smallest count
-// that keeps most CUs busy is taken; measured, 192 beat 256 at 16 tokens and
-// tied at 64.
-int splits_for(long tiles)
+// `tiles` x splits >= `target` blocks of 8 waves.  Every split adds f32
+// partial sums written here and read by a finishing pass (64 KB per split of
+// a 64-token tile), so the smallest count that keeps the CUs busy is taken.
+int splits_for(long tiles, long target)
 {
     int s = 1;
-    while (s < 16 && tiles * s < 192) s *= 2;
+    while (s < 16 && tiles * s < target) s *= 2;
     return s;
 }
+
+// Dense token batch: 192 blocks (three quarters of the CUs) while the tiles
+// are few; from 128 tiles on, 512 (two blocks on every CU), which the work of
+// a 64-token tile pays for.  Measured at 16 and 64 tokens (96 and 32 tiles),
+// 192 beat 256, 384 and 512 blocks; at 256 tokens, 512 blocks (gate_up split
+// in 2, down in 4) took 226 us against 240 us for 192 (gate_up not split,
+// down in 2), and at 128 tokens 142 us against 146 us.
+long batch_block_target(long tiles) { return tiles >= 128 ? 512 : 192; }
 
 BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T)
 {
@@ -1487,8 +1493,8 @@ BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T)
     const long ntb = (T + 16 * b.ntt - 1) / (16 * b.ntt);
     b.gu_tiles = (long)n_experts * ((d_ff + kTileRows - 1) / kTileRows) * ntb;
     b.dn_tiles = (long)((d_model + kTileRows - 1) / kTileRows) * ntb;
-    b.ks_gu = splits_for(b.gu_tiles);
-    b.ks_dn = splits_for(b.dn_tiles);
+    b.ks_gu = splits_for(b.gu_tiles, batch_block_target(b.gu_tiles));
+    b.ks_dn = splits_for(b.dn_tiles, batch_block_target(b.dn_tiles));
     b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
     b.dn_part_floats = b.ks_dn > 1 ? (size_t)b.dn_tiles * b.ks_dn * b.ntt * 4 * 512 : 0;
     return b;
@@ -1578,7 +1584,7 @@ BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k
     const long rbg = (d_ff + kTileRows - 1) / kTileRows;
     b.gu_tiles = (long)n_experts * rbg * ntb;
     b.dn_tiles = (long)n_experts * ((d_model + kTileRows - 1) / kTileRows) * ntb;
-    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg);
+    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg, 192);
     b.ks_dn = 1;
     b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
     b.dn_part_floats = 0;
