@@ -66,6 +66,8 @@ struct TbArgs {
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
     float *part_gu, *part_dn; // tiled kernels: per-tile partial sums of the K splits
+    unsigned *cnt_gu, *cnt_dn; // tiled kernels: per tile, the K splits done (k_tb_prep zeroes them)
+    int n_cnt;               // entries of cnt_gu and cnt_dn together (contiguous)
     // Routed mode (top_k > 0; tiled kernels only): slot s = t*top_k + j of token
     // t goes to expert ids[s] with weight slot_w[s].  list[e*T + p], p <
     // cnt[e], are expert e's slots in ascending order; the hidden rows,

@@ -275,9 +275,12 @@ __device__ __forceinline__ void unit_split(uint4 raw, CodeWords<BITS, KB> (&cw)[
 // columns in registers (d_model <= 8192), the block finds the row's largest
 // |x|, and every chunk is written as two 16-byte stores (hi, lo).
 __global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, int cols, _Float16 *__restrict__ xh,
-                                                 _Float16 *__restrict__ xl, int *__restrict__ xe)
+                                                 _Float16 *__restrict__ xl, int *__restrict__ xe,
+                                                 unsigned *__restrict__ cnt, int n_cnt)
 {
     __shared__ float s_max[4];
+    // The tiled kernels' split counters start every call at zero.
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += gridDim.x * 256) cnt[i] = 0u;
     const size_t base = (size_t)blockIdx.x * cols;
     const int nch = cols / 8;
     float v[4][8];
@@ -681,8 +684,9 @@ __global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
 // passed the barrier that ends the step reading it.  The K dimension (the
 // groups of d_model, or the (expert, group) pairs) is split over `ks` blocks
 // when there would otherwise be too few blocks: each writes its partial sums
-// to the workspace and a finishing kernel adds them in split order
-// (deterministic), then applies the epilogue.
+// to the workspace, and either the last of a tile's splits to finish or a
+// finishing kernel adds them in split order (deterministic) and applies the
+// epilogue.
 constexpr int kTileWaves = 8;
 constexpr int kTileRows = 16 * kTileWaves;
 
@@ -809,6 +813,64 @@ __device__ __forceinline__ void sum_partials(f32x4 (&acc)[N], const float *part,
     }
 }
 
+// Where a tile's K splits are added: in the tiled kernel itself for 16-token
+// tiles (a split's slab is 8 or 16 KB; two launches fewer per call, and at 16
+// tokens the host takes longer to launch a call's kernels than the GPU to run
+// them), in a finishing pass for larger tiles (there the tile's last split,
+// reading up to 15 slabs of 32 or 64 KB through memory, took longer than a
+// pass of 16-token blocks: 64 tokens 90 -> 107 us).
+template <int NTT>
+constexpr bool kSplitsInKernel = NTT == 1;
+
+__device__ __forceinline__ float *partial_slot(float *part, int k, int r)
+{
+    return part + ((size_t)(4 * k + r) * 512 + threadIdx.x);
+}
+
+// K splits of a tile, reduced in the kernel.  Every split block stores its
+// accumulators at agent scope (the stores go to memory, past this XCD's L2),
+// waits for them, and counts itself in on the tile's counter; the block that
+// completes the count adds all the splits' partial sums in split order (its
+// own from registers, the others read at agent scope) and goes on to the
+// tile's epilogue; the others are done.  The sum does not depend on which
+// block comes last: bitwise the same result every call.  Float r of
+// accumulator k of thread t sits at (4k + r) * 512 + t of a split's slab, so
+// that a wave's stores and loads are 256 contiguous bytes.  `last` is LDS.
+// Returns whether this block holds the tile's sum.
+template <int N>
+__device__ bool split_reduce(f32x4 (&acc)[N], float *part, size_t stride, int ks, int splits, unsigned *cnt,
+                             int *last)
+{
+    float *mine = part + (size_t)ks * stride;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(partial_slot(mine, k, r), acc[k][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores have reached memory
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)splits - 1;
+    __syncthreads();
+    if (!*last) return false;
+    f32x4 own[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) own[k] = acc[k];
+    for (int s = 0; s < splits; ++s) {
+        const float *ps = part + (size_t)s * stride;
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = s == ks ? own[k][r]
+                                        : __hip_atomic_load(partial_slot(const_cast<float *>(ps), k, r),
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc[k][r] = s == 0 ? v : acc[k][r] + v;
+            }
+    }
+    return true;
+}
+
 // gate_up epilogue of a tile: hidden = SiLU(gate) * up for the wave's 16 rows
 // and the tile's tokens (tot scaled by the tokens' 2^-xe), normalised per (token, H group) by a power of two,
 // stored as hi/lo halves in sigma order with the factor r[t][e] * 2^e for
@@ -887,6 +949,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     constexpr int TT = 16 * NTT;
     constexpr int group = 32 * KB;
     extern __shared__ __align__(16) unsigned char smem[];   // two tiles, then the epilogue's maxima
+    __shared__ int s_last;                                  // the K split reduction's verdict
     const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, n = lane & 15;
@@ -1032,8 +1095,15 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
 
     if (KSG > 1) {
         const int tile_id = (e * RB + rb) * NTB + tb;
-        store_partial<2 * NTT>(tot, a.part_gu + ((size_t)tile_id * KSG + ks) * (2 * NTT * 4 * 512));
-        return;
+        constexpr size_t stride = (size_t)2 * NTT * 4 * 512;
+        if constexpr (kSplitsInKernel<NTT>) {
+            if (!split_reduce<2 * NTT>(tot, a.part_gu + (size_t)tile_id * KSG * stride, stride, ks, KSG,
+                                       a.cnt_gu + tile_id, &s_last))
+                return;   // another split of the tile finishes it
+        } else {
+            store_partial<2 * NTT>(tot, a.part_gu + ((size_t)tile_id * KSG + ks) * stride);
+            return;   // k_tb_gu_finish adds the splits
+        }
     }
     gu_epilogue<KB, NTT>(a, tot, e, rb, tb, reinterpret_cast<float *>(smem + 2 * Sh::kBytes));
 }
@@ -1087,6 +1157,7 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     constexpr int TT = 16 * NTT;
     constexpr int group = 32 * KB;
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_last;   // the K split reduction's verdict
     const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
     constexpr size_t tb_bytes = TileShape<KB, NTT>::kBytes;
     float *fac = reinterpret_cast<float *>(smem + 2 * tb_bytes);  // [2][TT]
@@ -1246,8 +1317,16 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
         return;
     }
     if (KSD > 1) {
-        store_partial<NTT>(tot, a.part_dn + ((size_t)(rb * NTB + tb) * KSD + ks) * (NTT * 4 * 512));
-        return;
+        const int tile_id = rb * NTB + tb;
+        constexpr size_t stride = (size_t)NTT * 4 * 512;
+        if constexpr (kSplitsInKernel<NTT>) {
+            if (!split_reduce<NTT>(tot, a.part_dn + (size_t)tile_id * KSD * stride, stride, ks, KSD,
+                                   a.cnt_dn + tile_id, &s_last))
+                return;   // another split of the tile finishes it
+        } else {
+            store_partial<NTT>(tot, a.part_dn + ((size_t)tile_id * KSD + ks) * stride);
+            return;   // k_tb_dn_finish adds the splits
+        }
     }
     dn_store<NTT>(a, tot, rb, tb);
 }
@@ -1269,13 +1348,14 @@ __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
 template <int BITS, int KB, int NTT, int MG, int SB>
 hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
+    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe, a.cnt_gu,
+                       a.n_cnt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, SB>), dim3(pl.gu_blocks),
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.ks_gu > 1) {
+    if (a.ks_gu > 1 && !kSplitsInKernel<NTT>) {
         hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu * NTT), dim3(64 * kTileWaves),
                            (size_t)kTileWaves * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1283,7 +1363,7 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
     hipLaunchKernelGGL((k_tb_down_tiled<BITS, KB, NTT, SB>), dim3(pl.dn_blocks), dim3(64 * kTileWaves),
                        pl.dn_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.ks_dn > 1) {
+    if (a.ks_dn > 1 && !kSplitsInKernel<NTT>) {
         hipLaunchKernelGGL(k_tb_dn_finish<NTT>, dim3(pl.dn_blocks / a.ks_dn * NTT), dim3(64 * kTileWaves), 0, st,
                            a);
         err = hipGetLastError();
@@ -1363,12 +1443,13 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
                        a.cnt, a.slot_ok);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
+    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe, a.cnt_gu,
+                       a.n_cnt);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, SB>), dim3(pl.gu_blocks),
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.ks_gu > 1) {
+    if (a.ks_gu > 1 && !kSplitsInKernel<NTT>) {
         hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu * NTT), dim3(64 * kTileWaves),
                            (size_t)kTileWaves * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1408,7 +1489,8 @@ hipError_t launch_routed_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStr
 template <int BITS, int KB, int NTT, int RTG, int RTD, int SB>
 hipError_t launch_tb_kernels(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe);
+    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe,
+                       (unsigned *)nullptr, 0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((k_tb_gate_up<BITS, KB, NTT, RTG, SB>), dim3(pl.gu_blocks), dim3(64 * pl.gu_waves), pl.gu_lds,
@@ -1469,8 +1551,8 @@ int tile_ntt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 
 // Splits of K over blocks: the smallest power of two (at most 16) that gives
 // `tiles` x splits >= `target` blocks of 8 waves.  Every split adds f32
-// partial sums written here and read by a finishing pass (64 KB per split of
-// a 64-token tile), so the smallest count that keeps the CUs busy is taken.
+// partial sums written to memory and read back (64 KB per split of a
+// 64-token tile), so the smallest count that keeps the CUs busy is taken.
 int splits_for(long tiles, long target)
 {
     int s = 1;

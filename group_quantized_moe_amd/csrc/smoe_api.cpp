@@ -124,9 +124,12 @@ DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
 //   hh, hl  f16 [n_experts][T][d_ff]         hi/lo halves of the scaled hidden rows
 //   hf      f32 [n_experts][d_ff/group][Tp]  per (expert, group, token) factors, Tp = T rounded up to 64
 //   pg, pd  f32                              partial sums of the gate_up / down K splits, per tile
-// Everything is rewritten by each call before it is read.
+//   cnt     u32 [gate_up tiles + down tiles] K splits of each tile done
+// Everything is rewritten by each call before it is read (the counters are
+// zeroed by the call's first kernel).
 struct BatchWorkspace {
-    size_t xh, xl, xe, hh, hl, hf, pg, pd, total;
+    size_t xh, xl, xe, hh, hl, hf, pg, pd, cnt, total;
+    int n_cnt, n_cnt_gu;
 };
 
 int token_pad(int T) { return (T + smoe::kTokenPad - 1) / smoe::kTokenPad * smoe::kTokenPad; }
@@ -144,7 +147,10 @@ BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int 
     w.hf = w.hl + align256(nh * 2);
     w.pg = w.hf + align256((size_t)n_experts * (d_ff / group) * token_pad(T) * 4);
     w.pd = w.pg + align256(bs.gu_part_floats * 4);
-    w.total = w.pd + align256(bs.dn_part_floats * 4);
+    w.cnt = w.pd + align256(bs.dn_part_floats * 4);
+    w.n_cnt_gu = (int)bs.gu_tiles;
+    w.n_cnt = (int)(bs.gu_tiles + bs.dn_tiles);
+    w.total = w.cnt + align256((size_t)w.n_cnt * 4);
     return w;
 }
 
@@ -156,9 +162,12 @@ BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int 
 //   list    i32 [n_experts][T]       each expert's slots, ascending; cnt i32 [n_experts]
 //   ok      i32 [T*top_k]            slot processed
 //   ys      f32 [T*top_k][d_model]   weighted output row of each slot
-// Everything is rewritten by each call before it is read.
+//   tcnt    u32 [gate_up tiles]      K splits of each gate_up tile done
+// Everything is rewritten by each call before it is read (the counters are
+// zeroed by the call's activation pass).
 struct RoutedWorkspace {
-    size_t xh, xl, xe, hh, hl, hf, pg, list, cnt, ok, ys, total;
+    size_t xh, xl, xe, hh, hl, hf, pg, list, cnt, ok, ys, tcnt, total;
+    int n_tcnt;
 };
 
 RoutedWorkspace routed_workspace(int n_experts, int d_model, int d_ff, int T, int top_k)
@@ -177,7 +186,9 @@ RoutedWorkspace routed_workspace(int n_experts, int d_model, int d_ff, int T, in
     w.cnt = w.list + align256((size_t)n_experts * T * 4);
     w.ok = w.cnt + align256((size_t)n_experts * 4);
     w.ys = w.ok + align256(ns * 4);
-    w.total = w.ys + align256(ns * d_model * 4);
+    w.tcnt = w.ys + align256(ns * d_model * 4);
+    w.n_tcnt = (int)bs.gu_tiles;
+    w.total = w.tcnt + align256((size_t)w.n_tcnt * 4);
     return w;
 }
 
@@ -379,6 +390,9 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
         a.hf = reinterpret_cast<float *>(ws + w.hf);
         a.part_gu = reinterpret_cast<float *>(ws + w.pg);
         a.part_dn = reinterpret_cast<float *>(ws + w.pd);
+        a.cnt_gu = reinterpret_cast<unsigned *>(ws + w.cnt);
+        a.cnt_dn = a.cnt_gu + w.n_cnt_gu;
+        a.n_cnt = w.n_cnt;
         a.T = T;
         a.t_pad = token_pad(T);
         a.d_model = d_model;
@@ -475,6 +489,9 @@ int smoe_routed_ffn(const smoe_expert *experts, int n_experts, int fmt, int grou
     a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
     a.hf = reinterpret_cast<float *>(ws + w.hf);
     a.part_gu = reinterpret_cast<float *>(ws + w.pg);
+    a.cnt_gu = reinterpret_cast<unsigned *>(ws + w.tcnt);
+    a.cnt_dn = nullptr;
+    a.n_cnt = w.n_tcnt;
     a.list = reinterpret_cast<int *>(ws + w.list);
     a.cnt = reinterpret_cast<int *>(ws + w.cnt);
     a.slot_ok = reinterpret_cast<int *>(ws + w.ok);
