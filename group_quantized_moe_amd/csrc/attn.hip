@@ -13,8 +13,8 @@
 //      chunk holds the new token also normalises and rotates k and appends k
 //      and v to the caches.  Then the scores, the chunk's max and exp-sum per
 //      head, and the chunk's unnormalised output rows;
-//   3. k_attn_combine: one block per query head merges the chunks into the
-//      attention output, summing in a fixed order (deterministic);
+//   3. k_attn_combine: blocks of 32 columns of a query head merge the chunks
+//      into the attention output, summing in a fixed order (deterministic);
 //   4. the output projection as a bf16 matvec.
 // Everything is f32 but the rotation angles, which are formed and reduced to
 // [-pi, pi] in f64: pos * base^(-2i/hd) reaches thousands of radians, where an
@@ -222,17 +222,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(AttnArgs a)
     }
 }
 
-// Query head h: merge the chunks.  att[h][d] = sum_c e^(m_c - M) o_c[d] /
-// sum_c e^(m_c - M) l_c, M = max_c m_c.  The 1024 threads take column d and
-// one of P = 1024 / HD contiguous chunk ranges each (independent loads, all in
-// flight), and the P range sums are added in range order: deterministic.
+// Query head h, columns 32y .. 32y + 31 (block (h, y)): merge the chunks.
+// att[h][d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c, M = max_c m_c.
+// The 1024 threads take column d and one of P = 32 contiguous chunk ranges
+// each (independent loads, all in flight), and the P range sums are added in
+// range order: deterministic.  Four blocks per head of 128 (one per head,
+// each thread a range of 16 chunks, took 5.7 us against 4.6 us).
 constexpr int kCombineThreads = 1024;
+constexpr int kCombineCols = 32;   // columns of a head per block
 template <int HD>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
 {
-    constexpr int P = kCombineThreads / HD;
+    constexpr int P = kCombineThreads / kCombineCols;
     __shared__ float red[kCombineThreads / 64];
-    __shared__ float part_o[P][HD];
+    __shared__ float part_o[P][kCombineCols];
     __shared__ float part_l[P];
     const int h = blockIdx.x, t = threadIdx.x;
     const int G = a.n_head / a.n_kv, g = h / G, hq = h - g * G;
@@ -248,7 +251,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
     float M = red[0];
 #pragma unroll
     for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
-    const int d = t % HD, pr = t / HD;
+    const int dl = t % kCombineCols, pr = t / kCombineCols;
+    const int d = blockIdx.y * kCombineCols + dl;
     const int c0 = (int)((long)pr * nc / P), c1 = (int)((long)(pr + 1) * nc / P);
     const float *po = a.part_o + ((size_t)g * a.n_chunks * G + hq) * HD + d;
     float L = 0.0f, o = 0.0f;
@@ -258,14 +262,14 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnArgs a)
         L += w * ml[c * cstride + 1];
         o += w * po[(size_t)c * G * HD];
     }
-    part_o[pr][d] = o;
-    if (d == 0) part_l[pr] = L;
+    part_o[pr][dl] = o;
+    if (dl == 0) part_l[pr] = L;
     __syncthreads();
     if (pr == 0) {
-        float os = part_o[0][d], ls = part_l[0];
+        float os = part_o[0][dl], ls = part_l[0];
 #pragma unroll
         for (int q = 1; q < P; ++q) {
-            os += part_o[q][d];
+            os += part_o[q][dl];
             ls += part_l[q];
         }
         a.att[(size_t)h * HD + d] = os / ls;
@@ -279,7 +283,7 @@ hipError_t launch_attn_hd(const AttnArgs &a, hipStream_t st)
     hipLaunchKernelGGL(k_attn_partial<HD>, dim3(nc, a.n_kv), dim3(kAttnThreads), 0, st, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_attn_combine<HD>, dim3(a.n_head), dim3(kCombineThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_combine<HD>, dim3(a.n_head, HD / kCombineCols), dim3(kCombineThreads), 0, st, a);
     return hipGetLastError();
 }
 
