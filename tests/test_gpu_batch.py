@@ -82,6 +82,35 @@ def test_batch_deterministic(gq, q4_group8):
     assert np.array_equal(a, b)
 
 
+def test_batch_workspace_any_contents_and_reuse(gq, oracle_lib, q4_group8):
+    """16-token tiles add their K splits inside the tiled kernels through
+    per-tile counters kept in the workspace, which every call zeroes itself:
+    a workspace full of 0xFF bytes, reused for 16, 64 and again 16 tokens,
+    gives the oracle's rows and the same bits as a fresh zeroed one."""
+    import torch
+    g, de = q4_group8
+    X16, R16 = workloads.make_batch_inputs(16)
+    X64, R64 = workloads.make_batch_inputs(64)
+    nbytes = max(gq.smoe_expert_ffn_workspace(8, g.d_model, g.d_ff, T) for T in (16, 64))
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+
+    def call(X, R):
+        T = X.shape[0]
+        out = torch.empty(T * g.d_model, dtype=torch.float32, device="cuda")
+        gq.smoe_expert_ffn(de, 4, 64, dev(X), out, route_w=dev(R), workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().reshape(T, g.d_model)
+
+    first = call(X16, R16)
+    want = oracle_lib.expert_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X16, R16)
+    assert_parity(first, want, "T=16 on a 0xFF workspace")
+    mid = call(X64, R64)
+    assert np.array_equal(mid, run_ffn(gq, de, 4, 64, X64, route=R64)), "T=64 on a reused workspace"
+    again = call(X16, R16)
+    assert np.array_equal(first, again), "T=16 after T=64 on the same workspace"
+    assert np.array_equal(first, run_ffn(gq, de, 4, 64, X16, route=R16)), "0xFF workspace vs a zeroed one"
+
+
 BATCH_EDGE = [  # bits, group, d_model, d_ff, n_experts, T
     (4, 64, 256, 512, 2, 2),
     (4, 64, 256, 512, 1, 17),
