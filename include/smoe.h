@@ -143,14 +143,18 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  *               each call overwrites.  Calls that share a workspace must be
  *               ordered (one stream), or they race.
  * T == 1 runs the decode kernels (a gate_up launch and a down launch that also
- * combines the experts, deterministically: the sum over experts is taken in
- * ascending expert order).
+ * combines the experts, deterministically: each router-weighted expert row is
+ * rounded to a multiple of 2^-32 and summed exactly in 64-bit integers, so the
+ * result does not depend on the order in which experts finish).
  * 2 <= T <= SMOE_MAX_TOKENS runs the token-batch kernels on the matrix cores,
  * in which every expert processes every token: an activation pass, a gate_up
  * pass and a down pass that sums the experts in a fixed order (deterministic,
- * no atomics).  With few tokens the K dimension of either pass is split over
- * blocks whose partial sums a finishing pass adds in a fixed order.  They need group = 32, 64, 96 or 128 at 4 bits and 64 or 128 at
- * 2 bits, else SMOE_ERR_GROUP.  Activations are carried to the matrix cores
+ * no atomics in the sums).  With few tokens the K dimension of either pass
+ * is split over blocks whose partial sums are added in a fixed split order,
+ * by a finishing pass or, for tiles of 16 tokens, by the tile's last split
+ * block (one counter per tile in the workspace, zeroed by the call itself).
+ * They need group = 32, 64, 96 or 128 at 4 bits and 64 or 128 at 2 bits, else
+ * SMOE_ERR_GROUP.  Activations are carried to the matrix cores
  * as two f16 halves scaled by a power of two per group, about 22 significant
  * bits; non-finite inputs give non-finite outputs.
  * The workspace size depends on (n_experts, d_model, d_ff, T) only; for T > 1
