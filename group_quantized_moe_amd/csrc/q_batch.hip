@@ -949,7 +949,7 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     constexpr int TT = 16 * NTT;
     constexpr int group = 32 * KB;
     extern __shared__ __align__(16) unsigned char smem[];   // two tiles, then the epilogue's maxima
-    __shared__ int s_last;                                  // the K split reduction's verdict
+    __shared__ int s_last;                                  // whether this block adds the tile's K splits
     const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, n = lane & 15;
@@ -1157,7 +1157,7 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     constexpr int TT = 16 * NTT;
     constexpr int group = 32 * KB;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_last;   // the K split reduction's verdict
+    __shared__ int s_last;   // whether this block adds the tile's K splits
     const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
     constexpr size_t tb_bytes = TileShape<KB, NTT>::kBytes;
     float *fac = reinterpret_cast<float *>(smem + 2 * tb_bytes);  // [2][TT]
