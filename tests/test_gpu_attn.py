@@ -80,6 +80,15 @@ def test_attn_full_block(gq, oracle_lib, pos):
     check_block(gq, oracle_lib, spec, pos, f"attn full pos {pos}")
 
 
+@pytest.mark.parametrize("pos", [8191, 16383])
+def test_attn_long_context(gq, oracle_lib, pos):
+    """A 16384-position cache (512 chunks of 32, merged in 32 ranges of 16):
+    the last position and one in the middle of the cache."""
+    spec = dict(d_model=256, n_head=8, n_kv=2, head_dim=64, max_ctx=16384, seed=61, rope_base=1e6,
+                name="long")
+    check_block(gq, oracle_lib, spec, pos, f"attn long context pos {pos}")
+
+
 def test_attn_sequential_decode(gq, oracle_lib):
     """Forty tokens decoded in turn from an empty cache: each side keeps its own
     cache, and every step's output and appended rows agree."""
