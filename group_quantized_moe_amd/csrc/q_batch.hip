@@ -856,17 +856,31 @@ __device__ bool split_reduce(f32x4 (&acc)[N], float *part, size_t stride, int ks
     f32x4 own[N];
 #pragma unroll
     for (int k = 0; k < N; ++k) own[k] = acc[k];
-    for (int s = 0; s < splits; ++s) {
-        const float *ps = part + (size_t)s * stride;
+    // Slabs are read B at a time, all of a round's loads in flight together,
+    // then added in split order.
+    constexpr int B = N <= 2 ? 8 : 4;
+    for (int s0 = 0; s0 < splits; s0 += B) {
+        float v[B][N][4];
 #pragma unroll
-        for (int k = 0; k < N; ++k)
+        for (int b = 0; b < B; ++b) {
+            const int s = min(s0 + b, splits - 1);   // past the last split: re-read it, unused
+            const float *ps = part + (size_t)s * stride;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v = s == ks ? own[k][r]
-                                        : __hip_atomic_load(partial_slot(const_cast<float *>(ps), k, r),
-                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                acc[k][r] = s == 0 ? v : acc[k][r] + v;
-            }
+            for (int k = 0; k < N; ++k)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[b][k][r] = s == ks ? own[k][r]
+                                         : __hip_atomic_load(partial_slot(const_cast<float *>(ps), k, r),
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (s0 + b >= splits) break;
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[k][r] = s0 + b == 0 ? v[b][k][r] : acc[k][r] + v[b][k][r];
+        }
     }
     return true;
 }
