@@ -858,7 +858,7 @@ __device__ bool split_reduce(f32x4 (&acc)[N], float *part, size_t stride, int ks
     for (int k = 0; k < N; ++k) own[k] = acc[k];
     // Slabs are read B at a time, all of a round's loads in flight together,
     // then added in split order.
-    constexpr int B = N <= 2 ? 8 : 4;
+    constexpr int B = N <= 2 ? 8 : 16 / N;   // at most 64 floats in flight a thread
     for (int s0 = 0; s0 < splits; s0 += B) {
         float v[B][N][4];
 #pragma unroll
