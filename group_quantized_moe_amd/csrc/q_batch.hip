@@ -816,9 +816,10 @@ __device__ __forceinline__ void sum_partials(f32x4 (&acc)[N], const float *part,
 // Where a tile's K splits are added: in the tiled kernel itself for 16-token
 // tiles (a split's slab is 8 or 16 KB; two launches fewer per call, and at 16
 // tokens the host takes longer to launch a call's kernels than the GPU to run
-// them), in a finishing pass for larger tiles (there the tile's last split,
-// reading up to 15 slabs of 32 or 64 KB through memory, took longer than a
-// pass of 16-token blocks: 64 tokens 90 -> 107 us).
+// them), in a finishing pass for larger tiles (there every split block's
+// store, wait and count of a 32 or 64 KB slab, and the last one's reads,
+// sit in the kernel's tail: 64 tokens 93 against 90 us, 128 tokens 174
+// against 142, 256 tokens 259 against 232).
 template <int NTT>
 constexpr bool kSplitsInKernel = NTT == 1;
 
