@@ -541,7 +541,7 @@ __device__ __forceinline__ float acc_value(unsigned long long sum, int n)
     return (float)((double)fixed * (1.0 / 4294967296.0));
 }
 
-template <int BITS, int NCH, int LPR, int DEPTH, int SB>
+template <int BITS, int NCH, int LPR, int SB>
 __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
@@ -576,12 +576,8 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     load_vec_regs<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, hr);
     wait_vm_all();   // the hidden vector before the code loads, as in gate_up
     const bool busy = sb < se;
-    Stage<NCH, 1> S[DEPTH];
-    if (busy) {
-#pragma unroll
-        for (int i = 0; i < DEPTH; ++i)
-            if (sb + i < se) load(S[i], sb + i);
-    }
+    Stage<NCH, 1> S[2];
+    if (busy) load(S[0], sb);
 
     build_planes<BITS>(hr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
     ChunkVec<BITS> cv[NCH];
@@ -589,11 +585,17 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
     for (int k = 0; k < NCH; ++k)
         load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
 
-    for (int base = sb; base < se; base += DEPTH) {
+    // One step of loads in flight, in two register slots: a step's loads go
+    // out as soon as the previous step's have come back, before that step's
+    // arithmetic (measured 0.5 us faster than issuing them after it, and about
+    // 1 us faster than keeping two steps in flight).
+    for (int base = sb; base < se; base += 2) {
 #pragma unroll
-        for (int i = 0; i < DEPTH; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const int st = base + i;
             if (st < se) {
+                wait_vm_all();                                // this step's loads are in
+                if (st + 1 < se) load(S[i ^ 1], st + 1);     // the next step's go out first
                 float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv);
                 y = group_sum<LPR>(y);
                 const int r = st * rs + ln.slot;
@@ -604,7 +606,6 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
                         mine[(st - sb) * rs + ln.slot] = y * rw;
                 }
             }
-            if (st + DEPTH < se) load(S[i], st + DEPTH);
         }
     }
 
@@ -661,11 +662,11 @@ hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStr
     return hipGetLastError();
 }
 
-template <int BITS, int NCH, int LPR, int DEPTH, int SB>
+template <int BITS, int NCH, int LPR, int SB>
 hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
 {
     const int block = 64 * p.nw;
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, DEPTH, SB>);
+    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, SB>);
     const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
     // Resident blocks: the occupancy query's answer, but at most two blocks of
     // this size per CU (more were measured not to be co-resident, which puts a
@@ -678,7 +679,7 @@ hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
     const long waves = per_expert * p.nw;
     a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
     const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
-    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, DEPTH, SB>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
+    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, SB>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
                        a);
     return hipGetLastError();
 }
@@ -744,9 +745,10 @@ bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, Decod
     return true;
 }
 
-// Steps in flight per wave (the register ring of code and scale loads).
+// gate_up: steps in flight per wave (the register ring of code and scale
+// loads).  down has its own order: a step's loads go out once the previous
+// step's have come back, ahead of its arithmetic.
 constexpr int kGateUpDepth = 1;
-constexpr int kDownDepth = 1;
 
 // Kernels are compiled per (bits, chunks per lane, lanes per row): lanes per
 // row 16, 32 or 64; chunks per lane 1..4 (4-bit) or 1..2 (2-bit).
@@ -770,8 +772,8 @@ hipError_t launch_down(int bits, const DecodePlan &p, const DecodeArgs &a, int c
 {
 #define SMOE_RUN(B, N, L)                                                                  \
     if (bits == B && p.nch_d == N && p.lpr_d == L)                                         \
-        return a.scale_bytes == 2 ? run_down<B, N, L, kDownDepth, 2>(p, a, cus, st)        \
-                                  : run_down<B, N, L, kDownDepth, 4>(p, a, cus, st);
+        return a.scale_bytes == 2 ? run_down<B, N, L, 2>(p, a, cus, st)                    \
+                                  : run_down<B, N, L, 4>(p, a, cus, st);
     SMOE_FOR_ALL(SMOE_RUN)
 #undef SMOE_RUN
     return hipErrorInvalidConfiguration;
