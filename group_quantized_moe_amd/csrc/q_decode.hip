@@ -678,10 +678,10 @@ hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
     const int block = 64 * p.nw;
     const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, SB>);
     const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
-    // Resident blocks: the occupancy query's answer, but at most two blocks of
-    // this size per CU (more were measured not to be co-resident, which puts a
-    // second round of blocks after the first).
-    const long cap = (long)cus * std::min(2, blocks_per_cu(fn, block, planes + 4096));
+    // One block per CU: with a step's loads issued as soon as the previous
+    // step's are in, four row steps a wave on one block per CU measured 0.4 us
+    // faster than two on two (Q4 group; the same for Q2).
+    const long cap = (long)cus * std::min(1, blocks_per_cu(fn, block, planes + 4096));
     if (cap < a.n_experts) return hipErrorInvalidConfiguration;
     const int rs = 64 / p.lpr_d;
     const long steps = (a.d_model + rs - 1) / rs;
