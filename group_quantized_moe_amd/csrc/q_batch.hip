@@ -1684,7 +1684,11 @@ BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k
     const long rbg = (d_ff + kTileRows - 1) / kTileRows;
     b.gu_tiles = (long)n_experts * rbg * ntb;
     b.dn_tiles = (long)n_experts * ((d_model + kTileRows - 1) / kTileRows) * ntb;
-    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg, 192);
+    // K splits for gate_up from the expected active tiles: 192 blocks, or 384
+    // with 64-token tiles, whose work pays for the finishing pass (256 tokens
+    // x top-4 of 8: 225 -> 207 us; at top-2 with 32-token tiles the pass
+    // costs what the split gains, and at top-1 splitting further is slower).
+    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg, b.ntt == 4 ? 384 : 192);
     b.ks_dn = 1;
     b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
     b.dn_part_floats = 0;
