@@ -1134,10 +1134,32 @@ __global__ __launch_bounds__(512) void k_tb_gu_finish(TbArgs a)
     constexpr int TT = 16 * NTT;
     const int NTB = (a.T + TT - 1) / TT;
     const int RB = (a.d_ff + kTileRows - 1) / kTileRows;
-    const int tile_id = blockIdx.x / NTT, tt = blockIdx.x % NTT;
-    const int tb = tile_id % NTB, rb = (tile_id / NTB) % RB, e = tile_id / NTB / RB;
-    const int tb16 = tb * NTT + tt;   // the block's 16 tokens, as a 16-token tile
-    if (a.top_k && tb16 * 16 >= a.cnt[e]) return;   // routed mode: no slots there
+    int tile_id, tt, e, rb, tb16;
+    if (a.top_k) {
+        // Routed mode: block (row block rb, chunk c) takes the c-th 16-slot
+        // chunk of the experts' slot lists, taken in expert order; the grid
+        // holds at least as many chunks as there can be (T top_k / 16 +
+        // n_experts per row block), and blocks past the last one exit.
+        const int C = gridDim.x / RB;
+        rb = blockIdx.x / C;
+        int c = blockIdx.x % C;
+        for (e = 0; e < a.n_experts; ++e) {
+            const int n16 = (a.cnt[e] + 15) >> 4;
+            if (c < n16) break;
+            c -= n16;
+        }
+        if (e == a.n_experts) return;
+        tb16 = c;
+        tt = c % NTT;
+        tile_id = (e * RB + rb) * NTB + c / NTT;
+    } else {
+        tile_id = blockIdx.x / NTT;
+        tt = blockIdx.x % NTT;
+        const int tb = tile_id % NTB;
+        rb = (tile_id / NTB) % RB;
+        e = tile_id / NTB / RB;
+        tb16 = tb * NTT + tt;   // the block's 16 tokens, as a 16-token tile
+    }
     constexpr size_t stride = (size_t)2 * NTT * 4 * 512;
     f32x4 tot[2];
     sum_partials<2>(tot, a.part_gu + (size_t)tile_id * a.ks_gu * stride, stride, a.ks_gu, {tt, NTT + tt});
@@ -1465,7 +1487,10 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.ks_gu > 1 && !kSplitsInKernel<NTT>) {
-        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3(pl.gu_blocks / a.ks_gu * NTT), dim3(64 * kTileWaves),
+        // One block per 16-slot chunk of the slot lists and row block.
+        const long chunks = ((long)a.T * a.top_k + 15) / 16 + a.n_experts;
+        const long rbs = (a.d_ff + kTileRows - 1) / kTileRows;
+        hipLaunchKernelGGL((k_tb_gu_finish<KB, NTT>), dim3((unsigned)(rbs * chunks)), dim3(64 * kTileWaves),
                            (size_t)kTileWaves * 16 * 4, st, a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -1685,10 +1710,10 @@ BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k
     b.gu_tiles = (long)n_experts * rbg * ntb;
     b.dn_tiles = (long)n_experts * ((d_model + kTileRows - 1) / kTileRows) * ntb;
     // K splits for gate_up from the expected active tiles: 192 blocks, or 384
-    // with 64-token tiles, whose work pays for the finishing pass (256 tokens
-    // x top-4 of 8: 225 -> 207 us; at top-2 with 32-token tiles the pass
-    // costs what the split gains, and at top-1 splitting further is slower).
-    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg, b.ntt == 4 ? 384 : 192);
+    // with 32- or 64-token tiles, whose work pays for the finishing pass (256
+    // tokens x top-4 of 8: 225 -> 207 us, top-2: 150 -> 146 us; at top-1,
+    // where the splits are added in the kernel, more of them were slower).
+    b.ks_gu = splits_for((long)n_experts * rbg * ntb_avg, b.ntt >= 2 ? 384 : 192);
     b.ks_dn = 1;
     b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
     b.dn_part_floats = 0;
