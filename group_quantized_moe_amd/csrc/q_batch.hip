@@ -274,14 +274,14 @@ __device__ __forceinline__ void unit_split(uint4 raw, CodeWords<BITS, KB> (&cw)[
 // 256 threads per token, one pass: each thread keeps up to 4 chunks of 8
 // columns in registers (d_model <= 8192), the block finds the row's largest
 // |x|, and every chunk is written as two 16-byte stores (hi, lo).
-__global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, int cols, _Float16 *__restrict__ xh,
-                                                 _Float16 *__restrict__ xl, int *__restrict__ xe,
-                                                 unsigned *__restrict__ cnt, int n_cnt)
+__device__ __forceinline__ void prep_token(const float *__restrict__ x, int cols, _Float16 *__restrict__ xh,
+                                           _Float16 *__restrict__ xl, int *__restrict__ xe,
+                                           unsigned *__restrict__ cnt, int n_cnt, int tok, int ntok)
 {
     __shared__ float s_max[4];
     // The tiled kernels' split counters start every call at zero.
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += gridDim.x * 256) cnt[i] = 0u;
-    const size_t base = (size_t)blockIdx.x * cols;
+    for (int i = tok * 256 + threadIdx.x; i < n_cnt; i += ntok * 256) cnt[i] = 0u;
+    const size_t base = (size_t)tok * cols;
     const int nch = cols / 8;
     float v[4][8];
     float m = 0.0f;
@@ -319,7 +319,14 @@ __global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, in
             reinterpret_cast<half8 *>(xl + base)[c] = lo;
         }
     }
-    if (threadIdx.x == 0) xe[blockIdx.x] = e;
+    if (threadIdx.x == 0) xe[tok] = e;
+}
+
+__global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, int cols, _Float16 *__restrict__ xh,
+                                                 _Float16 *__restrict__ xl, int *__restrict__ xe,
+                                                 unsigned *__restrict__ cnt, int n_cnt)
+{
+    prep_token(x, cols, xh, xl, xe, cnt, n_cnt, blockIdx.x, gridDim.x);
 }
 
 // One step of the K loop: the activation fragments of NTT token tiles and
@@ -1416,11 +1423,11 @@ hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 // downstream are deterministic.  An expert keeps at most T slots (a token's
 // ids are distinct, so no slot is lost); slot_ok[s] marks the kept slots of
 // ids in [0, n_experts).
-__global__ __launch_bounds__(256) void k_route_bucket(const int *__restrict__ ids, int T, int top_k, int *list,
-                                                      int *cnt, int *slot_ok)
+__device__ __forceinline__ void route_bucket(const int *__restrict__ ids, int T, int top_k, int *list, int *cnt,
+                                             int *slot_ok, int e)
 {
     __shared__ int s_wave[4];
-    const int e = blockIdx.x, n = T * top_k;
+    const int n = T * top_k;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int base = 0;
     for (int c0 = 0; c0 < n; c0 += 256) {
@@ -1442,6 +1449,16 @@ __global__ __launch_bounds__(256) void k_route_bucket(const int *__restrict__ id
         __syncthreads();
     }
     if (threadIdx.x == 0) cnt[e] = min(base, T);
+}
+
+// The routed call's first launch: blocks 0 .. n_experts - 1 list the experts'
+// slots, the T blocks after them prepare the tokens (the two are independent).
+__global__ __launch_bounds__(256) void k_route_prep(TbArgs a)
+{
+    if ((int)blockIdx.x < a.n_experts)
+        route_bucket(a.ids, a.T, a.top_k, a.list, a.cnt, a.slot_ok, blockIdx.x);
+    else
+        prep_token(a.x, a.d_model, a.xh, a.xl, a.xe, a.cnt_gu, a.n_cnt, blockIdx.x - a.n_experts, a.T);
 }
 
 // out[t][:] = sum over the token's slots j (ascending) that were processed of
@@ -1476,13 +1493,9 @@ __global__ __launch_bounds__(256) void k_route_combine(const int *__restrict__ i
 template <int BITS, int KB, int NTT, int MG, int SB>
 hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_route_bucket, dim3((unsigned)a.n_experts), dim3(256), 0, st, a.ids, a.T, a.top_k, a.list,
-                       a.cnt, a.slot_ok);
+    hipLaunchKernelGGL(k_route_prep, dim3((unsigned)(a.n_experts + a.T)), dim3(256), 0, st, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe, a.cnt_gu,
-                       a.n_cnt);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL((k_tb_gate_up_tiled<BITS, KB, NTT, MG, SB>), dim3(pl.gu_blocks),
                        dim3(64 * kTileWaves), pl.gu_lds, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
