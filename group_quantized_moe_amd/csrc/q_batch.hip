@@ -984,14 +984,33 @@ __global__ __launch_bounds__(512) void k_tb_gate_up_tiled(TbArgs a)
     // XCD gets share codes across token tiles and activation tiles across row
     // blocks and experts).
     int b = xcd_logical(blockIdx.x, gridDim.x);
-    const int tb = b % NTB;
-    b /= NTB;
-    const int rb = b % RB;
-    b /= RB;
-    const int e = b % E;
-    const int ks = b / E;
+    int tb, rb, e, ks;
+    if (a.top_k) {
+        // Routed mode, order chunk, row block, split: chunk c is the c-th
+        // token tile of the experts' slot lists, taken in expert order (the
+        // grid holds an upper bound of them; blocks past the last exit).
+        const int C = gridDim.x / (RB * KSG);
+        int c = b % C;
+        b /= C;
+        rb = b % RB;
+        ks = b / RB;
+        for (e = 0; e < E; ++e) {
+            const int nt = (a.cnt[e] + TT - 1) / TT;
+            if (c < nt) break;
+            c -= nt;
+        }
+        if (e == E) return;   // whole block, before any barrier
+        tb = c;
+    } else {
+        tb = b % NTB;
+        b /= NTB;
+        rb = b % RB;
+        b /= RB;
+        e = b % E;
+        ks = b / E;
+    }
     const int t0 = tb * TT;
-    // Routed mode: the tile's rows are expert e's slots; tiles past its count are empty.
+    // Routed mode: the tile's rows are expert e's slots.
     const int rows = a.top_k ? a.cnt[e] : T;
     if (t0 >= rows) return;   // whole block, before any barrier
     const int wrow0 = rb * kTileRows + wave * 16;   // this wave's first d_ff row
@@ -1215,10 +1234,27 @@ __global__ __launch_bounds__(512) void k_tb_down_tiled(TbArgs a)
     // gets share codes across token tiles and hidden tiles across row blocks).
     const int RB = (d_model + kTileRows - 1) / kTileRows;
     int bid = xcd_logical(blockIdx.x, gridDim.x);
-    const int tb = bid % NTB;
-    bid /= NTB;
-    const int rb = bid % RB;
-    const int ks = bid / RB;   // routed mode (one split): the block's expert
+    int tb, rb, ks;   // routed mode (one split): ks is the block's expert
+    if (a.top_k) {
+        // Routed mode, order chunk, row block: chunk c is the c-th token tile
+        // of the experts' slot lists, taken in expert order (the grid holds an
+        // upper bound of them; blocks past the last exit).
+        const int C = gridDim.x / RB;
+        int c = bid % C;
+        rb = bid / C;
+        for (ks = 0; ks < E; ++ks) {
+            const int nt = (a.cnt[ks] + TT - 1) / TT;
+            if (c < nt) break;
+            c -= nt;
+        }
+        if (ks == E) return;   // whole block, before any barrier
+        tb = c;
+    } else {
+        tb = bid % NTB;
+        bid /= NTB;
+        rb = bid % RB;
+        ks = bid / RB;
+    }
     const int t0 = tb * TT;
     const int rows = a.top_k ? a.cnt[ks] : T;   // routed mode: expert ks's slots
     if (t0 >= rows) return;                      // whole block, before any barrier
@@ -1748,9 +1784,13 @@ bool plan_routed(int bits, int group, int d_model, int d_ff, int n_experts, int 
     while (G % p.mg) p.mg /= 2;
     p.ks_gu = std::min(bs.ks_gu, (G + 3) / 4);   // splits of whole 4-group iterations
     p.ks_dn = 1;
-    p.gu_blocks = bs.gu_tiles * p.ks_gu;
-    p.dn_blocks = bs.dn_tiles;
     const int tt = 16 * p.ntt;
+    // Grids of chunk x row block (x split): an expert's list of c slots takes
+    // ceil(c / tt) token tiles, at most T top_k / tt + n_experts over all of
+    // them (not n_experts x ceil(T / tt), most of which would be empty).
+    const long chunks = ((long)T * top_k + tt - 1) / tt + n_experts;
+    p.gu_blocks = (long)((d_ff + kTileRows - 1) / kTileRows) * p.ks_gu * chunks;
+    p.dn_blocks = (long)((d_model + kTileRows - 1) / kTileRows) * chunks;
     p.gu_lds = 2 * ((size_t)2 * tt * (p.mg * group + 8) * 2) + (size_t)kTileWaves * p.ntt * 16 * 4;
     p.dn_lds = 2 * ((size_t)2 * tt * (group + 8) * 2) + 2 * tt * 4;
     if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
