@@ -1748,11 +1748,12 @@ BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k
     // Lists are ragged (their lengths spread around the average), and a list's
     // last tile costs a full tile: 32-token tiles waste less of it than 64 and
     // measured faster up to an average of 96 (256 tokens x top-2 of 8: 194 ->
-    // 136 us of gate_up + down); with fuller lists 64-token tiles do better.
-    // Up to an average of 32, 16-token tiles (whose K splits are added in the
-    // kernel, no finishing pass): 256 tokens x top-1 of 8 147 -> 127 us, while
-    // at an average of 64 (top-2) they took 195 us against 150.
-    b.ntt = std::min(tile_ntt(T), avg > 96 ? 4 : avg > 32 ? 2 : 1);
+    // 136 us of gate_up + down, and with the grids over the actual tiles 128
+    // against 112 us for the call); with fuller lists 64-token tiles do
+    // better.  At an average of 32 (256 tokens x top-1 of 8) 32-token tiles
+    // took 94 us against 111 for 16-token ones, which are kept for averages
+    // up to 16.
+    b.ntt = std::min(tile_ntt(T), avg > 96 ? 4 : avg > 16 ? 2 : 1);
     const int tt = 16 * b.ntt;
     const long ntb = (T + tt - 1) / tt, ntb_avg = (std::min<long>(avg, T) + tt - 1) / tt;
     const long rbg = (d_ff + kTileRows - 1) / kTileRows;
