@@ -1749,11 +1749,12 @@ BatchSplits routed_splits(int n_experts, int d_model, int d_ff, int T, int top_k
     // last tile costs a full tile: 32-token tiles waste less of it than 64 and
     // measured faster up to an average of 96 (256 tokens x top-2 of 8: 194 ->
     // 136 us of gate_up + down, and with the grids over the actual tiles 128
-    // against 112 us for the call); with fuller lists 64-token tiles do
-    // better.  At an average of 32 (256 tokens x top-1 of 8) 32-token tiles
-    // took 94 us against 111 for 16-token ones, which are kept for averages
-    // up to 16.
-    b.ntt = std::min(tile_ntt(T), avg > 96 ? 4 : avg > 16 ? 2 : 1);
+    // against 112 us for the call; top-4, an average of 128: 198 against 177
+    // us); at an average of 256 (top-8) 64-token tiles do better (256 against
+    // 294 us), and the switch is put half way.  At an average of 32 (256
+    // tokens x top-1 of 8) 32-token tiles took 94 us against 111 for 16-token
+    // ones, which are kept for averages up to 16.
+    b.ntt = std::min(tile_ntt(T), avg > 192 ? 4 : avg > 16 ? 2 : 1);
     const int tt = 16 * b.ntt;
     const long ntb = (T + tt - 1) / tt, ntb_avg = (std::min<long>(avg, T) + tt - 1) / tt;
     const long rbg = (d_ff + kTileRows - 1) / kTileRows;

@@ -53,15 +53,16 @@ def test_routed_prefill_workload(gq, oracle_lib, q4_group8):
     assert np.array_equal(got, run_routed(gq, de, 4, 64, X, ids, w))
 
 
-def test_routed_prefill_top4(gq, oracle_lib, q4_group8):
-    """256 tokens, top-4 of 8 Q4 experts (64-token tiles, gate_up split in K):
+@pytest.mark.parametrize("k", [4, 8])
+def test_routed_prefill_top4_top8(gq, oracle_lib, q4_group8, k):
+    """256 tokens, top-4 and top-8 of 8 Q4 experts (32- and 64-token tiles):
     sampled tokens against the oracle."""
     g, de = q4_group8
-    X, ids, w = workloads.make_routed_inputs(256, 4, 4255)
+    X, ids, w = workloads.make_routed_inputs(256, k, 4251 + k)
     got = run_routed(gq, de, 4, 64, X, ids, w)
     rows = [0, 5, 63, 64, 130, 191, 255]
     want = oracle_lib.routed_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X[rows], ids[rows], w[rows])
-    assert_parity(got[rows], want, "routed T=256 top-4")
+    assert_parity(got[rows], want, f"routed T=256 top-{k}")
 
 
 def test_routed_full_routing_equals_dense(gq, q4_group8):
@@ -85,7 +86,7 @@ ROUTED_EDGE = [  # bits, group, d_model, d_ff, n_experts, T, top_k, routing
     (4, 64, 256, 512, 4, 20, 3, "holes"),       # some slots out of range
     (4, 64, 8192, 128, 2, 9, 1, "topk"),
     (4, 64, 384, 320, 3, 50, 2, "topk"),       # 6 and 5 groups: partial iterations in routed mode
-    (4, 64, 384, 320, 2, 130, 2, "topk"),      # 64-token tiles with gate_up split in 2 (finishing pass)
+    (4, 64, 384, 320, 2, 200, 2, "topk"),      # 64-token tiles with gate_up split in 2 (finishing pass)
 ]
 
 
