@@ -347,7 +347,7 @@ def routed_bench(args):
                    "replicas_rotated": replicas, "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm" if hbm_bound else "mfma",
-            "kernel": "one smoe_routed_ffn call (bucket, prep, gate_up [+ finish], down, combine)",
+            "kernel": "one smoe_routed_ffn call (slot lists with token prep, gate_up [+ finish], down, combine)",
             "achieved": round(gbs if hbm_bound else tflops, 2),
             "peak": PEAK_HBM_GBS if hbm_bound else PEAK_F16_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
