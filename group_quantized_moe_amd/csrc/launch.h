@@ -34,10 +34,9 @@ struct DecodeArgs {
     float *hidden;           // [n_experts][d_ff]
     const float *route_w;    // [n_experts] or null (weight 1)
     float *out;              // [d_model]
-    unsigned long long *row_acc;  // [d_model] exact expert sums, zero on entry and exit (n_experts > 1)
     int d_model, d_ff, group, n_experts;
     int scale_bytes;         // 4: f32 scales, 2: IEEE binary16 scales
-    int dn_rows_per_wave;    // set by the down launcher
+    int dn_steps_per_block;  // set by the down launcher: row steps each down block owns
 };
 
 bool plan_decode(int mode, int bits, int d_model, int d_ff, int n_experts, DecodePlan *plan);

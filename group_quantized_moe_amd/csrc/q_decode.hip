@@ -79,21 +79,49 @@ __device__ __forceinline__ int chunk_shift(float m)
     return m > 0.0f ? 22 - __builtin_amdgcn_frexp_expf(m) : 0;
 }
 
-// Six signed 4-bit digits of X (|X| <= 2^22) packed in nibbles 0..5:
-// X + 0x888888 has unsigned nibbles u_p, and t_p = u_p - 8 is the nibble u_p ^ 8
-// read as a signed 4-bit value.
-__device__ __forceinline__ uint32_t digits6(int X)
+// 8x8 transpose of nibbles: on return nibble i of w[p] is what nibble p of
+// w[i] was.  Three stages swap ever larger blocks between word pairs:
+// nibbles between words (2j, 2j+1) with bitfield inserts, then bytes between
+// (j, j+2) and 16-bit halves between (j, j+4) with byte permutes.
+__device__ __forceinline__ void transpose_nibbles(uint32_t w[8])
 {
-    return ((uint32_t)X + kDigitBias) ^ kDigitBias;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        const uint32_t a = w[j], b = w[j + 1];
+        w[j] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+        w[j + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = q + (q & 2);   // pairs (0,2) (1,3) (4,6) (5,7)
+        const uint32_t a = w[j], b = w[j + 2];
+        w[j] = __builtin_amdgcn_perm(b, a, 0x06020400u);      // a.byte0 b.byte0 a.byte2 b.byte2
+        w[j + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);  // a.byte1 b.byte1 a.byte3 b.byte3
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t a = w[j], b = w[j + 4];
+        w[j] = __builtin_amdgcn_perm(b, a, 0x05040100u);      // low halves
+        w[j + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // high halves
+    }
 }
 
 // Quantises one code dword's worth of columns (8 or 16 values) with shift k and
 // writes its digit planes to `words` (6 or 12 dwords).  Returns sum of X.
+//
+// X = rint(v * 2^k) with |X| <= 2^22: adding 1.5 * 2^23 to v * 2^k (|v * 2^k| <
+// 2^22) lands in [2^23, 2^24), where floats are the integers, so the one
+// rounding of the add is the rounding to the nearest integer and the result's
+// bits are 0x4B400000 + X.  X + 0x888888 is then positive and below 2^24, its
+// six nibbles u_p = t_p + 8 hold the signed digits of X = sum_p 16^p t_p,
+// t_p in [-8, 7], and u_p ^ 8 is t_p as a signed 4-bit value.  The nibble
+// transpose gathers digit p of the 8 columns into plane p, nibble i = column i.
 template <int BITS>
 __device__ __forceinline__ int make_planes(const float *v, int k, uint32_t *words)
 {
     constexpr int OCT = DigitLayout<BITS>::kOctPerDw;
-    int sum = 0;
+    constexpr uint32_t kMagic = 0x4B400000u;   // bits of 1.5 * 2^23
+    uint32_t bsum = 0;
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
         uint32_t w[8];
@@ -101,19 +129,15 @@ __device__ __forceinline__ int make_planes(const float *v, int k, uint32_t *word
         for (int i = 0; i < 8; ++i) {
             // 4-bit: columns in order; 2-bit: octet 0 = even columns, octet 1 = odd.
             const float val = v[OCT == 1 ? i : 2 * i + o];
-            const int X = (int)__builtin_rintf(__builtin_ldexpf(val, k));
-            sum += X;
-            w[i] = digits6(X);
+            const uint32_t bits = __float_as_uint(__builtin_ldexpf(val, k) + 12582912.0f);
+            bsum += bits;
+            w[i] = bits + (kDigitBias - kMagic);
         }
+        transpose_nibbles(w);
 #pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            uint32_t plane = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) plane |= ((w[i] >> (4 * p)) & 0xFu) << (4 * i);
-            words[6 * o + p] = plane;
-        }
+        for (int p = 0; p < 6; ++p) words[6 * o + p] = w[p] ^ 0x88888888u;
     }
-    return sum;
+    return (int)(bsum - (uint32_t)(8 * OCT) * kMagic);
 }
 
 // The input vector of a block, one code dword's worth of columns (8 at 4 bits,
@@ -146,52 +170,75 @@ __device__ __forceinline__ void load_vec_regs(const float *vec, int n, VecRegs<B
 }
 
 // Largest value over the 4 lanes of an aligned quad (every lane gets it).
-__device__ __forceinline__ float quad_max(float v)
+__device__ __forceinline__ uint32_t quad_umax(uint32_t v)
 {
-    v = fmaxf(v, dpp<0xB1>(v));  // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp<0x4E>(v));  // quad_perm [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
     return v;
 }
 
-// Block-wide: digit planes of the vector held in VecRegs, into LDS.  The four
-// code dwords of a chunk belong to four consecutive threads of one wave, so the
-// chunk's largest |v| is a quad reduction and one barrier suffices.
-//   cmax   : [chunks] largest |v| per chunk
+// Bit pattern of the largest |v| of a chunk: every finite value is below
+// 0x7f800000, an infinity equals it and a NaN lies above it, so the chunk is
+// finite exactly when the result is below 0x7f800000.
+constexpr uint32_t kInfBits = 0x7f800000u;
+
+// Digit planes of one code dword of a vector (its 8 or 16 values in v) into
+// LDS.  The four code dwords of a chunk belong to four consecutive lanes, which
+// must all call this together (the chunk's largest |v| is a quad reduction);
+// `ok` only gates the stores.
+//   cmax   : [chunks] largest |v| per chunk (an infinity or NaN if the chunk
+//            holds a non-finite value)
 //   dwsum  : [ndw]    sum of X per code dword
 //   planes : word w of chunk c at ((w / 4) * chunks + c) * 4 + w % 4, so that
 //            consecutive lanes reading consecutive chunks with 16-byte loads hit
 //            consecutive LDS addresses (no bank conflicts).
+template <int BITS>
+__device__ __forceinline__ void plane_dword(const float *v, int q, bool ok, int chunks, uint32_t *planes,
+                                            float *cmax, int *dwsum)
+{
+    using DL = DigitLayout<BITS>;
+    uint32_t mb = 0;
+#pragma unroll
+    for (int i = 0; i < DL::kColsPerDw; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7fffffffu);
+    mb = quad_umax(mb);
+    if (!ok) return;
+    const int c = q >> 2, dw = q & 3;
+    const bool fin = mb < kInfBits;
+    if (dw == 0) cmax[c] = __uint_as_float(mb);
+    // A non-finite chunk is quantised as zeros; its epilogue constant is NaN.
+    float vf[DL::kColsPerDw];
+#pragma unroll
+    for (int i = 0; i < DL::kColsPerDw; ++i) vf[i] = fin ? v[i] : 0.0f;
+    uint32_t w[DL::kWordsPerDw];
+    dwsum[q] = make_planes<BITS>(vf, fin ? chunk_shift(__uint_as_float(mb)) : 0, w);
+#pragma unroll
+    for (int i = 0; i < DL::kWordsPerDw; ++i) {
+        const int word = dw * DL::kWordsPerDw + i;
+        planes[((size_t)(word >> 2) * chunks + c) * 4 + (word & 3)] = w[i];
+    }
+}
+
+// Block-wide: digit planes of the vector held in VecRegs, into LDS, then one
+// barrier.  blockDim and the group stride are multiples of 4, so the four
+// dwords of a chunk sit in four consecutive threads of one wave.
 template <int BITS, int GPT>
 __device__ void build_planes(const VecRegs<BITS, GPT> &r, int chunks, uint32_t *planes, float *cmax, int *dwsum)
 {
-    using DL = DigitLayout<BITS>;
 #pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-        const int q = threadIdx.x + g * blockDim.x;
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < DL::kColsPerDw; ++i) m = fmaxf(m, fabsf(r.v[g][i]));
-        m = quad_max(m);  // blockDim and the group stride are multiples of 4
-        if (!r.ok[g]) continue;
-        const int c = q >> 2, dw = q & 3;
-        if (dw == 0) cmax[c] = m;
-        uint32_t w[DL::kWordsPerDw];
-        dwsum[q] = make_planes<BITS>(r.v[g], chunk_shift(m), w);
-#pragma unroll
-        for (int i = 0; i < DL::kWordsPerDw; ++i) {
-            const int word = dw * DL::kWordsPerDw + i;
-            planes[((size_t)(word >> 2) * chunks + c) * 4 + (word & 3)] = w[i];
-        }
-    }
+    for (int g = 0; g < GPT; ++g)
+        plane_dword<BITS>(r.v[g], threadIdx.x + g * blockDim.x, r.ok[g], chunks, planes, cmax, dwsum);
     __syncthreads();
 }
 
-// A lane's view of one chunk of the vector: its digit planes and the two
-// epilogue constants, contribution = s * (float(I) * alpha + beta).
+// A lane's view of one chunk of the vector: its digit planes and the
+// epilogue constants, contribution = s * ldexp(float(I) / Z + beta, -k).
+// Scaling by 2^-k last keeps a chunk of tiny values (k above 126) from
+// underflowing before its sum is formed.
 template <int BITS>
 struct ChunkVec {
     uint32_t w[DigitLayout<BITS>::kWordsPerChunk];
-    float alpha, beta;
+    float beta;
+    int nk;   // -k
 };
 
 template <int BITS>
@@ -211,15 +258,16 @@ __device__ __forceinline__ void load_chunk_vec(const uint32_t *planes, const flo
         cv.w[4 * i + 3] = valid ? t.w : 0u;
     }
     const int q = 4 * cc;
-    const int k = chunk_shift(cmax[cc]);
+    const float m = cmax[cc];
+    const bool fin = __float_as_uint(m) < kInfBits;
+    const int k = fin ? chunk_shift(m) : 0;
     const int S = dwsum[q] + dwsum[q + 1] + dwsum[q + 2] + dwsum[q + 3];  // |S| <= 2^28
-    const float sx = __builtin_ldexpf((float)S, -k);                        // sum of quantised x
-    const float alpha = __builtin_ldexpf(QFormat<BITS>::kInvZ, -k);
-    // 4-bit: code - Z = (code - 8) + 1/2, and the dot uses code - 8.
-    // 2-bit: code - Z = code - 3/2, and the dot uses code itself.
-    const float beta = BITS == 4 ? sx * (0.5f * QFormat<BITS>::kInvZ) : -sx;
-    cv.alpha = valid ? alpha : 0.0f;
-    cv.beta = valid ? beta : 0.0f;
+    // In units of 2^-k, the chunk's sum of (code - Z) X / Z is I / Z + beta:
+    // 4-bit: code - Z = (code - 8) + 1/2 and the dot uses code - 8, so beta = S / (2Z);
+    // 2-bit: (code - Z) / Z = code / Z - 1 and the dot uses code itself, so beta = -S.
+    const float beta = BITS == 4 ? (float)S * (0.5f * QFormat<BITS>::kInvZ) : -(float)S;
+    cv.beta = valid ? (fin ? beta : __builtin_nanf("")) : 0.0f;
+    cv.nk = valid ? -k : 0;
 }
 
 // I = sum over the chunk of c_j * X_j, exact (|I| <= 2^30).  c_j = code - 8 at
@@ -268,7 +316,7 @@ __device__ __forceinline__ int chunk_idot(const uint4 q, const ChunkVec<BITS> &c
 template <int BITS>
 __device__ __forceinline__ float chunk_contrib(const uint4 q, float s, const ChunkVec<BITS> &cv)
 {
-    return s * fmaf((float)chunk_idot<BITS>(q, cv), cv.alpha, cv.beta);
+    return s * __builtin_ldexpf(fmaf((float)chunk_idot<BITS>(q, cv), QFormat<BITS>::kInvZ, cv.beta), cv.nk);
 }
 
 // Dynamic LDS: the input vector's digit planes,
@@ -514,131 +562,151 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     }
 }
 
+// One batch of a vector for the wave-level plane build: B code dwords a lane
+// (32 values), dword q0 + lane + 64 b in slot b.
+template <int BITS>
+struct WaveVec {
+    static constexpr int kB = 32 / DigitLayout<BITS>::kColsPerDw;
+    float v[kB][DigitLayout<BITS>::kColsPerDw];
+};
+
+// Loads one batch.  Every slot is loaded (past the end: the last dword again),
+// so the number of loads is fixed and the compiler can wait for exactly these
+// while loads issued after them stay in flight (a uniform test per slot turns
+// those waits into waits for every load).
+template <int BITS>
+__device__ __forceinline__ void wave_vec_load(const float *vec, int ndw, int q0, WaveVec<BITS> &r)
+{
+    constexpr int C = DigitLayout<BITS>::kColsPerDw;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int b = 0; b < WaveVec<BITS>::kB; ++b) {
+        const int q = min(q0 + lane + 64 * b, ndw - 1);
+        const float4 *src = reinterpret_cast<const float4 *>(vec + (size_t)q * C);
+#pragma unroll
+        for (int i = 0; i < C / 4; ++i) {
+            const float4 t = src[i];
+            r.v[b][4 * i] = t.x; r.v[b][4 * i + 1] = t.y; r.v[b][4 * i + 2] = t.z; r.v[b][4 * i + 3] = t.w;
+        }
+    }
+}
+
+// Digit planes of one batch into the wave's own LDS region (no block barrier).
+template <int BITS>
+__device__ __forceinline__ void wave_vec_planes(const WaveVec<BITS> &r, int ndw, int q0, const PlaneLds<BITS> &lds)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int b = 0; b < WaveVec<BITS>::kB; ++b) {
+        const int q = q0 + lane + 64 * b;
+        if (q0 + 64 * b < ndw)  // uniform: a slot is used by every lane's quad or by none
+            plane_dword<BITS>(r.v[b], q, q < ndw, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
+    }
+}
+
 // down: out = sum_e r_e * (D_e hidden_e).
 //
-// Blocks are bound to one expert (block b serves expert b % E) and build that
-// expert's hidden digit planes in LDS once; waves then stream whole rows on
-// their own as in gate_up.  With one expert the rows go straight to out.  With
-// several, the experts' router-weighted rows are summed exactly: each
-// contribution is rounded to a multiple of 2^-32 (an error of at most 2^-33 per
-// term, far below f32 resolution for outputs of order one, and at most
-// E * 2^-33 in absolute terms) and added as a 64-bit integer to a per-row
-// accumulator whose top five bits count the experts in.  Integer addition is
-// associative, so the sum does not depend on the order in which experts
-// arrive: the result is bitwise reproducible.  The expert whose addition
-// completes the count converts the exact sum to f32 once, writes out, and
-// re-zeroes the accumulator for the next call.  One atomic per row and
-// expert, deferred to the end of the wave, is the only cross-block traffic.
-// A contribution of magnitude 2^20 or more does not fit the accumulator; it is
-// added as a NaN marker so that the row comes out NaN rather than wrong.
-constexpr int kAccCountShift = 59;
-constexpr unsigned long long kAccBias = 1ull << 52;    // keeps every term non-negative
-constexpr unsigned long long kAccNan = 1ull << 58;     // set in the sum when a term overflowed
-
-__device__ __forceinline__ unsigned long long acc_term(float v)
-{
-    const double t = (double)v * 4294967296.0;  // v * 2^32
-    if (!(fabs(t) < 4503599627370496.0))        // |v| < 2^20 (also false for NaN)
-        return (1ull << kAccCountShift) | kAccNan;
-    return (1ull << kAccCountShift) + kAccBias + (unsigned long long)(long long)__builtin_rint(t);
-}
-
-__device__ __forceinline__ float acc_value(unsigned long long sum, int n)
-{
-    if (sum & kAccNan) return __builtin_nanf("");
-    const unsigned long long mag = sum & ((1ull << kAccCountShift) - 1);
-    const long long fixed = (long long)(mag - (unsigned long long)n * kAccBias);
-    return (float)((double)fixed * (1.0 / 4294967296.0));
-}
-
-template <int BITS, int NCH, int LPR, int SB>
+// Blocks own output rows: block b covers `spb` row steps (rs rows each) for
+// every expert.  Its work is the list of (expert, step) pairs in expert-major
+// order, split into contiguous ranges over its waves, so a wave mostly serves
+// one expert.  For each expert it serves, a wave issues the loads of the
+// expert's hidden vector and right behind them the code and scale loads of
+// its first DEPTH steps, so that all of them are in flight together; it
+// waits for the hidden vector only, builds its digit planes in the wave's own
+// LDS region (no block barrier), copies its chunks' planes into registers
+// and reduces its steps as their loads come in, writing each row's sum to an
+// LDS slab [E][rows of the block].  After one barrier the block's threads add
+// the experts' rows in ascending expert order in f64, each weighted by its
+// router weight, and write out.  The sum has a fixed order (bitwise
+// reproducible), no atomics and no range limit, and nothing in the workspace
+// has to be zero.
+template <int BITS, int NCH, int LPR, int SB, int DEPTH>
 __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
 {
     constexpr int CPC = QFormat<BITS>::kCodesPerChunk;
+    constexpr int rs = RowLanes<NCH, LPR>::kRows;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int E = a.n_experts;
     const int cpr = a.d_ff / CPC;
-    const size_t row_bytes = (size_t)a.d_ff * BITS / 8;
+    const unsigned row_bytes = (unsigned)a.d_ff * BITS / 8;
     const int gpr = a.d_ff / a.group;
+    const int ndw = a.d_ff / DigitLayout<BITS>::kColsPerDw;
     const RowLanes<NCH, LPR> ln(cpr, CPC, a.group);
-    const PlaneLds<BITS> lds(smem, a.d_ff);
-    constexpr int rs = RowLanes<NCH, LPR>::kRows;
-    const int e = blockIdx.x % E;
-    const int bpe = gridDim.x / E;                 // blocks per expert
-    const int We = bpe * nw;                       // waves per expert
+    const int spb = a.dn_steps_per_block;
     const int nsteps = (a.d_model + rs - 1) / rs;
-    const int iw = (blockIdx.x / E) * nw + wave;   // this wave among its expert's waves
-    const int sb = (int)((long)iw * nsteps / We), se = (int)((long)(iw + 1) * nsteps / We);
-    const uint8_t *dcodes[1] = {a.down[e].codes};
-    const void *dscales[1] = {a.down[e].scales};
-    const float rw = a.route_w ? a.route_w[e] : 1.0f;
-    // This wave's router-weighted rows, kept until the deferred combine.
-    float *mine = reinterpret_cast<float *>(smem + ((plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15))) +
-                  wave * a.dn_rows_per_wave;
-    auto load = [&](Stage<NCH, 1> &t, int step) {
-        load_stage<NCH, LPR, 1, SB>(t, dcodes, dscales, ln, step * rs, a.d_model, (unsigned)row_bytes, gpr);
-    };
+    const int s0 = blockIdx.x * spb;
+    const int ns = min(spb, nsteps - s0);   // row steps of this block
+    const int items = E * ns;               // (expert, step) pairs, expert-major
+    const int ib = (int)((long)wave * items / nw), ie = (int)((long)(wave + 1) * items / nw);
+    const size_t pbytes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
+    const PlaneLds<BITS> lds(smem + wave * pbytes, a.d_ff);
+    const int brows = spb * rs;
+    float *slab = reinterpret_cast<float *>(smem + nw * pbytes);   // [E][brows]
+    float *rws = slab + E * brows;                                  // [E] router weights
+    // The router weights are loaded first and stored to LDS only before the
+    // barrier: they are needed after it, and no wait for them sits in front
+    // of the first loads.
+    const bool rw_lane = (int)threadIdx.x < E;
+    const float my_rw = rw_lane ? (a.route_w ? a.route_w[threadIdx.x] : 1.0f) : 0.0f;
 
-    if ((int)blockIdx.x >= bpe * E) return;  // whole block idle: no barrier follows for it
-    VecRegs<BITS, kGroupsPerThread<BITS>> hr;
-    load_vec_regs<BITS>(a.hidden + (size_t)e * a.d_ff, a.d_ff, hr);
-    wait_vm_all();   // the hidden vector before the code loads, as in gate_up
-    const bool busy = sb < se;
-    Stage<NCH, 1> S[2];
-    if (busy) load(S[0], sb);
-
-    build_planes<BITS>(hr, lds.chunks, lds.planes, lds.cmax, lds.dwsum);
-    ChunkVec<BITS> cv[NCH];
+    for (int it = ib; it < ie;) {
+        const int e = it / ns;
+        const int iend = min(ie, (e + 1) * ns);   // this wave's items of expert e
+        const int n = iend - it;
+        const uint8_t *dcodes[1] = {a.down[e].codes};
+        const void *dscales[1] = {a.down[e].scales};
+        auto load = [&](Stage<NCH, 1> &t, int item) {
+            load_stage<NCH, LPR, 1, SB>(t, dcodes, dscales, ln, (s0 + item - e * ns) * rs, a.d_model, row_bytes,
+                                        gpr);
+        };
+        const float *hid = a.hidden + (size_t)e * a.d_ff;
+        WaveVec<BITS> hv;
+        wave_vec_load<BITS>(hid, ndw, 0, hv);
+        Stage<NCH, 1> S[DEPTH];
 #pragma unroll
-    for (int k = 0; k < NCH; ++k)
-        load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
-
-    // One step of loads in flight, in two register slots: a step's loads go
-    // out as soon as the previous step's have come back, before that step's
-    // arithmetic (measured 0.5 us faster than issuing them after it, and about
-    // 1 us faster than keeping two steps in flight).
-    for (int base = sb; base < se; base += 2) {
+        for (int i = 0; i < DEPTH; ++i) load(S[i], it + min(i, n - 1));   // a short range repeats its last step
+        // Keeps the code loads above the plane build.
+        asm volatile("" ::: "memory");
+        wave_vec_planes<BITS>(hv, ndw, 0, lds);
+        for (int q0 = 64 * WaveVec<BITS>::kB; q0 < ndw; q0 += 64 * WaveVec<BITS>::kB) {
+            wave_vec_load<BITS>(hid, ndw, q0, hv);
+            wave_vec_planes<BITS>(hv, ndw, q0, lds);
+        }
+        // The wave reads its planes back with its own LDS loads, which the LDS
+        // serves in order after its stores; this keeps the compiler from
+        // hoisting them.
+        asm volatile("" ::: "memory");
+        ChunkVec<BITS> cv[NCH];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int st = base + i;
-            if (st < se) {
-                wait_vm_all();                                // this step's loads are in
-                if (st + 1 < se) load(S[i ^ 1], st + 1);     // the next step's go out first
-                float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv);
-                y = group_sum<LPR>(y);
-                const int r = st * rs + ln.slot;
-                if (ln.writer() && r < a.d_model) {
-                    if (E == 1)
-                        a.out[r] = y * rw;
-                    else
-                        mine[(st - sb) * rs + ln.slot] = y * rw;
+        for (int k = 0; k < NCH; ++k)
+            load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
+
+        // Steps are reduced in order as their loads come in; a slot is
+        // reloaded with the step DEPTH further on once it has been reduced.
+        for (int base = 0; base < n; base += DEPTH) {
+#pragma unroll
+            for (int i = 0; i < DEPTH; ++i) {
+                const int j = base + i;
+                if (j < n) {
+                    float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv);
+                    y = group_sum<LPR>(y);
+                    const int r = (it + j - e * ns) * rs + ln.slot;  // row within the block
+                    if (ln.writer() && s0 * rs + r < a.d_model) slab[e * brows + r] = y;
+                    if (j + DEPTH < n) load(S[i], it + j + DEPTH);
                 }
             }
         }
+        it = iend;
     }
-
-    if (E > 1) {
-        // One 64-bit addition per row of this wave (lane j takes its j-th row);
-        // the rows were written to LDS by lanes of this same wave, whose LDS
-        // accesses complete in order.
-        __builtin_amdgcn_wave_barrier();
-        const int r0 = sb * rs;
-        const int my_rows = min(se * rs, a.d_model) - r0;
-        for (int j0 = 0; j0 < my_rows; j0 += 64) {
-            const int j = j0 + lane;
-            if (j < my_rows) {
-                const int r = r0 + j;
-                const unsigned long long term = acc_term(mine[j]);
-                const unsigned long long sum =
-                    __hip_atomic_fetch_add(a.row_acc + r, term, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + term;
-                if ((int)(sum >> kAccCountShift) == E) {
-                    a.out[r] = acc_value(sum, E);
-                    __hip_atomic_store(a.row_acc + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        }
+    if (rw_lane) rws[threadIdx.x] = my_rw;
+    __syncthreads();
+    const int nrows = min(ns * rs, a.d_model - s0 * rs);
+    for (int t = threadIdx.x; t < nrows; t += blockDim.x) {
+        double acc = 0.0;
+        for (int e = 0; e < E; ++e) acc += (double)rws[e] * (double)slab[e * brows + t];
+        a.out[s0 * rs + t] = (float)acc;
     }
 }
 
@@ -672,25 +740,44 @@ hipError_t run_gate_up(const DecodePlan &p, const DecodeArgs &a, int cus, hipStr
     return hipGetLastError();
 }
 
+// LDS one down block may take: per-wave planes plus the slab and the router
+// weights.
+constexpr size_t kDownLdsCap = 64 * 1024;
+
+// Steps of loads a down wave keeps in flight: all of its steps of an expert,
+// up to 4.
+int down_depth(long steps_per_wave) { return steps_per_wave <= 1 ? 1 : steps_per_wave <= 2 ? 2 : 4; }
+
 template <int BITS, int NCH, int LPR, int SB>
 hipError_t run_down(const DecodePlan &p, DecodeArgs a, int cus, hipStream_t st)
 {
-    const int block = 64 * p.nw;
-    const void *fn = reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, SB>);
-    const size_t planes = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
-    // One block per CU: with a step's loads issued as soon as the previous
-    // step's are in, four row steps a wave on one block per CU measured 0.4 us
-    // faster than two on two (Q4 group; the same for Q2).
-    const long cap = (long)cus * std::min(1, blocks_per_cu(fn, block, planes + 4096));
-    if (cap < a.n_experts) return hipErrorInvalidConfiguration;
     const int rs = 64 / p.lpr_d;
-    const long steps = (a.d_model + rs - 1) / rs;
-    const long per_expert = std::max(1L, std::min(cap / a.n_experts, (steps + p.nw - 1) / p.nw));
-    const long waves = per_expert * p.nw;
-    a.dn_rows_per_wave = (int)(((steps + waves - 1) / waves) * rs);
-    const size_t lds = planes + (a.n_experts > 1 ? (size_t)p.nw * a.dn_rows_per_wave * sizeof(float) : 0);
-    hipLaunchKernelGGL((k_down<BITS, NCH, LPR, SB>), dim3((unsigned)(per_expert * a.n_experts)), dim3(block), lds, st,
-                       a);
+    const long nsteps = (a.d_model + rs - 1) / rs;
+    // One block per CU, each owning an equal share of the row steps.
+    const long spb = std::max(1L, (nsteps + cus - 1) / cus);
+    const long blocks = (nsteps + spb - 1) / spb;
+    const size_t pb = (plane_lds_bytes<BITS>(a.d_ff) + 15) & ~size_t(15);
+    const size_t slab = (size_t)a.n_experts * (spb * rs + 1) * sizeof(float);
+    // Waves per block: no more than its (expert, step) pairs, and as many
+    // per-wave plane regions as fit beside the slab.
+    const long items = (long)a.n_experts * spb;
+    long nw = std::min<long>(p.nw, items);
+    if (slab + pb > kDownLdsCap) return hipErrorInvalidConfiguration;
+    nw = std::min<long>(nw, (long)((kDownLdsCap - slab) / pb));
+    const size_t lds = nw * pb + slab;
+    const int depth = down_depth((items + nw - 1) / nw);
+    const void *fn = depth == 1   ? reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, SB, 1>)
+                     : depth == 2 ? reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, SB, 2>)
+                                  : reinterpret_cast<const void *>(&k_down<BITS, NCH, LPR, SB, 4>);
+    if (blocks_per_cu(fn, (int)(64 * nw), lds) < 1) return hipErrorInvalidConfiguration;
+    a.dn_steps_per_block = (int)spb;
+    const dim3 grid((unsigned)blocks), block((unsigned)(64 * nw));
+    if (depth == 1)
+        hipLaunchKernelGGL((k_down<BITS, NCH, LPR, SB, 1>), grid, block, lds, st, a);
+    else if (depth == 2)
+        hipLaunchKernelGGL((k_down<BITS, NCH, LPR, SB, 2>), grid, block, lds, st, a);
+    else
+        hipLaunchKernelGGL((k_down<BITS, NCH, LPR, SB, 4>), grid, block, lds, st, a);
     return hipGetLastError();
 }
 

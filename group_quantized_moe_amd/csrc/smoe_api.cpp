@@ -101,22 +101,9 @@ bool overlaps_qmat(const void *out, size_t nout, const smoe_qmat *m, const Fmt &
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SMOE_OK : SMOE_ERR_LAUNCH; }
 
-// Workspace layout of the decode path (T == 1), every piece 256-byte aligned:
-//   hidden    f32 [n_experts][d_ff]
-//   row_acc   u64 [d_model]          exact per-row sums of the experts' outputs
-// row_acc must be zero before the first call; every call leaves it zero.
-struct DecodeWorkspace {
-    size_t hidden, row_acc, total;
-};
-
-DecodeWorkspace decode_workspace(int n_experts, int d_model, int d_ff)
-{
-    DecodeWorkspace w;
-    w.hidden = 0;
-    w.row_acc = w.hidden + align256((size_t)n_experts * d_ff * 4);
-    w.total = w.row_acc + align256((size_t)d_model * 8);
-    return w;
-}
+// Workspace of the decode path (T == 1): the hidden rows f32 [n_experts][d_ff],
+// written by gate_up and read by down; nothing in it needs to be zero.
+size_t decode_workspace(int n_experts, int d_ff) { return align256((size_t)n_experts * d_ff * 4); }
 
 // Workspace layout of the token-batch path (T > 1), every piece 256-byte aligned:
 //   xh, xl  f16 [T][d_model]                 hi/lo halves of the scaled activations
@@ -326,7 +313,7 @@ int smoe_down(const smoe_qmat *down, int fmt, int group, int d_model, int d_ff, 
 size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
 {
     if (n_experts <= 0 || d_model <= 0 || d_ff <= 0 || T <= 0) return 0;
-    if (T == 1) return decode_workspace(n_experts, d_model, d_ff).total;
+    if (T == 1) return decode_workspace(n_experts, d_ff);
     if (T > SMOE_MAX_TOKENS) return 0;
     return batch_workspace(n_experts, d_model, d_ff, T, kMinBatchGroup).total;
 }
@@ -412,15 +399,12 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     DeviceInfo dev;
     if ((rc = check_device(&dev))) return rc;
 
-    const DecodeWorkspace w = decode_workspace(n_experts, d_model, d_ff);
-    char *ws = static_cast<char *>(workspace);
     smoe::DecodeArgs a{};
     fill_experts(a, experts, n_experts);
     a.x = x;
-    a.hidden = reinterpret_cast<float *>(ws + w.hidden);
+    a.hidden = static_cast<float *>(workspace);
     a.route_w = route_w;
     a.out = out;
-    a.row_acc = reinterpret_cast<unsigned long long *>(ws + w.row_acc);
     a.d_model = d_model;
     a.d_ff = d_ff;
     a.group = group;

@@ -40,7 +40,18 @@
  *   at 2 bits.  group must be a multiple of 32 (4-bit) or 64 (2-bit) and
  *   divide cols, so no 16-byte chunk of codes straddles two groups.
  *
- * Activations are f32 throughout (x, hidden, out, y, router weights).
+ * Activations are f32 throughout (x, hidden, out, y, router weights).  The
+ * vectors a kernel stages in 16-byte pieces (x of every call, hidden of
+ * smoe_down) must be 16-byte aligned; outputs and router weights 4-byte.
+ *
+ * Numerics of the one-token (decode) kernels: each 16-byte chunk of the input
+ * vector (32 columns at 4 bits, 64 at 2 bits) is carried as 22-bit fixed
+ * point with one power-of-two exponent per chunk, so column j is off by at
+ * most 2^-22 of its chunk's largest |x|; the code dot products are exact in
+ * int32 and the per-chunk epilogue and row sums are f32.  There is no range
+ * limit below f32's own: an input of any finite magnitude gives the result to
+ * that precision at its own scale.  A non-finite element (NaN or an infinity)
+ * makes every row that reads its chunk NaN, which is every output row.
  *
  * Memory and streams: every data pointer is a DEVICE pointer owned by the
  * caller; the library never allocates, frees or copies device memory inside a
@@ -71,7 +82,9 @@ enum {
     SMOE_ERR_BITS = -2,      /* bits is not 2 or 4 */
     SMOE_ERR_GROUP = -3,     /* group not a multiple of 32 (4-bit) / 64 (2-bit), or does not divide cols */
     SMOE_ERR_SHAPE = -4,     /* a size is <= 0, not a multiple of the chunk width, or above the kernel limits */
-    SMOE_ERR_ALIGN = -5,     /* codes / W not 16-byte aligned, or f32 data not 4-byte aligned */
+    SMOE_ERR_ALIGN = -5,     /* codes, W, or an f32 input vector read in 16-byte pieces (x, hidden,
+                                the KV caches) not 16-byte aligned; other f32 data not 4-byte aligned;
+                                a workspace not 256-byte aligned */
     SMOE_ERR_WORKSPACE = -6, /* workspace NULL or smaller than *_workspace() asks for */
     SMOE_ERR_ALIAS = -7,     /* an output range overlaps an input or the workspace */
     SMOE_ERR_DEVICE = -8,    /* current device is not gfx950, or a device query failed */
@@ -111,8 +124,8 @@ typedef struct smoe_expert {
 /*
  * hidden[i] = SiLU((G x)[i]) * (U x)[i],  i < d_ff, for one expert.
  *   gate, up : [d_ff x d_model] quantised matrices (host structs, device data)
- *   x        : f32 [d_model]
- *   hidden   : f32 [d_ff], must not overlap x or the weights
+ *   x        : f32 [d_model], 16-byte aligned
+ *   hidden   : f32 [d_ff], 4-byte aligned, must not overlap x or the weights
  * SiLU(t) = t / (1 + exp(-t)).
  */
 int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group,
@@ -121,8 +134,8 @@ int smoe_gate_up(const smoe_qmat *gate, const smoe_qmat *up, int bits, int group
 /*
  * out[j] = (D hidden)[j],  j < d_model, for one expert.
  *   down   : [d_model x d_ff] quantised matrix
- *   hidden : f32 [d_ff]
- *   out    : f32 [d_model], must not overlap hidden or the weights
+ *   hidden : f32 [d_ff], 16-byte aligned
+ *   out    : f32 [d_model], 4-byte aligned, must not overlap hidden or the weights
  */
 int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
               const float *hidden, float *out, void *stream);
@@ -131,21 +144,20 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  * Routed experts over T tokens:
  *   out[t][:] = sum_e route_w[t][e] * down_e( SiLU(gate_e x[t]) * (up_e x[t]) )
  *   experts   : host array of n_experts expert descriptors (1..SMOE_MAX_EXPERTS)
- *   route_w   : f32 [T][n_experts] device array, or NULL for weight 1 everywhere
- *   x         : f32 [T][d_model]
- *   out       : f32 [T][d_model], must not overlap x, route_w, workspace or weights
+ *   route_w   : f32 [T][n_experts] device array (4-byte aligned), or NULL for
+ *               weight 1 everywhere
+ *   x         : f32 [T][d_model], 16-byte aligned
+ *   out       : f32 [T][d_model], 4-byte aligned, must not overlap x, route_w,
+ *               workspace or weights
  *   workspace : device scratch of at least smoe_expert_ffn_workspace(...) bytes,
- *               256-byte aligned.  It must be ZERO-FILLED before its first use
- *               (e.g. allocated with torch.zeros or cleared once with
- *               hipMemset): part of it holds per-row counters through which
- *               the experts' outputs are combined, and every completed call
- *               leaves those counters zero again.  The rest is scratch that
- *               each call overwrites.  Calls that share a workspace must be
- *               ordered (one stream), or they race.
- * T == 1 runs the decode kernels (a gate_up launch and a down launch that also
- * combines the experts, deterministically: each router-weighted expert row is
- * rounded to a multiple of 2^-32 and summed exactly in 64-bit integers, so the
- * result does not depend on the order in which experts finish).
+ *               256-byte aligned.  Every call rewrites what it reads of it;
+ *               nothing in it needs to be zero.  Calls that share a workspace
+ *               must be ordered (one stream), or they race.
+ * T == 1 runs the decode kernels: a gate_up launch that writes every expert's
+ * hidden row to the workspace, and a down launch whose blocks each own a range
+ * of output rows for all experts and add the experts' f32 rows in ascending
+ * expert order in f64, each times its router weight, rounding once to f32
+ * (deterministic, no atomics, no range limit).
  * 2 <= T <= SMOE_MAX_TOKENS runs the token-batch kernels on the matrix cores,
  * in which every expert processes every token: an activation pass, a gate_up
  * pass and a down pass that sums the experts in a fixed order (deterministic,

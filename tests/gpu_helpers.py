@@ -1,9 +1,11 @@
 """Moving the seeded host workloads onto the GPU, and the parity bar.
 
 The bar (f32 GPU output against the f64 oracle): max |gpu - oracle| <=
-1e-4 * max(1, max |oracle|), the agreement level for this path; the pages
-report ~1e-6 for a reassociated f32 reduction, so results are also expected
-to sit far below the bar.
+1e-4 * max(1, max |oracle|), the agreement level for this path.  The Metal
+Compute Kernels page ("Not bit-exact -- by construction") reports about 1e-6
+for a reassociated f32 reduction, and an error far above 1e-5 of the output
+scale signals a bug even inside the bar, so every parity check also asserts
+that expected level: max |gpu - oracle| <= 1e-5 * max(1, max |oracle|).
 """
 from __future__ import annotations
 
@@ -12,6 +14,7 @@ from dataclasses import dataclass
 import numpy as np
 
 TOL = 1e-4
+LEVEL = 1e-5
 
 
 def parity(got, want, tol=TOL):
@@ -25,11 +28,39 @@ def parity(got, want, tol=TOL):
     return err, bound
 
 
-def assert_parity(got, want, what, tol=TOL):
+def assert_parity(got, want, what, tol=TOL, level=LEVEL):
+    """The bar, then the expected level (both relative to max(1, max|want|))."""
     err, bound = parity(got, want, tol)
     print(f"[parity] {what}: max|diff| = {err:.3e} (bound {bound:.3e})", flush=True)
     assert err <= bound, f"{what}: max|diff| {err:.3e} > {bound:.3e}"
+    lbound = bound * (level / tol)
+    assert err <= lbound, f"{what}: max|diff| {err:.3e} within the bar but above the expected level {lbound:.3e}"
     return err
+
+
+def assert_relative(got, want, what, level=LEVEL):
+    """max |gpu - oracle| <= level * max|oracle|: the expected level at the
+    output's own scale, for inputs scaled far from 1 (where max(1, .) would
+    make the absolute bar meaningless)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    scale = float(np.max(np.abs(want)))
+    err = float(np.max(np.abs(got - want)))
+    print(f"[parity] {what}: max|diff| = {err:.3e} (relative bound {level * scale:.3e})", flush=True)
+    assert err <= level * scale, f"{what}: max|diff| {err:.3e} > {level * scale:.3e}"
+    return err
+
+
+def assert_nonfinite_like(got, want, what):
+    """Non-finite input: the GPU output is non-finite exactly where the
+    oracle's is."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    gmask, wmask = ~np.isfinite(got), ~np.isfinite(want)
+    print(f"[nonfinite] {what}: oracle {int(wmask.sum())} / gpu {int(gmask.sum())} of {got.size} non-finite",
+          flush=True)
+    assert np.array_equal(gmask, wmask), f"{what}: non-finite positions differ"
 
 
 def dev(a):
