@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsmoe.so")
+# bench.py's streaming-read ceiling kernel, a library of its own (not libsmoe's ABI).
+BENCH_SRC = os.path.join(HERE, "bench", "stream_read.hip")
+BENCH_LIB = os.path.join(HERE, "libsmoe_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 instructions are switched off for all device code.
@@ -53,6 +56,14 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-x", "hip", BENCH_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {BENCH_SRC}:\n{r.stderr}")
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 

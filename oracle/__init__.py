@@ -51,6 +51,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, l, i = ctypes.c_void_p, ctypes.c_long, ctypes.c_int
         L.oracle_threads.restype = i
+        L.oracle_set_threads.argtypes = [i]
+        L.oracle_set_threads.restype = None
         L.oracle_unpack.argtypes = [vp, i, l, l, vp]
         L.oracle_dequant.argtypes = [vp, vp, i, i, l, l, vp]
         L.oracle_qmatvec.argtypes = [vp, vp, i, i, l, l, vp, vp]
@@ -87,6 +89,11 @@ def _ok(rc, what):
 
 def threads() -> int:
     return lib().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's row loops from now on (results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
 
 
 def unpack(codes, bits, rows, cols):

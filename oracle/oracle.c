@@ -26,6 +26,16 @@ int oracle_threads(void)
 #endif
 }
 
+/* Threads of the row loops from now on (n >= 1); results do not depend on it. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Affine zero point of a b-bit code: the midpoint of 0 .. 2^b-1.  The page
  * ("Fused FFN Kernels", affine weight definition) gives 7.5 at Q4 and 1.5 at Q2. */
 static double zero_point(int bits)

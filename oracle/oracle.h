@@ -61,6 +61,8 @@ int oracle_f16_widen(const uint16_t *h, long n, float *out);
 
 /* Number of OpenMP threads the oracle's row loops use (1 without OpenMP). */
 int oracle_threads(void);
+/* Sets the threads of the row loops (results do not depend on it). */
+void oracle_set_threads(int n);
 
 /* One code per output byte: out[r*cols + j] = code of row r, column j. */
 int oracle_unpack(const uint8_t *codes, int bits, long rows, long cols, uint8_t *out);
