@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libsmoe.so")
 SMOE_OK = 0
 SMOE_MAX_EXPERTS = 16
 SMOE_SCALE_F16 = 0x100   # ORed into `bits`: 2-byte IEEE binary16 scales instead of f32
+SMOE_NOALLOC_SCRATCH_BYTES = 1 << 20
 
-EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
+EXPORTS = ("smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn", "smoe_expert_ffn_noalloc",
            "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_routed_ffn_workspace",
            "smoe_routed_ffn", "smoe_attn_decode_workspace", "smoe_attn_decode", "smoe_status_str")
 SMOE_MAX_BF16_JOBS = 16
@@ -67,6 +68,7 @@ def lib():
         L.smoe_expert_ffn_workspace.argtypes = [i, i, i, i]
         L.smoe_expert_ffn_workspace.restype = sz
         L.smoe_expert_ffn.argtypes = [vp, i, vp, i, i, i, i, i, vp, vp, vp, sz, vp]
+        L.smoe_expert_ffn_noalloc.argtypes = [vp, i, vp, i, i, i, i, i, vp, vp, vp]
         L.matvec_bf16_workspace.argtypes = [i, i]
         L.matvec_bf16_workspace.restype = sz
         L.matvec_bf16.argtypes = [vp, i, i, vp, vp, vp, sz, vp]
@@ -80,7 +82,7 @@ def lib():
         L.smoe_attn_decode.restype = i
         L.smoe_status_str.argtypes = [i]
         L.smoe_status_str.restype = ctypes.c_char_p
-        for name in ("smoe_gate_up", "smoe_down", "smoe_expert_ffn", "matvec_bf16"):
+        for name in ("smoe_gate_up", "smoe_down", "smoe_expert_ffn", "smoe_expert_ffn_noalloc", "matvec_bf16"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -186,6 +188,19 @@ def smoe_expert_ffn(experts, bits, group, x, out, route_w=None, workspace=None, 
     _check("smoe_expert_ffn", lib().smoe_expert_ffn(
         arr, len(experts), pr, bits, group, d_model, d_ff, T, _dev(x, torch.float32, "x"),
         _dev(out, torch.float32, "out"), pw, workspace.numel(), _stream(stream)))
+
+
+def smoe_expert_ffn_noalloc(experts, bits, group, x, out, route_w=None, stream=None):
+    """smoe_expert_ffn on the library's static per-GPU scratch array: no
+    workspace, nothing allocated.  Calls that may overlap on one GPU race."""
+    import torch
+    d_ff, d_model = _dims(_first_gate_codes(experts), bits)
+    T = x.numel() // d_model
+    arr = _expert_array(experts, bits)
+    pr = None if route_w is None else _dev(route_w, torch.float32, "route_w")
+    _check("smoe_expert_ffn_noalloc", lib().smoe_expert_ffn_noalloc(
+        arr, len(experts), pr, bits, group, d_model, d_ff, T, _dev(x, torch.float32, "x"),
+        _dev(out, torch.float32, "out"), _stream(stream)))
 
 
 def matvec_bf16_workspace(rows, cols) -> int:

@@ -21,11 +21,19 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// Device properties, queried once per device (limits come from the device,
-// never from constants).
+// The scratch memory of smoe_expert_ffn_noalloc: one array per GPU, alive
+// until the process ends.  In host code this name is a host-side stand-in,
+// not a device address: the device address comes from hipGetSymbolAddress,
+// once per device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SMOE_NOALLOC_SCRATCH_BYTES];
+
+// Device properties, queried once per device with that device current (limits
+// come from the device, never from constants), and the device address of the
+// scratch array on that device (null if the lookup failed).
 struct DeviceInfo {
     bool ok;
     int cus;
+    void *scratch;
 };
 
 DeviceInfo g_dev[kMaxDevices];
@@ -37,10 +45,15 @@ int check_device(DeviceInfo *out)
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SMOE_ERR_DEVICE;
     std::call_once(g_dev_once[dev], [dev] {
         hipDeviceProp_t p;
-        DeviceInfo d{false, 0};
+        DeviceInfo d{false, 0, nullptr};
         if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
             d.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
             d.cus = p.multiProcessorCount;
+        }
+        if (d.ok) {
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr) d.scratch = ptr;
+            else (void)hipGetLastError();   // the failure is reported by the call that needs the array
         }
         g_dev[dev] = d;
     });
@@ -318,9 +331,11 @@ size_t smoe_expert_ffn_workspace(int n_experts, int d_model, int d_ff, int T)
     return batch_workspace(n_experts, d_model, d_ff, T, kMinBatchGroup).total;
 }
 
-int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int fmt,
-                    int group, int d_model, int d_ff, int T, const float *x, float *out,
-                    void *workspace, size_t workspace_bytes, void *stream)
+// smoe_expert_ffn, with the caller's workspace or (noalloc) the device's
+// static scratch array.
+static int expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int fmt, int group,
+                      int d_model, int d_ff, int T, const float *x, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream, bool noalloc)
 {
     Fmt f;
     int rc = check_format(fmt, group, &f);
@@ -340,23 +355,39 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
         return SMOE_ERR_GROUP;
 
     const size_t need = smoe_expert_ffn_workspace(n_experts, d_model, d_ff, T);
-    if (!workspace || workspace_bytes < need) return SMOE_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return SMOE_ERR_ALIGN;
+    if (noalloc ? need > SMOE_NOALLOC_SCRATCH_BYTES : (!workspace || workspace_bytes < need))
+        return SMOE_ERR_WORKSPACE;
+    if (!noalloc && !aligned(workspace, 256)) return SMOE_ERR_ALIGN;
     const size_t no = (size_t)T * d_model * 4;
-    if (overlap(out, no, x, (size_t)T * d_model * 4) || overlap(out, no, workspace, need) ||
-        overlap(out, no, route_w, route_w ? (size_t)T * n_experts * 4 : 0) ||
-        overlap(workspace, need, x, (size_t)T * d_model * 4) ||
-        overlap(workspace, need, route_w, route_w ? (size_t)T * n_experts * 4 : 0))
+    if (overlap(out, no, x, (size_t)T * d_model * 4) ||
+        overlap(out, no, route_w, route_w ? (size_t)T * n_experts * 4 : 0))
         return SMOE_ERR_ALIAS;
     for (int e = 0; e < n_experts; ++e) {
         const smoe_expert &ex = experts[e];
         if (overlaps_qmat(out, no, &ex.gate, f, group, d_ff, d_model) ||
             overlaps_qmat(out, no, &ex.up, f, group, d_ff, d_model) ||
-            overlaps_qmat(out, no, &ex.down, f, group, d_model, d_ff) ||
-            overlaps_qmat(workspace, need, &ex.gate, f, group, d_ff, d_model) ||
-            overlaps_qmat(workspace, need, &ex.up, f, group, d_ff, d_model) ||
-            overlaps_qmat(workspace, need, &ex.down, f, group, d_model, d_ff))
+            overlaps_qmat(out, no, &ex.down, f, group, d_model, d_ff))
             return SMOE_ERR_ALIAS;
+    }
+    if (noalloc) {
+        // The device's scratch array (a static device array: no caller
+        // buffer can overlap it).
+        DeviceInfo dev;
+        if ((rc = check_device(&dev))) return rc;
+        if (!dev.scratch) return SMOE_ERR_DEVICE;
+        workspace = dev.scratch;
+        workspace_bytes = SMOE_NOALLOC_SCRATCH_BYTES;
+    } else {
+        if (overlap(out, no, workspace, need) || overlap(workspace, need, x, (size_t)T * d_model * 4) ||
+            overlap(workspace, need, route_w, route_w ? (size_t)T * n_experts * 4 : 0))
+            return SMOE_ERR_ALIAS;
+        for (int e = 0; e < n_experts; ++e) {
+            const smoe_expert &ex = experts[e];
+            if (overlaps_qmat(workspace, need, &ex.gate, f, group, d_ff, d_model) ||
+                overlaps_qmat(workspace, need, &ex.up, f, group, d_ff, d_model) ||
+                overlaps_qmat(workspace, need, &ex.down, f, group, d_model, d_ff))
+                return SMOE_ERR_ALIAS;
+        }
     }
     hipStream_t st = (hipStream_t)stream;
     if (T > 1) {
@@ -412,6 +443,21 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
     a.n_experts = n_experts;
     if ((rc = launch_status(smoe::launch_gate_up(f.bits, plan, a, dev.cus, st)))) return rc;
     return launch_status(smoe::launch_down(f.bits, plan, a, dev.cus, st));
+}
+
+int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *route_w, int fmt,
+                    int group, int d_model, int d_ff, int T, const float *x, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    return expert_ffn(experts, n_experts, route_w, fmt, group, d_model, d_ff, T, x, out, workspace,
+                      workspace_bytes, stream, false);
+}
+
+int smoe_expert_ffn_noalloc(const smoe_expert *experts, int n_experts, const float *route_w, int fmt,
+                            int group, int d_model, int d_ff, int T, const float *x, float *out, void *stream)
+{
+    return expert_ffn(experts, n_experts, route_w, fmt, group, d_model, d_ff, T, x, out, nullptr, 0, stream,
+                      true);
 }
 
 size_t smoe_routed_ffn_workspace(int n_experts, int d_model, int d_ff, int T, int top_k)

@@ -178,6 +178,34 @@ int smoe_expert_ffn(const smoe_expert *experts, int n_experts, const float *rout
                     const float *x, float *out, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* Bytes of the static device scratch array behind smoe_expert_ffn_noalloc
+ * (one array per GPU, held until the process ends). */
+#define SMOE_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+/*
+ * smoe_expert_ffn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * smoe_expert_ffn (the same kernels run), except:
+ *   - the scratch memory is a static device array of
+ *     SMOE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, in place of the caller's
+ *     workspace; a call whose smoe_expert_ffn_workspace(...) size exceeds it
+ *     returns SMOE_ERR_WORKSPACE with nothing launched.  Every one-token
+ *     (T == 1) call up to the shape limits fits; small token batches fit.
+ *   - nothing is allocated, freed or cleared by the host (no hipMalloc,
+ *     hipFree, hipMemset or allocating library call); the kernels rewrite
+ *     every part of the array they read, so its leftover contents from an
+ *     earlier call never matter.
+ *   - all calls on one GPU share that GPU's array: calls that may overlap on
+ *     one GPU (different streams without ordering, several host threads) race
+ *     and give undefined results.  Order them on one stream.
+ * The array's device address is looked up once per device, on the first call
+ * of any entry point with that device current; SMOE_ERR_DEVICE if that failed.
+ */
+int smoe_expert_ffn_noalloc(const smoe_expert *experts, int n_experts, const float *route_w,
+                            int bits, int group, int d_model, int d_ff, int T,
+                            const float *x, float *out, void *stream);
+
 /*
  * y[r] = sum_j float(W[r][j]) * x[j],  r < rows.
  *   W : bf16 bit patterns [rows x cols], 16-byte aligned, cols % 8 == 0

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {
-        "smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn",
+        "smoe_gate_up", "smoe_down", "smoe_expert_ffn_workspace", "smoe_expert_ffn", "smoe_expert_ffn_noalloc",
         "matvec_bf16_workspace", "matvec_bf16", "matvec_bf16_batch", "smoe_routed_ffn_workspace",
         "smoe_routed_ffn", "smoe_attn_decode_workspace", "smoe_attn_decode", "smoe_status_str"}
 
@@ -190,6 +190,32 @@ def test_expert_ffn_refusals(gq):
     assert call(out=WS + 256) == -7                # out inside the workspace
     assert call(out=A + 0x100) == -7               # out inside expert 0's gate codes
     assert call() == -8
+
+
+def test_expert_ffn_noalloc_refusals(gq):
+    """The no-allocation variant checks what smoe_expert_ffn checks, and
+    refuses a call whose workspace would exceed its static scratch array
+    before it looks at the device."""
+    L = gq.lib()
+    n = 8
+    arr = (gq.Expert * n)()
+    for k in range(n):
+        b = A + k * 0x10000000
+        arr[k] = gq.Expert(gq.QMat(b, b + 0x1000000), gq.QMat(b + 0x2000000, b + 0x3000000),
+                           gq.QMat(b + 0x4000000, b + 0x5000000))
+    X, OUT = 0x900000000, 0xA00000000
+    call = lambda **kw: L.smoe_expert_ffn_noalloc(
+        arr, kw.get("n", n), None, kw.get("bits", 4), 64, kw.get("dm", 4096), kw.get("dff", 1536),
+        kw.get("T", 1), kw.get("x", X), kw.get("out", OUT), None)
+    assert gq.SMOE_NOALLOC_SCRATCH_BYTES == 1 << 20
+    assert L.smoe_expert_ffn_workspace(16, 8192, 8192, 1) <= gq.SMOE_NOALLOC_SCRATCH_BYTES  # every decode call fits
+    assert L.smoe_expert_ffn_workspace(8, 4096, 1536, 64) > gq.SMOE_NOALLOC_SCRATCH_BYTES
+    assert call(T=64) == -6                        # beyond the scratch array
+    assert call(n=0) == -4
+    assert call(bits=3) == -2
+    assert call(x=X + 4) == -5
+    assert call(out=A + 0x100) == -7               # out inside expert 0's gate codes
+    assert call() == -8                            # all valid: no gfx950 device here
 
 
 def test_expert_ffn_batch_refusals(gq):
