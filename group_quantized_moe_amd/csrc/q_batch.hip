@@ -56,16 +56,20 @@ struct Half8Parts {
 // Position of column c (0..7) of an 8-column block in sigma order.
 __device__ __forceinline__ int sigma_pos(int c) { return (c & 3) * 2 + (c >> 2); }
 
-// f16 pair (1024 + a, 1024 + b) from bytes a, b (< 16) of src picked by sel,
-// shifted to (a - Z, b - Z).  Both subtractions are exact in f16.
+// f16 pair (c_a - Z, c_b - Z) from bytes a, b of src picked by sel, whose
+// codes sit in their top bits (bits 4..7 of a byte at 4 bits, 6..7 at 2
+// bits).  Under the high byte 0x48 (the exponent of 8.0) such a byte reads as
+// the f16 value 8 + c/8 (4-bit) or 8 + c/2 (2-bit); one packed FMA then gives
+// 8 (8 + c/8) - 71.5 = c - 7.5 or 2 (8 + c/2) - 17.5 = c - 1.5.  Every
+// operand and result is an f16 value, so the conversion is exact.
 template <int BITS>
 __device__ __forceinline__ half2v code_pair(uint32_t src, uint32_t sel)
 {
-    const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, src, sel);
-    half2v h = __builtin_bit_cast(half2v, bits);
-    h = h - (half2v){(_Float16)1024.0f, (_Float16)1024.0f};
-    constexpr float z = QFormat<BITS>::kZ;
-    return h - (half2v){(_Float16)z, (_Float16)z};
+    const uint32_t bits = __builtin_amdgcn_perm(0x48484848u, src, sel);
+    const half2v h = __builtin_bit_cast(half2v, bits);
+    constexpr float mul = BITS == 4 ? 8.0f : 2.0f;
+    constexpr float add = BITS == 4 ? -71.5f : -17.5f;
+    return h * (half2v){(_Float16)mul, (_Float16)mul} + (half2v){(_Float16)add, (_Float16)add};
 }
 
 // Codes per lane per quantisation group: KB K-blocks of 8 codes.
@@ -103,19 +107,21 @@ __device__ __forceinline__ half8 code_frag(const CodeWords<BITS, KB> &c, int j)
 {
     Half8Parts f;
     if constexpr (BITS == 4) {
-        // Nibbles n0..n7 of one dword: lo holds bytes (n0,n2,n4,n6), hi (n1,n3,n5,n7).
+        // Nibbles n0..n7 of one dword: lo holds bytes (n0,n2,n4,n6), hi (n1,n3,n5,n7),
+        // each nibble in the top half of its byte.
         const uint32_t d = c.w[j];
-        const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = (d << 4) & 0xF0F0F0F0u, hi = d & 0xF0F0F0F0u;
         f.v[0] = code_pair<4>(lo, 0x04020400u);  // n0, n4
         f.v[1] = code_pair<4>(hi, 0x04020400u);  // n1, n5
         f.v[2] = code_pair<4>(lo, 0x04030401u);  // n2, n6
         f.v[3] = code_pair<4>(hi, 0x04030401u);  // n3, n7
     } else {
-        // 16 two-bit codes c0..c15 per dword; a_k holds bytes (c_k, c_4+k, c_8+k, c_12+k).
+        // 16 two-bit codes c0..c15 per dword; a_k holds bytes (c_k, c_4+k, c_8+k, c_12+k),
+        // each code in the top two bits of its byte.
         const uint32_t d = c.w[j >> 1];
         const uint32_t sel = (j & 1) ? 0x04030402u : 0x04010400u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) f.v[k] = code_pair<2>((d >> (2 * k)) & 0x03030303u, sel);
+        for (int k = 0; k < 4; ++k) f.v[k] = code_pair<2>((d << (6 - 2 * k)) & 0xC0C0C0C0u, sel);
     }
     return __builtin_bit_cast(half8, f);
 }
