@@ -416,12 +416,23 @@ __device__ __forceinline__ float silu_hw(float t)
 }
 
 // Code and scale registers of one step: NCH chunks of M matrices for the
-// lane's row.
+// lane's row.  Scales are kept as loaded (f32 bits, or binary16 bits in the
+// low half) and widened where they are used: a widening next to the load
+// would wait for the load right there.
 template <int NCH, int M>
 struct Stage {
     uint4 q[NCH][M];
-    float s[NCH][M];
+    uint32_t s[NCH][M];
 };
+
+template <int SB>
+__device__ __forceinline__ float stage_scale(uint32_t bits)
+{
+    if constexpr (SB == 4)
+        return __uint_as_float(bits);
+    else
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
 
 // Loads of one stage: the lane's row is row0 + slot, clamped to the last row
 // (a partial last step re-reads it; its results are never stored).
@@ -441,20 +452,20 @@ __device__ __forceinline__ void load_stage(Stage<NCH, M> &t, const uint8_t *cons
             t.q[k][m] = *reinterpret_cast<const uint4 *>(codes[m] + (crow + ln.coff[k]));
             const uint8_t *sb = reinterpret_cast<const uint8_t *>(scales[m]);
             if constexpr (SB == 4)
-                t.s[k][m] = *reinterpret_cast<const float *>(sb + (srow + ln.soff[k]));
+                t.s[k][m] = *reinterpret_cast<const uint32_t *>(sb + (srow + ln.soff[k]));
             else
-                t.s[k][m] = (float)*reinterpret_cast<const _Float16 *>(sb + ((srow + ln.soff[k]) >> 1));
+                t.s[k][m] = *reinterpret_cast<const uint16_t *>(sb + ((srow + ln.soff[k]) >> 1));
         }
     }
 }
 
 // Row sums of matrix m for the lane's chunks (before the cross-lane sum).
-template <int BITS, int NCH, int M>
+template <int BITS, int NCH, int M, int SB>
 __device__ __forceinline__ float stage_dot(const Stage<NCH, M> &t, int m, const ChunkVec<BITS> *cv)
 {
     float y = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][m], t.s[k][m], cv[k]);
+    for (int k = 0; k < NCH; ++k) y += chunk_contrib<BITS>(t.q[k][m], stage_scale<SB>(t.s[k][m]), cv[k]);
     return y;
 }
 
@@ -549,8 +560,8 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
                     wait_vm_all();               // this step's loads (and the last hidden store) are in
                     load_next(S[(i + 1) % NS_]); // the next step's go out first
                 }
-                float g = stage_dot<BITS, NCH, 2>(S[i], 0, cv);
-                float u = stage_dot<BITS, NCH, 2>(S[i], 1, cv);
+                float g = stage_dot<BITS, NCH, 2, SB>(S[i], 0, cv);
+                float u = stage_dot<BITS, NCH, 2, SB>(S[i], 1, cv);
                 g = group_sum<LPR>(g);
                 u = group_sum<LPR>(u);
                 const int r = cc.s * rs + ln.slot;
@@ -690,7 +701,7 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
             for (int i = 0; i < DEPTH; ++i) {
                 const int j = base + i;
                 if (j < n) {
-                    float y = stage_dot<BITS, NCH, 1>(S[i], 0, cv);
+                    float y = stage_dot<BITS, NCH, 1, SB>(S[i], 0, cv);
                     y = group_sum<LPR>(y);
                     const int r = (it + j - e * ns) * rs + ln.slot;  // row within the block
                     if (ln.writer() && s0 * rs + r < a.d_model) slab[e * brows + r] = y;
