@@ -64,10 +64,10 @@ struct TbArgs {
     int *xe;                 // [T]
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
-    float *part_gu, *part_dn; // tiled kernels: per-tile partial sums of the K splits
-    unsigned *cnt_gu, *cnt_dn; // tiled kernels: per tile, the K splits done (k_tb_prep zeroes them)
+    float *part_gu, *part_dn; // per-tile partial sums of the K splits
+    unsigned *cnt_gu, *cnt_dn; // per tile, the K splits done (k_tb_prep zeroes them)
     int n_cnt;               // entries of cnt_gu and cnt_dn together (contiguous)
-    // Routed mode (top_k > 0; tiled kernels only): slot s = t*top_k + j of token
+    // Routed mode (top_k > 0): slot s = t*top_k + j of token
     // t goes to expert ids[s] with weight slot_w[s].  list[e*T + p], p <
     // cnt[e], are expert e's slots in ascending order; the hidden rows,
     // factors and partial sums of expert e are indexed by p instead of the
@@ -80,22 +80,19 @@ struct TbArgs {
     float *ys;
     int T, t_pad, d_model, d_ff, group, n_experts;
     int scale_bytes;         // 4: f32 scales, 2: IEEE binary16 scales
-    int ks_gu, rw_gu;        // gate_up waves per block: rw_gu row slices x ks_gu K slices
-    int ks_dn, rw_dn;        // down: rw_dn row slices x ks_dn (expert, group) slices, as waves of one
-                             // block; for the tiled kernels ks_gu / ks_dn are splits over blocks
+    int ks_gu, ks_dn;        // K splits over blocks of gate_up and down
 };
 
-// Tiling of the three token-batch launches: 16*ntt tokens per block, rt_gu row
-// tiles per gate_up wave; waves per block, block counts and dynamic LDS bytes
-// of gate_up and down.
+// Tiling of the token-batch launches: 16*ntt tokens per block, gate_up steps
+// of mg quantisation groups, K splits, block counts and dynamic LDS bytes of
+// gate_up and down.
 struct TbPlan {
-    bool tiled;              // tiled kernels (groups of 32 and 64 columns)
-    int mg;                  // tiled gate_up: quantisation groups per step
-    int ntt, rt_gu;
-    int rw_gu, ks_gu, gu_waves;
+    int mg;
+    int ntt;
+    int ks_gu;
     long gu_blocks;
     size_t gu_lds;
-    int rw_dn, ks_dn, dn_waves;
+    int ks_dn;
     long dn_blocks;
     size_t dn_lds;
 };
@@ -104,9 +101,9 @@ struct TbPlan {
 constexpr int kTokenPad = 64;
 
 // False if the shape is outside what the token-batch kernels cover (group
-// must be 32, 64, 96 or 128 columns at 4 bits, 64 or 128 at 2 bits).
+// must be 32 or 64 columns at 4 bits, 64 at 2 bits).
 bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T, TbPlan *plan);
-// Tiling of the tiled token-batch kernels that depends on the shape only (not
+// Tiling of the token-batch kernels that depends on the shape only (not
 // the group): tokens per tile / 16, tile counts, the largest K splits and the
 // partial-sum floats they need in the workspace.
 struct BatchSplits {

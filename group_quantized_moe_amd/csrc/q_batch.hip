@@ -79,28 +79,6 @@ struct CodeWords {
     uint32_t w[kDwords];
 };
 
-template <int BITS, int KB>
-__device__ __forceinline__ void load_codes(const uint8_t *p, CodeWords<BITS, KB> &c)
-{
-    constexpr int n = CodeWords<BITS, KB>::kDwords;
-    if constexpr (n == 1) {
-        c.w[0] = *reinterpret_cast<const uint32_t *>(p);
-    } else if constexpr (n == 2) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(p);
-        c.w[0] = v.x;
-        c.w[1] = v.y;
-    } else if constexpr (n == 4) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(p);
-        c.w[0] = v.x;
-        c.w[1] = v.y;
-        c.w[2] = v.z;
-        c.w[3] = v.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < n; ++i) c.w[i] = reinterpret_cast<const uint32_t *>(p)[i];
-    }
-}
-
 // B fragment of K-block j: the lane's 8 codes in sigma order as f16 (c - Z).
 template <int BITS, int KB>
 __device__ __forceinline__ half8 code_frag(const CodeWords<BITS, KB> &c, int j)
@@ -160,7 +138,6 @@ __device__ __forceinline__ float row16_max(float v)
 // data format, as the memory instructions expect for untyped loads.
 using BufRes = __amdgpu_buffer_rsrc_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ BufRes buf_res(const void *base, size_t bytes)
 {
@@ -174,40 +151,6 @@ __device__ __forceinline__ uint4 buf_load16(BufRes r, unsigned voff, unsigned so
 __device__ __forceinline__ unsigned buf_load4(BufRes r, unsigned voff, unsigned soff)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-}
-
-// Scale g of a row whose f32 scales would start `row_off4` bytes into the
-// buffer: f32 (SB = 4), or IEEE binary16 widened exactly to f32 (SB = 2, at half
-// the offsets).
-template <int SB>
-__device__ __forceinline__ float buf_load_scale(BufRes r, unsigned row_off4, unsigned g)
-{
-    if constexpr (SB == 4) {
-        return __uint_as_float(buf_load4(r, row_off4, g * 4u));
-    } else {
-        const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(row_off4 >> 1), (int)(g * 2u), 0);
-        return (float)__builtin_bit_cast(_Float16, h);
-    }
-}
-
-template <int BITS, int KB>
-__device__ __forceinline__ void buf_load_codes(BufRes r, unsigned voff, unsigned soff, CodeWords<BITS, KB> &c)
-{
-    constexpr int n = CodeWords<BITS, KB>::kDwords;
-    if constexpr (n == 4) {
-        const uint4 v = buf_load16(r, voff, soff);
-        c.w[0] = v.x;
-        c.w[1] = v.y;
-        c.w[2] = v.z;
-        c.w[3] = v.w;
-    } else if constexpr (n == 2) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
-        c.w[0] = v.x;
-        c.w[1] = v.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < n; ++i) c.w[i] = buf_load4(r, voff + 4 * i, soff);
-    }
 }
 
 // Raw bits of scale element idx (f32, or binary16 in the low half), and its
@@ -285,7 +228,7 @@ __device__ __forceinline__ void prep_token(const float *__restrict__ x, int cols
                                            unsigned *__restrict__ cnt, int n_cnt, int tok, int ntok)
 {
     __shared__ float s_max[4];
-    // The tiled kernels' split counters start every call at zero.
+    // The split counters start every call at zero.
     for (int i = tok * 256 + threadIdx.x; i < n_cnt; i += ntok * 256) cnt[i] = 0u;
     const size_t base = (size_t)tok * cols;
     const int nch = cols / 8;
@@ -335,360 +278,8 @@ __global__ __launch_bounds__(256) void k_tb_prep(const float *__restrict__ x, in
     prep_token(x, cols, xh, xl, xe, cnt, n_cnt, blockIdx.x, gridDim.x);
 }
 
-// One step of the K loop: the activation fragments of NTT token tiles and
-// the codes and scales of NB row tiles, for one quantisation group.
-template <int BITS, int KB, int NTT, int NB>
-struct TbStage {
-    half8 ah[NTT][KB], al[NTT][KB];
-    CodeWords<BITS, KB> cw[NB];
-    float s[NB];
-};
-
-// sum over the step's K-blocks of (hi + lo) x codes, for token tile tt and
-// row tile b: one f32 accumulator per quantisation group.
-template <int BITS, int KB, int NTT, int NB>
-__device__ __forceinline__ f32x4 group_mfma(const TbStage<BITS, KB, NTT, NB> &st, const half8 *bf, int tt)
-{
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-        acc = mfma(st.ah[tt][j], bf[j], acc);
-        acc = mfma(st.al[tt][j], bf[j], acc);
-    }
-    return acc;
-}
-
 // -------------------------------------------------------------------------
-// Gate and up for one expert, one quantisation group of d_ff rows (the
-// block's "H group") and 16*NTT tokens.  Wave (rw, ks) covers rows
-// rw*16*RT .. +16*RT of the H group in both matrices and quantisation groups
-// [ks*G/KS, (ks+1)*G/KS) of d_model; partial sums over ks are added in LDS in
-// a fixed order.  The hidden rows are normalised per (token, H group), split
-// into hi/lo halves and stored with the factor r[t][e] * 2^e for down.
-template <int BITS, int KB, int NTT, int RT, int SB>
-__global__ __launch_bounds__(512) void k_tb_gate_up(TbArgs a)
-{
-    extern __shared__ float lds[];
-    constexpr int NB = 2 * RT;            // gate row tiles, then up row tiles
-    constexpr int kTot = NB * NTT * 4;    // accumulator floats per lane
-    constexpr int DEPTH = 2;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int KS = a.ks_gu, RW = a.rw_gu;
-    const int ks = wave % KS, rw = wave / KS;
-    const int q = lane >> 4, n = lane & 15;
-    const int group = a.group, d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
-    const int G = d_model / group, HG = d_ff / group;
-    const int NTB = (T + 16 * NTT - 1) / (16 * NTT);
-    int b = blockIdx.x;
-    const int tb = b % NTB;
-    b /= NTB;
-    const int hg = b % HG;
-    const int e = b / HG;
-    const int row0 = hg * group + rw * 16 * RT;   // first d_ff row of this wave
-    const int t0 = tb * 16 * NTT;
-    // Fixed 32-bit lane offsets into buffer resources; a step moves only the
-    // uniform offsets (a matrix has at most 8192 x 8192 entries; X at most
-    // 65536 x 8192 halves).
-    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * SB;
-    const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
-    const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
-    const BufRes xhr = buf_res(a.xh, (size_t)T * d_model * 2), xlr = buf_res(a.xl, (size_t)T * d_model * 2);
-    unsigned coff[RT], soff[RT], xoff[NTT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const unsigned row = (unsigned)(row0 + rt * 16 + n);
-        coff[rt] = row * (unsigned)(d_model * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
-        soff[rt] = row * (unsigned)G * 4u;
-    }
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-        xoff[tt] = ((unsigned)min(t0 + tt * 16 + n, T - 1) * (unsigned)d_model + (unsigned)(q * 8 * KB)) * 2u;
-    using Stage = TbStage<BITS, KB, NTT, NB>;
-    auto load = [&](Stage &st, int g) {
-        const unsigned xs = (unsigned)g * (unsigned)group * 2u;
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                st.ah[tt][j] = __builtin_bit_cast(half8, buf_load16(xhr, xoff[tt] + 16 * j, xs));
-                st.al[tt][j] = __builtin_bit_cast(half8, buf_load16(xlr, xoff[tt] + 16 * j, xs));
-            }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                buf_load_codes<BITS, KB>(cr[m], coff[rt], (unsigned)g * (unsigned)(group * BITS / 8),
-                                         st.cw[m * RT + rt]);
-                st.s[m * RT + rt] = buf_load_scale<SB>(sr[m], soff[rt], (unsigned)g);
-            }
-    };
-
-    f32x4 tot[NB][NTT];
-#pragma unroll
-    for (int bt = 0; bt < NB; ++bt)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) tot[bt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    // Every wave has at least one group (KS <= G).  The loop is branch-free
-    // so that waiting for one stage leaves the others in flight: loads past
-    // the wave's last group re-read it, and those steps count with scale 0.
-    const int gbeg = ks * G / KS, gend = (ks + 1) * G / KS;
-    Stage S[DEPTH];
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-        load(S[i], min(gbeg + i, gend - 1));
-        __builtin_amdgcn_sched_barrier(0);   // keep the stages' loads in issue order
-    }
-    for (int base = gbeg; base < gend; base += DEPTH) {
-#pragma unroll
-        for (int i = 0; i < DEPTH; ++i) {
-            const int g = base + i;
-#pragma unroll
-            for (int bt = 0; bt < NB; ++bt) {
-                half8 bf[KB];
-#pragma unroll
-                for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].cw[bt], j);
-                const float s = g < gend ? S[i].s[bt] * QFormat<BITS>::kInvZ : 0.0f;
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) {
-                    const f32x4 acc = group_mfma<BITS, KB, NTT, NB>(S[i], bf, tt);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[bt][tt][r] = fmaf(s, acc[r], tot[bt][tt][r]);
-                }
-            }
-            load(S[i], min(g + DEPTH, gend - 1));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // Sum the KS partials: tot(0) + (tot(1) + (... + tot(KS-1))).
-    float *buf = lds + (size_t)rw * kTot * 64;
-    if (KS > 1) {
-        for (int s = KS - 1; s >= 1; --s) {
-            if (ks == s) {
-                int r = 0;
-#pragma unroll
-                for (int bt = 0; bt < NB; ++bt)
-#pragma unroll
-                    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i, ++r) {
-                            float v = tot[bt][tt][i];
-                            if (s != KS - 1) v += buf[r * 64 + lane];
-                            buf[r * 64 + lane] = v;
-                        }
-            }
-            __syncthreads();
-        }
-    }
-
-    // hidden = SiLU(gate) * up for tokens 4q + i of each token tile, rows n
-    // of each row tile; then each token's largest |hidden| over this wave's
-    // rows (a DPP row holds the 16 rows of a tile for the same 4 tokens).
-    float *mx = lds + (KS > 1 ? (size_t)RW * kTot * 64 : 0);  // [RW][NTT][16]
-    float h[RT][NTT][4];
-    if (ks == 0) {
-        int r = 0;
-#pragma unroll
-        for (int bt = 0; bt < NB; ++bt)
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i, ++r)
-                    if (KS > 1) tot[bt][tt][i] += buf[r * 64 + lane];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = min(t0 + tt * 16 + 4 * q + i, T - 1);
-                const int xe = a.xe[t];
-                float m = 0.0f;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const float gv = ldexpf(tot[rt][tt][i], xe), uv = ldexpf(tot[RT + rt][tt][i], xe);
-                    h[rt][tt][i] = silu(gv) * uv;
-                    m = fmaxf(m, fabsf(h[rt][tt][i]));
-                }
-                m = row16_max(m);
-                if (n == 0) mx[(rw * NTT + tt) * 16 + 4 * q + i] = m;
-            }
-        }
-    }
-    __syncthreads();
-    if (ks != 0) return;
-
-    // Normalise per (token, H group), split into hi/lo halves, store in sigma
-    // order, and store each token's factor for down.
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tl = 4 * q + i;
-            float m = 0.0f;
-            for (int w = 0; w < RW; ++w) m = fmaxf(m, mx[(w * NTT + tt) * 16 + tl]);
-            const int ee = norm_exponent(m);
-            const int t = t0 + tt * 16 + tl;
-            if (t < T) {
-                const size_t hrow = ((size_t)e * T + t) * d_ff;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const float v = ldexpf(h[rt][tt][i], -ee);
-                    const _Float16 hv = (_Float16)v;
-                    const int r = row0 + rt * 16 + n;
-                    const size_t pos = hrow + (r & ~7) + sigma_pos(r & 7);
-                    a.hh[pos] = hv;
-                    a.hl[pos] = (_Float16)(v - (float)hv);
-                }
-                if (rw == 0 && n == 0) {
-                    const float rwt = a.route_w ? a.route_w[(size_t)t * E + e] : 1.0f;
-                    a.hf[((size_t)e * HG + hg) * a.t_pad + t] = ldexpf(rwt, ee);
-                }
-            }
-        }
-    }
-}
-
-// -------------------------------------------------------------------------
-// Down for 16*RT*RW rows of d_model and 16*NTT tokens, summed over all
-// experts.  Wave (rw, ks): rows rw*16*RT .. +16*RT of the block, (expert,
-// group) pairs [ks*P/KS, (ks+1)*P/KS) of P = E * d_ff/group in ascending
-// order; partials over ks are added in LDS in a fixed order.
-template <int BITS, int KB, int NTT, int RT, int SB>
-__global__ __launch_bounds__(512) void k_tb_down(TbArgs a)
-{
-    extern __shared__ float lds[];
-    constexpr int kTot = RT * NTT * 4;
-    constexpr int DEPTH = 2;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int KS = a.ks_dn, RW = a.rw_dn;
-    const int ks = wave % KS, rw = wave / KS;
-    const int q = lane >> 4, n = lane & 15;
-    const int group = a.group, d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
-    const int Gd = d_ff / group;
-    const int NTB = (T + 16 * NTT - 1) / (16 * NTT);
-    const int tb = blockIdx.x % NTB, rb = blockIdx.x / NTB;
-    const int row0 = (rb * RW + rw) * 16 * RT;
-    const int t0 = tb * 16 * NTT;
-    // Fixed 32-bit lane offsets; a step moves only uniform offsets (one
-    // expert's hidden half has at most 65536 x 8192 entries).
-    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * SB;
-    const size_t hbytes = (size_t)T * d_ff * 2;
-    const BufRes fres = buf_res(a.hf, (size_t)E * Gd * a.t_pad * 4);
-    unsigned coff[RT], soff[RT], hoff[NTT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const unsigned row = (unsigned)min(row0 + rt * 16 + n, d_model - 1);
-        coff[rt] = row * (unsigned)(d_ff * BITS / 8) + (unsigned)(q * 8 * KB * BITS / 8);
-        soff[rt] = row * (unsigned)Gd * 4u;
-    }
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-        hoff[tt] = ((unsigned)min(t0 + tt * 16 + n, T - 1) * (unsigned)d_ff + (unsigned)(q * 8 * KB)) * 2u;
-
-    struct Stage {
-        TbStage<BITS, KB, NTT, RT> v;
-        f32x4 f[NTT];  // factors of tokens 4q..4q+3 of each token tile
-    };
-    auto load = [&](Stage &st, int p) {
-        const int e = p / Gd, g = p - e * Gd;
-        const size_t he = (size_t)e * T * d_ff;
-        const BufRes hr = buf_res(a.hh + he, hbytes), lr = buf_res(a.hl + he, hbytes);
-        const unsigned hs = (unsigned)g * (unsigned)group * 2u;
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-#pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                st.v.ah[tt][j] = __builtin_bit_cast(half8, buf_load16(hr, hoff[tt] + 16 * j, hs));
-                st.v.al[tt][j] = __builtin_bit_cast(half8, buf_load16(lr, hoff[tt] + 16 * j, hs));
-            }
-            st.f[tt] = __builtin_bit_cast(f32x4, buf_load16(fres, (unsigned)(tt * 16 + 4 * q) * 4u,
-                                                            (unsigned)(((size_t)e * Gd + g) * a.t_pad + t0) * 4u));
-        }
-        const BufRes dc = buf_res(a.down[e].codes, cbytes), ds = buf_res(a.down[e].scales, sbytes);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            buf_load_codes<BITS, KB>(dc, coff[rt], (unsigned)g * (unsigned)(group * BITS / 8), st.v.cw[rt]);
-            st.v.s[rt] = buf_load_scale<SB>(ds, soff[rt], (unsigned)g);
-        }
-    };
-
-    f32x4 tot[RT][NTT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) tot[rt][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    // Every wave has at least one pair (KS <= P); branch-free ring as in
-    // gate_up (steps past the wave's last pair count with scale 0).
-    const int P = E * Gd;
-    const int pbeg = ks * P / KS, pend = (ks + 1) * P / KS;
-    Stage S[DEPTH];
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-        load(S[i], min(pbeg + i, pend - 1));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int base = pbeg; base < pend; base += DEPTH) {
-#pragma unroll
-        for (int i = 0; i < DEPTH; ++i) {
-            const int p = base + i;
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                half8 bf[KB];
-#pragma unroll
-                for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(S[i].v.cw[rt], j);
-                const float s = p < pend ? S[i].v.s[rt] * QFormat<BITS>::kInvZ : 0.0f;
-#pragma unroll
-                for (int tt = 0; tt < NTT; ++tt) {
-                    const f32x4 acc = group_mfma<BITS, KB, NTT, RT>(S[i].v, bf, tt);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[rt][tt][r] = fmaf(s * S[i].f[tt][r], acc[r], tot[rt][tt][r]);
-                }
-            }
-            load(S[i], min(p + DEPTH, pend - 1));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    float *buf = lds + (size_t)rw * kTot * 64;
-    if (KS > 1) {
-        for (int s = KS - 1; s >= 1; --s) {
-            if (ks == s) {
-                int r = 0;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i, ++r) {
-                            float v = tot[rt][tt][i];
-                            if (s != KS - 1) v += buf[r * 64 + lane];
-                            buf[r * 64 + lane] = v;
-                        }
-            }
-            __syncthreads();
-        }
-    }
-    if (ks != 0) return;
-    int r = 0;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i, ++r) {
-                float v = tot[rt][tt][i];
-                if (KS > 1) v += buf[r * 64 + lane];
-                const int t = t0 + tt * 16 + 4 * q + i;
-                const int row = row0 + rt * 16 + n;
-                if (t < T && row < d_model) a.out[(size_t)t * d_model + row] = v;
-            }
-}
-
-// -------------------------------------------------------------------------
-// Tiled kernels (groups of 32 and 64 columns): a block of 8 waves covers a
+// Kernels (groups of 32 and 64 columns): a block of 8 waves covers a
 // tile of TT = 16 * NTT tokens and 128 weight rows (one 16-row tile per wave).
 // For each quantisation group (gate_up) or (expert, group) pair (down) the
 // block loads the tile's activation halves once, with coalesced 16-byte loads,
@@ -1581,59 +1172,22 @@ hipError_t launch_routed_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStr
     return hipErrorInvalidValue;
 }
 
-template <int BITS, int KB, int NTT, int RTG, int RTD, int SB>
-hipError_t launch_tb_kernels(const TbPlan &pl, const TbArgs &a, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_tb_prep, dim3((unsigned)a.T), dim3(256), 0, st, a.x, a.d_model, a.xh, a.xl, a.xe,
-                       (unsigned *)nullptr, 0);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_gate_up<BITS, KB, NTT, RTG, SB>), dim3(pl.gu_blocks), dim3(64 * pl.gu_waves), pl.gu_lds,
-                       st, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_tb_down<BITS, KB, NTT, RTD, SB>), dim3(pl.dn_blocks), dim3(64 * pl.dn_waves), pl.dn_lds, st,
-                       a);
-    return hipGetLastError();
-}
-
 template <int BITS, int KB, int SB>
 hipError_t launch_tb_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    if constexpr (KB <= 2) {
-        if (pl.tiled) {
-            if (pl.ntt == 1) {
-                if (pl.mg == 2) return launch_tb_tiled<BITS, KB, 1, 2, SB>(pl, a, st);
-                return launch_tb_tiled<BITS, KB, 1, 1, SB>(pl, a, st);
-            }
-            if (pl.ntt == 2) return launch_tb_tiled<BITS, KB, 2, 1, SB>(pl, a, st);
-            return launch_tb_tiled<BITS, KB, 4, 1, SB>(pl, a, st);
-        }
+    if (pl.ntt == 1) {
+        if (pl.mg == 2) return launch_tb_tiled<BITS, KB, 1, 2, SB>(pl, a, st);
+        return launch_tb_tiled<BITS, KB, 1, 1, SB>(pl, a, st);
     }
-    // Direct kernels (groups of 96 and 128 columns).  gate_up row tiles: 2
-    // (more would not fit the registers); down: 4 row tiles for 16-token
-    // tiles, 2 for 32.
-    if (pl.ntt == 1) return launch_tb_kernels<BITS, KB, 1, 2, 4, SB>(pl, a, st);
-    return launch_tb_kernels<BITS, KB, 2, 2, 2, SB>(pl, a, st);
+    if (pl.ntt == 2) return launch_tb_tiled<BITS, KB, 2, 1, SB>(pl, a, st);
+    return launch_tb_tiled<BITS, KB, 4, 1, SB>(pl, a, st);
 }
 
 template <int SB>
 hipError_t launch_tb_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    const int kb = a.group / 32;
-    if (bits == 4) {
-        switch (kb) {
-        case 1: return launch_tb_kb<4, 1, SB>(pl, a, st);
-        case 2: return launch_tb_kb<4, 2, SB>(pl, a, st);
-        case 3: return launch_tb_kb<4, 3, SB>(pl, a, st);
-        case 4: return launch_tb_kb<4, 4, SB>(pl, a, st);
-        default: return hipErrorInvalidValue;
-        }
-    }
-    switch (kb) {
-    case 2: return launch_tb_kb<2, 2, SB>(pl, a, st);
-    case 4: return launch_tb_kb<2, 4, SB>(pl, a, st);
-    default: return hipErrorInvalidValue;
-    }
+    if (bits == 4) return a.group == 32 ? launch_tb_kb<4, 1, SB>(pl, a, st) : launch_tb_kb<4, 2, SB>(pl, a, st);
+    return launch_tb_kb<2, 2, SB>(pl, a, st);
 }
 
 }  // namespace
@@ -1641,7 +1195,7 @@ hipError_t launch_tb_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStream_
 // Dynamic LDS per block is kept within 64 KB.
 constexpr size_t kMaxBlockLds = 64 * 1024;
 
-// Tokens per tile of the tiled kernels: 16, 32 or 64.
+// Tokens per tile: 16, 32 or 64.
 int tile_ntt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 
 // Splits of K over blocks: the smallest power of two (at most 16) that gives
@@ -1680,64 +1234,26 @@ BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T)
 bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T, TbPlan *pl)
 {
     if (T < 2 || n_experts < 1) return false;
-    const int kb = group / 32;
-    if (bits == 4 ? (kb < 1 || kb > 4) : (kb != 2 && kb != 4)) return false;
+    if (bits == 4 ? (group != 32 && group != 64) : group != 64) return false;
     if (d_model % group || d_ff % group) return false;
+    // 16 * ntt tokens x 128 rows per 8-wave block, K split over blocks as the
+    // workspace allows (at most one split per 4-group iteration).
+    const BatchSplits bs = batch_splits(n_experts, d_model, d_ff, T);
     TbPlan p{};
-    if (group == 32 || group == 64) {
-        // Tiled kernels: 16 * ntt tokens x 128 rows per 8-wave block, K split
-        // over blocks as the workspace allows (at most one split per 4-group
-        // iteration).
-        const BatchSplits bs = batch_splits(n_experts, d_model, d_ff, T);
-        p.tiled = true;
-        p.ntt = bs.ntt;
-        p.gu_waves = p.dn_waves = kTileWaves;
-        // gate_up steps of mg groups: 2 for 16-token tiles, else 1 (1 if 2 does
-        // not divide the groups of d_model).
-        const int G = d_model / group;
-        p.mg = p.ntt == 1 ? 2 : 1;
-        while (G % p.mg) p.mg /= 2;
-        p.ks_gu = std::min(bs.ks_gu, (G + 3) / 4);   // splits of whole 4-group iterations
-        p.ks_dn = std::min(bs.ks_dn, n_experts * ((d_ff / group + 3) / 4));
-        p.gu_blocks = bs.gu_tiles * p.ks_gu;
-        p.dn_blocks = bs.dn_tiles * p.ks_dn;
-        const int tt = 16 * p.ntt;
-        const size_t gtile = (size_t)2 * tt * (p.mg * group + 8) * 2;
-        p.gu_lds = 2 * gtile + (size_t)kTileWaves * p.ntt * 16 * 4;
-        p.dn_lds = 2 * ((size_t)2 * tt * (group + 8) * 2) + 2 * tt * 4;
-        if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
-        *pl = p;
-        return true;
-    }
-    p.ntt = T <= 16 ? 1 : 2;
-    const int ntb = (T + 16 * p.ntt - 1) / (16 * p.ntt);
+    p.ntt = bs.ntt;
+    // gate_up steps of mg groups: 2 for 16-token tiles, else 1 (1 if 2 does
+    // not divide the groups of d_model).
     const int G = d_model / group;
-    // gate_up: the block covers one quantisation group of d_ff rows.
-    p.rt_gu = 2;
-    p.rw_gu = group / (16 * p.rt_gu);
-    if (p.rw_gu < 1 || p.rw_gu > 8 || p.rw_gu * 16 * p.rt_gu != group) return false;
-    const long gu_blocks = (long)n_experts * (d_ff / group) * ntb;
-    const int gu_tot = 2 * p.rt_gu * p.ntt * 4;   // accumulator floats per lane
-    const size_t gu_buf = (size_t)p.rw_gu * gu_tot * 64 * 4;
-    const size_t gu_max = (size_t)p.rw_gu * p.ntt * 16 * 4;
-    p.ks_gu = 1;
-    while (p.ks_gu < 8 && p.rw_gu * p.ks_gu * 2 <= 8 && p.ks_gu * 2 <= G && gu_buf + gu_max <= kMaxBlockLds &&
-           gu_blocks * p.rw_gu * p.ks_gu < 2048)
-        p.ks_gu *= 2;
-    p.gu_waves = p.rw_gu * p.ks_gu;
-    p.gu_blocks = gu_blocks;
-    p.gu_lds = (p.ks_gu > 1 ? gu_buf : 0) + gu_max;
-    // down: the block covers 16*rt*rw_dn rows of d_model; waves split the
-    // (expert, group) pairs.
-    const int rt_dn = p.ntt == 1 ? 4 : 2;
-    p.rw_dn = 1;
-    const int P = n_experts * (d_ff / group);
-    const int rows_per_block = 16 * rt_dn * p.rw_dn;
-    p.dn_blocks = (long)((d_model + rows_per_block - 1) / rows_per_block) * ntb;
-    p.ks_dn = 1;
-    while (p.ks_dn < 8 && p.ks_dn * 2 <= P && p.dn_blocks * p.ks_dn < 2048) p.ks_dn *= 2;
-    p.dn_waves = p.rw_dn * p.ks_dn;
-    p.dn_lds = p.ks_dn > 1 ? (size_t)p.rw_dn * rt_dn * p.ntt * 4 * 64 * 4 : 0;
+    p.mg = p.ntt == 1 ? 2 : 1;
+    while (G % p.mg) p.mg /= 2;
+    p.ks_gu = std::min(bs.ks_gu, (G + 3) / 4);   // splits of whole 4-group iterations
+    p.ks_dn = std::min(bs.ks_dn, n_experts * ((d_ff / group + 3) / 4));
+    p.gu_blocks = bs.gu_tiles * p.ks_gu;
+    p.dn_blocks = bs.dn_tiles * p.ks_dn;
+    const int tt = 16 * p.ntt;
+    const size_t gtile = (size_t)2 * tt * (p.mg * group + 8) * 2;
+    p.gu_lds = 2 * gtile + (size_t)kTileWaves * p.ntt * 16 * 4;
+    p.dn_lds = 2 * ((size_t)2 * tt * (group + 8) * 2) + 2 * tt * 4;
     if (p.gu_lds > kMaxBlockLds || p.dn_lds > kMaxBlockLds) return false;
     *pl = p;
     return true;
@@ -1784,9 +1300,7 @@ bool plan_routed(int bits, int group, int d_model, int d_ff, int n_experts, int 
     if (d_model % group || d_ff % group) return false;
     const BatchSplits bs = routed_splits(n_experts, d_model, d_ff, T, top_k);
     TbPlan p{};
-    p.tiled = true;
     p.ntt = bs.ntt;
-    p.gu_waves = p.dn_waves = kTileWaves;
     const int G = d_model / group;
     p.mg = p.ntt == 1 ? 2 : 1;
     while (G % p.mg) p.mg /= 2;

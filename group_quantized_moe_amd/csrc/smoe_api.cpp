@@ -419,9 +419,7 @@ static int expert_ffn(const smoe_expert *experts, int n_experts, const float *ro
         a.scale_bytes = f.sb;
         a.n_experts = n_experts;
         a.ks_gu = tplan.ks_gu;
-        a.rw_gu = tplan.rw_gu;
         a.ks_dn = tplan.ks_dn;
-        a.rw_dn = tplan.rw_dn;
         return launch_status(smoe::launch_batch(f.bits, tplan, a, st));
     }
 

@@ -165,8 +165,8 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  * is split over blocks whose partial sums are added in a fixed split order,
  * by a finishing pass or, for tiles of 16 tokens, by the tile's last split
  * block (one counter per tile in the workspace, zeroed by the call itself).
- * They need group = 32, 64, 96 or 128 at 4 bits and 64 or 128 at 2 bits, else
- * SMOE_ERR_GROUP.  Activations are carried to the matrix cores
+ * They need group = 32 or 64 at 4 bits and 64 at 2 bits, else SMOE_ERR_GROUP
+ * (wider groups are served at T = 1 only).  Activations are carried to the matrix cores
  * as two f16 halves scaled by a power of two per group, about 22 significant
  * bits; non-finite inputs give non-finite outputs.
  * The workspace size depends on (n_experts, d_model, d_ff, T) only; for T > 1

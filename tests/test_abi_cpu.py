@@ -237,6 +237,10 @@ def test_expert_ffn_batch_refusals(gq):
         arr, n, None, kw.get("bits", 4), kw.get("group", 64), 320, 640, kw.get("T", T), X, OUT, WS,
         kw.get("wsb", need), None)
     assert call(group=160) == -3                   # valid for decode, not for the batch tiling
+    # Groups of 96 and 128 columns are decode-only (T = 1); the batch takes 32 or 64.
+    call2 = lambda bits, group: L.smoe_expert_ffn(arr, n, None, bits, group, 384, 768, T, X, OUT, WS, 1 << 30, None)
+    assert call2(4, 96) == -3 and call2(4, 128) == -3 and call2(2, 128) == -3
+    assert call2(4, 64) == -8 and call2(4, 32) == -8 and call2(2, 64) == -8
     assert call(bits=2, group=32) == -3
     assert call(T=65537) == -4
     assert call(wsb=need - 1) == -6

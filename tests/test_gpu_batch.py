@@ -107,13 +107,10 @@ BATCH_EDGE = [  # bits, group, d_model, d_ff, n_experts, T
     (4, 64, 256, 512, 1, 17),
     (4, 32, 96, 160, 3, 5),
     (4, 32, 96, 160, 3, 33),
-    (4, 96, 192, 288, 2, 20),
-    (4, 128, 512, 384, 2, 70),
     (4, 64, 8192, 128, 1, 3),
     (4, 64, 64, 8192, 2, 18),
     (4, 64, 256, 64, 16, 4),
     (2, 64, 256, 384, 3, 20),
-    (2, 128, 512, 256, 2, 9),
     (2, 64, 192, 128, 1, 65),
     (4, 64, 384, 320, 2, 9),     # 6 gate_up groups in 2 K splits (the second ends in a dead step), 5 down groups
     (2, 64, 320, 448, 3, 40),    # 5 and 7 groups: partial 4-group code units and scale quads on both passes
