@@ -239,14 +239,26 @@ def decode_measure(spec, steps, warmup, n_experts=None, replicas=None):
                 gbs=nbytes / (us * 1e-6) / 1e9)
 
 
-def decode_row(spec, steps, warmup, n_experts=None, replicas=None, note=None):
+def decode_row(spec, steps, warmup, n_experts=None, replicas=None, note=None, profile=None):
     m = decode_measure(spec, steps, warmup, n_experts, replicas)
     row = {"us": round(m["us"], 3), "gbs": round(m["gbs"], 1), "frac": round(m["gbs"] / PEAK_HBM_GBS, 4),
            "bound": "hbm", "per_call_us": m["spread"], "algorithmic_bytes": m["nbytes"],
            "replicas_rotated": m["replicas"]}
+    if profile:
+        row["kernels"] = row_kernels(profile, "decode")
     if note:
         row["note"] = note
     return row
+
+
+def row_kernels(name, kind):
+    """Median / p10 / p90 kernel durations (us) from the committed kernel
+    trace of a workload (profiles/<name>_kernels.json) when it was taken on
+    the current kernel sources, else None."""
+    k = load_kernels(name, kind)
+    if not k:
+        return None
+    return {n: {f: v[f] for f in ("median_us", "p10_us", "p90_us") if f in v} for n, v in k.items()}
 
 
 def read_ceiling(nbytes, steps, warmup):
@@ -314,11 +326,11 @@ def decode_line(args, spec, profile, with_rows=False):
     }
     if with_rows:
         line["us_per_expert"] = decode_row(spec, args.steps, args.warmup, n_experts=1)["us"]
-        rc = read_ceiling(nbytes, args.steps, args.warmup)
-        if rc:
-            rc["path_time_over_ceiling"] = round(m["us"] / rc["us"], 3)
-            rc["path_frac_of_ceiling"] = round(rc["us"] / m["us"], 4)
-        line["read_ceiling"] = rc
+    rc = read_ceiling(nbytes, args.steps, args.warmup)
+    if rc:
+        rc["path_time_over_ceiling"] = round(m["us"] / rc["us"], 3)
+        rc["path_frac_of_ceiling"] = round(rc["us"] / m["us"], 4)
+    line["read_ceiling"] = rc
     cpu = None
     if args.cpu_budget > 0:
         import oracle
@@ -379,7 +391,8 @@ def prefill_row(T, steps, warmup):
             "bound": "hbm" if hbm else "mfma",
             "frac": round(m["gbs"] / PEAK_HBM_GBS if hbm else m["tflops"] / PEAK_F16_TFLOPS, 4),
             "frac_hbm": round(m["gbs"] / PEAK_HBM_GBS, 4), "frac_mfma": round(m["tflops"] / PEAK_F16_TFLOPS, 4),
-            "per_call_us": m["spread"], "algorithmic_flops": m["flops"], "algorithmic_bytes": m["nbytes"]}
+            "per_call_us": m["spread"], "algorithmic_flops": m["flops"], "algorithmic_bytes": m["nbytes"],
+            "kernels": row_kernels(f"prefill_t{T}", "prefill")}
 
 
 def prefill_line(args):
@@ -549,6 +562,10 @@ def bf16_row(shape_name, steps, warmup):
     row = {"us": round(m["us"], 3), "gbs": round(m["gbs"], 1), "frac": round(m["gbs"] / PEAK_HBM_GBS, 4),
            "bound": "hbm", "per_call_us": m["spread"], "algorithmic_bytes": m["nbytes"],
            "replicas_rotated": m["replicas"]}
+    rc = read_ceiling(m["nbytes"], steps, warmup)
+    if rc:
+        row["read_ceiling_us"] = rc["us"]
+    row["kernels"] = row_kernels(f"bf16_{m['role']}", "bf16")
     if m["kind"] == "tile":
         row["note"] = "weights: the seed's first 8192 rows repeated (timing input)"
     return row
@@ -588,6 +605,7 @@ def bf16_line(args):
             "traffic": load_traffic(f"bf16_{role}", "bf16"),
             "kernels": load_kernels(f"bf16_{role}", "bf16"),
         },
+        "read_ceiling": read_ceiling(nbytes, args.steps, args.warmup),
         "cpu_baseline": cpu,
     }
 
@@ -762,12 +780,15 @@ def collect_rows(args):
               flush=True)
 
     add("decode_q4_tiny_1expert_256x512",
-        lambda: decode_row(workloads.TINY, s, w, replicas=16,
+        lambda: decode_row(workloads.TINY, s, w, replicas=16, profile="tiny",
                            note="latency-bound: the 16 rotated replicas fit in the caches (hot)"))
-    add("decode_q4_1expert_4096x1536", lambda: decode_row(workloads.Q4_GROUP8, s, w, n_experts=1))
-    add("decode_q2_8expert_4096x1536", lambda: decode_row(workloads.Q2_GROUP8, s, w))
-    add("decode_q4_8expert_4096x1536_f16scales", lambda: decode_row(workloads.Q4_GROUP8_S16, s, w))
-    add("decode_q2_8expert_4096x1536_f16scales", lambda: decode_row(workloads.Q2_GROUP8_S16, s, w))
+    add("decode_q4_1expert_4096x1536",
+        lambda: decode_row(workloads.Q4_GROUP8, s, w, n_experts=1, profile="decode_q4_e1"))
+    add("decode_q2_8expert_4096x1536", lambda: decode_row(workloads.Q2_GROUP8, s, w, profile="decode_q2"))
+    add("decode_q4_8expert_4096x1536_f16scales",
+        lambda: decode_row(workloads.Q4_GROUP8_S16, s, w, profile="decode_q4_s16"))
+    add("decode_q2_8expert_4096x1536_f16scales",
+        lambda: decode_row(workloads.Q2_GROUP8_S16, s, w, profile="decode_q2_s16"))
     for rows_, cols, role, _ in workloads.BF16_SHAPES:
         add(f"bf16_{role}_{rows_}x{cols}", lambda role=role: bf16_row(role, s, w))
     for T in sorted(workloads.BATCH_TOKENS):
