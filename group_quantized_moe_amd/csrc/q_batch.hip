@@ -442,6 +442,16 @@ __device__ __forceinline__ float *partial_slot(float *part, int k, int r)
 // accumulator k of thread t sits at (4k + r) * 512 + t of a split's slab, so
 // that a wave's stores and loads are 256 contiguous bytes.  `last` is LDS.
 // Returns whether this block holds the tile's sum.
+//
+// Ordering.  The counter is a relaxed atomic, and what orders the slabs
+// before it is the machine's: on gfx950 an agent-scope atomic store is a
+// store with the sc1 bit, performed at the agent's coherence point rather
+// than in the XCD's L2, and s_waitcnt vmcnt(0) returns once it is performed;
+// an agent-scope atomic load (sc1) reads from that point.  An agent-scope
+// release / acquire pair on the counter would add to exactly these steps an
+// L2 write-back before the count (for prior plain stores, of which the slabs
+// have none) and an L2 invalidate after it (for later plain loads, likewise
+// none), and measured 4.8 us slower per 16-token call.
 template <int N>
 __device__ bool split_reduce(f32x4 (&acc)[N], float *part, size_t stride, int ks, int splits, unsigned *cnt,
                              int *last)
