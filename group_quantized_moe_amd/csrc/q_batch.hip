@@ -21,10 +21,12 @@
 //    f32 result is multiplied by its scale into the running output.
 //
 // Launch sequence (one stream): k_tb_prep (X -> hi/lo halves + per-token
-// exponent), k_tb_gate_up (both projections, SiLU, hidden rows -> hi/lo halves
+// exponent), k_tb_gate_up_tiled (both projections, SiLU, hidden rows -> hi/lo halves
 // + one factor per (expert, group, token) that folds the group's power of two
-// and the router weight), k_tb_down (all experts summed in a fixed order, so
-// the result is deterministic; no atomics).
+// and the router weight), k_tb_down_tiled (all experts summed in a fixed order, so
+// the result is deterministic; no atomics in the sums), each followed by its
+// finishing pass when its K dimension is split over blocks of 32- or 64-token
+// tiles.
 //
 // Orientation: tokens are the MFMA's M side, weight rows its N side.  For
 // v_mfma_f32_16x16x32_f16 (lane l, q = l / 16, n = l % 16):
