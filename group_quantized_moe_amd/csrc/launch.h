@@ -63,9 +63,10 @@ struct TbArgs {
     _Float16 *xh, *xl;       // [T][d_model]
     int *xe;                 // [T]
     _Float16 *hh, *hl;       // [n_experts][T][d_ff]
+    float *hid;              // streaming path: f32 hidden rows [n_experts][T][d_ff] (over hh and hl)
     float *hf;               // [n_experts][d_ff / group][t_pad]: r[t][e] * 2^e(t, group)
     float *part_gu, *part_dn; // per-tile partial sums of the K splits
-    unsigned *cnt_gu, *cnt_dn; // per tile, the K splits done (k_tb_prep zeroes them)
+    unsigned *cnt_gu, *cnt_dn; // per tile, the K splits done (zeroed by the call's first kernel)
     int n_cnt;               // entries of cnt_gu and cnt_dn together (contiguous)
     // Routed mode (top_k > 0): slot s = t*top_k + j of token
     // t goes to expert ids[s] with weight slot_w[s].  list[e*T + p], p <
@@ -83,10 +84,11 @@ struct TbArgs {
     int ks_gu, ks_dn;        // K splits over blocks of gate_up and down
 };
 
-// Tiling of the token-batch launches: 16*ntt tokens per block, gate_up steps
-// of mg quantisation groups, K splits, block counts and dynamic LDS bytes of
-// gate_up and down.
+// Tiling of the token-batch launches: the streaming kernels (T <= 16) or the
+// tiled ones with 16*ntt tokens per block, gate_up steps of mg quantisation
+// groups and K splits; block counts and dynamic LDS bytes of gate_up and down.
 struct TbPlan {
+    int stream;
     int mg;
     int ntt;
     int ks_gu;

@@ -20,13 +20,16 @@
 //    lo go through two MFMAs into one accumulator per group, and the group's
 //    f32 result is multiplied by its scale into the running output.
 //
-// Launch sequence (one stream): k_tb_prep (X -> hi/lo halves + per-token
-// exponent), k_tb_gate_up_tiled (both projections, SiLU, hidden rows -> hi/lo halves
-// + one factor per (expert, group, token) that folds the group's power of two
-// and the router weight), k_tb_down_tiled (all experts summed in a fixed order, so
-// the result is deterministic; no atomics in the sums), each followed by its
-// finishing pass when its K dimension is split over blocks of 32- or 64-token
-// tiles.
+// Launch sequence (one stream), T > 16: k_tb_prep (X -> hi/lo halves +
+// per-token exponent), k_tb_gate_up_tiled (both projections, SiLU, hidden rows
+// -> hi/lo halves + one factor per (expert, group, token) that folds the
+// group's power of two and the router weight), k_tb_down_tiled (all experts
+// summed in a fixed order, so the result is deterministic; no atomics in the
+// sums), each followed by its finishing pass when its K dimension is split
+// over blocks of 32- or 64-token tiles.  T <= 16: k_tb_gate_up_stream (X
+// staged per phase of 16 groups into LDS by every block; f32 hidden rows) and
+// k_tb_down_stream (hidden rows staged and split per group; the chunks of a
+// row group added in the kernel in chunk order).
 //
 // Orientation: tokens are the MFMA's M side, weight rows its N side.  For
 // v_mfma_f32_16x16x32_f16 (lane l, q = l / 16, n = l % 16):
@@ -1034,6 +1037,496 @@ __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
     dn_store<1>(a, tot, tile_id / NTB, (tile_id % NTB) * NTT + tt);
 }
 
+// -------------------------------------------------------------------------
+// Streaming kernels for batches of at most 16 tokens (one token tile).
+//
+// There a quantisation group of codes carries 16 tokens of matrix work, and
+// what bounds a pass is how many code bytes each CU keeps in flight.  These
+// kernels hold the tokens' activations for a long stretch of K in LDS, issue
+// each wave's codes and scales a whole phase ahead of their use, and meet at
+// a barrier twice per phase of 16 groups instead of once per group.
+//
+// gate_up: a block of 12 waves owns 3 row tiles (16 rows of gate and of up
+// each) over all of d_model, so K is not split: wave (r, k) takes groups
+// 4k .. 4k+3 of every 16-group phase for row tile r, and the four K quarters
+// of a row tile are added in LDS at the end.  X enters each phase as f32: the
+// block scales it per token by the power of two of the phase's largest |x|
+// (one exponent per token and phase), splits it into f16 hi/lo halves in
+// sigma order in LDS, and the phase's sums are scaled back by the same power
+// of two.  The hidden rows SiLU(g) * u leave as f32.
+//
+// down: a block of 16 waves owns 8 row tiles (128 rows of d_model) and one
+// chunk of 1536 columns of one expert's d_ff (all of it at d_ff = 1536).  The
+// hidden rows are scaled per (token, group) by the power of two of the
+// group's largest |h| and split into hi/lo halves on the way into LDS, and the
+// router weight joins that power of two in the group's factor, as in the
+// tiled path.  The two K halves of a row tile are added in LDS, the chunks
+// of a row group in the kernel through the row group's counter, in chunk
+// order (the counters are zeroed by gate_up, which runs before down).
+constexpr int kGsRows = 3, kGsK = 4, kGsWaves = kGsRows * kGsK;
+constexpr int kPhaseGroups = 16;
+constexpr int kDsRows = 8, kDsK = 2, kDsWaves = kDsRows * kDsK;
+constexpr int kDsCols = 1536;
+
+// 8 f32 values of a 32-byte piece (two 16-byte loads), or zeros.
+__device__ __forceinline__ void piece_values(const uint4 (&raw)[2], bool ok, float (&v)[8])
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        v[4 * h + 0] = ok ? __uint_as_float(raw[h].x) : 0.0f;
+        v[4 * h + 1] = ok ? __uint_as_float(raw[h].y) : 0.0f;
+        v[4 * h + 2] = ok ? __uint_as_float(raw[h].z) : 0.0f;
+        v[4 * h + 3] = ok ? __uint_as_float(raw[h].w) : 0.0f;
+    }
+}
+
+// hi/lo halves of v * 2^-e in sigma order, stored as two 16-byte LDS writes
+// (hi rounded once, as packed pairs, and widened back from them).
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void store_hilo(const float (&v)[8], int e, _Float16 *hi, _Float16 *lo)
+{
+    constexpr int kSigma[8] = {0, 4, 1, 5, 2, 6, 3, 7};   // column at each sigma position
+    f32x8 sv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[kSigma[i]], -e);
+    const half8 h = __builtin_convertvector(sv, half8);
+    const half8 l = __builtin_convertvector(sv - __builtin_convertvector(h, f32x8), half8);
+    *reinterpret_cast<half8 *>(hi) = h;
+    *reinterpret_cast<half8 *>(lo) = l;
+}
+
+template <int BITS, int KB, int SB>
+__global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
+{
+    using CU = CodeUnit<BITS, KB>;
+    constexpr int kG = CU::kGroups, kDw = CU::kDw;
+    constexpr int kWG = kPhaseGroups / kGsK;   // groups of a phase per wave
+    constexpr int kU = kWG / kG;               // code units of a phase per wave
+    static_assert(kWG == 4 && kU * kG == kWG, "a wave takes one scale quad and whole code units per phase");
+    constexpr int group = 32 * KB;
+    constexpr int KC = kPhaseGroups * group;   // columns per phase
+    constexpr int kStride = KC + 8;            // halfs per LDS token row
+    constexpr int kTile = 2 * 16 * kStride;    // halfs per tile: hi [16][kStride], lo [16][kStride]
+    constexpr int kNT = 64 * kGsWaves;
+    constexpr int kPR = KC / 8;                // 8-column pieces per token row
+    constexpr int kPieces = 16 * kPR;
+    constexpr int kPPT = (kPieces + kNT - 1) / kNT;
+    extern __shared__ __align__(16) unsigned char smem[];   // two tiles
+    __shared__ unsigned s_max[3][16];                       // per phase mod 3 and token: largest |x| (bits)
+    __shared__ __align__(16) int s_exp[2][16];              // per phase parity and token: its exponent
+    _Float16 *tiles = reinterpret_cast<_Float16 *>(smem);
+
+    const int d_model = a.d_model, d_ff = a.d_ff, T = a.T;
+    const int lane = threadIdx.x & 63, q = lane >> 4, n = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rl = wave / kGsK, wk = wave % kGsK;
+    const int G = d_model / group;
+    const int P = (G + kPhaseGroups - 1) / kPhaseGroups;   // phases of 16 groups
+    const int RT = d_ff / 16, NRT = a.n_experts * RT;
+
+    // The down pass's chunk counters start every call at zero.
+    for (int i = blockIdx.x * kNT + threadIdx.x; i < a.n_cnt; i += gridDim.x * kNT) a.cnt_gu[i] = 0u;
+    if (threadIdx.x < 48) s_max[threadIdx.x >> 4][threadIdx.x & 15] = 0u;
+
+    // The wave's row tile (past the last one: a copy of it that stores nothing).
+    const int rtg = blockIdx.x * kGsRows + rl;
+    const bool live = rtg < NRT;
+    const int rtc = min(rtg, NRT - 1);
+    const int e = rtc / RT;
+    const int wrow0 = (rtc - e * RT) * 16;
+    const unsigned row = (unsigned)(wrow0 + n);
+    const unsigned crow = row * (unsigned)(d_model * BITS / 8) + 16u * (unsigned)(q % kDw);
+    const int cq = q / kDw;
+    const unsigned srow = row * (unsigned)G;
+    const int cb = CU::cb(q);
+    const size_t cbytes = (size_t)d_ff * d_model * BITS / 8, sbytes = (size_t)d_ff * G * SB;
+    const BufRes cr[2] = {buf_res(a.gate[e].codes, cbytes), buf_res(a.up[e].codes, cbytes)};
+    const BufRes sr[2] = {buf_res(a.gate[e].scales, sbytes), buf_res(a.up[e].scales, sbytes)};
+    const BufRes xr = buf_res(a.x, (size_t)T * d_model * 4);
+
+    // Loads complete in issue order, so X (an L2 read) is always issued
+    // before the codes (HBM) that are not needed as soon.  Codes and scales
+    // of phase ph are issued one phase ahead, once phase ph - 1's are
+    // unpacked (groups past the last clamp to it and count with scale 0); the
+    // thread's pieces of X for phase ph go to registers two phases ahead
+    // (tokens past T and columns past d_model read as zero).
+    uint4 craw[2][kU];
+    unsigned sraw[2];
+    auto load_codes = [&](int ph) {
+        const int g0 = ph * kPhaseGroups + wk * kWG;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const unsigned off = crow + (unsigned)min(g0 + u * kG + cq, G - 1) * (unsigned)(16 * kDw);
+                craw[m][u] = buf_load16(cr[m], off, 0u);
+            }
+            sraw[m] = buf_load_scale_bits<SB>(sr[m], srow + (unsigned)min(g0 + q, G - 1));
+        }
+    };
+    auto piece_ok = [&](int k, int ph, int &t, int &b8) {
+        const int c = threadIdx.x + kNT * k;
+        t = c / kPR;
+        b8 = c - t * kPR;
+        return c < kPieces && t < T && ph * KC + 8 * b8 < d_model;
+    };
+    auto load_x = [&](uint4 (&xv)[kPPT][2], int ph) {
+#pragma unroll
+        for (int k = 0; k < kPPT; ++k) {
+            int t, b8;
+            const bool ok = piece_ok(k, ph, t, b8);
+            const unsigned off = ok ? (unsigned)(t * d_model + ph * KC + 8 * b8) * 4u : 0u;
+            xv[k][0] = buf_load16(xr, off, 0u);
+            xv[k][1] = buf_load16(xr, off + 16u, 0u);
+        }
+    };
+    // The per-token maxima of phase ph's X, into s_max[ph % 3] (read after
+    // the next barrier).
+    auto max_x = [&](const uint4 (&xv)[kPPT][2], int ph) {
+        unsigned *mx = s_max[ph % 3];
+#pragma unroll
+        for (int k = 0; k < kPPT; ++k) {
+            int t, b8;
+            const bool ok = piece_ok(k, ph, t, b8);
+            float v[8];
+            piece_values(xv[k], ok, v);
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+            if (threadIdx.x + kNT * k < kPieces) atomicMax(&mx[t], __float_as_uint(m));
+        }
+    };
+    // Phase ph's X into tile ph & 1 as hi/lo halves scaled by the tokens'
+    // exponents, which go to s_exp[ph & 1].
+    auto convert_x = [&](const uint4 (&xv)[kPPT][2], int ph) {
+        const unsigned *mx = s_max[ph % 3];
+        _Float16 *hi = tiles + (ph & 1) * kTile, *lo = hi + 16 * kStride;
+        if (threadIdx.x < 16) s_exp[ph & 1][threadIdx.x] = norm_exponent(__uint_as_float(mx[threadIdx.x]));
+#pragma unroll
+        for (int k = 0; k < kPPT; ++k) {
+            int t, b8;
+            const bool ok = piece_ok(k, ph, t, b8);
+            if (threadIdx.x + kNT * k < kPieces) {
+                float v[8];
+                piece_values(xv[k], ok, v);
+                store_hilo(v, norm_exponent(__uint_as_float(mx[t])), hi + t * kStride + 8 * b8,
+                           lo + t * kStride + 8 * b8);
+            }
+        }
+    };
+
+    f32x4 tot[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // gate, up
+    // The MFMAs of phase ph from tile ph & 1 and the unpacked codes, added into
+    // tot with the phase's exponents.
+    auto compute = [&](int ph, const CodeWords<BITS, KB> (&cw)[2][kU][kG], const float (&sc)[2][4]) {
+        const _Float16 *hi = tiles + (ph & 1) * kTile, *lo = hi + 16 * kStride;
+        f32x4 tp[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int gi = 0; gi < kWG; ++gi) {
+            const int lg = wk * kWG + gi;   // group within the phase
+            half8 bf[2][KB];
+            float s[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int j = 0; j < KB; ++j) bf[m][j] = code_frag<BITS, KB>(cw[m][gi / kG][gi % kG], j);
+                s[m] = ph * kPhaseGroups + lg < G ? sc[m][gi] : 0.0f;
+            }
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int off = n * kStride + lg * group + cb * 8 * KB + 8 * j;
+                const half8 h = load_half8(hi + off), l = load_half8(lo + off);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    acc[m] = mfma(h, bf[m][j], acc[m]);
+                    acc[m] = mfma(l, bf[m][j], acc[m]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tp[m][r] = fmaf(s[m], acc[m][r], tp[m][r]);
+        }
+        const int4 ex = *reinterpret_cast<const int4 *>(&s_exp[ph & 1][4 * q]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            tot[m][0] += ldexpf(tp[m][0], ex.x);
+            tot[m][1] += ldexpf(tp[m][1], ex.y);
+            tot[m][2] += ldexpf(tp[m][2], ex.z);
+            tot[m][3] += ldexpf(tp[m][3], ex.w);
+        }
+    };
+    // The loaded codes and scales, unpacked.
+    auto unpack = [&](CodeWords<BITS, KB> (&cw)[2][kU][kG], float (&sc)[2][4]) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) unit_split<BITS, KB>(craw[m][u], cw[m][u]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sc[m][j] = scale_value<SB>((unsigned)__builtin_amdgcn_ds_bpermute((n + 16 * j) * 4, (int)sraw[m])) *
+                           QFormat<BITS>::kInvZ;
+        }
+    };
+
+    // Phase ph of the loop (one barrier per phase): tile ph is complete and
+    // the maxima of phase ph + 1 are in; X of phase ph + 1 goes into the other
+    // tile (last read in phase ph - 1) while the waves run phase ph, whose
+    // codes are unpacked before phase ph + 1's take their registers.  Phase
+    // ph + 2's maxima join before the barrier; s_max[ph % 3] was last read in
+    // phase ph - 1 and is cleared for phase ph + 3.
+    uint4 xv[kPPT][2], xv1[kPPT][2];
+    __syncthreads();   // the maxima are zero
+    load_x(xv, 0);
+    load_x(xv1, 1);
+    load_codes(0);
+    max_x(xv, 0);
+    max_x(xv1, 1);
+    __builtin_amdgcn_sched_barrier(0);   // nothing that waits for the codes moves above a barrier
+    __syncthreads();
+    convert_x(xv, 0);
+#pragma unroll
+    for (int k = 0; k < kPPT; ++k) xv[k][0] = xv1[k][0], xv[k][1] = xv1[k][1];
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    // Branch-free, so that the compiler's load waits are exact: the loads
+    // and conversions past the last phase are of phases with no columns.
+    for (int p = 0; p < P; ++p) {
+        convert_x(xv, p + 1);
+        CodeWords<BITS, KB> cw[2][kU][kG];
+        float sc[2][4];
+        unpack(cw, sc);
+        load_x(xv, p + 2);
+        load_codes(p + 1);
+        compute(p, cw, sc);
+        if (threadIdx.x < 16) s_max[p % 3][threadIdx.x] = 0u;
+        max_x(xv, p + 2);
+        __syncthreads();
+    }
+
+    // The four K quarters of each row tile, added in LDS in quarter order
+    // (the tiles are no longer read after the last barrier).
+    float *red = reinterpret_cast<float *>(smem);
+    if (wk > 0) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(((rl * (kGsK - 1) + wk - 1) * 2 + m) * 4 + r) * 64 + lane] = tot[m][r];
+    }
+    __syncthreads();
+    if (wk != 0 || !live) return;
+#pragma unroll
+    for (int w = 1; w < kGsK; ++w)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[m][r] += red[(((rl * (kGsK - 1) + w - 1) * 2 + m) * 4 + r) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i;
+        if (t < T) a.hid[((size_t)e * T + t) * d_ff + wrow0 + n] = silu(tot[0][i]) * tot[1][i];
+    }
+}
+
+template <int BITS, int KB, int SB>
+__global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
+{
+    using CU = CodeUnit<BITS, KB>;
+    constexpr int kG = CU::kGroups, kDw = CU::kDw;
+    constexpr int group = 32 * KB;
+    constexpr int KDG = kDsCols / group;   // groups per block
+    constexpr int kWG = KDG / kDsK;        // groups per wave
+    constexpr int kU = kWG / kG;           // code units per wave
+    constexpr int kQ = kWG / 4;            // scale quads per wave
+    static_assert(kU * kG == kWG && kQ * 4 == kWG, "a wave takes whole code units and scale quads");
+    constexpr int kStride = kDsCols + 8;
+    constexpr int kNT = 64 * kDsWaves;
+    constexpr int kPR = kDsCols / 8;       // 8-column pieces per token row
+    constexpr int kPieces = 16 * kPR;
+    constexpr int kPPT = kPieces / kNT;
+    static_assert(kPPT * kNT == kPieces, "every thread takes the same number of pieces");
+    constexpr int kPG = group / 8;         // pieces per group
+    extern __shared__ __align__(16) unsigned char smem[];   // hi [16][kStride], lo [16][kStride], factors [KDG][16]
+    __shared__ int s_last;
+    _Float16 *hs_hi = reinterpret_cast<_Float16 *>(smem), *hs_lo = hs_hi + 16 * kStride;
+    float *fac = reinterpret_cast<float *>(smem + (size_t)2 * 16 * kStride * 2);
+
+    const int d_model = a.d_model, d_ff = a.d_ff, T = a.T, E = a.n_experts;
+    const int lane = threadIdx.x & 63, q = lane >> 4, n = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rl = wave / kDsK, kh = wave % kDsK;
+    const int Gd = d_ff / group;
+    const int SPE = (d_ff + kDsCols - 1) / kDsCols, S = E * SPE;
+    const int RG = (d_model + 16 * kDsRows - 1) / (16 * kDsRows);
+    // Logical order chunk, row group: the blocks an XCD gets share a chunk of
+    // hidden rows.
+    const int b = xcd_logical(blockIdx.x, gridDim.x);
+    const int sp = b / RG, rg = b - sp * RG;
+    const int e = sp / SPE, kc = sp - e * SPE;
+    const int wrow0 = rg * 16 * kDsRows + rl * 16;
+    const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
+    const unsigned crow = row * (unsigned)(d_ff * BITS / 8) + 16u * (unsigned)(q % kDw);
+    const int cq = q / kDw;
+    const unsigned srow = row * (unsigned)Gd;
+    const int cb = CU::cb(q);
+    const size_t cbytes = (size_t)d_model * d_ff * BITS / 8, sbytes = (size_t)d_model * Gd * SB;
+    const BufRes cres = buf_res(a.down[e].codes, cbytes), sres = buf_res(a.down[e].scales, sbytes);
+
+    // The chunk's hidden rows, then all of the wave's codes and scales (loads
+    // complete in issue order: the hidden rows are staged while the codes
+    // arrive).
+    const int wg0 = kc * KDG + kh * kWG;   // the wave's first group of d_ff
+    const BufRes hr = buf_res(a.hid + (size_t)e * T * d_ff, (size_t)T * d_ff * 4);
+    const int c0 = kc * kDsCols;
+    // Router weights of the pieces' tokens (with the hidden rows: a load
+    // issued after the codes would be waited for behind all of them).
+    const BufRes rr = buf_res(a.route_w ? a.route_w : a.out, a.route_w ? (size_t)T * E * 4 : 4);
+    uint4 hv[kPPT][2];
+    unsigned rw[kPPT];
+#pragma unroll
+    for (int k = 0; k < kPPT; ++k) {
+        const int c = threadIdx.x + kNT * k, t = c / kPR, b8 = c - t * kPR;
+        const bool ok = t < T && c0 + 8 * b8 < d_ff;
+        const unsigned off = ok ? (unsigned)(t * d_ff + c0 + 8 * b8) * 4u : 0u;
+        hv[k][0] = buf_load16(hr, off, 0u);
+        hv[k][1] = buf_load16(hr, off + 16u, 0u);
+        rw[k] = buf_load4(rr, a.route_w && t < T ? (unsigned)(t * E + e) * 4u : 0u, 0u);
+    }
+    uint4 craw[kU];
+    unsigned sraw[kQ];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        craw[u] = buf_load16(cres, crow + (unsigned)min(wg0 + u * kG + cq, Gd - 1) * (unsigned)(16 * kDw), 0u);
+#pragma unroll
+    for (int k = 0; k < kQ; ++k) sraw[k] = buf_load_scale_bits<SB>(sres, srow + (unsigned)min(wg0 + 4 * k + q, Gd - 1));
+    // Per (token, group): the largest |h| over the group's kPG pieces, held
+    // by kPG consecutive lanes (kNT and kPR are multiples of 8).
+#pragma unroll
+    for (int k = 0; k < kPPT; ++k) {
+        const int c = threadIdx.x + kNT * k, t = c / kPR, b8 = c - t * kPR;
+        const bool ok = t < T && c0 + 8 * b8 < d_ff;
+        float v[8];
+        piece_values(hv[k], ok, v);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+        for (int s = 1; s < kPG; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
+        const int ex = norm_exponent(m);
+        store_hilo(v, ex, hs_hi + t * kStride + 8 * b8, hs_lo + t * kStride + 8 * b8);
+        if (b8 % kPG == 0) {
+            const float rwt = t >= T ? 0.0f : a.route_w ? __uint_as_float(rw[k]) : 1.0f;
+            fac[(b8 / kPG) * 16 + t] = ldexpf(rwt, ex);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // nothing that waits for the codes moves above the barrier
+    __syncthreads();
+
+    CodeWords<BITS, KB> cw[kU][kG];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) unit_split<BITS, KB>(craw[u], cw[u]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kQ; ++k) {
+        float sc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sc[j] = scale_value<SB>((unsigned)__builtin_amdgcn_ds_bpermute((n + 16 * j) * 4, (int)sraw[k])) *
+                    QFormat<BITS>::kInvZ;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+            const int gi = 4 * k + j4, lg = kh * kWG + gi;   // group of the wave, of the chunk
+            half8 bf[KB];
+#pragma unroll
+            for (int j = 0; j < KB; ++j) bf[j] = code_frag<BITS, KB>(cw[gi / kG][gi % kG], j);
+            const float s = wg0 + gi < Gd ? sc[j4] : 0.0f;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int off = n * kStride + lg * group + cb * 8 * KB + 8 * j;
+                acc = mfma(load_half8(hs_hi + off), bf[j], acc);
+                acc = mfma(load_half8(hs_lo + off), bf[j], acc);
+            }
+            const f32x4 f = *reinterpret_cast<const f32x4 *>(fac + lg * 16 + 4 * q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[r] = fmaf(s * f[r], acc[r], tot[r]);
+        }
+    }
+
+    // The two K halves of each row tile, added in LDS.
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);
+    if (kh == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(rl * 4 + r) * 64 + lane] = tot[r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[r] += red[(rl * 4 + r) * 64 + lane];
+    }
+
+    // The row group's chunks, added by the last of its blocks to finish, in
+    // chunk order (published and read as the tiled kernels' K splits are).
+    if (S > 1) {
+        float *slabs = a.part_dn + (size_t)rg * S * (kDsRows * 256);
+        if (kh == 0) {
+            float *mine = slabs + ((size_t)sp * kDsRows + rl) * 256;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(mine + r * 64 + lane, tot[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores have reached memory
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(a.cnt_dn + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (unsigned)S - 1;
+        __syncthreads();
+        if (!s_last || kh != 0) return;
+        const f32x4 own = tot;
+        constexpr int B = 8;   // slabs in flight at once
+        for (int s0 = 0; s0 < S; s0 += B) {
+            float v[B][4];
+#pragma unroll
+            for (int bb = 0; bb < B; ++bb) {
+                const int s = min(s0 + bb, S - 1);   // past the last chunk: re-read it, unused
+                const float *ps = slabs + ((size_t)s * kDsRows + rl) * 256;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[bb][r] = s == sp ? own[r]
+                                       : __hip_atomic_load(const_cast<float *>(ps) + r * 64 + lane, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int bb = 0; bb < B; ++bb) {
+                if (s0 + bb >= S) break;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tot[r] = s0 + bb == 0 ? v[bb][r] : tot[r] + v[bb][r];
+            }
+        }
+    } else if (kh != 0) {
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i, r = wrow0 + n;
+        if (t < T && r < d_model) a.out[(size_t)t * d_model + r] = tot[i];
+    }
+}
+
+template <int BITS, int KB, int SB>
+hipError_t launch_tb_stream(const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_tb_gate_up_stream<BITS, KB, SB>), dim3(pl.gu_blocks), dim3(64 * kGsWaves), pl.gu_lds,
+                       st, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_tb_down_stream<BITS, KB, SB>), dim3(pl.dn_blocks), dim3(64 * kDsWaves), pl.dn_lds, st,
+                       a);
+    return hipGetLastError();
+}
+
 template <int BITS, int KB, int NTT, int MG, int SB>
 hipError_t launch_tb_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
@@ -1202,10 +1695,26 @@ hipError_t launch_tb_fmt(int bits, const TbPlan &pl, const TbArgs &a, hipStream_
     return launch_tb_kb<2, 2, SB>(pl, a, st);
 }
 
+template <int SB>
+hipError_t launch_stream_fmt(int bits, const TbArgs &a, const TbPlan &pl, hipStream_t st)
+{
+    if (bits == 4) return a.group == 32 ? launch_tb_stream<4, 1, SB>(pl, a, st) : launch_tb_stream<4, 2, SB>(pl, a, st);
+    return launch_tb_stream<2, 2, SB>(pl, a, st);
+}
+
 }  // namespace
 
-// Dynamic LDS per block is kept within 64 KB.
+// Dynamic LDS per block: the tiled kernels keep within 64 KB (two blocks a
+// CU), the streaming kernels take up to the CU's 160 KB (one block a CU).
 constexpr size_t kMaxBlockLds = 64 * 1024;
+constexpr size_t kMaxStreamLds = 160 * 1024;
+
+// Streaming down grid: row groups of 128 rows x chunks of 1536 columns of
+// each expert's d_ff; each block's partial sums take 8 x 256 floats.
+long stream_down_blocks(int n_experts, int d_model, int d_ff)
+{
+    return (long)((d_model + 16 * kDsRows - 1) / (16 * kDsRows)) * n_experts * ((d_ff + kDsCols - 1) / kDsCols);
+}
 
 // Tokens per tile: 16, 32 or 64.
 int tile_ntt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
@@ -1240,6 +1749,9 @@ BatchSplits batch_splits(int n_experts, int d_model, int d_ff, int T)
     b.ks_dn = splits_for(b.dn_tiles, batch_block_target(b.dn_tiles));
     b.gu_part_floats = b.ks_gu > 1 ? (size_t)b.gu_tiles * b.ks_gu * 2 * b.ntt * 4 * 512 : 0;
     b.dn_part_floats = b.ks_dn > 1 ? (size_t)b.dn_tiles * b.ks_dn * b.ntt * 4 * 512 : 0;
+    if (T <= 16)   // the streaming down pass's chunk sums (its counters are the down tiles')
+        b.dn_part_floats = std::max(b.dn_part_floats, (size_t)stream_down_blocks(n_experts, d_model, d_ff) *
+                                                          kDsRows * 256);
     return b;
 }
 
@@ -1248,6 +1760,21 @@ bool plan_batch(int bits, int group, int d_model, int d_ff, int n_experts, int T
     if (T < 2 || n_experts < 1) return false;
     if (bits == 4 ? (group != 32 && group != 64) : group != 64) return false;
     if (d_model % group || d_ff % group) return false;
+    if (T <= 16) {
+        // Streaming kernels: gate_up blocks of 3 row tiles over all of K,
+        // down blocks of 128 rows x one 1536-column chunk of one expert.
+        TbPlan p{};
+        p.stream = 1;
+        p.ntt = 1;
+        p.mg = 1;
+        p.gu_blocks = ((long)n_experts * (d_ff / 16) + kGsRows - 1) / kGsRows;
+        p.gu_lds = (size_t)2 * 2 * 16 * (kPhaseGroups * group + 8) * 2;   // two tiles of hi/lo halves
+        p.dn_blocks = stream_down_blocks(n_experts, d_model, d_ff);
+        p.dn_lds = (size_t)2 * 16 * (kDsCols + 8) * 2 + (size_t)(kDsCols / group) * 16 * 4;
+        if (p.gu_lds > kMaxStreamLds || p.dn_lds > kMaxStreamLds) return false;
+        *pl = p;
+        return true;
+    }
     // 16 * ntt tokens x 128 rows per 8-wave block, K split over blocks as the
     // workspace allows (at most one split per 4-group iteration).
     const BatchSplits bs = batch_splits(n_experts, d_model, d_ff, T);
@@ -1339,6 +1866,7 @@ hipError_t launch_routed(int bits, const TbPlan &pl, const TbArgs &a, hipStream_
 
 hipError_t launch_batch(int bits, const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
+    if (pl.stream) return a.scale_bytes == 2 ? launch_stream_fmt<2>(bits, a, pl, st) : launch_stream_fmt<4>(bits, a, pl, st);
     return a.scale_bytes == 2 ? launch_tb_fmt<2>(bits, pl, a, st) : launch_tb_fmt<4>(bits, pl, a, st);
 }
 

@@ -121,10 +121,12 @@ size_t decode_workspace(int n_experts, int d_ff) { return align256((size_t)n_exp
 // Workspace layout of the token-batch path (T > 1), every piece 256-byte aligned:
 //   xh, xl  f16 [T][d_model]                 hi/lo halves of the scaled activations
 //   xe      i32 [T]                          their per-token exponents
-//   hh, hl  f16 [n_experts][T][d_ff]         hi/lo halves of the scaled hidden rows
+//   hh, hl  f16 [n_experts][T][d_ff]         hi/lo halves of the scaled hidden rows (T <= 16: the
+//                                            two together hold the f32 hidden rows [n_experts][T][d_ff])
 //   hf      f32 [n_experts][d_ff/group][Tp]  per (expert, group, token) factors, Tp = T rounded up to 64
 //   pg, pd  f32                              partial sums of the gate_up / down K splits, per tile
-//   cnt     u32 [gate_up tiles + down tiles] K splits of each tile done
+//                                            (T <= 16: of the down pass's chunks, per row group)
+//   cnt     u32 [gate_up tiles + down tiles] K splits (chunks) of each tile (row group) done
 // Everything is rewritten by each call before it is read (the counters are
 // zeroed by the call's first kernel).
 struct BatchWorkspace {
@@ -405,6 +407,7 @@ static int expert_ffn(const smoe_expert *experts, int n_experts, const float *ro
         a.xe = reinterpret_cast<int *>(ws + w.xe);
         a.hh = reinterpret_cast<_Float16 *>(ws + w.hh);
         a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
+        a.hid = reinterpret_cast<float *>(ws + w.hh);   // f32 rows over hh and hl, which are adjacent
         a.hf = reinterpret_cast<float *>(ws + w.hf);
         a.part_gu = reinterpret_cast<float *>(ws + w.pg);
         a.part_dn = reinterpret_cast<float *>(ws + w.pd);

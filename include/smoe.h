@@ -159,12 +159,14 @@ int smoe_down(const smoe_qmat *down, int bits, int group, int d_model, int d_ff,
  * expert order in f64, each times its router weight, rounding once to f32
  * (deterministic, no atomics, no range limit).
  * 2 <= T <= SMOE_MAX_TOKENS runs the token-batch kernels on the matrix cores,
- * in which every expert processes every token: an activation pass, a gate_up
- * pass and a down pass that sums the experts in a fixed order (deterministic,
- * no atomics in the sums).  With few tokens the K dimension of either pass
- * is split over blocks whose partial sums are added in a fixed split order,
- * by a finishing pass or, for tiles of 16 tokens, by the tile's last split
- * block (one counter per tile in the workspace, zeroed by the call itself).
+ * in which every expert processes every token: for T > 16 an activation pass,
+ * a gate_up pass and a down pass that sums the experts in a fixed order
+ * (deterministic, no atomics in the sums), for T <= 16 a gate_up pass that
+ * stages the activations itself and a down pass.  With few tokens the K
+ * dimension of a pass is split over blocks whose partial sums are added in a
+ * fixed split order, by a finishing pass or by the last block of the split
+ * to finish (one counter per tile in the workspace, zeroed by the call
+ * itself).
  * They need group = 32 or 64 at 4 bits and 64 at 2 bits, else SMOE_ERR_GROUP
  * (wider groups are served at T = 1 only).  Activations are carried to the matrix cores
  * as two f16 halves scaled by a power of two per group, about 22 significant

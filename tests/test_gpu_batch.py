@@ -74,10 +74,11 @@ def test_batch_deterministic(gq, q4_group8):
 
 
 def test_batch_workspace_any_contents_and_reuse(gq, oracle_lib, q4_group8):
-    """16-token tiles add their K splits inside the tiled kernels through
-    per-tile counters kept in the workspace, which every call zeroes itself:
-    a workspace full of 0xFF bytes, reused for 16, 64 and again 16 tokens,
-    gives the oracle's rows and the same bits as a fresh zeroed one."""
+    """Batches of at most 16 tokens add the down pass's chunk sums inside the
+    kernel through per-row-group counters kept in the workspace, which every
+    call zeroes itself: a workspace full of 0xFF bytes, reused for 16, 64 and
+    again 16 tokens, gives the oracle's rows and the same bits as a fresh
+    zeroed one."""
     import torch
     g, de = q4_group8
     X16, R16 = workloads.make_batch_inputs(16)
