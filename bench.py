@@ -12,6 +12,10 @@ bytes / time), microseconds per group and per expert, and fraction of the
                  counter-based HBM traffic (null once the kernels changed)
   read_ceiling   a plain streaming read of the same number of bytes, timed in
                  the same run (one reduction launch over rotated buffers)
+  mfma_ceiling   (with the rows; token-batch lines) the rate the token batch's
+                 matrix instruction sustains on register operands in the same
+                 run, against which each token-batch row's f16 matrix work (twice
+                 its algorithmic flops: hi and lo halves) is also given
   cpu_baseline   the f64 oracle on the host: all threads, and one thread
   rows           every other workload of the path timed in the same run, each
                  back to back like the headline: the tiny single expert, one
@@ -294,6 +298,53 @@ def read_ceiling(nbytes, steps, warmup):
                       + ("one-pass grid" if bpc == 0 else f"{bpc} blocks per CU")}
 
 
+_MFMA_CEILING = {}
+
+
+def mfma_ceiling(repeats=10):
+    """The rate the token batch's matrix instruction (v_mfma_f32_16x16x32_f16)
+    sustains on this GPU with nothing else in the way: the register-only
+    kernel of libsmoe_bench.so, 8 blocks of 4 waves per compute unit, timed
+    between HIP events (median of `repeats` launches); the 32x32x16 form
+    beside it.  Measured once per run."""
+    if _MFMA_CEILING:
+        return dict(_MFMA_CEILING)
+    import torch
+    import group_quantized_moe_amd as gq
+    path = os.path.join(os.path.dirname(gq.LIB_PATH), "libsmoe_bench.so")
+    if not os.path.exists(path):
+        return None
+    B = ctypes.CDLL(path)
+    B.smoe_bench_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream, sp = stream_ptr()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bpc, iters = 8, 2000
+    out = {}
+    for shape, name, fl in ((0, "v_mfma_f32_16x16x32_f16", 16384), (1, "v_mfma_f32_32x32x16_f16", 32768)):
+        flops = cus * bpc * 4 * iters * 4 * fl
+        times = []
+        for r in range(repeats + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if B.smoe_bench_mfma_rate(shape, bpc, iters, sink.data_ptr(), sp) != 0:
+                raise RuntimeError("mfma rate launch failed")
+            e1.record(stream)
+            e1.synchronize()
+            if r >= 2:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        out[name] = round(flops / float(np.median(times)) / 1e12, 1)
+    _MFMA_CEILING.update({
+        "instruction": "v_mfma_f32_16x16x32_f16",
+        "tflops": out["v_mfma_f32_16x16x32_f16"],
+        "frac_of_peak": round(out["v_mfma_f32_16x16x32_f16"] / PEAK_F16_TFLOPS, 4),
+        "tflops_32x32x16": out["v_mfma_f32_32x32x16_f16"],
+        "kernel": "k_mfma_rate (libsmoe_bench.so): 4 independent accumulator chains a wave on register operands, "
+                  f"{bpc} blocks of 4 waves per CU, median of {repeats} launches",
+    })
+    return dict(_MFMA_CEILING)
+
+
 def decode_line(args, spec, profile, with_rows=False):
     m = decode_measure(spec, args.steps, args.warmup)
     g, E, nbytes = m["g"], m["E"], m["nbytes"]
@@ -348,6 +399,7 @@ def decode_line(args, spec, profile, with_rows=False):
     line["cpu_baseline"] = cpu
     if with_rows:
         line["rows"] = collect_rows(args)
+        line["mfma_ceiling"] = mfma_ceiling()
     return line
 
 
@@ -384,6 +436,16 @@ def prefill_measure(T, steps, warmup):
                 wall=wall, tflops=flops / (us * 1e-6) / 1e12, gbs=nbytes / (us * 1e-6) / 1e9)
 
 
+def matrix_work(tflops):
+    """The f16 matrix work behind an algorithmic rate (hi and lo halves: twice
+    the flops) against the measured rate of the instruction that does it."""
+    mc = mfma_ceiling()
+    if not mc:
+        return None
+    return {"f16_work_tflops": round(2 * tflops, 2), "instruction_tflops": mc["tflops"],
+            "frac_of_instruction_rate": round(2 * tflops / mc["tflops"], 4)}
+
+
 def prefill_row(T, steps, warmup):
     m = prefill_measure(T, steps, warmup)
     hbm = T <= 16
@@ -391,6 +453,7 @@ def prefill_row(T, steps, warmup):
             "bound": "hbm" if hbm else "mfma",
             "frac": round(m["gbs"] / PEAK_HBM_GBS if hbm else m["tflops"] / PEAK_F16_TFLOPS, 4),
             "frac_hbm": round(m["gbs"] / PEAK_HBM_GBS, 4), "frac_mfma": round(m["tflops"] / PEAK_F16_TFLOPS, 4),
+            "matrix_work": matrix_work(m["tflops"]),
             "per_call_us": m["spread"], "algorithmic_flops": m["flops"], "algorithmic_bytes": m["nbytes"],
             "kernels": row_kernels(f"prefill_t{T}", "prefill")}
 
@@ -436,7 +499,9 @@ def prefill_line(args):
             "frac": round((m["gbs"] / PEAK_HBM_GBS) if hbm_bound else (m["tflops"] / PEAK_F16_TFLOPS), 4),
             "traffic": load_traffic(f"prefill_t{T}", "prefill"),
             "kernels": load_kernels(f"prefill_t{T}", "prefill"),
+            "matrix_work": matrix_work(m["tflops"]),
         },
+        "mfma_ceiling": mfma_ceiling(),
         "cpu_baseline": cpu,
     }
 
@@ -506,7 +571,9 @@ def routed_line(args):
             "frac": round((gbs / PEAK_HBM_GBS) if hbm_bound else (tflops / PEAK_F16_TFLOPS), 4),
             "traffic": load_traffic(f"routed_t{T}_k{k}", "prefill"),
             "kernels": load_kernels(f"routed_t{T}_k{k}", "prefill"),
+            "matrix_work": matrix_work(tflops),
         },
+        "mfma_ceiling": mfma_ceiling(),
         "cpu_baseline": cpu,
     }
 
