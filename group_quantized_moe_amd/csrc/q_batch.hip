@@ -1044,7 +1044,8 @@ __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
 // what bounds a pass is how many code bytes each CU keeps in flight.  These
 // kernels hold the tokens' activations for a long stretch of K in LDS, issue
 // each wave's codes and scales a whole phase ahead of their use, and meet at
-// a barrier twice per phase of 16 groups instead of once per group.
+// a barrier once per phase of 16 groups (gate_up) or once per chunk (down)
+// instead of once per group.
 //
 // gate_up: a block of 12 waves owns 3 row tiles (16 rows of gate and of up
 // each) over all of d_model, so K is not split: wave (r, k) takes groups
