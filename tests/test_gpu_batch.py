@@ -115,6 +115,11 @@ BATCH_EDGE = [  # bits, group, d_model, d_ff, n_experts, T
     (2, 64, 192, 128, 1, 65),
     (4, 64, 384, 320, 2, 9),     # 6 gate_up groups in 2 K splits (the second ends in a dead step), 5 down groups
     (2, 64, 320, 448, 3, 40),    # 5 and 7 groups: partial 4-group code units and scale quads on both passes
+    # T <= 16 (streaming kernels):
+    (2, 64, 256, 384, 3, 7),     # 2-bit codes, one phase of 4 groups (the rest of it dead)
+    (4, 64, 64, 8192, 2, 12),    # d_ff 8192: six down chunks per expert, the last partial; half a row group
+    (4, 32, 1088, 96, 2, 16),    # 34 groups: three phases (an odd count), the last partial; one sparse chunk
+    (2, 64, 320, 448, 3, 16),    # 5 and 7 groups: a partial phase and a partial chunk, 2-bit codes
 ]
 
 
