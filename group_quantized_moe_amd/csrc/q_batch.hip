@@ -169,6 +169,15 @@ __device__ __forceinline__ unsigned buf_load_scale_bits(BufRes r, unsigned idx)
     else
         return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(idx * 2u), 0, 0);
 }
+// The same at a byte offset: lane part voff, uniform part soff.
+template <int SB>
+__device__ __forceinline__ unsigned buf_load_scale_at(BufRes r, unsigned voff, unsigned soff)
+{
+    if constexpr (SB == 4)
+        return buf_load4(r, voff, soff);
+    else
+        return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
 template <int SB>
 __device__ __forceinline__ float scale_value(unsigned bits)
 {
@@ -1069,15 +1078,19 @@ constexpr int kPhaseGroups = 16;
 constexpr int kDsRows = 8, kDsK = 2, kDsWaves = kDsRows * kDsK;
 constexpr int kDsCols = 1536;
 
-// 8 f32 values of a 32-byte piece (two 16-byte loads), or zeros.
-__device__ __forceinline__ void piece_values(const uint4 (&raw)[2], bool ok, float (&v)[8])
+// A buffer load at or past this byte offset is outside every buffer here
+// (extents are below 2^31) and returns zeros.
+constexpr unsigned kPastExtent = 0x80000000u;
+
+// 8 f32 values of a 32-byte piece (two 16-byte loads).
+__device__ __forceinline__ void piece_values(const uint4 (&raw)[2], float (&v)[8])
 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        v[4 * h + 0] = ok ? __uint_as_float(raw[h].x) : 0.0f;
-        v[4 * h + 1] = ok ? __uint_as_float(raw[h].y) : 0.0f;
-        v[4 * h + 2] = ok ? __uint_as_float(raw[h].z) : 0.0f;
-        v[4 * h + 3] = ok ? __uint_as_float(raw[h].w) : 0.0f;
+        v[4 * h + 0] = __uint_as_float(raw[h].x);
+        v[4 * h + 1] = __uint_as_float(raw[h].y);
+        v[4 * h + 2] = __uint_as_float(raw[h].z);
+        v[4 * h + 3] = __uint_as_float(raw[h].w);
     }
 }
 
@@ -1148,21 +1161,25 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
     // Loads complete in issue order, so X (an L2 read) is always issued
     // before the codes (HBM) that are not needed as soon.  Codes and scales
     // of phase ph are issued one phase ahead, once phase ph - 1's are
-    // unpacked (groups past the last clamp to it and count with scale 0); the
-    // thread's pieces of X for phase ph go to registers two phases ahead
-    // (tokens past T and columns past d_model read as zero).
+    // unpacked; the thread's pieces of X for phase ph go to registers two
+    // phases ahead (tokens past T and columns past d_model read as zero).
+    // A code or scale load is a fixed lane offset plus the phase's first
+    // group as a uniform offset.  Groups past the last read the next row's
+    // bytes (or zeros past the matrix): they count with scale 0 against
+    // activation columns of zeros, so what they read never matters.
     uint4 craw[2][kU];
     unsigned sraw[2];
+    unsigned cvo[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) cvo[u] = crow + (unsigned)((u * kG + cq) * 16 * kDw);
+    const unsigned svo = (srow + (unsigned)q) * SB;
     auto load_codes = [&](int ph) {
-        const int g0 = ph * kPhaseGroups + wk * kWG;
+        const unsigned g0 = (unsigned)(ph * kPhaseGroups + wk * kWG);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const unsigned off = crow + (unsigned)min(g0 + u * kG + cq, G - 1) * (unsigned)(16 * kDw);
-                craw[m][u] = buf_load16(cr[m], off, 0u);
-            }
-            sraw[m] = buf_load_scale_bits<SB>(sr[m], srow + (unsigned)min(g0 + q, G - 1));
+            for (int u = 0; u < kU; ++u) craw[m][u] = buf_load16(cr[m], cvo[u], g0 * (16u * kDw));
+            sraw[m] = buf_load_scale_at<SB>(sr[m], svo, g0 * SB);
         }
     };
     auto piece_ok = [&](int k, int ph, int &t, int &b8) {
@@ -1171,12 +1188,14 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
         b8 = c - t * kPR;
         return c < kPieces && t < T && ph * KC + 8 * b8 < d_model;
     };
+    // A piece outside X gets an offset past the buffer's extent, where a
+    // buffer load returns zeros.
     auto load_x = [&](uint4 (&xv)[kPPT][2], int ph) {
 #pragma unroll
         for (int k = 0; k < kPPT; ++k) {
             int t, b8;
             const bool ok = piece_ok(k, ph, t, b8);
-            const unsigned off = ok ? (unsigned)(t * d_model + ph * KC + 8 * b8) * 4u : 0u;
+            const unsigned off = ok ? (unsigned)(t * d_model + ph * KC + 8 * b8) * 4u : kPastExtent;
             xv[k][0] = buf_load16(xr, off, 0u);
             xv[k][1] = buf_load16(xr, off + 16u, 0u);
         }
@@ -1187,10 +1206,9 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
         unsigned *mx = s_max[ph % 3];
 #pragma unroll
         for (int k = 0; k < kPPT; ++k) {
-            int t, b8;
-            const bool ok = piece_ok(k, ph, t, b8);
+            const int t = (threadIdx.x + kNT * k) / kPR;
             float v[8];
-            piece_values(xv[k], ok, v);
+            piece_values(xv[k], v);
             float m = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -1205,11 +1223,11 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
         if (threadIdx.x < 16) s_exp[ph & 1][threadIdx.x] = norm_exponent(__uint_as_float(mx[threadIdx.x]));
 #pragma unroll
         for (int k = 0; k < kPPT; ++k) {
-            int t, b8;
-            const bool ok = piece_ok(k, ph, t, b8);
-            if (threadIdx.x + kNT * k < kPieces) {
+            const int c = threadIdx.x + kNT * k;
+            if (c < kPieces) {
+                const int t = c / kPR, b8 = c - t * kPR;
                 float v[8];
-                piece_values(xv[k], ok, v);
+                piece_values(xv[k], v);
                 store_hilo(v, norm_exponent(__uint_as_float(mx[t])), hi + t * kStride + 8 * b8,
                            lo + t * kStride + 8 * b8);
             }
@@ -1389,7 +1407,7 @@ __global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
     for (int k = 0; k < kPPT; ++k) {
         const int c = threadIdx.x + kNT * k, t = c / kPR, b8 = c - t * kPR;
         const bool ok = t < T && c0 + 8 * b8 < d_ff;
-        const unsigned off = ok ? (unsigned)(t * d_ff + c0 + 8 * b8) * 4u : 0u;
+        const unsigned off = ok ? (unsigned)(t * d_ff + c0 + 8 * b8) * 4u : kPastExtent;   // zeros past X
         hv[k][0] = buf_load16(hr, off, 0u);
         hv[k][1] = buf_load16(hr, off + 16u, 0u);
         rw[k] = buf_load4(rr, a.route_w && t < T ? (unsigned)(t * E + e) * 4u : 0u, 0u);
@@ -1406,9 +1424,8 @@ __global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
 #pragma unroll
     for (int k = 0; k < kPPT; ++k) {
         const int c = threadIdx.x + kNT * k, t = c / kPR, b8 = c - t * kPR;
-        const bool ok = t < T && c0 + 8 * b8 < d_ff;
         float v[8];
-        piece_values(hv[k], ok, v);
+        piece_values(hv[k], v);
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
