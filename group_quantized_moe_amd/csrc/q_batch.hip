@@ -1163,10 +1163,13 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
     // of phase ph are issued one phase ahead, once phase ph - 1's are
     // unpacked; the thread's pieces of X for phase ph go to registers two
     // phases ahead (tokens past T and columns past d_model read as zero).
-    // A code or scale load is a fixed lane offset plus the phase's first
-    // group as a uniform offset.  Groups past the last read the next row's
-    // bytes (or zeros past the matrix): they count with scale 0 against
-    // activation columns of zeros, so what they read never matters.
+    // Where all of the wave's groups of a phase exist, a code or scale load
+    // is a fixed lane offset plus the phase's first group as a uniform
+    // offset, and stays inside the lane's row.  Otherwise (a partial last
+    // phase, or the phase after the last, which the last iteration loads)
+    // each lane's group is clamped to the last one, whole offset per lane;
+    // groups past the last count with scale 0 against activation columns of
+    // zeros.
     uint4 craw[2][kU];
     unsigned sraw[2];
     unsigned cvo[kU];
@@ -1174,12 +1177,22 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
     for (int u = 0; u < kU; ++u) cvo[u] = crow + (unsigned)((u * kG + cq) * 16 * kDw);
     const unsigned svo = (srow + (unsigned)q) * SB;
     auto load_codes = [&](int ph) {
-        const unsigned g0 = (unsigned)(ph * kPhaseGroups + wk * kWG);
+        const int g0 = ph * kPhaseGroups + wk * kWG;
+        if (g0 + kWG <= G) {   // uniform
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < 2; ++m) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) craw[m][u] = buf_load16(cr[m], cvo[u], g0 * (16u * kDw));
-            sraw[m] = buf_load_scale_at<SB>(sr[m], svo, g0 * SB);
+                for (int u = 0; u < kU; ++u) craw[m][u] = buf_load16(cr[m], cvo[u], (unsigned)g0 * (16u * kDw));
+                sraw[m] = buf_load_scale_at<SB>(sr[m], svo, (unsigned)g0 * SB);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int u = 0; u < kU; ++u)
+                    craw[m][u] = buf_load16(cr[m], crow + (unsigned)min(g0 + u * kG + cq, G - 1) * (16u * kDw), 0u);
+                sraw[m] = buf_load_scale_at<SB>(sr[m], (srow + (unsigned)min(g0 + q, G - 1)) * SB, 0u);
+            }
         }
     };
     auto piece_ok = [&](int k, int ph, int &t, int &b8) {
