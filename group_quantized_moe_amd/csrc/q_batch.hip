@@ -1065,6 +1065,11 @@ __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
 // sigma order in LDS, and the phase's sums are scaled back by the same power
 // of two.  The hidden rows SiLU(g) * u leave as f32.
 //
+// Routed mode (slot lists, T <= 16, d_ff <= 1536): a gate_up block's row
+// tiles are one expert's and its token rows the expert's slots; a down
+// block's chunk is one expert's d_ff, and it writes each slot's weighted row
+// for the combine pass instead of adding the experts.
+//
 // down: a block of 16 waves owns 8 row tiles (128 rows of d_model) and one
 // chunk of 1536 columns of one expert's d_ff (all of it at d_ff = 1536).  The
 // hidden rows are scaled per (token, group) by the power of two of the
@@ -1138,16 +1143,37 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
     const int P = (G + kPhaseGroups - 1) / kPhaseGroups;   // phases of 16 groups
     const int RT = d_ff / 16, NRT = a.n_experts * RT;
 
-    // The down pass's chunk counters start every call at zero.
-    for (int i = blockIdx.x * kNT + threadIdx.x; i < a.n_cnt; i += gridDim.x * kNT) a.cnt_gu[i] = 0u;
+    // The wave's row tile (past the last one: a copy of it that stores
+    // nothing), and the tile's token rows: the batch (dense), or the slots
+    // of the block's expert, whose row tiles its blocks cover in turn
+    // (routed; a block of an expert without slots has nothing to do).
+    int e, rt, rows;
+    bool live;
+    if (a.top_k) {
+        const int bpe = (RT + kGsRows - 1) / kGsRows;
+        e = blockIdx.x / bpe;
+        const int rtb = (blockIdx.x - e * bpe) * kGsRows + rl;
+        live = rtb < RT;
+        rt = min(rtb, RT - 1);
+        rows = a.cnt[e];
+        if (rows == 0) return;   // whole block, before any barrier
+    } else {
+        const int rtg = blockIdx.x * kGsRows + rl;
+        live = rtg < NRT;
+        const int rtc = min(rtg, NRT - 1);
+        e = rtc / RT;
+        rt = rtc - e * RT;
+        rows = T;
+        // The down pass's chunk counters start every call at zero.
+        for (int i = blockIdx.x * kNT + threadIdx.x; i < a.n_cnt; i += gridDim.x * kNT) a.cnt_gu[i] = 0u;
+    }
     if (threadIdx.x < 48) s_max[threadIdx.x >> 4][threadIdx.x & 15] = 0u;
-
-    // The wave's row tile (past the last one: a copy of it that stores nothing).
-    const int rtg = blockIdx.x * kGsRows + rl;
-    const bool live = rtg < NRT;
-    const int rtc = min(rtg, NRT - 1);
-    const int e = rtc / RT;
-    const int wrow0 = (rtc - e * RT) * 16;
+    const int *list = a.top_k ? a.list + (size_t)e * T : nullptr;
+    // Routed mode: the expert's first block keeps each position's slot
+    // weight for the down pass.
+    if (list && blockIdx.x % ((RT + kGsRows - 1) / kGsRows) == 0 && threadIdx.x < rows)
+        a.hf[(size_t)e * T + threadIdx.x] = a.slot_w[list[threadIdx.x]];
+    const int wrow0 = rt * 16;
     const unsigned row = (unsigned)(wrow0 + n);
     const unsigned crow = row * (unsigned)(d_model * BITS / 8) + 16u * (unsigned)(q % kDw);
     const int cq = q / kDw;
@@ -1195,20 +1221,21 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
             }
         }
     };
-    auto piece_ok = [&](int k, int ph, int &t, int &b8) {
-        const int c = threadIdx.x + kNT * k;
-        t = c / kPR;
-        b8 = c - t * kPR;
-        return c < kPieces && t < T && ph * KC + 8 * b8 < d_model;
-    };
+    // Row of X behind each of the thread's pieces (-1: past the tile's rows).
+    int xrow[kPPT];
+#pragma unroll
+    for (int k = 0; k < kPPT; ++k) {
+        const int c = threadIdx.x + kNT * k, p = c / kPR;
+        xrow[k] = c < kPieces && p < rows ? (list ? list[p] / a.top_k : p) : -1;
+    }
     // A piece outside X gets an offset past the buffer's extent, where a
     // buffer load returns zeros.
     auto load_x = [&](uint4 (&xv)[kPPT][2], int ph) {
 #pragma unroll
         for (int k = 0; k < kPPT; ++k) {
-            int t, b8;
-            const bool ok = piece_ok(k, ph, t, b8);
-            const unsigned off = ok ? (unsigned)(t * d_model + ph * KC + 8 * b8) * 4u : kPastExtent;
+            const int c = threadIdx.x + kNT * k, b8 = c % kPR, col = ph * KC + 8 * b8;
+            const bool ok = xrow[k] >= 0 && col < d_model;
+            const unsigned off = ok ? (unsigned)(xrow[k] * d_model + col) * 4u : kPastExtent;
             xv[k][0] = buf_load16(xr, off, 0u);
             xv[k][1] = buf_load16(xr, off + 16u, 0u);
         }
@@ -1356,8 +1383,8 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
             for (int r = 0; r < 4; ++r) tot[m][r] += red[(((rl * (kGsK - 1) + w - 1) * 2 + m) * 4 + r) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int t = 4 * q + i;
-        if (t < T) a.hid[((size_t)e * T + t) * d_ff + wrow0 + n] = silu(tot[0][i]) * tot[1][i];
+        const int p = 4 * q + i;   // token (dense) or position in the expert's slot list (routed)
+        if (p < rows) a.hid[((size_t)e * T + p) * d_ff + wrow0 + n] = silu(tot[0][i]) * tot[1][i];
     }
 }
 
@@ -1396,6 +1423,10 @@ __global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
     const int b = xcd_logical(blockIdx.x, gridDim.x);
     const int sp = b / RG, rg = b - sp * RG;
     const int e = sp / SPE, kc = sp - e * SPE;
+    // Token rows of the chunk: the batch (dense), or the positions of the
+    // expert's slot list (routed, one chunk per expert; none: nothing to do).
+    const int rows = a.top_k ? a.cnt[e] : T;
+    if (rows == 0) return;   // whole block, before any barrier
     const int wrow0 = rg * 16 * kDsRows + rl * 16;
     const unsigned row = (unsigned)min(wrow0 + n, d_model - 1);
     const unsigned crow = row * (unsigned)(d_ff * BITS / 8) + 16u * (unsigned)(q % kDw);
@@ -1411,19 +1442,24 @@ __global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
     const int wg0 = kc * KDG + kh * kWG;   // the wave's first group of d_ff
     const BufRes hr = buf_res(a.hid + (size_t)e * T * d_ff, (size_t)T * d_ff * 4);
     const int c0 = kc * kDsCols;
-    // Router weights of the pieces' tokens (with the hidden rows: a load
-    // issued after the codes would be waited for behind all of them).
-    const BufRes rr = buf_res(a.route_w ? a.route_w : a.out, a.route_w ? (size_t)T * E * 4 : 4);
+    // Router weights of the pieces' rows, loaded with the hidden rows (a load
+    // issued after the codes would be waited for behind all of them): the
+    // token's weight for the expert (dense), or the slot's weight, which
+    // gate_up kept by position (routed).
+    const bool rwv = a.top_k || a.route_w;
+    const BufRes rr = a.top_k ? buf_res(a.hf + (size_t)e * T, (size_t)T * 4)
+                              : buf_res(a.route_w ? a.route_w : a.out, a.route_w ? (size_t)T * E * 4 : 4);
     uint4 hv[kPPT][2];
     unsigned rw[kPPT];
 #pragma unroll
     for (int k = 0; k < kPPT; ++k) {
         const int c = threadIdx.x + kNT * k, t = c / kPR, b8 = c - t * kPR;
-        const bool ok = t < T && c0 + 8 * b8 < d_ff;
+        const bool ok = t < rows && c0 + 8 * b8 < d_ff;
         const unsigned off = ok ? (unsigned)(t * d_ff + c0 + 8 * b8) * 4u : kPastExtent;   // zeros past X
         hv[k][0] = buf_load16(hr, off, 0u);
         hv[k][1] = buf_load16(hr, off + 16u, 0u);
-        rw[k] = buf_load4(rr, a.route_w && t < T ? (unsigned)(t * E + e) * 4u : 0u, 0u);
+        const unsigned woff = a.top_k ? (unsigned)t * 4u : (unsigned)(t * E + e) * 4u;
+        rw[k] = buf_load4(rr, rwv && t < rows ? woff : 0u, 0u);
     }
     uint4 craw[kU];
     unsigned sraw[kQ];
@@ -1447,7 +1483,7 @@ __global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
         const int ex = norm_exponent(m);
         store_hilo(v, ex, hs_hi + t * kStride + 8 * b8, hs_lo + t * kStride + 8 * b8);
         if (b8 % kPG == 0) {
-            const float rwt = t >= T ? 0.0f : a.route_w ? __uint_as_float(rw[k]) : 1.0f;
+            const float rwt = t >= rows ? 0.0f : rwv ? __uint_as_float(rw[k]) : 1.0f;
             fac[(b8 / kPG) * 16 + t] = ldexpf(rwt, ex);
         }
     }
@@ -1498,6 +1534,17 @@ __global__ __launch_bounds__(64 * kDsWaves) void k_tb_down_stream(TbArgs a)
         for (int r = 0; r < 4; ++r) tot[r] += red[(rl * 4 + r) * 64 + lane];
     }
 
+    // Routed mode: each slot's weighted output row (k_route_combine adds a
+    // token's slots).
+    if (a.top_k) {
+        if (kh != 0) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = 4 * q + i, r = wrow0 + n;
+            if (p < rows && r < d_model) a.ys[(size_t)a.list[(size_t)e * T + p] * d_model + r] = tot[i];
+        }
+        return;
+    }
     // The row group's chunks, added by the last of its blocks to finish, in
     // chunk order (published and read as the tiled kernels' K splits are).
     if (S > 1) {
@@ -1684,9 +1731,24 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
     return hipGetLastError();
 }
 
+// Routed mode of the streaming kernels (T <= 16, d_ff <= 1536): slot lists
+// (k_route_prep's first n_experts blocks only), gate_up, down, combine.
+template <int BITS, int KB, int SB>
+hipError_t launch_routed_stream(const TbPlan &pl, const TbArgs &a, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_route_prep, dim3((unsigned)a.n_experts), dim3(256), 0, st, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if ((err = launch_tb_stream<BITS, KB, SB>(pl, a, st)) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_route_combine, dim3((unsigned)a.T, (unsigned)((a.d_model + 1023) / 1024)), dim3(256), 0, st,
+                       a.ids, a.slot_ok, a.ys, a.top_k, a.n_experts, a.d_model, a.out);
+    return hipGetLastError();
+}
+
 template <int BITS, int KB, int SB>
 hipError_t launch_routed_kb(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
+    if (pl.stream) return launch_routed_stream<BITS, KB, SB>(pl, a, st);
     if (pl.ntt == 1) {
         if (pl.mg == 2) return launch_routed_tiled<BITS, KB, 1, 2, SB>(pl, a, st);
         return launch_routed_tiled<BITS, KB, 1, 1, SB>(pl, a, st);
@@ -1868,6 +1930,22 @@ bool plan_routed(int bits, int group, int d_model, int d_ff, int n_experts, int 
     if (T < 1 || n_experts < 1 || top_k < 1) return false;
     if (!(group == 32 && bits == 4) && group != 64) return false;
     if (d_model % group || d_ff % group) return false;
+    if (T <= 16 && d_ff <= kDsCols) {
+        // Streaming kernels: an expert's slots are one token tile; gate_up
+        // blocks of 3 row tiles of one expert, down blocks of 128 rows x one
+        // expert.
+        TbPlan p{};
+        p.stream = 1;
+        p.ntt = 1;
+        p.mg = 1;
+        p.gu_blocks = (long)n_experts * ((d_ff / 16 + kGsRows - 1) / kGsRows);
+        p.gu_lds = (size_t)2 * 2 * 16 * (kPhaseGroups * group + 8) * 2;
+        p.dn_blocks = stream_down_blocks(n_experts, d_model, d_ff);
+        p.dn_lds = (size_t)2 * 16 * (kDsCols + 8) * 2 + (size_t)(kDsCols / group) * 16 * 4;
+        if (p.gu_lds > kMaxStreamLds || p.dn_lds > kMaxStreamLds) return false;
+        *pl = p;
+        return true;
+    }
     const BatchSplits bs = routed_splits(n_experts, d_model, d_ff, T, top_k);
     TbPlan p{};
     p.ntt = bs.ntt;

@@ -158,8 +158,10 @@ BatchWorkspace batch_workspace(int n_experts, int d_model, int d_ff, int T, int 
 
 // Workspace layout of the routed path, every piece 256-byte aligned:
 //   xh, xl, xe                     as the token batch, [T] tokens
-//   hh, hl  f16 [n_experts][T][d_ff] hidden rows by position in the expert's slot list
-//   hf      f32 [n_experts][d_ff/32][Tp] their factors (slot weight * 2^e)
+//   hh, hl  f16 [n_experts][T][d_ff] hidden rows by position in the expert's slot list (T <= 16:
+//                                    the two together hold them as f32 [n_experts][T][d_ff])
+//   hf      f32 [n_experts][d_ff/32][Tp] their factors (slot weight * 2^e; T <= 16: the slot
+//                                    weights by position, [n_experts][T])
 //   pg      f32                      partial sums of the gate_up K splits
 //   list    i32 [n_experts][T]       each expert's slots, ascending; cnt i32 [n_experts]
 //   ok      i32 [T*top_k]            slot processed
@@ -518,6 +520,7 @@ int smoe_routed_ffn(const smoe_expert *experts, int n_experts, int fmt, int grou
     a.xe = reinterpret_cast<int *>(ws + w.xe);
     a.hh = reinterpret_cast<_Float16 *>(ws + w.hh);
     a.hl = reinterpret_cast<_Float16 *>(ws + w.hl);
+    a.hid = reinterpret_cast<float *>(ws + w.hh);   // f32 rows over hh and hl, which are adjacent
     a.hf = reinterpret_cast<float *>(ws + w.hf);
     a.part_gu = reinterpret_cast<float *>(ws + w.pg);
     a.cnt_gu = reinterpret_cast<unsigned *>(ws + w.tcnt);

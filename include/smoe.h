@@ -237,8 +237,9 @@ int matvec_bf16(const uint16_t *W, int rows, int cols, const float *x, float *y,
  * 1 <= T <= SMOE_MAX_TOKENS, 1 <= top_k <= SMOE_MAX_EXPERTS.  Only each slot's
  * expert processes the token: a device pass lists every expert's slots in
  * ascending order, the gate_up and down passes run per expert over those
- * lists on the matrix cores, and a last pass adds each token's slots in slot
- * order (deterministic, no atomics).  Needs group 32 (4-bit) or 64, else
+ * lists on the matrix cores (for T <= 16 and d_ff <= 1536 the streaming
+ * kernels of the token batch, an expert's slots being one tile), and a last
+ * pass adds each token's slots in slot order (deterministic, no atomics).  Needs group 32 (4-bit) or 64, else
  * SMOE_ERR_GROUP.  `bits` may carry SMOE_SCALE_F16.
  */
 size_t smoe_routed_ffn_workspace(int n_experts, int d_model, int d_ff, int T, int top_k);

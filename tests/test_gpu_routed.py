@@ -85,6 +85,12 @@ ROUTED_EDGE = [  # bits, group, d_model, d_ff, n_experts, T, top_k, routing
     (4, 64, 8192, 128, 2, 9, 1, "topk"),
     (4, 64, 384, 320, 3, 50, 2, "topk"),       # 6 and 5 groups: partial iterations in routed mode
     (4, 64, 384, 320, 2, 200, 2, "topk"),      # 64-token tiles with gate_up split in 2 (finishing pass)
+    # T <= 16 with d_ff <= 1536 (streaming kernels, one token tile per expert):
+    (4, 64, 256, 512, 6, 12, 2, "sparse"),     # experts 2..5 without slots: their blocks have nothing to do
+    (4, 64, 256, 512, 4, 9, 3, "holes"),       # slots out of range are never processed
+    (2, 64, 256, 384, 4, 10, 2, "topk"),       # 2-bit codes
+    (4, 32, 96, 160, 3, 7, 2, "topk"),         # 32-column groups, partial row tiles of an expert
+    (4, 64, 64, 2048, 2, 8, 1, "topk"),        # d_ff 2048 > 1536: the tiled kernels instead
 ]
 
 
@@ -99,6 +105,9 @@ def test_routed_edge_shapes(gq, oracle_lib, bits, group, d_model, d_ff, n, T, k,
     if routing == "holes":
         ids[::3, 1] = -1
         ids[1::4, 2] = n
+    if routing == "sparse":   # every token to experts 0 and 1 only
+        ids[:, 0] = 0
+        ids[:, 1] = 1
     got = run_routed(gq, dev_experts(g), bits, group, X, ids, w)
     want = oracle_lib.routed_ffn(g.experts, bits, group, d_model, d_ff, X, ids, w)
     assert_parity(got, want, f"routed Q{bits} g{group} {d_model}x{d_ff} E={n} T={T} k={k} {routing}")
