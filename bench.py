@@ -20,8 +20,9 @@ bytes / time), microseconds per group and per expert, and fraction of the
   rows           every other workload of the path timed in the same run, each
                  back to back like the headline: the tiny single expert, one
                  expert of the group, the Q2 group, both groups with 2-byte
-                 scales, the four bf16 matvec shapes and the token batch at
-                 T = 16, 64 and 256
+                 scales, the four bf16 matvec shapes, the token batch at
+                 T = 16, 64 and 256 and the routed batch (16 and 256 tokens,
+                 top-2)
 
 `--workload W` prints one line for a single workload instead (used for the
 rocprofv3 runs behind profiles/): decode_q4, decode_q2, decode_q4_s16,
@@ -506,6 +507,18 @@ def prefill_line(args):
     }
 
 
+def routed_row(T, k, steps, warmup):
+    """The routed call of routed_line as a row of the headline line."""
+    import types
+    l = routed_line(types.SimpleNamespace(steps=steps, warmup=warmup, cpu_budget=0, tokens=T, topk=k))
+    rf = l["roofline"]
+    return {"us": l["us_per_call"], "tflops": l["tflops"], "gbs": l["hbm_gbs"], "bound": rf["bound"],
+            "frac": rf["frac"], "matrix_work": rf["matrix_work"], "per_call_us": l["per_call_us"],
+            "experts_used": l["config"]["experts_used"], "algorithmic_flops": l["config"]["algorithmic_flops"],
+            "algorithmic_bytes": l["config"]["algorithmic_bytes"],
+            "kernels": row_kernels(f"routed_t{T}_k{k}", "prefill")}
+
+
 def routed_line(args):
     """Routed prefill: T tokens, each through its top_k of the 8 Q4 experts."""
     import torch
@@ -860,6 +873,8 @@ def collect_rows(args):
         add(f"bf16_{role}_{rows_}x{cols}", lambda role=role: bf16_row(role, s, w))
     for T in sorted(workloads.BATCH_TOKENS):
         add(f"prefill_q4_8expert_T{T}", lambda T=T: prefill_row(T, s, w))
+    for T, k in ((16, 2), (256, 2)):
+        add(f"routed_q4_8expert_T{T}_top{k}", lambda T=T, k=k: routed_row(T, k, s, w))
     return rows
 
 
