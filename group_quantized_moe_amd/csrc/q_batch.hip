@@ -1065,10 +1065,10 @@ __global__ __launch_bounds__(512) void k_tb_dn_finish(TbArgs a)
 // sigma order in LDS, and the phase's sums are scaled back by the same power
 // of two.  The hidden rows SiLU(g) * u leave as f32.
 //
-// Routed mode (slot lists, T <= 16, d_ff <= 1536): a gate_up block's row
-// tiles are one expert's and its token rows the expert's slots; a down
-// block's chunk is one expert's d_ff, and it writes each slot's weighted row
-// for the combine pass instead of adding the experts.
+// Routed mode (T <= 16, d_ff <= 1536): a gate_up block's row tiles are one
+// expert's and its token rows the expert's slots, which it lists itself; a
+// down block's chunk is one expert's d_ff, and it writes each slot's
+// weighted row for the combine pass instead of adding the experts.
 //
 // down: a block of 16 waves owns 8 row tiles (128 rows of d_model) and one
 // chunk of 1536 columns of one expert's d_ff (all of it at d_ff = 1536).  The
@@ -1149,14 +1149,38 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
     // (routed; a block of an expert without slots has nothing to do).
     int e, rt, rows;
     bool live;
+    __shared__ int s_list[16];   // routed: the expert's slots, ascending
+    __shared__ int s_wcnt[4];
+    const int bpe = (RT + kGsRows - 1) / kGsRows;
     if (a.top_k) {
-        const int bpe = (RT + kGsRows - 1) / kGsRows;
         e = blockIdx.x / bpe;
         const int rtb = (blockIdx.x - e * bpe) * kGsRows + rl;
         live = rtb < RT;
         rt = min(rtb, RT - 1);
-        rows = a.cnt[e];
-        if (rows == 0) return;   // whole block, before any barrier
+        // The expert's slots (T * top_k <= 256 of them: the first four waves
+        // take one each) in ascending order, by ballot prefix counts; an
+        // expert keeps at most T slots (a token's ids are distinct, so none
+        // is lost).  The expert's first block publishes the list, its length
+        // and the slots' flags for the down and combine passes.
+        const int ns = T * a.top_k, sl = threadIdx.x;
+        const bool mine = sl < 256 && sl < ns && a.ids[sl] == e;
+        const unsigned long long mask = __ballot(mine);
+        if (lane == 0 && wave < 4) s_wcnt[wave] = __popcll(mask);
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave && w < 4; ++w) before += s_wcnt[w];
+        const int pos = before + __popcll(mask & ((1ull << lane) - 1ull));
+        rows = min(s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3], T);
+        if (mine && pos < T) s_list[pos] = sl;
+        if (blockIdx.x % bpe == 0) {
+            if (mine) {
+                if (pos < T) a.list[(size_t)e * T + pos] = sl;
+                a.slot_ok[sl] = pos < T;
+            }
+            if (threadIdx.x == 0) a.cnt[e] = rows;
+        }
+        __syncthreads();
+        if (rows == 0) return;   // whole block (rows is the same for every thread)
     } else {
         const int rtg = blockIdx.x * kGsRows + rl;
         live = rtg < NRT;
@@ -1168,10 +1192,10 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
         for (int i = blockIdx.x * kNT + threadIdx.x; i < a.n_cnt; i += gridDim.x * kNT) a.cnt_gu[i] = 0u;
     }
     if (threadIdx.x < 48) s_max[threadIdx.x >> 4][threadIdx.x & 15] = 0u;
-    const int *list = a.top_k ? a.list + (size_t)e * T : nullptr;
+    const int *list = a.top_k ? s_list : nullptr;
     // Routed mode: the expert's first block keeps each position's slot
     // weight for the down pass.
-    if (list && blockIdx.x % ((RT + kGsRows - 1) / kGsRows) == 0 && threadIdx.x < rows)
+    if (list && blockIdx.x % bpe == 0 && threadIdx.x < rows)
         a.hf[(size_t)e * T + threadIdx.x] = a.slot_w[list[threadIdx.x]];
     const int wrow0 = rt * 16;
     const unsigned row = (unsigned)(wrow0 + n);
@@ -1731,15 +1755,13 @@ hipError_t launch_routed_tiled(const TbPlan &pl, const TbArgs &a, hipStream_t st
     return hipGetLastError();
 }
 
-// Routed mode of the streaming kernels (T <= 16, d_ff <= 1536): slot lists
-// (k_route_prep's first n_experts blocks only), gate_up, down, combine.
+// Routed mode of the streaming kernels (T <= 16, d_ff <= 1536): gate_up
+// (which lists each expert's slots itself), down, combine.
 template <int BITS, int KB, int SB>
 hipError_t launch_routed_stream(const TbPlan &pl, const TbArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_route_prep, dim3((unsigned)a.n_experts), dim3(256), 0, st, a);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_tb_stream<BITS, KB, SB>(pl, a, st);
     if (err != hipSuccess) return err;
-    if ((err = launch_tb_stream<BITS, KB, SB>(pl, a, st)) != hipSuccess) return err;
     hipLaunchKernelGGL(k_route_combine, dim3((unsigned)a.T, (unsigned)((a.d_model + 1023) / 1024)), dim3(256), 0, st,
                        a.ids, a.slot_ok, a.ys, a.top_k, a.n_experts, a.d_model, a.out);
     return hipGetLastError();
