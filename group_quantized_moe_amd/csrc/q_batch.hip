@@ -1157,8 +1157,8 @@ __global__ __launch_bounds__(64 * kGsWaves) void k_tb_gate_up_stream(TbArgs a)
         const int rtb = (blockIdx.x - e * bpe) * kGsRows + rl;
         live = rtb < RT;
         rt = min(rtb, RT - 1);
-        // The expert's slots (T * top_k <= 256 of them: the first four waves
-        // take one each) in ascending order, by ballot prefix counts; an
+        // The expert's slots (T * top_k <= 256 of them, one per thread of the
+        // first four waves) in ascending order, by ballot prefix counts; an
         // expert keeps at most T slots (a token's ids are distinct, so none
         // is lost).  The expert's first block publishes the list, its length
         // and the slots' flags for the down and combine passes.
