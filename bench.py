@@ -299,6 +299,38 @@ def read_ceiling(nbytes, steps, warmup):
                       + ("one-pass grid" if bpc == 0 else f"{bpc} blocks per CU")}
 
 
+def read_ceiling_pair(na, nb, steps, warmup):
+    """The same plain read, as two launches per step on one stream: `na`
+    bytes, then `nb` bytes (the byte counts of a two-launch path's kernels),
+    each rotating >= 1 GiB of buffers; the faster of the two grid shapes."""
+    import torch
+    import group_quantized_moe_amd as gq
+    path = os.path.join(os.path.dirname(gq.LIB_PATH), "libsmoe_bench.so")
+    if not os.path.exists(path):
+        return None
+    B = ctypes.CDLL(path)
+    B.smoe_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+    sizes = [-(-na // 16) * 16, -(-nb // 16) * 16]
+    reps = replica_count(sum(sizes))
+    bufs = [[torch.full((n,), i & 0x7F, dtype=torch.uint8, device="cuda") for n in sizes] for i in range(reps)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream, sp = stream_ptr()
+    best = None
+    for bpc in (0, 4):
+        def step(i, bpc=bpc):
+            for buf, n in zip(bufs[i % reps], sizes):
+                if B.smoe_bench_stream_read(buf.data_ptr(), n, sink.data_ptr(), bpc, sp) != 0:
+                    raise RuntimeError("stream read launch failed")
+        us, spread, _ = time_calls(step, steps, warmup, stream)
+        if best is None or us < best[0]:
+            best = (us, spread, bpc)
+    del bufs
+    us, spread, bpc = best
+    return {"us": round(us, 3), "bytes": sizes, "per_call_us": spread,
+            "kernel": "k_stream_read twice per step, " + ("one-pass grids" if bpc == 0 else f"{bpc} blocks per CU")}
+
+
 _MFMA_CEILING = {}
 
 
@@ -382,6 +414,12 @@ def decode_line(args, spec, profile, with_rows=False):
     if rc:
         rc["path_time_over_ceiling"] = round(m["us"] / rc["us"], 3)
         rc["path_frac_of_ceiling"] = round(rc["us"] / m["us"], 4)
+        # The same bytes read as the path's two launches read them.
+        gu = g.byte_count() // spec["n_experts"] * E * 2 // 3 + 4 * g.d_model
+        pair = read_ceiling_pair(gu, nbytes - gu, args.steps, args.warmup)
+        if pair:
+            pair["path_time_over"] = round(m["us"] / pair["us"], 3)
+            rc["two_launches"] = pair
     line["read_ceiling"] = rc
     cpu = None
     if args.cpu_budget > 0:
