@@ -60,6 +60,12 @@
  * Scratch memory comes from the caller's workspace, sized by the matching
  * *_workspace() function.  Structures passed by host pointer (smoe_qmat,
  * smoe_expert) are read during the call and may be reused afterwards.
+ * A call enqueues kernel launches only (no memset, copy or host callback), so
+ * it can be captured into a HIP graph and replayed; a replay reads and writes
+ * the addresses the call was captured with, and counters in the workspace are
+ * cleared by the call's own kernels on every replay.  Calls on different
+ * streams may run at the same time when none of them writes memory another
+ * reads or writes (each with its own workspace and outputs).
  *
  * Errors: every call checks all of its arguments on the host before it
  * enqueues anything and returns a negative SMOE_ERR_* code when an argument
