@@ -124,3 +124,45 @@ def test_routed_f16_scales_and_duplicate_tokens(gq, oracle_lib):
     got = run_routed(gq, dev_experts(g), 4 | gq.SMOE_SCALE_F16, 64, X, ids, w)
     assert_parity(got, oracle_lib.routed_ffn(g.experts, 4, 64, 256, 512, X, ids, w), "routed f16 scales")
     assert np.array_equal(got[7], got[2])
+
+
+def test_cross_block_sums_repeated(gq, oracle_lib, q4_group8):
+    """The sums that blocks hand to one another through the workspace (each
+    writes its partial sums at agent scope, waits for them, then counts
+    itself in; the block that completes the count adds them all), run 100
+    times back to back on one workspace without a synchronisation between
+    calls: every output bitwise equal to the first, the first against the
+    oracle.  64 tokens x top-2 of 8 experts is the routed path with 16-token
+    tiles, whose gate_up K splits are added this way; a 12-token batch with
+    d_ff 8192 is the streaming down pass, whose six column chunks per row
+    group are added this way."""
+    import torch
+    reps = 100
+    g, de = q4_group8
+    X, ids, w = workloads.make_routed_inputs(64, 2, 4301)
+    want = oracle_lib.routed_ffn(g.experts, 4, 64, g.d_model, g.d_ff, X, ids, w)
+    Xd, idd, wd = dev(X), dev(ids), dev(w)
+    ws = torch.empty(gq.smoe_routed_ffn_workspace(8, g.d_model, g.d_ff, 64, 2), dtype=torch.uint8, device="cuda")
+    outs = torch.empty(reps, 64 * g.d_model, dtype=torch.float32, device="cuda")
+    for r in range(reps):
+        gq.smoe_routed_ffn(de, 4, 64, Xd, idd, wd, outs[r], ws)
+    torch.cuda.synchronize()
+    got = outs.cpu().numpy()
+    assert_parity(got[0].reshape(64, -1), want, "routed T=64 top-2, first of 100 calls")
+    for r in range(1, reps):
+        assert np.array_equal(got[r], got[0]), f"routed T=64 top-2: call {r} differs from the first"
+
+    gs = workloads.expert_group(4302, 2, 64, 8192, 4, 64)
+    Xs = workloads.activation_batch(4303, 12, 64)
+    Rs = workloads.router_weights(4304, 2, 12)
+    wants = oracle_lib.expert_ffn(gs.experts, 4, 64, 64, 8192, Xs, Rs)
+    des, Xsd, Rsd = dev_experts(gs), dev(Xs), dev(Rs)
+    ws2 = torch.empty(gq.smoe_expert_ffn_workspace(2, 64, 8192, 12), dtype=torch.uint8, device="cuda")
+    outs2 = torch.empty(reps, 12 * 64, dtype=torch.float32, device="cuda")
+    for r in range(reps):
+        gq.smoe_expert_ffn(des, 4, 64, Xsd, outs2[r], route_w=Rsd, workspace=ws2)
+    torch.cuda.synchronize()
+    got2 = outs2.cpu().numpy()
+    assert_parity(got2[0].reshape(12, -1), wants, "batch T=12 d_ff 8192, first of 100 calls")
+    for r in range(1, reps):
+        assert np.array_equal(got2[r], got2[0]), f"batch T=12 d_ff 8192: call {r} differs from the first"
