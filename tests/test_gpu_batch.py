@@ -162,3 +162,14 @@ def test_batch_refuses_unsupported_group(gq):
     with pytest.raises(gq.SmoeError) as ei:
         gq.smoe_expert_ffn(de, 4, 160, X, out, workspace=ws)
     assert ei.value.status == -3
+
+
+def test_batch_most_tokens(gq, oracle_lib):
+    """The largest batch a call takes, 65536 tokens (1024 tiles of 64), through
+    two small Q4 experts: every token against the oracle."""
+    T = 65536
+    g = workloads.expert_group(4411, 2, 64, 128, 4, 64)
+    X = workloads.activation_batch(4412, T, 64)
+    R = workloads.router_weights(4413, 2, T)
+    want = oracle_lib.expert_ffn(g.experts, 4, 64, 64, 128, X, R)
+    assert_parity(run_ffn(gq, dev_experts(g), 4, 64, X, route=R), want, "batch T=65536")

@@ -224,3 +224,15 @@ def test_gpu_refuses_misaligned_codes(gq):
     with pytest.raises(gq.SmoeError) as ei:
         gq.smoe_gate_up(shifted, de.gate.scales, de.up.codes, de.up.scales, 4, 64, dev(x), h)
     assert ei.value.status == -5
+
+
+def test_decode_every_maximum(gq, oracle_lib):
+    """One decode call at every shape limit at once: 16 experts (the most one
+    call takes) whose gate, up and down matrices are all 8192 x 8192 (the
+    widest rows on both passes), 4-bit codes, about 1.6 GB of weights; every
+    output row against the oracle."""
+    g = workloads.expert_group(4401, 16, 8192, 8192, 4, 64)
+    x = workloads.activation(4402, 8192)
+    r = workloads.router_weights(4403, 16)[0]
+    want = oracle_lib.expert_ffn(g.experts, 4, 64, 8192, 8192, x, r[None])
+    assert_parity(run_ffn(gq, dev_experts(g), 4, 64, x, route=r), want, "decode 16 experts of 8192 x 8192")

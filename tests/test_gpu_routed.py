@@ -166,3 +166,14 @@ def test_cross_block_sums_repeated(gq, oracle_lib, q4_group8):
     assert_parity(got2[0].reshape(12, -1), wants, "batch T=12 d_ff 8192, first of 100 calls")
     for r in range(1, reps):
         assert np.array_equal(got2[r], got2[0]), f"batch T=12 d_ff 8192: call {r} differs from the first"
+
+
+def test_routed_most_tokens(gq, oracle_lib):
+    """65536 tokens, top-2 of 4 small Q4 experts (32768 slots per expert on
+    average): every token against the oracle."""
+    T = 65536
+    g = workloads.expert_group(4421, 4, 64, 128, 4, 64)
+    X = workloads.activation_batch(4412, T, 64)
+    ids, w = workloads.top_k_routing(4422, T, 4, 2)
+    want = oracle_lib.routed_ffn(g.experts, 4, 64, 64, 128, X, ids, w)
+    assert_parity(run_routed(gq, dev_experts(g), 4, 64, X, ids, w), want, "routed T=65536 top-2")
