@@ -518,6 +518,13 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     // code loads go out (behind those, the vector's loads took a few
     // microseconds to come back, and the first steps waited for the planes);
     // then the digit planes are built while the code loads are in flight.
+    // 2-bit codes: a wave's set-up (the vector, the planes, its chunks'
+    // planes) runs at a higher issue priority than the step loops of the
+    // other block on its CU, which start first and would otherwise hold back
+    // the later block's set-up (the tail of the kernel; Q2 group gate_up
+    // 9.4-9.6 -> 9.1 us in kernel traces, alternating with the earlier build
+    // on one GPU).  At 4 bits it measured no faster.
+    if constexpr (BITS == 2) __builtin_amdgcn_s_setprio(3);
     VecRegs<BITS, kGroupsPerThread<BITS>> xr;
     load_vec_regs<BITS>(a.x, a.d_model, xr);
     wait_vm_all();
@@ -550,6 +557,7 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     for (int k = 0; k < NCH; ++k)
         load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
 
+    if constexpr (BITS == 2) __builtin_amdgcn_s_setprio(0);
     Cursor cc;
     cc.init(sb, spe);
     for (int base = sb; base < se; base += NS_) {
