@@ -522,8 +522,9 @@ __global__ __launch_bounds__(512) void k_gate_up(const DecodeArgs a)
     // planes) runs at a higher issue priority than the step loops of the
     // other block on its CU, which start first and would otherwise hold back
     // the later block's set-up (the tail of the kernel; Q2 group gate_up
-    // 9.4-9.6 -> 9.1 us in kernel traces, alternating with the earlier build
-    // on one GPU).  At 4 bits it measured no faster.
+    // 9.4-9.6 -> 9.1 us in kernel traces, the call 18.7 -> 18.3 us
+    // event-timed, alternating builds on one GPU).  At 4 bits it measured no
+    // faster.
     if constexpr (BITS == 2) __builtin_amdgcn_s_setprio(3);
     VecRegs<BITS, kGroupsPerThread<BITS>> xr;
     load_vec_regs<BITS>(a.x, a.d_model, xr);
@@ -680,6 +681,11 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
             load_stage<NCH, LPR, 1, SB>(t, dcodes, dscales, ln, (s0 + item - e * ns) * rs, a.d_model, row_bytes,
                                         gpr);
         };
+        // 2-bit codes: the expert's set-up (hidden vector, planes, chunk planes)
+        // at a raised issue priority over other waves' step loops, as in
+        // gate_up (Q2 group 18.3 -> 18.0 us on top of gate_up's change,
+        // event-timed, alternating builds on one GPU).
+        if constexpr (BITS == 2) __builtin_amdgcn_s_setprio(3);
         const float *hid = a.hidden + (size_t)e * a.d_ff;
         WaveVec<BITS> hv;
         wave_vec_load<BITS>(hid, ndw, 0, hv);
@@ -702,6 +708,7 @@ __global__ __launch_bounds__(512) void k_down(const DecodeArgs a)
         for (int k = 0; k < NCH; ++k)
             load_chunk_vec<BITS>(lds.planes, lds.cmax, lds.dwsum, lds.chunks, ln.c[k], ln.valid[k], cv[k]);
 
+        if constexpr (BITS == 2) __builtin_amdgcn_s_setprio(0);
         // Steps are reduced in order as their loads come in; a slot is
         // reloaded with the step DEPTH further on once it has been reduced.
         for (int base = 0; base < n; base += DEPTH) {
