@@ -181,7 +181,8 @@ def cmd_pmc(workload, fetch, write, copy_fetch, copy_write):
         f.write("\n")
 
 
-def cmd_render(workload):
+def render_text(workload):
+    """The markdown summary of a workload from its committed JSON files."""
     with open(os.path.join(ROOT, "profiles", f"{workload}_kernels.json")) as f:
         d = json.load(f)
     title = DECODE[workload][2]
@@ -227,8 +228,12 @@ def cmd_render(workload):
                       f"the algorithmic bytes (`profiles/{workload}_pmc.json`)."]
     L += ["", f"Machine-readable: `profiles/{workload}_kernels.json` (kernel source hash {d['kernel_source_hash']}; "
               "bench.py reports these figures only while the kernel sources hash the same)."]
+    return "\n".join(L) + "\n"
+
+
+def cmd_render(workload):
     with open(os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md"), "w") as f:
-        f.write("\n".join(L) + "\n")
+        f.write(render_text(workload))
 
 
 def main(argv):
