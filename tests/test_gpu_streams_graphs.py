@@ -140,3 +140,73 @@ def test_graph_replays(gq, setup):
         assert np.array_equal(o_dec.cpu().numpy(), ref["x" + which]), f"replay {k}: decode"
         assert np.array_equal(o_na.cpu().numpy(), ref["x" + which]), f"replay {k}: no-allocation decode"
         assert np.array_equal(o_bat.cpu().numpy(), ref["X" + which]), f"replay {k}: batch"
+
+
+def test_graph_replays_attention_and_bf16(gq):
+    """A captured graph of the decode attention block (the small workload,
+    appending at a fixed position of device caches) and of the batched bf16
+    q/k/v matvecs: four replays, the caches reset and the inputs switched
+    between two vectors by eager copies between them, each bitwise equal to
+    the eager call (output and appended cache rows)."""
+    import torch
+    spec = workloads.ATTN_SMALL
+    w, x1, K0, V0 = workloads.make_attn_inputs(spec)
+    x2 = workloads.activation(79, spec["d_model"])
+    pos = spec["pos"]
+    wd = [dev(w.wq), dev(w.wk), dev(w.wv), dev(w.wo), dev(w.q_norm), dev(w.k_norm)]
+    ws = torch.empty(gq.smoe_attn_decode_workspace(spec["d_model"], spec["n_head"], spec["n_kv"], spec["head_dim"],
+                                                   spec["max_ctx"]), dtype=torch.uint8, device="cuda")
+    Ws, xb1 = workloads.make_bf16_batch()
+    xb2 = workloads.activation(80, xb1.size)
+    Wd = [dev(W) for W in Ws]
+
+    def attn_eager(x):
+        Kd, Vd = dev(K0), dev(V0)
+        out = torch.empty(spec["d_model"], dtype=torch.float32, device="cuda")
+        gq.smoe_attn_decode(*wd, dev(x), pos, spec["rope_base"], Kd, Vd, out, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), Kd[:, pos].cpu().numpy(), Vd[:, pos].cpu().numpy()
+
+    def bf16_eager(x):
+        ys = [torch.empty(W.shape[0], dtype=torch.float32, device="cuda") for W in Wd]
+        gq.matvec_bf16_batch([(W, dev(x), y) for W, y in zip(Wd, ys)])
+        torch.cuda.synchronize()
+        return [y.cpu().numpy() for y in ys]
+
+    ref = {"1": (attn_eager(x1), bf16_eager(xb1)), "2": (attn_eager(x2), bf16_eager(xb2))}
+    Kd, Vd = dev(K0), dev(V0)
+    K0d, V0d = dev(K0), dev(V0)
+    xa, xb = dev(x1).clone(), dev(xb1).clone()
+    out = torch.empty(spec["d_model"], dtype=torch.float32, device="cuda")
+    ys = [torch.empty(W.shape[0], dtype=torch.float32, device="cuda") for W in Wd]
+
+    def calls():
+        gq.smoe_attn_decode(*wd, xa, pos, spec["rope_base"], Kd, Vd, out, ws)
+        gq.matvec_bf16_batch([(W, xb, y) for W, y in zip(Wd, ys)])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for k, which in enumerate(("1", "2", "1", "2")):
+        Kd.copy_(K0d)
+        Vd.copy_(V0d)
+        xa.copy_(dev(x1 if which == "1" else x2))
+        xb.copy_(dev(xb1 if which == "1" else xb2))
+        out.fill_(float("nan"))
+        for y in ys:
+            y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        (o_ref, k_ref, v_ref), y_ref = ref[which]
+        assert np.array_equal(out.cpu().numpy(), o_ref), f"replay {k}: attention output"
+        assert np.array_equal(Kd[:, pos].cpu().numpy(), k_ref), f"replay {k}: appended k"
+        assert np.array_equal(Vd[:, pos].cpu().numpy(), v_ref), f"replay {k}: appended v"
+        for j, (y, yr) in enumerate(zip(ys, y_ref)):
+            assert np.array_equal(y.cpu().numpy(), yr), f"replay {k}: bf16 job {j}"
