@@ -41,3 +41,25 @@ def test_kernel_names():
     assert ps.short_name("_ZN4smoe12_GLOBAL__N_19k_tb_prepEPKfiPDF16_S3_PiPji", 64) == "k_tb_prep"
     assert ps.short_name("(anonymous namespace)::k_stream_read(uint4 const*, unsigned long, unsigned int*)", 1024) == \
         "k_stream_read (grid 1024 blocks)"
+
+
+def test_counter_parsing_and_calibration(tmp_path):
+    """Median counter value per kernel over its dispatches, and the copy's
+    calibration factor: known bytes over what the counter reads for it."""
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Workgroup_Size", "Counter_Name", "Counter_Value"]
+    rows = [
+        [1, 131072, "void smoe::(anonymous namespace)::k_gate_up<4, 2, 64, 1, 4>(smoe::DecodeArgs)", 512,
+         "FETCH_SIZE", 100.0],
+        [2, 131072, "void smoe::(anonymous namespace)::k_gate_up<4, 2, 64, 1, 4>(smoe::DecodeArgs)", 512,
+         "FETCH_SIZE", 300.0],
+        [3, 131072, "void smoe::(anonymous namespace)::k_gate_up<4, 2, 64, 1, 4>(smoe::DecodeArgs)", 512,
+         "FETCH_SIZE", 200.0],
+        [4, 16777216, "void at::native::copy_kernel(char*)", 256, "FETCH_SIZE", 131072.0],
+        [5, 16777216, "void at::native::fill_kernel(char*)", 256, "FETCH_SIZE", 8.0],
+    ]
+    path = tmp_path / "c.csv"
+    path.write_text("\n".join(",".join(f'"{v}"' if isinstance(v, str) else str(v) for v in r)
+                              for r in [cols] + rows) + "\n")
+    m = ps.counter_medians(str(path))
+    assert m["k_gate_up<4, 2, 64, 1, 4>"] == 200.0
+    assert ps.copy_scale(str(path)) == (256 << 20) / (131072.0 * 1024)   # 2.0: the counter reads half
